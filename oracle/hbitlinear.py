@@ -1,0 +1,253 @@
+"""fp64 NumPy oracle of the H-BitLinear forward — TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check and the bench's CPU-baseline leg may call this.
+Nothing here is used by, or uses, the HIP library.
+
+Sources (the pages the method is taken from):
+  [engine]  Quillan-Ronin "bitnet_v2_engine.py" page: a PyTorch restatement of
+            BitNet v2 (arXiv 2504.18415). Its module docstring lists Eq. 1-8;
+            functions fast_hadamard_transform, quantize_weight_ternary,
+            quantize_act_int8, quantize_act_int4 and class HBitLinear.
+  [edge]    Quillan-Ronin "bitnet_cpp_edge.py" page: bitnet.cpp kernel
+            simulation (arXiv 2502.11880), Table 1 taxonomy, I2_S kernel.
+  [blog]    youngju.dev "BitNet 论文解析" page: BitLinear_b158 code block.
+
+Precision: every floating-point step is fp64 (the pages compute in fp32; the
+fp64 oracle plus a +-1 code-flip band of 1e-4 around .5 rounding boundaries is
+the acceptance rule of this library).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# [engine] every quantizer and HBitLinear default to eps = 1e-7. The edge and
+# blog pages use 1e-5; the engine page is the only one that defines
+# H-BitLinear and the sqrt(7) int4 scale, so its value is taken.
+EPS = 1e-7
+# [engine] Eq. 5: int8 absmax scale 127, clip [-128, 127].
+INT8_SCALE = 127.0
+# [engine] Eq. 6: int4 absmean scale sqrt(7), clip [-8, 7].
+INT4_SCALE = math.sqrt(7.0)
+
+_QUANT = {8: (INT8_SCALE, -128, 127), 4: (INT4_SCALE, -8, 7)}
+
+
+def _is_pow2(n: int) -> bool:
+    return n > 0 and (n & (n - 1)) == 0
+
+
+def widen_input(x: np.ndarray, x_dtype: str) -> np.ndarray:
+    """Exact widening of the layer input to fp64.
+
+    bf16 inputs arrive as uint16 bit patterns; a bf16 value is the fp32 value
+    whose upper 16 bits are those bits and whose lower 16 bits are zero."""
+    if x_dtype == "fp32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if x_dtype == "bf16":
+        u32 = np.asarray(x, dtype=np.uint16).astype(np.uint32) * np.uint32(65536)
+        return u32.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown input dtype {x_dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# Hadamard transform — [engine] module docstring item 2 (Eq. 3, 4, 7) and
+# fast_hadamard_transform.
+# ---------------------------------------------------------------------------
+
+def hadamard_matrix(n: int) -> np.ndarray:
+    """Orthonormal Sylvester-Hadamard matrix H_n in closed form.
+
+    Unrolling the recursion H_m = (1/sqrt 2) [[H_{m-1}, H_{m-1}], [H_{m-1}, -H_{m-1}]],
+    H_0 = [1] ([engine] Eq. 3-4) gives H[i, j] = (-1)^popcount(i & j) / sqrt(n)."""
+    if not _is_pow2(n):
+        raise ValueError(f"Hadamard dimension {n} must be a power of 2")
+    i = np.arange(n, dtype=np.int64)
+    anded = i[:, None] & i[None, :]
+    parity = np.zeros_like(anded)
+    while np.any(anded):
+        parity ^= anded & 1
+        anded >>= 1
+    return np.where(parity == 1, -1.0, 1.0) / math.sqrt(n)
+
+
+def fwht_dense(x: np.ndarray) -> np.ndarray:
+    """The definition written out: x_r = x H along the last axis (H = H^T)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    return x @ hadamard_matrix(n)
+
+
+def fwht(x: np.ndarray) -> np.ndarray:
+    """Fast Walsh-Hadamard transform along the last axis, fp64.
+
+    [engine] fast_hadamard_transform: reject a non-power-of-2 length; then for
+    half-widths h = 1, 2, 4, ..., n/2 pair element i with element i + h inside
+    every aligned block of 2h elements and replace (u, v) by
+    ((u + v)/sqrt 2, (u - v)/sqrt 2). The page casts the result back to the
+    input dtype; here it stays fp64 (no intermediate rounding)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    if not _is_pow2(n):
+        raise ValueError(f"Hadamard transform dimension {n} must be a power of 2")
+    lead = x.shape[:-1]
+    y = x.reshape(-1, n).copy()
+    r = 1.0 / math.sqrt(2.0)
+    h = 1
+    while h < n:
+        blocks = y.reshape(y.shape[0], n // (2 * h), 2, h)
+        first = blocks[:, :, 0, :]
+        second = blocks[:, :, 1, :]
+        y = np.stack(((first + second) * r, (first - second) * r), axis=2).reshape(-1, n)
+        h *= 2
+    return y.reshape(*lead, n)
+
+
+# ---------------------------------------------------------------------------
+# Ternary weights — [engine] docstring item 3, Eq. 1-2, quantize_weight_ternary.
+# ---------------------------------------------------------------------------
+
+def absmean_alpha(W: np.ndarray) -> float:
+    """alpha = mean(|W|) over the whole tensor ([engine] Eq. 2, per-tensor)."""
+    W = np.asarray(W, dtype=np.float64)
+    return float(np.sum(np.abs(W)) / W.size)
+
+
+def ternarize(W: np.ndarray, eps: float = EPS):
+    """t = RoundClip(W / (alpha + eps), -1, 1) ([engine] Eq. 1).
+
+    Returns (t int8 [N, K], alpha, p) where p = W / (alpha + eps) is the
+    pre-rounding value (kept for the rounding-boundary rule). RoundClip rounds
+    half to even, as torch.round does."""
+    W64 = np.asarray(W, dtype=np.float32).astype(np.float64)
+    alpha = absmean_alpha(W64)
+    p = W64 / (alpha + eps)
+    t = np.clip(np.rint(p), -1.0, 1.0).astype(np.int8)
+    return t, alpha, p
+
+
+# ---------------------------------------------------------------------------
+# 2-bit packing (4 weights per byte, 2 bits per weight as in the edge page's
+# I2_S format, Table 1). The code value t + 1 in {0, 1, 2} follows the blog
+# page's LUT simulation (w -> w + 1). The placement of weights inside a block
+# is this library's contract, not the pages':
+#   K is cut into blocks of 64 weights; block g of row n is bytes 16g..16g+15
+#   of that row; byte b of a block holds the weights at block offsets
+#   b, 16 + b, 32 + b, 48 + b in bit pairs 0-1, 2-3, 4-5, 6-7.
+# ---------------------------------------------------------------------------
+
+BLOCK = 64
+
+
+def pack_2bit(t: np.ndarray) -> np.ndarray:
+    t = np.asarray(t)
+    N, K = t.shape
+    if K % BLOCK:
+        raise ValueError(f"K={K} must be a multiple of {BLOCK}")
+    if t.size and (t.min() < -1 or t.max() > 1):
+        raise ValueError("ternary values must lie in {-1, 0, 1}")
+    code = (t.astype(np.int16) + 1).astype(np.uint8)
+    # axis 2 = which quarter of the block (bit pair), axis 3 = byte in block
+    quarters = code.reshape(N, K // BLOCK, 4, BLOCK // 4)
+    packed = np.zeros((N, K // BLOCK, BLOCK // 4), dtype=np.uint8)
+    for j in range(4):
+        packed |= quarters[:, :, j, :] << np.uint8(2 * j)
+    return packed.reshape(N, K // 4)
+
+
+def unpack_2bit(packed: np.ndarray) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8)
+    N, KB = packed.shape
+    K = KB * 4
+    if K % BLOCK:
+        raise ValueError(f"K={K} must be a multiple of {BLOCK}")
+    blocks = packed.reshape(N, K // BLOCK, BLOCK // 4)
+    out = np.empty((N, K // BLOCK, 4, BLOCK // 4), dtype=np.int8)
+    for j in range(4):
+        out[:, :, j, :] = ((blocks >> np.uint8(2 * j)) & np.uint8(3)).astype(np.int8) - 1
+    return out.reshape(N, K)
+
+
+# ---------------------------------------------------------------------------
+# Activation quantization — [engine] Eq. 5 (quantize_act_int8) and Eq. 6
+# (quantize_act_int4), per token along the last axis.
+# ---------------------------------------------------------------------------
+
+def quantize_activations(x: np.ndarray, bits: int, eps: float = EPS):
+    """Per-token quantization.
+
+    bits=8: s = max|x| + eps, q = RoundClip(127 x / s, -128, 127)   (Eq. 5)
+    bits=4: s = mean|x| + eps, q = RoundClip(sqrt7 x / s, -8, 7)     (Eq. 6)
+    Returns (q int8 [M, K], s fp64 [M], p fp64 [M, K] pre-rounding)."""
+    if bits not in _QUANT:
+        raise ValueError(f"bits must be 4 or 8, got {bits}")
+    c, lo, hi = _QUANT[bits]
+    x = np.asarray(x, dtype=np.float64)
+    if bits == 8:
+        stat = np.max(np.abs(x), axis=-1, keepdims=True)
+    else:
+        stat = np.mean(np.abs(x), axis=-1, keepdims=True)
+    s = stat + eps
+    p = (c / s) * x
+    q = np.clip(np.rint(p), lo, hi).astype(np.int8)
+    return q, s[..., 0], p
+
+
+def quant_boundary_distance(p: np.ndarray) -> np.ndarray:
+    """Distance of each pre-rounding value from the nearest .5 boundary."""
+    p = np.asarray(p, dtype=np.float64)
+    return np.abs(p - (np.floor(p) + 0.5))
+
+
+# ---------------------------------------------------------------------------
+# Integer product and dequantization — [engine] HBitLinear.forward ends in
+# F.linear(x_q, w_q); the blog's BitLinear_b158 computes the same product on
+# the integer codes and rescales by (w_scale * x_scale) / Qb afterwards.
+# ---------------------------------------------------------------------------
+
+def ternary_matmul_i64(q: np.ndarray, t: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k q[m, k] * t[n, k], exact.
+
+    Computed as an fp64 matrix product of integer-valued arrays; every partial
+    sum is an integer below 2^53 (|q| <= 128, |t| <= 1, K <= 2^40), so the
+    product is exact."""
+    q = np.asarray(q)
+    t = np.asarray(t)
+    if q.shape[1] != t.shape[1]:
+        raise ValueError("inner dimensions differ")
+    if q.shape[1] >= 2 ** 40:
+        raise ValueError("K too large for an exact fp64 product")
+    acc = q.astype(np.float64) @ t.astype(np.float64).T
+    return np.rint(acc).astype(np.int64)
+
+
+def dequantize(acc: np.ndarray, alpha: float, s: np.ndarray, bits: int) -> np.ndarray:
+    """y = acc * alpha * s / c (c = 127 or sqrt 7), fp64.
+
+    [engine] the quantizers return (s / c) * q with s = stat + eps, and the
+    weight quantizer returns alpha * t; by linearity of F.linear the output is
+    acc * alpha * s / c."""
+    c = _QUANT[bits][0]
+    return np.asarray(acc, dtype=np.float64) * (alpha * np.asarray(s, dtype=np.float64)[:, None] / c)
+
+
+def forward_from_codes(q, s, t, alpha, bits):
+    acc = ternary_matmul_i64(q, t)
+    y64 = dequantize(acc, alpha, s, bits)
+    return acc, y64
+
+
+def forward(x: np.ndarray, x_dtype: str, t: np.ndarray, alpha: float, bits: int,
+            hadamard: int, eps: float = EPS) -> dict:
+    """H-BitLinear forward from already-ternarized weights.
+
+    [engine] HBitLinear.forward minus its RMSNorm prologue: x_r = FWHT(x) if
+    hadamard, then per-token quantization, then the ternary product and the
+    dequantization. Returns a dict with y (fp32), y64, acc, q, s, p."""
+    x64 = widen_input(x, x_dtype)
+    xr = fwht(x64) if hadamard else x64
+    q, s, p = quantize_activations(xr, bits, eps)
+    acc, y64 = forward_from_codes(q, s, t, alpha, bits)
+    return {"y": y64.astype(np.float32), "y64": y64, "acc": acc, "q": q, "s": s, "p": p, "xr": xr}
