@@ -1,0 +1,275 @@
+"""Throughput of the H-BitLinear forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY] [--no-extra]
+
+A step is one H-BitLinear forward call (transform + quantization kernel, then
+the ternary product with its fused dequantization) over one batch of seeded
+synthetic input already resident in HBM. The headline workload is the decode
+GEMV (M=1, K=2560, N=6912, int8 absmax, no Hadamard); its metric is
+packed-weight GB/s (N*K/4 bytes per step), timed cold: the step rotates over
+enough copies of the packed weights (> 512 MB) that none is served from the
+256 MB Infinity Cache.
+
+The JSON line also carries:
+  roofline      the dominant kernel (the ternary product) timed per launch with
+                HIP events on the launch stream, against the 8 TB/s HBM peak
+                (decode) or the 5.03 POP/s dense int8 MFMA peak (prefill);
+  cpu_baseline  the fp64 CPU oracle on the host cores, on a bounded sample;
+  per_workload  every measured workload at full size (prefill TOPS, decode
+                GB/s, the on-device ternarize+pack pass).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "H-BitLinear fwd: prefill int8-TOPS & decode weight-GB/s, % of MI355X roofline"
+HEADLINE = "decode_int8_m1_k2560_n6912"
+HBM_PEAK_GBS = 8000.0
+INT8_MFMA_PEAK_TOPS = 5033.2  # 256 CU x 2.4 GHz x 8192 int8 ops/clk/CU (dense)
+COLD_BYTES = 512 * 2 ** 20
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _dev_x(torch, x_np, x_dtype, dev):
+    if x_dtype == "bf16":
+        return torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(x_np).to(dev)
+
+
+def _copies_for_cold(nbytes):
+    return max(1, math.ceil(COLD_BYTES / max(nbytes, 1)) + 1)
+
+
+def _time_loop(torch, fn, steps, warmup):
+    """Average ms per call of fn(i) over `steps` back-to-back calls on the
+    current stream, bracketed by synchronizations."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def _time_per_launch(torch, fn, launches, warmup):
+    """Average and median ms of single launches, each bracketed by its own
+    pair of HIP events recorded on the launch stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(warmup + i)
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(ms.mean()), float(np.median(ms))
+
+
+class Prepared:
+    """Device-resident inputs of one workload."""
+
+    def __init__(self, torch, bl, key, dev, cold=True):
+        from bit_activation_linear_amd import workloads
+        self.wl = wl = workloads.WORKLOADS[key]
+        case = workloads.make_workload(key, seed=0)
+        self.case = case
+        self.x = _dev_x(torch, case["x"], wl.x_dtype, dev)
+        self.W = torch.from_numpy(case["W"]).to(dev)
+        Wp, alpha = bl.ternarize_weights(self.W)
+        self.alpha = alpha
+        wbytes = Wp.numel()
+        # Rotate copies only where the weights are big enough to matter; the
+        # tiny single-layer case is a latency measurement.
+        self.copies = _copies_for_cold(wbytes) if (cold and wbytes >= 2 ** 20) else 1
+        self.Wp = [Wp] + [Wp.clone() for _ in range(self.copies - 1)]
+        self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+        self.ws = torch.empty((bl.forward_workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.hadamard),),
+                              dtype=torch.uint8, device=dev)
+        self.codes, self.scales = bl.quantize_activations(self.x, wl.bits, wl.hadamard)
+        torch.cuda.synchronize()
+
+    def forward(self, bl, i):
+        wl = self.wl
+        bl.hbitlinear_forward(self.x, self.Wp[i % self.copies], self.alpha, wl.bits, wl.hadamard,
+                              out=self.y, workspace=self.ws)
+
+    def matmul_only(self, bl, i):
+        bl.ternary_linear_dequant(self.codes, self.scales, self.Wp[i % self.copies], self.alpha,
+                                  self.wl.bits, out=self.y)
+
+    def free_latent(self):
+        self.W = None
+
+
+def _work_units(wl):
+    return {"weight_bytes": wl.N * wl.K // 4, "ops": 2 * wl.M * wl.N * wl.K}
+
+
+def _measure_workload(torch, bl, key, dev, steps, warmup):
+    p = Prepared(torch, bl, key, dev)
+    wl = p.wl
+    u = _work_units(wl)
+    fwd_ms = _time_loop(torch, lambda i: p.forward(bl, i), steps, warmup)
+    mm_mean, mm_med = _time_per_launch(torch, lambda i: p.matmul_only(bl, i), steps, warmup)
+    res = {
+        "M": wl.M, "K": wl.K, "N": wl.N, "bits": wl.bits, "hadamard": wl.hadamard,
+        "x_dtype": wl.x_dtype, "cold_weight_copies": p.copies,
+        "forward_us": fwd_ms * 1e3,
+        "matmul_kernel_us_mean": mm_mean * 1e3, "matmul_kernel_us_median": mm_med * 1e3,
+        "forward_weight_GBs": u["weight_bytes"] / (fwd_ms * 1e-3) / 1e9,
+        "forward_TOPS": u["ops"] / (fwd_ms * 1e-3) / 1e12,
+        "matmul_weight_GBs": u["weight_bytes"] / (mm_mean * 1e-3) / 1e9,
+        "matmul_TOPS": u["ops"] / (mm_mean * 1e-3) / 1e12,
+    }
+    if wl.M <= 16:
+        res["matmul_hbm_frac"] = res["matmul_weight_GBs"] / HBM_PEAK_GBS
+    else:
+        res["matmul_mfma_frac"] = res["matmul_TOPS"] / INT8_MFMA_PEAK_TOPS
+    if key == "prefill_int8_m8192_k4096_n14336" or key == "int4_hadamard_m4_k256_n256":
+        # on-device ternarize + pack: two fp32 reads of W plus the packed write
+        Wp = p.Wp[0]
+        tern_ms = _time_loop(torch, lambda i: bl.ternarize_weights(p.W, out=Wp, alpha=p.alpha),
+                             max(5, steps // 4), 2)
+        tbytes = 2 * wl.N * wl.K * 4 + wl.N * wl.K // 4
+        res["ternarize_us"] = tern_ms * 1e3
+        res["ternarize_GBs"] = tbytes / (tern_ms * 1e-3) / 1e9
+    if key == "int4_hadamard_m4_k256_n256":
+        # whole layer including weight preparation, latency only
+        def full(i):
+            bl.ternarize_weights(p.W, out=p.Wp[0], alpha=p.alpha)
+            p.forward(bl, 0)
+        res["ternarize_plus_forward_us"] = _time_loop(torch, full, steps, warmup) * 1e3
+    return p, res
+
+
+def _cpu_baseline(key, budget_s):
+    """fp64 oracle on a bounded number of whole forward calls of the workload."""
+    import oracle
+    from bit_activation_linear_amd import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    wl = workloads.WORKLOADS[key]
+    case = workloads.make_workload(key, seed=0)
+    t, alpha, _ = oracle.ternarize(case["W"])
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward(case["x"], wl.x_dtype, t, alpha, wl.bits, wl.hadamard)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 10000:
+            break
+    per = el / reps
+    return {
+        "value": (wl.N * wl.K / 4) / per / 1e9, "unit": "GB/s", "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{reps} whole forward calls of {key} (M={wl.M}, K={wl.K}, N={wl.N}) from "
+                  f"ternary int8 weights, fp64 NumPy, {el:.1f} s; weight-prep excluded",
+        "seconds_per_call": per,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is a design note). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_activation_linear_amd as bl
+    from bit_activation_linear_amd import _lib, workloads
+
+    _lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    key = args.workload
+    wl = workloads.WORKLOADS[key]
+    _log(f"[bench] headline workload {key}")
+    p, head = _measure_workload(torch, bl, key, dev, args.steps, args.warmup)
+    ms = head["forward_us"] / 1e3
+    decode = wl.M <= 16
+    if decode:
+        value, unit = head["forward_weight_GBs"], "GB/s"
+        roof = {"bound": "hbm", "achieved": head["matmul_weight_GBs"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": head["matmul_weight_GBs"] / HBM_PEAK_GBS}
+    else:
+        value, unit = head["forward_TOPS"], "TOPS"
+        roof = {"bound": "mfma", "achieved": head["matmul_TOPS"], "peak": INT8_MFMA_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": head["matmul_TOPS"] / INT8_MFMA_PEAK_TOPS}
+    roof["kernel"] = "ternary_gemv_kernel" if decode else "ternary_gemm_kernel"
+    roof["algorithmic"] = ("N*K/4 packed weight bytes per launch" if decode
+                           else "2*M*N*K int8 ops per launch")
+    roof["launch_us_mean"] = head["matmul_kernel_us_mean"]
+    roof["traffic"] = None
+    _log(f"[bench] {key}: forward {head['forward_us']:.2f} us, matmul {head['matmul_kernel_us_mean']:.2f} us")
+    del p
+
+    per = {key: head}
+    if not args.no_extra:
+        for other in workloads.WORKLOAD_ORDER:
+            if other == key:
+                continue
+            _log(f"[bench] workload {other}")
+            po, r = _measure_workload(torch, bl, other, dev, max(20, args.steps // 4),
+                                      max(5, args.warmup // 2))
+            del po
+            torch.cuda.empty_cache()
+            per[other] = r
+            _log(f"[bench] {other}: forward {r['forward_us']:.2f} us, matmul {r['matmul_kernel_us_mean']:.2f} us")
+
+    cpu = None
+    if not args.no_cpu:
+        _log("[bench] CPU oracle baseline")
+        cpu = _cpu_baseline(key, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": key, "M": wl.M, "K": wl.K, "N": wl.N, "bits": wl.bits,
+                   "hadamard": wl.hadamard, "x_dtype": wl.x_dtype,
+                   "cold_weight_copies": head["cold_weight_copies"]},
+        "roofline": roof, "cpu_baseline": cpu, "per_workload": per,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

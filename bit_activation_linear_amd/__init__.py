@@ -1,0 +1,19 @@
+"""H-BitLinear forward (BitNet v2) on AMD MI355X.
+
+The compute path is the HIP library libbitnet_mi355x.so (C ABI in
+include/bitnet_mi355x.h); this package is its thin torch binding. Importing
+the package does not load the library; the first call does, and fails loudly
+if it has not been built.
+"""
+
+from .api import (  # noqa: F401
+    HBitLinear,
+    forward_workspace_bytes,
+    hbitlinear_forward,
+    pack_2bit,
+    quantize_activations,
+    ternarize_weights,
+    ternary_gemm_i32,
+    ternary_linear_dequant,
+)
+from ._lib import BitNetError  # noqa: F401

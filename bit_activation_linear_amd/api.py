@@ -1,0 +1,178 @@
+"""Torch-facing binding of the H-BitLinear library.
+
+PyTorch provides device memory and the current HIP stream; each function
+checks dtype, device and contiguity, allocates outputs/workspace with torch,
+and hands raw pointers to the C ABI. All arithmetic happens in the library's
+HIP kernels.
+
+Names follow the BitNet v2 engine page (Quillan-Ronin bitnet_v2_engine.py):
+HBitLinear, quantize_weight_ternary (here: ternarize_weights, which also
+packs), and the per-token activation quantizers of Eq. 5-6.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+
+def _stream_ptr(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _x_dtype(x: torch.Tensor) -> int:
+    return _lib.BF16 if x.dtype == torch.bfloat16 else _lib.F32
+
+
+def ternarize_weights(W: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      alpha: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Absmean-ternarize fp32 W [N, K] and pack it (block-64, 2 bits per weight).
+
+    Returns (Wpacked uint8 [N, K/4], alpha fp32 [1] on the device)."""
+    _require(W, "W", (torch.float32,), 2)
+    N, K = W.shape
+    if out is None:
+        out = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    if alpha is None:
+        alpha = torch.empty((1,), dtype=torch.float32, device=W.device)
+    ws_bytes = _lib.load().bitnet_ternarize_workspace_bytes(N, K)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
+    _lib.call("bitnet_ternarize_weights", W.data_ptr(), N, K, out.data_ptr(), alpha.data_ptr(),
+              ws.data_ptr(), ws_bytes, _stream_ptr(W))
+    return out, alpha
+
+
+def pack_2bit(T: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Pack ternary int8 T [N, K] into the block-64 2-bit layout."""
+    _require(T, "T", (torch.int8,), 2)
+    N, K = T.shape
+    if out is None:
+        out = torch.empty((N, K // 4), dtype=torch.uint8, device=T.device)
+    _lib.call("bitnet_pack_2bit", T.data_ptr(), N, K, out.data_ptr(), _stream_ptr(T))
+    return out
+
+
+def forward_workspace_bytes(M: int, K: int, N: int, bits: int, hadamard: int) -> int:
+    return int(_lib.load().bitnet_forward_workspace_bytes(M, K, N, bits, int(hadamard)))
+
+
+def hbitlinear_forward(x: torch.Tensor, Wpacked: torch.Tensor, alpha: torch.Tensor, bits: int,
+                       hadamard: int, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y fp32 [M, N] = H-BitLinear forward of x [M, K] (fp32 or bf16)."""
+    _require(x, "x", (torch.float32, torch.bfloat16), 2)
+    _require(Wpacked, "Wpacked", (torch.uint8,), 2)
+    _require(alpha, "alpha", (torch.float32,), 1)
+    M, K = x.shape
+    N = Wpacked.shape[0]
+    if Wpacked.shape[1] * 4 != K:
+        raise ValueError(f"Wpacked has {Wpacked.shape[1]} bytes per row, expected K/4 = {K // 4}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = forward_workspace_bytes(M, K, N, bits, hadamard)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _lib.call("bitnet_hbitlinear_forward", x.data_ptr(), _x_dtype(x), M, K, Wpacked.data_ptr(), N,
+              alpha.data_ptr(), int(bits), int(hadamard), out.data_ptr(), workspace.data_ptr(),
+              workspace.numel(), _stream_ptr(x))
+    return out
+
+
+def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
+                         codes: Optional[torch.Tensor] = None,
+                         scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(codes int8 [M, K], scales fp32 [M]) of the transform + quantization stage."""
+    _require(x, "x", (torch.float32, torch.bfloat16), 2)
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _lib.call("bitnet_quantize_activations", x.data_ptr(), _x_dtype(x), M, K, int(bits),
+              int(hadamard), codes.data_ptr(), scales.data_ptr(), _stream_ptr(x))
+    return codes, scales
+
+
+def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """acc int32 [M, N] = codes . t^T (exact)."""
+    _require(codes, "codes", (torch.int8,), 2)
+    _require(Wpacked, "Wpacked", (torch.uint8,), 2)
+    M, K = codes.shape
+    N = Wpacked.shape[0]
+    if Wpacked.shape[1] * 4 != K:
+        raise ValueError("Wpacked row length does not match K/4")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=codes.device)
+    _lib.call("bitnet_ternary_gemm_i32", codes.data_ptr(), M, K, Wpacked.data_ptr(), N,
+              out.data_ptr(), _stream_ptr(codes))
+    return out
+
+
+def ternary_linear_dequant(codes: torch.Tensor, scales: torch.Tensor, Wpacked: torch.Tensor,
+                           alpha: torch.Tensor, bits: int,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y fp32 [M, N] = (codes . t^T) * alpha * scales / c."""
+    _require(codes, "codes", (torch.int8,), 2)
+    _require(scales, "scales", (torch.float32,), 1)
+    _require(Wpacked, "Wpacked", (torch.uint8,), 2)
+    _require(alpha, "alpha", (torch.float32,), 1)
+    M, K = codes.shape
+    N = Wpacked.shape[0]
+    if Wpacked.shape[1] * 4 != K:
+        raise ValueError("Wpacked row length does not match K/4")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    _lib.call("bitnet_ternary_linear_dequant", codes.data_ptr(), scales.data_ptr(), M, K,
+              Wpacked.data_ptr(), N, alpha.data_ptr(), int(bits), out.data_ptr(),
+              _stream_ptr(codes))
+    return out
+
+
+class HBitLinear:
+    """Prepared H-BitLinear layer: weights ternarized and packed once on the
+    device, then forward(x) many times (the prepare-once / forward-many split
+    of the bitnet.cpp simulation page's edge linear layer).
+
+    The RMSNorm of the engine page's HBitLinear is not applied: x is taken to
+    be the normalized input."""
+
+    def __init__(self, weight: torch.Tensor, bits: int = 4, hadamard: bool = True):
+        if bits not in (4, 8):
+            raise ValueError("bits must be 4 or 8")
+        K = weight.shape[1]
+        if hadamard and (K & (K - 1)) != 0:
+            raise ValueError(f"H-BitLinear in_features ({K}) must be a power of 2")
+        self.bits = bits
+        self.hadamard = int(bool(hadamard))
+        self.in_features = K
+        self.out_features = weight.shape[0]
+        self.Wpacked, self.alpha = ternarize_weights(weight.contiguous())
+        self._ws = None
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        M = x.shape[0]
+        need = forward_workspace_bytes(M, self.in_features, self.out_features, self.bits,
+                                       self.hadamard)
+        if self._ws is None or self._ws.numel() < need or self._ws.device != x.device:
+            self._ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+        return hbitlinear_forward(x, self.Wpacked, self.alpha, self.bits, self.hadamard,
+                                  workspace=self._ws)
+
+    __call__ = forward

@@ -1,0 +1,223 @@
+// C ABI of the H-BitLinear library: argument validation, workspace layout and
+// dispatch to the gfx950 kernels. No entry point allocates, frees or
+// synchronizes; no C++ exception crosses the ABI; nothing is launched when
+// validation fails. Loading the library makes no HIP call.
+#include "../../include/bitnet_mi355x.h"
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bitnet_status fail(bitnet_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bitnet_status ok() {
+  g_last_error.clear();
+  return BITNET_OK;
+}
+
+bitnet_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BITNET_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Largest M the prefill grid addresses (grid.y <= 65535 tiles of 128 rows).
+constexpr int64_t kMaxM = (int64_t)65535 * 128;
+
+bitnet_status check_dims(const char* fn, int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 0 || N < 0)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: negative size (M=%lld K=%lld N=%lld)", fn,
+                (long long)M, (long long)K, (long long)N);
+  if (K == 0 || K % 64 != 0)
+    return fail(BITNET_ERR_ALIGN, "%s: K=%lld must be a positive multiple of 64", fn, (long long)K);
+  if (M > kMaxM || N > INT_MAX)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: M=%lld or N=%lld too large", fn, (long long)M,
+                (long long)N);
+  return BITNET_OK;
+}
+
+bitnet_status check_quant_args(const char* fn, int64_t K, int bits, int hadamard, int x_dtype) {
+  if (bits != 4 && bits != 8)
+    return fail(BITNET_ERR_BAD_BITS, "%s: bits=%d must be 4 or 8", fn, bits);
+  if (K > BITNET_MAX_K)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: K=%lld exceeds BITNET_MAX_K=%d", fn, (long long)K,
+                BITNET_MAX_K);
+  if (hadamard && !is_pow2(K))
+    return fail(BITNET_ERR_NOT_POW2, "%s: K=%lld must be a power of two with hadamard=1", fn,
+                (long long)K);
+  if (x_dtype != BITNET_F32 && x_dtype != BITNET_BF16)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: unknown x dtype %d", fn, x_dtype);
+  return BITNET_OK;
+}
+
+struct ForwardWorkspace {
+  int8_t* codes;
+  float* scales;
+};
+
+size_t forward_ws_bytes(int64_t M, int64_t K) {
+  return round_up((size_t)M * (size_t)K) + round_up((size_t)M * sizeof(float));
+}
+
+ForwardWorkspace carve_forward(void* ws, int64_t M, int64_t K) {
+  char* base = static_cast<char*>(ws);
+  ForwardWorkspace w;
+  w.codes = reinterpret_cast<int8_t*>(base);
+  w.scales = reinterpret_cast<float*>(base + round_up((size_t)M * (size_t)K));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitnet_abi_version(void) { return BITNET_ABI_VERSION; }
+
+const char* bitnet_last_error(void) { return g_last_error.c_str(); }
+
+size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return round_up(sizeof(double) * bitnet::kAbsPartials);
+}
+
+bitnet_status bitnet_ternarize_weights(const float* W, int64_t N, int64_t K, uint8_t* Wpacked,
+                                       float* alpha, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  const char* fn = "bitnet_ternarize_weights";
+  if (bitnet_status st = check_dims(fn, 0, K, N)) return st;
+  if (N == 0) return fail(BITNET_ERR_INVALID_ARG, "%s: N must be >= 1 (mean of an empty tensor)", fn);
+  if (!W || !Wpacked || !alpha || !ws)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (ws_bytes < bitnet_ternarize_workspace_bytes(N, K))
+    return fail(BITNET_ERR_INVALID_ARG, "%s: workspace %zu B < required %zu B", fn, ws_bytes,
+                bitnet_ternarize_workspace_bytes(N, K));
+  if (!aligned(W, 16) || !aligned(Wpacked, 16) || !aligned(ws, 16) || !aligned(alpha, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  double* partials = static_cast<double*>(ws);
+  int n_partials = 0;
+  hipError_t e = bitnet::launch_absmean_partial(W, N * K, partials, &n_partials, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  e = bitnet::launch_ternarize_pack(W, N, K, partials, n_partials, Wpacked, alpha, stream);
+  return hip_status(e, fn);
+}
+
+bitnet_status bitnet_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* Wpacked,
+                               hipStream_t stream) {
+  const char* fn = "bitnet_pack_2bit";
+  if (bitnet_status st = check_dims(fn, 0, K, N)) return st;
+  if (N == 0) return ok();
+  if (!T || !Wpacked) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(T, 16) || !aligned(Wpacked, 16))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bitnet::launch_pack_2bit(T, N, K, Wpacked, stream), fn);
+}
+
+size_t bitnet_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits, int hadamard) {
+  (void)N;
+  (void)bits;
+  (void)hadamard;
+  if (M < 0 || K < 0) return 0;
+  return forward_ws_bytes(M, K);
+}
+
+bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, int64_t M,
+                                          int64_t K, int bits, int hadamard, int8_t* codes,
+                                          float* scales, hipStream_t stream) {
+  const char* fn = "bitnet_quantize_activations";
+  if (bitnet_status st = check_dims(fn, M, K, 0)) return st;
+  if (bitnet_status st = check_quant_args(fn, K, bits, hadamard, x_dtype)) return st;
+  if (M == 0) return ok();
+  if (!x || !codes || !scales) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, codes,
+                                            scales, stream),
+                    fn);
+}
+
+bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
+                                      const uint8_t* Wpacked, int64_t N, int32_t* acc,
+                                      hipStream_t stream) {
+  const char* fn = "bitnet_ternary_gemm_i32";
+  if (bitnet_status st = check_dims(fn, M, K, N)) return st;
+  if (K > BITNET_MAX_K)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: K=%lld exceeds BITNET_MAX_K=%d", fn, (long long)K,
+                BITNET_MAX_K);
+  if (M == 0 || N == 0) return ok();
+  if (!codes || !Wpacked || !acc) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(codes, 16) || !aligned(Wpacked, 16) || !aligned(acc, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bitnet::launch_ternary_matmul(codes, nullptr, M, (int)K, Wpacked, N, nullptr,
+                                                  8, nullptr, acc, stream),
+                    fn);
+}
+
+bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* scales, int64_t M,
+                                            int64_t K, const uint8_t* Wpacked, int64_t N,
+                                            const float* alpha, int bits, float* y,
+                                            hipStream_t stream) {
+  const char* fn = "bitnet_ternary_linear_dequant";
+  if (bitnet_status st = check_dims(fn, M, K, N)) return st;
+  if (bits != 4 && bits != 8) return fail(BITNET_ERR_BAD_BITS, "%s: bits=%d must be 4 or 8", fn, bits);
+  if (K > BITNET_MAX_K)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: K=%lld exceeds BITNET_MAX_K=%d", fn, (long long)K,
+                BITNET_MAX_K);
+  if (M == 0 || N == 0) return ok();
+  if (!codes || !scales || !Wpacked || !alpha || !y)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(codes, 16) || !aligned(Wpacked, 16) || !aligned(y, 4) || !aligned(scales, 4) ||
+      !aligned(alpha, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bitnet::launch_ternary_matmul(codes, scales, M, (int)K, Wpacked, N, alpha,
+                                                  bits, y, nullptr, stream),
+                    fn);
+}
+
+bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int64_t M, int64_t K,
+                                        const uint8_t* Wpacked, int64_t N, const float* alpha,
+                                        int bits, int hadamard, float* y, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "bitnet_hbitlinear_forward";
+  if (bitnet_status st = check_dims(fn, M, K, N)) return st;
+  if (bitnet_status st = check_quant_args(fn, K, bits, hadamard, x_dtype)) return st;
+  if (M == 0 || N == 0) return ok();
+  if (!x || !Wpacked || !alpha || !y || !ws)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  const size_t need = bitnet_forward_workspace_bytes(M, K, N, bits, hadamard);
+  if (ws_bytes < need)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: workspace %zu B < required %zu B", fn, ws_bytes, need);
+  if (!aligned(x, 16) || !aligned(Wpacked, 16) || !aligned(ws, 16) || !aligned(y, 4) ||
+      !aligned(alpha, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  const ForwardWorkspace w = carve_forward(ws, M, K);
+  hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
+                                         w.scales, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
+                                    nullptr, stream);
+  return hip_status(e, fn);
+}
+
+}  // extern "C"

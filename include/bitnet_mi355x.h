@@ -1,0 +1,153 @@
+/*
+ * bitnet_mi355x.h — C ABI of the H-BitLinear forward library for AMD MI355X (gfx950).
+ *
+ * The layer (BitNet v2 "H-BitLinear", as restated on the Quillan-Ronin
+ * bitnet_v2_engine.py page, class HBitLinear and Eq. 1-7) computes, per token
+ * row x of X [M, K]:
+ *     x_r  = H_K x                    (orthonormal Walsh-Hadamard, optional)
+ *     q, s = per-token quantization   (int8 absmax or int4 absmean*sqrt7)
+ *     y    = (q . t^T) * alpha * s / c
+ * with t = RoundClip(W / (alpha + eps), -1, 1) the absmean-ternarized weights
+ * and alpha = mean|W| (Eq. 1-2). The RMSNorm that precedes the transform in
+ * that class is not part of this library: X is taken to be already normalized.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer (HBM of the current HIP device),
+ *     row-major, allocated and owned by the caller. The library never
+ *     allocates, frees or synchronizes; every call only enqueues kernels on
+ *     `stream` (0 = the null stream) and returns.
+ *   - Returns BITNET_OK (0) on success. On any error nothing is launched and
+ *     bitnet_last_error() returns a message (per calling thread). A failed
+ *     kernel launch returns BITNET_ERR_HIP. Device-side faults surface, as for
+ *     any HIP work, at the caller's next synchronization.
+ *   - Pointers to tensors must be 16-byte aligned; the alpha and scale
+ *     pointers 4-byte aligned.
+ *   - eps = 1e-7 (BITNET_EPS), the engine page's default for every quantizer.
+ *   - Calls that share a workspace must not overlap in time.
+ *   - M = 0 or N = 0 is a no-op that returns BITNET_OK.
+ *
+ * Packed-weight layout ("block-64", 2 bits per weight, 4 weights per byte)
+ *   Wpacked is uint8 [N, K/4]. Each ternary weight is stored as the 2-bit
+ *   code t + 1 in {0, 1, 2} (3 is never written). K is cut into blocks of 64
+ *   consecutive weights; block g of row n occupies bytes 16g .. 16g+15 of that
+ *   row, and byte b of the block holds the weights at block offsets
+ *   b, 16+b, 32+b, 48+b in its bit pairs 0-1, 2-3, 4-5, 6-7 (LSB first).
+ *   Shifting a 32-bit word of the block right by 2j and masking 0x03030303
+ *   yields four consecutive weights, which is why this order was chosen.
+ *   K must therefore be a multiple of 64.
+ */
+#ifndef BITNET_MI355X_H
+#define BITNET_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITNET_ABI_VERSION 1
+#define BITNET_EPS 1e-7f
+/* Largest K the fused transform + quantizer stages in one CU's LDS (fp32). */
+#define BITNET_MAX_K 32768
+
+typedef enum {
+  BITNET_OK = 0,
+  BITNET_ERR_INVALID_ARG = 1, /* null pointer, negative size, workspace too small */
+  BITNET_ERR_NOT_POW2 = 2,    /* hadamard=1 with K not a power of two */
+  BITNET_ERR_BAD_BITS = 3,    /* bits not in {4, 8} */
+  BITNET_ERR_ALIGN = 4,       /* K not a multiple of 64, or a misaligned pointer */
+  BITNET_ERR_UNSUPPORTED = 5, /* K above BITNET_MAX_K, or dtype not supported */
+  BITNET_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+} bitnet_status;
+
+typedef enum { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype;
+
+/* Version of this ABI (BITNET_ABI_VERSION). Makes no HIP call. */
+int bitnet_abi_version(void);
+
+/* Message of the last error on the calling thread ("" if none). Makes no HIP call. */
+const char* bitnet_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Weight preparation                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace bitnet_ternarize_weights needs for an [N, K] tensor. */
+size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K);
+
+/* Absmean ternarization and 2-bit packing of fp32 latent weights.
+ * Engine page, Eq. 1-2 (quantize_weight_ternary): alpha = mean|W| over the
+ * whole tensor, t = RoundClip(W / (alpha + eps), -1, 1) with round-half-even.
+ *   W        fp32 [N, K], K contiguous (out_features x in_features).
+ *   Wpacked  uint8 [N, K/4], block-64 layout (above). Written.
+ *   alpha    one fp32 on the device. Written (stays on the device, so the
+ *            forward can consume it without a host round trip).
+ *   ws       workspace of at least bitnet_ternarize_workspace_bytes(N, K).
+ * The |W| sum is a fixed-order two-stage reduction accumulated in fp64, so
+ * results are bitwise reproducible. Requires K % 64 == 0 and N >= 1. */
+bitnet_status bitnet_ternarize_weights(const float* W, int64_t N, int64_t K, uint8_t* Wpacked,
+                                       float* alpha, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/* Packs ternary values held one per int8 [N, K] into the block-64 layout.
+ * Values are mapped by sign (negative -> -1, zero -> 0, positive -> +1).
+ * Requires K % 64 == 0. */
+bitnet_status bitnet_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* Wpacked,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Forward                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace bitnet_hbitlinear_forward needs (codes, scales). */
+size_t bitnet_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits, int hadamard);
+
+/* H-BitLinear forward (engine page, HBitLinear.forward after its RMSNorm;
+ * Eq. 3-7):
+ *   x_r = hadamard ? H_K x : x          fp32, never rounded to a narrower type
+ *   bits == 8: s = max|x_r| + eps,  q = RoundClip(127 x_r / s, -128, 127)  (Eq. 5)
+ *   bits == 4: s = mean|x_r| + eps, q = RoundClip(sqrt7 x_r / s, -8, 7)    (Eq. 6)
+ *   acc = q . t^T                       exact int32
+ *   y   = acc * alpha * s / c           fp32, c = 127 or sqrt 7
+ *   x        [M, K] in x_dtype (BITNET_F32 or BITNET_BF16).
+ *   Wpacked  uint8 [N, K/4], block-64 layout; alpha: one fp32 on the device.
+ *   y        fp32 [M, N]. Written.
+ *   ws       workspace of at least bitnet_forward_workspace_bytes(...).
+ * Requires K % 64 == 0, K <= BITNET_MAX_K, and a power-of-two K when
+ * hadamard != 0. */
+bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int64_t M, int64_t K,
+                                        const uint8_t* Wpacked, int64_t N, const float* alpha,
+                                        int bits, int hadamard, float* y, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+
+/* The two stages of the forward, exposed for inspection and timing. They run
+ * the same kernels as bitnet_hbitlinear_forward. */
+
+/* Transform + per-token quantization only (Eq. 3-6): writes int8 codes
+ * [M, K] and fp32 scales s [M] (s = stat + eps, the value the dequantization
+ * multiplies by). Same requirements as the forward. */
+bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, int64_t M,
+                                          int64_t K, int bits, int hadamard, int8_t* codes,
+                                          float* scales, hipStream_t stream);
+
+/* Exact integer product only: acc[m, n] = sum_k codes[m, k] * t[n, k], int32.
+ * codes: int8 [M, K] with values in [-128, 127]. Requires K % 64 == 0. */
+bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
+                                      const uint8_t* Wpacked, int64_t N, int32_t* acc,
+                                      hipStream_t stream);
+
+/* Integer product with the fused dequantization epilogue:
+ * y = (codes . t^T) * alpha * scales[m] / c, c = 127 (bits 8) or sqrt 7 (bits 4). */
+bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* scales, int64_t M,
+                                            int64_t K, const uint8_t* Wpacked, int64_t N,
+                                            const float* alpha, int bits, float* y,
+                                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_MI355X_H */

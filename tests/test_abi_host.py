@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load without a device, export every function the header
+declares, and reject every invalid argument before touching HIP.
+"""
+
+import ctypes
+
+import pytest
+
+from bit_activation_linear_amd import _lib
+
+FAKE = 0x10000  # a 16-B aligned non-null address; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _lib.header_declared_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks a signature for {name}"
+    assert set(_lib.SIGNATURES) == set(declared)
+
+
+def test_version_and_empty_error(lib):
+    assert lib.bitnet_abi_version() == 1
+
+
+def test_workspace_sizes(lib):
+    # codes M*K bytes + scales 4*M bytes, each rounded up to 256 B
+    assert lib.bitnet_forward_workspace_bytes(4, 256, 256, 4, 1) == 1024 + 256
+    assert lib.bitnet_forward_workspace_bytes(2048, 8192, 2048, 4, 1) == 2048 * 8192 + 8192
+    assert lib.bitnet_forward_workspace_bytes(0, 64, 8, 8, 0) == 0
+    assert lib.bitnet_ternarize_workspace_bytes(14336, 4096) >= 8 * 1024
+
+
+def _fwd(lib, x=FAKE, xt=_lib.BF16, M=4, K=256, Wp=FAKE, N=256, alpha=FAKE, bits=4, had=1,
+         y=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.bitnet_hbitlinear_forward(x, xt, M, K, Wp, N, alpha, bits, had, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), _lib.ERR_INVALID_ARG),
+    (dict(Wp=None), _lib.ERR_INVALID_ARG),
+    (dict(alpha=None), _lib.ERR_INVALID_ARG),
+    (dict(y=None), _lib.ERR_INVALID_ARG),
+    (dict(ws=None), _lib.ERR_INVALID_ARG),
+    (dict(ws_bytes=10), _lib.ERR_INVALID_ARG),
+    (dict(M=-1), _lib.ERR_INVALID_ARG),
+    (dict(N=-3), _lib.ERR_INVALID_ARG),
+    (dict(bits=6), _lib.ERR_BAD_BITS),
+    (dict(bits=0), _lib.ERR_BAD_BITS),
+    (dict(K=192, had=1), _lib.ERR_NOT_POW2),
+    (dict(K=100), _lib.ERR_ALIGN),
+    (dict(K=0), _lib.ERR_ALIGN),
+    (dict(K=65536), _lib.ERR_UNSUPPORTED),
+    (dict(K=32768 + 64, had=0), _lib.ERR_UNSUPPORTED),
+    (dict(xt=7), _lib.ERR_UNSUPPORTED),
+    (dict(x=FAKE + 2), _lib.ERR_ALIGN),
+    (dict(Wp=FAKE + 8), _lib.ERR_ALIGN),
+    (dict(ws=FAKE + 4), _lib.ERR_ALIGN),
+    (dict(y=FAKE + 1), _lib.ERR_ALIGN),
+])
+def test_forward_validation(lib, kwargs, status):
+    assert _fwd(lib, **kwargs) == status
+    assert lib.bitnet_last_error() != b""
+
+
+def test_forward_empty_is_noop(lib):
+    # M = 0 / N = 0 return OK without launching (pointers are not touched).
+    assert _fwd(lib, M=0, x=None, y=None, ws=None) == _lib.OK
+    assert _fwd(lib, N=0, Wp=None, y=None, ws=None) == _lib.OK
+    assert lib.bitnet_last_error() == b""
+
+
+def test_ternarize_validation(lib):
+    f = lib.bitnet_ternarize_weights
+    assert f(None, 4, 64, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    assert f(FAKE, 4, 60, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.ERR_ALIGN
+    assert f(FAKE, 0, 64, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    assert f(FAKE, 4, 64, FAKE, FAKE, FAKE, 8, None) == _lib.ERR_INVALID_ARG
+    assert f(FAKE, 4, 64, FAKE, FAKE + 2, FAKE, 1 << 20, None) == _lib.ERR_ALIGN
+
+
+def test_pack_validation(lib):
+    f = lib.bitnet_pack_2bit
+    assert f(None, 4, 64, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert f(FAKE, 4, 96, FAKE, None) == _lib.ERR_ALIGN
+    assert f(FAKE, 0, 64, None, None) == _lib.OK
+
+
+def test_stage_entry_points_validation(lib):
+    q = lib.bitnet_quantize_activations
+    assert q(FAKE, _lib.F32, 2, 64, 5, 0, FAKE, FAKE, None) == _lib.ERR_BAD_BITS
+    assert q(FAKE, _lib.F32, 2, 320, 8, 1, FAKE, FAKE, None) == _lib.ERR_NOT_POW2
+    assert q(None, _lib.F32, 2, 64, 8, 0, FAKE, FAKE, None) == _lib.ERR_INVALID_ARG
+    g = lib.bitnet_ternary_gemm_i32
+    assert g(FAKE, 2, 70, FAKE, 3, FAKE, None) == _lib.ERR_ALIGN
+    assert g(None, 2, 64, FAKE, 3, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert g(FAKE, 0, 64, FAKE, 3, None, None) == _lib.OK
+    d = lib.bitnet_ternary_linear_dequant
+    assert d(FAKE, FAKE, 2, 64, FAKE, 3, FAKE, 3, FAKE, None) == _lib.ERR_BAD_BITS
+    assert d(FAKE, None, 2, 64, FAKE, 3, FAKE, 8, FAKE, None) == _lib.ERR_INVALID_ARG
+
+
+def test_binding_raises_typed_error(lib):
+    with pytest.raises(_lib.BitNetError) as ei:
+        _lib.call("bitnet_pack_2bit", None, 4, 64, FAKE, None)
+    assert ei.value.status == _lib.ERR_INVALID_ARG
+    assert "null pointer" in str(ei.value)
+
+
+def test_last_error_is_per_thread(lib):
+    import threading
+    assert lib.bitnet_pack_2bit(None, 4, 64, FAKE, None) == _lib.ERR_INVALID_ARG
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.bitnet_last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == b""
+    assert lib.bitnet_last_error() != b""

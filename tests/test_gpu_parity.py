@@ -1,0 +1,237 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
+
+Small cases span several tiles with ragged M, N and K tails and both kernel
+shapes (M <= 16 streams the weights, M > 16 runs the prefill tile); the five
+measured workloads run at full size in the launch configuration the bench
+times, compared in full where the oracle is quick and on sampled rows
+otherwise.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import bit_activation_linear_amd as bl
+from bit_activation_linear_amd import workloads
+from parity_util import assert_codes_match, assert_packed_match, assert_y_close
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev_x(x_np, x_dtype):
+    if x_dtype == "bf16":
+        return torch.from_numpy(x_np.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(x_np).to(DEV)
+
+
+def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=1.0):
+    _say(f"case M={M} K={K} N={N} bits={bits} hadamard={had} x={x_dtype} seed={seed}")
+    case = workloads.make_case(M, K, N, x_dtype=x_dtype, dist=dist, n_out=n_out, factor=factor,
+                               seed=seed)
+    x = _to_dev_x(case["x"], x_dtype)
+    W = torch.from_numpy(case["W"]).to(DEV)
+
+    Wp, alpha = bl.ternarize_weights(W)
+    codes, scales = bl.quantize_activations(x, bits, had)
+    y = bl.hbitlinear_forward(x, Wp, alpha, bits, had)
+    acc = bl.ternary_gemm_i32(codes, Wp)
+    y2 = bl.ternary_linear_dequant(codes, scales, Wp, alpha, bits)
+    torch.cuda.synchronize()
+
+    t_ref, a_ref, p_w = oracle.ternarize(case["W"])
+    assert_packed_match(Wp.cpu().numpy(), t_ref, p_w)
+    assert abs(alpha.item() - a_ref) <= 1e-6 * a_ref
+
+    ref = oracle.forward(case["x"], x_dtype, t_ref, a_ref, bits, had)
+    q_gpu = codes.cpu().numpy()
+    assert_codes_match(q_gpu, ref["q"], ref["p"])
+    np.testing.assert_allclose(scales.cpu().numpy(), ref["s"], rtol=2e-6)
+
+    # int32 accumulators exact on identical codes, both ways round.
+    t_gpu = oracle.unpack_2bit(Wp.cpu().numpy())
+    np.testing.assert_array_equal(acc.cpu().numpy(), oracle.ternary_matmul_i64(q_gpu, t_gpu))
+    acc_from_ref = bl.ternary_gemm_i32(torch.from_numpy(ref["q"]).to(DEV), Wp)
+    np.testing.assert_array_equal(acc_from_ref.cpu().numpy(), oracle.ternary_matmul_i64(ref["q"], t_gpu))
+
+    assert_y_close(y.cpu().numpy(), ref["y64"])
+    # the forward is the two stages back to back
+    np.testing.assert_array_equal(y.cpu().numpy(), y2.cpu().numpy())
+
+
+# M <= 16: weight-streaming shape ------------------------------------------
+@pytest.mark.parametrize("M,K,N,bits,had,xdt", [
+    (1, 64, 1, 8, 0, "bf16"),
+    (1, 2560, 200, 8, 0, "bf16"),
+    (3, 320, 47, 4, 0, "fp32"),
+    (16, 1024, 130, 4, 1, "bf16"),
+    (7, 4096, 33, 8, 1, "fp32"),
+    (16, 16384, 64, 4, 1, "bf16"),
+    (2, 192, 31, 8, 1 - 1, "bf16"),
+    (5, 32768, 40, 8, 0, "fp32"),
+])
+def test_parity_decode_shapes(M, K, N, bits, had, xdt):
+    _run_case(M, K, N, bits, had, xdt, seed=M * 7 + K + N, n_out=max(1, K // 100), factor=30.0)
+
+
+# M > 16: prefill tile ------------------------------------------------------
+@pytest.mark.parametrize("M,K,N,bits,had,xdt", [
+    (17, 64, 33, 8, 0, "bf16"),
+    (129, 192, 257, 4, 0, "bf16"),
+    (300, 1024, 260, 8, 1, "bf16"),
+    (256, 256, 256, 4, 1, "fp32"),
+    (130, 2560, 129, 8, 0, "bf16"),
+    (40, 32768, 16, 4, 1, "bf16"),
+    (513, 4096, 384, 4, 1, "bf16"),
+])
+def test_parity_prefill_shapes(M, K, N, bits, had, xdt):
+    _run_case(M, K, N, bits, had, xdt, seed=M + K * 3 + N, n_out=max(1, K // 200), factor=50.0)
+
+
+def test_parity_student_t_inputs():
+    _run_case(16, 2048, 96, 4, 1, "bf16", seed=5, dist="student_t3")
+    _run_case(64, 2048, 96, 4, 1, "bf16", seed=6, dist="student_t3")
+
+
+# Full-size workloads ------------------------------------------------------
+SAMPLE_ROWS = 96
+
+
+@pytest.mark.parametrize("key", workloads.WORKLOAD_ORDER)
+def test_parity_full_workload(key):
+    wl = workloads.WORKLOADS[key]
+    _say(f"workload {key}")
+    case = workloads.make_workload(key, seed=0)
+    x = _to_dev_x(case["x"], wl.x_dtype)
+    W = torch.from_numpy(case["W"]).to(DEV)
+    Wp, alpha = bl.ternarize_weights(W)
+    y = bl.hbitlinear_forward(x, Wp, alpha, wl.bits, wl.hadamard)
+    codes, scales = bl.quantize_activations(x, wl.bits, wl.hadamard)
+    torch.cuda.synchronize()
+    del W
+
+    t_ref, a_ref, p_w = oracle.ternarize(case["W"])
+    assert_packed_match(Wp.cpu().numpy(), t_ref, p_w)
+    assert abs(alpha.item() - a_ref) <= 1e-6 * a_ref
+    del p_w
+
+    x64 = oracle.widen_input(case["x"], wl.x_dtype)
+    xr = oracle.fwht(x64) if wl.hadamard else x64
+    q_ref, s_ref, p_ref = oracle.quantize_activations(xr, wl.bits)
+    del xr, x64
+    q_gpu = codes.cpu().numpy()
+    assert_codes_match(q_gpu, q_ref, p_ref)
+    np.testing.assert_allclose(scales.cpu().numpy(), s_ref, rtol=2e-6)
+    del p_ref
+
+    if wl.M <= SAMPLE_ROWS:
+        rows = np.arange(wl.M)
+    else:
+        rng = np.random.default_rng(1)
+        rows = np.unique(np.concatenate([[0, wl.M - 1], rng.choice(wl.M, SAMPLE_ROWS - 2, replace=False)]))
+    acc_ref, y_ref = oracle.forward_from_codes(q_ref[rows], s_ref[rows], t_ref, a_ref, wl.bits)
+    assert_y_close(y.cpu().numpy()[rows], y_ref)
+    # exact integer product of the GPU's own codes on the sampled rows
+    acc = bl.ternary_gemm_i32(codes[torch.from_numpy(rows).to(DEV)].contiguous(), Wp)
+    t_gpu = oracle.unpack_2bit(Wp.cpu().numpy())
+    np.testing.assert_array_equal(acc.cpu().numpy(), oracle.ternary_matmul_i64(q_gpu[rows], t_gpu))
+
+
+# Edge and degenerate cases ------------------------------------------------
+def test_zero_weights_give_zero_output():
+    _say("zero weights")
+    x = torch.randn(5, 256, device=DEV)
+    W = torch.zeros(40, 256, device=DEV)
+    Wp, alpha = bl.ternarize_weights(W)
+    y = bl.hbitlinear_forward(x, Wp, alpha, 4, 1)
+    torch.cuda.synchronize()
+    assert alpha.item() == 0.0
+    assert np.all(Wp.cpu().numpy() == 0x55)
+    assert torch.count_nonzero(y).item() == 0
+
+
+def test_zero_rows_and_constant_weights():
+    _say("zero rows, constant weights")
+    x = torch.randn(20, 128, device=DEV)
+    x[3] = 0
+    x[17] = 0
+    W = torch.full((24, 128), -0.25, device=DEV)
+    Wp, alpha = bl.ternarize_weights(W)
+    codes, scales = bl.quantize_activations(x, 8, 1)
+    y = bl.hbitlinear_forward(x, Wp, alpha, 8, 1)
+    torch.cuda.synchronize()
+    assert alpha.item() == pytest.approx(0.25)
+    assert np.all(oracle.unpack_2bit(Wp.cpu().numpy()) == -1)
+    assert torch.count_nonzero(codes[3]).item() == 0 and torch.count_nonzero(y[17]).item() == 0
+    assert scales[3].item() == pytest.approx(1e-7)
+
+
+def test_empty_batch_is_noop():
+    _say("empty batch")
+    W = torch.randn(8, 64, device=DEV) * 0.02
+    Wp, alpha = bl.ternarize_weights(W)
+    x = torch.empty(0, 64, device=DEV)
+    y = bl.hbitlinear_forward(x, Wp, alpha, 8, 0)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 8)
+
+
+def test_pack_2bit_matches_oracle():
+    _say("pack_2bit")
+    rng = np.random.default_rng(3)
+    t = rng.integers(-1, 2, size=(77, 640)).astype(np.int8)
+    Wp = bl.pack_2bit(torch.from_numpy(t).to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Wp.cpu().numpy(), oracle.pack_2bit(t))
+
+
+def test_integer_extremes_exact():
+    _say("integer extremes")
+    K = 32768
+    codes = torch.full((18, K), 127, dtype=torch.int8, device=DEV)
+    codes[1] = -128
+    codes[5, ::3] = -128
+    t = np.ones((33, K), dtype=np.int8)
+    t[2] = -1
+    t[7, ::2] = 0
+    Wp = bl.pack_2bit(torch.from_numpy(t).to(DEV))
+    for m in (18, 2):  # prefill tile and the streaming shape
+        acc = bl.ternary_gemm_i32(codes[:m].contiguous(), Wp)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy(),
+                                      oracle.ternary_matmul_i64(codes[:m].cpu().numpy(), t))
+
+
+def test_bitwise_deterministic():
+    _say("determinism")
+    case = workloads.make_case(300, 4096, 200, x_dtype="bf16", n_out=20, factor=20.0, seed=9)
+    x = _to_dev_x(case["x"], "bf16")
+    W = torch.from_numpy(case["W"]).to(DEV)
+    outs = []
+    for _ in range(2):
+        Wp, alpha = bl.ternarize_weights(W)
+        y = bl.hbitlinear_forward(x, Wp, alpha, 4, 1)
+        torch.cuda.synchronize()
+        outs.append((Wp.cpu().numpy(), alpha.item(), y.cpu().numpy()))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    assert outs[0][1] == outs[1][1]
+    np.testing.assert_array_equal(outs[0][2], outs[1][2])
+
+
+def test_module_wrapper():
+    _say("HBitLinear wrapper")
+    case = workloads.make_case(9, 512, 70, x_dtype="fp32", n_out=5, factor=40.0, seed=12)
+    layer = bl.HBitLinear(torch.from_numpy(case["W"]).to(DEV), bits=4, hadamard=True)
+    y = layer(torch.from_numpy(case["x"]).to(DEV))
+    torch.cuda.synchronize()
+    t, a, _ = oracle.ternarize(case["W"])
+    ref = oracle.forward(case["x"], "fp32", t, a, 4, 1)
+    assert_y_close(y.cpu().numpy(), ref["y64"])
