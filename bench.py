@@ -55,37 +55,42 @@ def _copies_for_cold(nbytes):
     return max(1, math.ceil(COLD_BYTES / max(nbytes, 1)) + 1)
 
 
-def _time_loop(torch, fn, steps, warmup):
-    """Average ms per call of fn(i) over `steps` back-to-back calls on the
-    current stream, bracketed by synchronizations."""
+def _capture(torch, fn, calls):
+    """HIP graph of `calls` consecutive calls fn(0) .. fn(calls-1)."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(calls):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_steps(torch, fn, steps, warmup):
+    """ms per call over exactly `steps` calls replayed from one HIP graph.
+
+    `warmup` eager calls and one untimed replay come first; the timed replay
+    is bracketed by synchronizations and a pair of HIP events on the stream
+    the kernels run on. Launching from a graph keeps the host's per-call
+    Python overhead out of the GPU's timeline."""
     for i in range(warmup):
         fn(i)
+    torch.cuda.synchronize()
+    g = _capture(torch, fn, steps)
+    g.replay()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        fn(warmup + i)
+    g.replay()
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
-
-
-def _time_per_launch(torch, fn, launches, warmup):
-    """Average and median ms of single launches, each bracketed by its own
-    pair of HIP events recorded on the launch stream."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(launches)]
-    for i, (a, b) in enumerate(evs):
-        a.record()
-        fn(warmup + i)
-        b.record()
-    torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
-    return float(ms.mean()), float(np.median(ms))
+    ms = start.elapsed_time(end) / steps
+    del g
+    return ms
 
 
 class Prepared:
@@ -109,16 +114,18 @@ class Prepared:
         self.ws = torch.empty((bl.forward_workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.hadamard),),
                               dtype=torch.uint8, device=dev)
         self.codes, self.scales = bl.quantize_activations(self.x, wl.bits, wl.hadamard)
+        self.lin_ws = bl.linear_workspace(wl.M, wl.K, wl.N, dev)
+        self.fused = bl.forward_workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.hadamard) == 0
         torch.cuda.synchronize()
 
     def forward(self, bl, i):
         wl = self.wl
         bl.hbitlinear_forward(self.x, self.Wp[i % self.copies], self.alpha, wl.bits, wl.hadamard,
-                              out=self.y, workspace=self.ws)
+                              out=self.y, workspace=self.ws if self.ws.numel() else None)
 
     def matmul_only(self, bl, i):
         bl.ternary_linear_dequant(self.codes, self.scales, self.Wp[i % self.copies], self.alpha,
-                                  self.wl.bits, out=self.y)
+                                  self.wl.bits, out=self.y, workspace=self.lin_ws)
 
     def free_latent(self):
         self.W = None
@@ -132,13 +139,17 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
     p = Prepared(torch, bl, key, dev)
     wl = p.wl
     u = _work_units(wl)
-    fwd_ms = _time_loop(torch, lambda i: p.forward(bl, i), steps, warmup)
-    mm_mean, mm_med = _time_per_launch(torch, lambda i: p.matmul_only(bl, i), steps, warmup)
+    fwd_ms = _time_steps(torch, lambda i: p.forward(bl, i), steps, warmup)
+    if p.fused:
+        # the forward is one kernel: it is the product kernel
+        mm_mean = fwd_ms
+    else:
+        mm_mean = _time_steps(torch, lambda i: p.matmul_only(bl, i), steps, warmup)
     res = {
         "M": wl.M, "K": wl.K, "N": wl.N, "bits": wl.bits, "hadamard": wl.hadamard,
-        "x_dtype": wl.x_dtype, "cold_weight_copies": p.copies,
+        "x_dtype": wl.x_dtype, "cold_weight_copies": p.copies, "fused_single_kernel": p.fused,
         "forward_us": fwd_ms * 1e3,
-        "matmul_kernel_us_mean": mm_mean * 1e3, "matmul_kernel_us_median": mm_med * 1e3,
+        "matmul_kernel_us_mean": mm_mean * 1e3,
         "forward_weight_GBs": u["weight_bytes"] / (fwd_ms * 1e-3) / 1e9,
         "forward_TOPS": u["ops"] / (fwd_ms * 1e-3) / 1e12,
         "matmul_weight_GBs": u["weight_bytes"] / (mm_mean * 1e-3) / 1e9,
@@ -151,17 +162,23 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
     if key == "prefill_int8_m8192_k4096_n14336" or key == "int4_hadamard_m4_k256_n256":
         # on-device ternarize + pack: two fp32 reads of W plus the packed write
         Wp = p.Wp[0]
-        tern_ms = _time_loop(torch, lambda i: bl.ternarize_weights(p.W, out=Wp, alpha=p.alpha),
-                             max(5, steps // 4), 2)
+        tws = torch.empty((bl.api._lib.load().bitnet_ternarize_workspace_bytes(wl.N, wl.K),),
+                          dtype=torch.uint8, device=dev)
+        tern_ms = _time_steps(torch, lambda i: bl.ternarize_weights(p.W, out=Wp, alpha=p.alpha,
+                                                                    workspace=tws),
+                              max(5, steps // 4), 2)
         tbytes = 2 * wl.N * wl.K * 4 + wl.N * wl.K // 4
         res["ternarize_us"] = tern_ms * 1e3
         res["ternarize_GBs"] = tbytes / (tern_ms * 1e-3) / 1e9
     if key == "int4_hadamard_m4_k256_n256":
         # whole layer including weight preparation, latency only
+        tws1 = torch.empty((bl.api._lib.load().bitnet_ternarize_workspace_bytes(wl.N, wl.K),),
+                           dtype=torch.uint8, device=dev)
+
         def full(i):
-            bl.ternarize_weights(p.W, out=p.Wp[0], alpha=p.alpha)
+            bl.ternarize_weights(p.W, out=p.Wp[0], alpha=p.alpha, workspace=tws1)
             p.forward(bl, 0)
-        res["ternarize_plus_forward_us"] = _time_loop(torch, full, steps, warmup) * 1e3
+        res["ternarize_plus_forward_us"] = _time_steps(torch, full, steps, warmup) * 1e3
     return p, res
 
 
@@ -233,10 +250,14 @@ def main():
         value, unit = head["forward_TOPS"], "TOPS"
         roof = {"bound": "mfma", "achieved": head["matmul_TOPS"], "peak": INT8_MFMA_PEAK_TOPS,
                 "unit": "TFLOP/s", "frac": head["matmul_TOPS"] / INT8_MFMA_PEAK_TOPS}
-    roof["kernel"] = "ternary_gemv_kernel" if decode else "ternary_gemm_kernel"
+    if decode:
+        roof["kernel"] = "fused_decode_kernel" if head["fused_single_kernel"] else "ternary_gemv_kernel"
+    else:
+        roof["kernel"] = "ternary_gemm_kernel"
     roof["algorithmic"] = ("N*K/4 packed weight bytes per launch" if decode
                            else "2*M*N*K int8 ops per launch")
     roof["launch_us_mean"] = head["matmul_kernel_us_mean"]
+    roof["timing"] = "HIP events around one HIP-graph replay of back-to-back launches"
     roof["traffic"] = None
     _log(f"[bench] {key}: forward {head['forward_us']:.2f} us, matmul {head['matmul_kernel_us_mean']:.2f} us")
     del p
@@ -263,6 +284,7 @@ def main():
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "timing": "HIP graph replay of exactly `steps` forward calls, HIP events on the launch stream",
         "config": {"workload": key, "M": wl.M, "K": wl.K, "N": wl.N, "bits": wl.bits,
                    "hadamard": wl.hadamard, "x_dtype": wl.x_dtype,
                    "cold_weight_copies": head["cold_weight_copies"]},

@@ -41,7 +41,8 @@ def _x_dtype(x: torch.Tensor) -> int:
 
 
 def ternarize_weights(W: torch.Tensor, out: Optional[torch.Tensor] = None,
-                      alpha: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                      alpha: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Absmean-ternarize fp32 W [N, K] and pack it (block-64, 2 bits per weight).
 
     Returns (Wpacked uint8 [N, K/4], alpha fp32 [1] on the device)."""
@@ -51,10 +52,11 @@ def ternarize_weights(W: torch.Tensor, out: Optional[torch.Tensor] = None,
         out = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
     if alpha is None:
         alpha = torch.empty((1,), dtype=torch.float32, device=W.device)
-    ws_bytes = _lib.load().bitnet_ternarize_workspace_bytes(N, K)
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
+    if workspace is None:
+        ws_bytes = _lib.load().bitnet_ternarize_workspace_bytes(N, K)
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
     _lib.call("bitnet_ternarize_weights", W.data_ptr(), N, K, out.data_ptr(), alpha.data_ptr(),
-              ws.data_ptr(), ws_bytes, _stream_ptr(W))
+              workspace.data_ptr(), workspace.numel(), _stream_ptr(W))
     return out, alpha
 
 
@@ -86,12 +88,33 @@ def hbitlinear_forward(x: torch.Tensor, Wpacked: torch.Tensor, alpha: torch.Tens
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     need = forward_workspace_bytes(M, K, N, bits, hadamard)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    ws_ptr, ws_len = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
     _lib.call("bitnet_hbitlinear_forward", x.data_ptr(), _x_dtype(x), M, K, Wpacked.data_ptr(), N,
-              alpha.data_ptr(), int(bits), int(hadamard), out.data_ptr(), workspace.data_ptr(),
-              workspace.numel(), _stream_ptr(x))
+              alpha.data_ptr(), int(bits), int(hadamard), out.data_ptr(), ws_ptr, ws_len,
+              _stream_ptr(x))
     return out
+
+
+def linear_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(_lib.load().bitnet_linear_workspace_bytes(M, K, N))
+
+
+def linear_workspace(M: int, K: int, N: int, device) -> Optional[torch.Tensor]:
+    """Zero-filled workspace for ternary_gemm_i32 / ternary_linear_dequant
+    (None when the shape needs none). It can be reused by later calls of the
+    same shape: every call leaves it zeroed again."""
+    need = linear_workspace_bytes(M, K, N)
+    if need == 0:
+        return None
+    return torch.zeros((need,), dtype=torch.uint8, device=device)
+
+
+def _ws_args(workspace: Optional[torch.Tensor]):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel()
 
 
 def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
@@ -110,7 +133,8 @@ def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
 
 
 def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
-                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """acc int32 [M, N] = codes . t^T (exact)."""
     _require(codes, "codes", (torch.int8,), 2)
     _require(Wpacked, "Wpacked", (torch.uint8,), 2)
@@ -120,14 +144,17 @@ def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
         raise ValueError("Wpacked row length does not match K/4")
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=codes.device)
+    if workspace is None:
+        workspace = linear_workspace(M, K, N, codes.device)
     _lib.call("bitnet_ternary_gemm_i32", codes.data_ptr(), M, K, Wpacked.data_ptr(), N,
-              out.data_ptr(), _stream_ptr(codes))
+              out.data_ptr(), *_ws_args(workspace), _stream_ptr(codes))
     return out
 
 
 def ternary_linear_dequant(codes: torch.Tensor, scales: torch.Tensor, Wpacked: torch.Tensor,
                            alpha: torch.Tensor, bits: int,
-                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y fp32 [M, N] = (codes . t^T) * alpha * scales / c."""
     _require(codes, "codes", (torch.int8,), 2)
     _require(scales, "scales", (torch.float32,), 1)
@@ -139,9 +166,11 @@ def ternary_linear_dequant(codes: torch.Tensor, scales: torch.Tensor, Wpacked: t
         raise ValueError("Wpacked row length does not match K/4")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    if workspace is None:
+        workspace = linear_workspace(M, K, N, codes.device)
     _lib.call("bitnet_ternary_linear_dequant", codes.data_ptr(), scales.data_ptr(), M, K,
               Wpacked.data_ptr(), N, alpha.data_ptr(), int(bits), out.data_ptr(),
-              _stream_ptr(codes))
+              *_ws_args(workspace), _stream_ptr(codes))
     return out
 
 
@@ -170,9 +199,9 @@ class HBitLinear:
         M = x.shape[0]
         need = forward_workspace_bytes(M, self.in_features, self.out_features, self.bits,
                                        self.hadamard)
-        if self._ws is None or self._ws.numel() < need or self._ws.device != x.device:
-            self._ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+        if need > 0 and (self._ws is None or self._ws.numel() < need or self._ws.device != x.device):
+            self._ws = torch.empty((need,), dtype=torch.uint8, device=x.device)
         return hbitlinear_forward(x, self.Wpacked, self.alpha, self.bits, self.hadamard,
-                                  workspace=self._ws)
+                                  workspace=self._ws if need > 0 else None)
 
     __call__ = forward

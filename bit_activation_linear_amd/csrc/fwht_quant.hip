@@ -6,208 +6,370 @@
 //   - quantize_act_int8 / Eq. 5: s = max|x| + eps, q = RoundClip(127 x / s, -128, 127).
 //   - quantize_act_int4 / Eq. 6: s = mean|x| + eps, q = RoundClip(sqrt7 x / s, -8, 7).
 //
-// One workgroup per token row. The row is widened to fp32 and staged in LDS
-// (K <= 32768 floats fits the 160 KiB of one CU); it is never rounded to a
-// narrower type and never written back to HBM. The transform's stages commute
-// (H_K is a Kronecker product of H_2 factors), so they are grouped into passes
-// of up to five index bits: each thread pulls a group of 2^nb elements that
-// differ only in those bits into registers, runs the nb butterfly stages
-// there, and writes them back. The 1/sqrt2 of each stage is folded into one
-// multiplier applied with the quantization scale.
+// One workgroup per token row; the row is widened to fp32 and never rounded
+// to a narrower type or written back to HBM. The transform's stages commute
+// (H_K is a Kronecker product of H_2 factors), so they are grouped by index
+// bit:
+//   phase A  each thread loads 16-B vectors (8 consecutive elements) from E/8
+//            places spread K/(E/8) apart, and runs the butterflies of index
+//            bits 0-2 and of the top log2(E)-3 bits in registers;
+//   middle   the remaining index bits (those that tell threads apart) are
+//            covered in chunks of up to log2(E) bits: the row goes through
+//            LDS, each thread pulls the groups of elements that differ only
+//            in the chunk's bits, and runs those butterflies in registers;
+//   last     the final chunk stays in registers: the per-token statistic is
+//            reduced over the workgroup and the codes are written straight
+//            from there.
+// The 1/sqrt2 of every stage is folded into one multiplier applied with the
+// quantization scale. LDS layout: element i at float index i + i/32.
 //
-// LDS layout: element i lives at float index i + i/32 (one pad word per 32),
-// which keeps both the unit-stride and the 32-stride passes free of bank
-// conflicts.
+// Without the transform the row stays in registers end to end.
 #include "kernels.h"
-
-#include <cmath>
 
 namespace bitnet {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr float kEps = 1e-7f;
 
 __device__ __forceinline__ int pad_idx(int i) { return i + (i >> 5); }
 
-template <typename XT>
-struct Loader;
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
 
-template <>
-struct Loader<float> {
-  // 8 consecutive elements.
-  __device__ static void load8(const float* p, float (&v)[8]) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+// bf16 -> fp32 widening is a 16-bit left shift.
+__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+  const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+  const unsigned w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
-};
+}
 
-template <>
-struct Loader<uint16_t> {
-  // 8 consecutive bf16 values: widening is a 16-bit left shift.
-  __device__ static void load8(const uint16_t* p, float (&v)[8]) {
-    const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-    const unsigned w[4] = {a.x, a.y, a.z, a.w};
+// Unnormalized butterflies over all log2(N) index bits of a register array.
+template <int N>
+__device__ __forceinline__ void fwht_regs(float* v) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  }
-};
-
-// One pass of NB butterfly stages over index bits [b0, b0 + NB).
-template <int NB>
-__device__ void fwht_pass(float* lds, int K, int b0) {
-  constexpr int R = 1 << NB;
-  const int groups = K >> NB;
-  const int lo_mask = (1 << b0) - 1;
-  for (int g = threadIdx.x; g < groups; g += kThreads) {
-    const int base = (g & lo_mask) | ((g >> b0) << (b0 + NB));
-    float v[R];
+  for (int h = 1; h < N; h <<= 1) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) v[i] = lds[pad_idx(base + (i << b0))];
-#pragma unroll
-    for (int h = 1; h < R; h <<= 1) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        if ((i & h) == 0) {
-          const float a = v[i], b = v[i + h];
-          v[i] = a + b;
-          v[i + h] = a - b;
-        }
+    for (int i = 0; i < N; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
       }
     }
-#pragma unroll
-    for (int i = 0; i < R; ++i) lds[pad_idx(base + (i << b0))] = v[i];
   }
 }
 
-__device__ inline float wave_max(float v) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+// Butterfly reductions over groups of W lanes (W = 64, or the whole
+// workgroup when it is smaller than a wave, so no lane outside it is read).
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = W / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, W));
   return v;
 }
-__device__ inline float wave_sum(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, W);
   return v;
 }
 
-template <typename XT, int BITS, bool HAD>
-__global__ __launch_bounds__(kThreads) void fwht_quant_kernel(const XT* __restrict__ x, int K,
-                                                              int logK, int8_t* __restrict__ codes,
-                                                              float* __restrict__ scales) {
-  extern __shared__ float lds[];
-  __shared__ float red[4];
-  const int row = blockIdx.x;
-  const XT* xr = x + (size_t)row * (size_t)K;
-
-  // 1. HBM -> fp32 LDS, 16-B (bf16) or 2x16-B (fp32) loads per thread.
-  for (int base = threadIdx.x * 8; base < K; base += kThreads * 8) {
-    float v[8];
-    Loader<XT>::load8(xr + base, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lds[pad_idx(base + e)] = v[e];
-  }
-  __syncthreads();
-
-  // 2. Unnormalized butterflies, five index bits per pass.
-  float norm = 1.0f;
-  if (HAD) {
-    for (int b0 = 0; b0 < logK; b0 += 5) {
-      const int nb = min(5, logK - b0);
-      switch (nb) {
-        case 1: fwht_pass<1>(lds, K, b0); break;
-        case 2: fwht_pass<2>(lds, K, b0); break;
-        case 3: fwht_pass<3>(lds, K, b0); break;
-        case 4: fwht_pass<4>(lds, K, b0); break;
-        default: fwht_pass<5>(lds, K, b0); break;
-      }
-      __syncthreads();
-    }
-    // prod of logK factors 1/sqrt2 = 2^(-logK/2).
-    norm = ldexpf(1.0f, -(logK >> 1));
-    if (logK & 1) norm *= 0.70710678118654752f;
-  }
-
-  // 3. Per-token statistic on the transformed row (fixed-order reduction).
-  const int K4 = K >> 2;
-  float stat = 0.0f;
-  for (int i4 = threadIdx.x; i4 < K4; i4 += kThreads) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = fabsf(lds[pad_idx(4 * i4 + e)]);
-      stat = (BITS == 8) ? fmaxf(stat, a) : stat + a;
-    }
-  }
-  stat = (BITS == 8) ? wave_max(stat) : wave_sum(stat);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = stat;
-  __syncthreads();
-  if (BITS == 8) {
-    stat = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+// Workgroup reduction of the per-thread statistic (fixed order), T threads.
+template <int BITS, int T>
+__device__ __forceinline__ float block_stat(float s, float* red) {
+  constexpr int W = T < 64 ? T : 64;
+  s = (BITS == 8) ? group_max<W>(s) : group_sum<W>(s);
+  constexpr int NW = (T + 63) / 64;
+  if (T >= 64) {
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   } else {
-    stat = ((red[0] + red[1]) + (red[2] + red[3])) / (float)K;
+    // fewer than 64 threads: the whole group is one (partial) wave
+    if (threadIdx.x == 0) red[0] = s;
   }
-  // s is the scale of the normalized row: stat(H x) = norm * stat(unnormalized).
-  const float s = stat * norm + kEps;
-  const float c = (BITS == 8) ? 127.0f : 2.6457513110645906f;
-  const float mult = (c * norm) / s;
-  const float lo = (BITS == 8) ? -128.0f : -8.0f;
-  const float hi = (BITS == 8) ? 127.0f : 7.0f;
-  if (threadIdx.x == 0) scales[row] = s;
-
-  // 4. Quantize with round-half-even and store four codes per thread.
-  int8_t* cr = codes + (size_t)row * (size_t)K;
-  for (int i4 = threadIdx.x; i4 < K4; i4 += kThreads) {
-    unsigned word = 0;
+  __syncthreads();
+  float r = red[0];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float q = __builtin_rintf(lds[pad_idx(4 * i4 + e)] * mult);
-      q = fminf(fmaxf(q, lo), hi);
-      word |= ((unsigned)(int)q & 0xFFu) << (8 * e);
+  for (int w = 1; w < NW; ++w) r = (BITS == 8) ? fmaxf(r, red[w]) : r + red[w];
+  return r;
+}
+
+__device__ __forceinline__ float quant_clip(float v, float mult, float lo, float hi) {
+  return fminf(fmaxf(__builtin_rintf(v * mult), lo), hi);
+}
+
+template <int BITS>
+struct QConst {
+  static constexpr float c = (BITS == 8) ? 127.0f : 2.6457513110645906f;
+  static constexpr float lo = (BITS == 8) ? -128.0f : -8.0f;
+  static constexpr float hi = (BITS == 8) ? 127.0f : 7.0f;
+};
+
+// One middle chunk: butterflies over index bits [B0, B0 + NB). Thread t owns
+// the groups g = t + T*gi (gi < E >> NB); a group is the 2^NB elements
+// base(g) + (j << B0). LAST: quantize from registers and store the codes.
+template <int L, int LT, int B0, int NB, bool LAST, int BITS>
+__device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_t* crow,
+                                         float* scale_out) {
+  constexpr int T = 1 << LT;
+  constexpr int E = 1 << (L - LT);
+  constexpr int R = 1 << NB;
+  constexpr int G = E / R;
+  const int t = threadIdx.x;
+  int base[G];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const int g = t + T * gi;
+    base[gi] = (g & ((1 << B0) - 1)) | ((g >> B0) << (B0 + NB));
+  }
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[gi * R + j] = lds[pad_idx(base[gi] + (j << B0))];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) fwht_regs<R>(v + gi * R);
+
+  if (!LAST) {
+    // A thread writes back exactly the elements it read, so only the next
+    // pass needs the barrier.
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int j = 0; j < R; ++j) lds[pad_idx(base[gi] + (j << B0))] = v[gi * R + j];
+    __syncthreads();
+    return;
+  }
+
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) s = (BITS == 8) ? fmaxf(s, fabsf(v[i])) : s + fabsf(v[i]);
+  float stat = block_stat<BITS, T>(s, red);
+  // prod of L factors 1/sqrt2 = 2^(-L/2)
+  float norm = __builtin_ldexpf(1.0f, -(L >> 1));
+  if (L & 1) norm *= 0.70710678118654752f;
+  if (BITS == 4) stat = stat / (float)(1 << L);
+  const float sc = stat * norm + kEps;
+  const float mult = (QConst<BITS>::c * norm) / sc;
+  if (t == 0) *scale_out = sc;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float q = quant_clip(v[gi * R + j], mult, QConst<BITS>::lo, QConst<BITS>::hi);
+      crow[base[gi] + (j << B0)] = (int8_t)(int)q;
     }
-    reinterpret_cast<unsigned*>(cr)[i4] = word;
+}
+
+template <int A, int B>
+struct Min {
+  static constexpr int value = A < B ? A : B;
+};
+
+template <typename XT, int BITS, int L, int LT>
+__global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restrict__ x,
+                                                             int8_t* __restrict__ codes,
+                                                             float* __restrict__ scales,
+                                                             unsigned* __restrict__ clear,
+                                                             int n_clear) {
+  constexpr int K = 1 << L;
+  constexpr int T = 1 << LT;
+  constexpr int E = K / T;
+  constexpr int e = L - LT;
+  static_assert(E >= 8, "at least one 8-element vector per thread");
+  extern __shared__ float lds[];
+  __shared__ float red[(T + 63) / 64];
+  const int t = threadIdx.x;
+  const int row = blockIdx.x;
+  if (row == 0) {
+    for (int i = t; i < n_clear; i += T) clear[i] = 0u;
+  }
+  const XT* xr = x + (size_t)row * K;
+  int8_t* crow = codes + (size_t)row * K;
+
+  // Phase A: vectors of 8 from E/8 places, butterflies of the register bits.
+  float v[E];
+#pragma unroll
+  for (int rh = 0; rh < E / 8; ++rh) load8(xr + 8 * t + 8 * T * rh, v + 8 * rh);
+  fwht_regs<E>(v);
+#pragma unroll
+  for (int rh = 0; rh < E / 8; ++rh)
+#pragma unroll
+    for (int lo = 0; lo < 8; ++lo) lds[pad_idx(8 * t + 8 * T * rh + lo)] = v[8 * rh + lo];
+  __syncthreads();
+
+  // Middle bits [3, 3 + LT) in chunks of up to e bits.
+  constexpr int NB0 = Min<e, LT>::value;
+  constexpr int R1 = LT - NB0;
+  constexpr int NB1 = Min<e, (R1 > 0 ? R1 : 1)>::value;
+  constexpr int R2 = R1 - NB1;
+  constexpr int NB2 = Min<e, (R2 > 0 ? R2 : 1)>::value;
+  constexpr int R3 = R2 - NB2;
+  constexpr int NB3 = Min<e, (R3 > 0 ? R3 : 1)>::value;
+  static_assert(R3 <= NB3, "at most four middle chunks");
+  float* sc = scales + row;
+  if constexpr (R1 <= 0) {
+    mid_pass<L, LT, 3, NB0, true, BITS>(v, lds, red, crow, sc);
+  } else {
+    mid_pass<L, LT, 3, NB0, false, BITS>(v, lds, red, crow, sc);
+    if constexpr (R2 <= 0) {
+      mid_pass<L, LT, 3 + NB0, NB1, true, BITS>(v, lds, red, crow, sc);
+    } else {
+      mid_pass<L, LT, 3 + NB0, NB1, false, BITS>(v, lds, red, crow, sc);
+      if constexpr (R3 <= 0) {
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS>(v, lds, red, crow, sc);
+      } else {
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS>(v, lds, red, crow, sc);
+        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS>(v, lds, red, crow, sc);
+      }
+    }
   }
 }
 
-template <typename XT, int BITS, bool HAD>
-hipError_t launch_one(const void* x, int64_t M, int K, int logK, int8_t* codes, float* scales,
-                      hipStream_t stream) {
-  const size_t lds_bytes = (size_t)(K + K / 32) * sizeof(float);
-  auto kern = fwht_quant_kernel<XT, BITS, HAD>;
-  if (lds_bytes > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds_bytes);
-    if (e != hipSuccess) return e;
+// No transform: thread t owns the 8-element vectors at 8t + 2048c, c < CH.
+template <typename XT, int BITS, int CH>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ x, int K,
+                                                         int8_t* __restrict__ codes,
+                                                         float* __restrict__ scales,
+                                                         unsigned* __restrict__ clear,
+                                                         int n_clear) {
+  constexpr int T = 256;
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  const int row = blockIdx.x;
+  if (row == 0) {
+    for (int i = t; i < n_clear; i += T) clear[i] = 0u;
   }
-  kern<<<dim3((unsigned)M), dim3(kThreads), lds_bytes, stream>>>(
-      reinterpret_cast<const XT*>(x), K, logK, codes, scales);
+  const XT* xr = x + (size_t)row * K;
+  float v[CH][8];
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = 8 * t + 8 * T * c;
+    if (idx < K) {
+      load8(xr + idx, v[c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = (BITS == 8) ? fmaxf(s, fabsf(v[c][e])) : s + fabsf(v[c][e]);
+  }
+  float stat = block_stat<BITS, T>(s, red);
+  if (BITS == 4) stat = stat / (float)K;
+  const float sc = stat + kEps;
+  const float mult = QConst<BITS>::c / sc;
+  if (t == 0) scales[row] = sc;
+  int8_t* crow = codes + (size_t)row * K;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = 8 * t + 8 * T * c;
+    if (idx < K) {
+      unsigned w[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float q = quant_clip(v[c][e], mult, QConst<BITS>::lo, QConst<BITS>::hi);
+        w[e >> 2] |= ((unsigned)(int)q & 0xFFu) << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(crow + idx) = make_uint2(w[0], w[1]);
+    }
+  }
+}
+
+template <typename Kern>
+hipError_t ensure_lds(Kern kern, size_t bytes) {
+  if (bytes <= 48 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <typename XT, int BITS, int L, int LT>
+hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, unsigned* clear,
+                       int n_clear, hipStream_t stream) {
+  constexpr int K = 1 << L;
+  const size_t lds = (size_t)(K + K / 32) * sizeof(float);
+  auto kern = fwht_quant_kernel<XT, BITS, L, LT>;
+  hipError_t e = ensure_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  kern<<<dim3((unsigned)M), dim3(1 << LT), lds, stream>>>(reinterpret_cast<const XT*>(x), codes,
+                                                          scales, clear, n_clear);
   return hipGetLastError();
 }
 
-template <typename XT>
-hipError_t launch_dtype(const void* x, int64_t M, int K, int logK, int bits, int hadamard,
-                        int8_t* codes, float* scales, hipStream_t stream) {
-  if (bits == 8) {
-    return hadamard ? launch_one<XT, 8, true>(x, M, K, logK, codes, scales, stream)
-                    : launch_one<XT, 8, false>(x, M, K, logK, codes, scales, stream);
+// Threads per row: 256 for batches (many rows in flight), 1024 for a
+// handful of long rows (decode), never fewer than 8 elements per thread.
+template <typename XT, int BITS, int L>
+hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales, unsigned* clear,
+                         int n_clear, hipStream_t stream) {
+  constexpr int LT_BATCH = (L - 3 < 8) ? L - 3 : 8;
+  constexpr int LT_FEW = (L - 3 < 10) ? L - 3 : 10;
+  if (M <= 64 && LT_FEW != LT_BATCH)
+    return launch_fwht<XT, BITS, L, LT_FEW>(x, M, codes, scales, clear, n_clear, stream);
+  return launch_fwht<XT, BITS, L, LT_BATCH>(x, M, codes, scales, clear, n_clear, stream);
+}
+
+template <typename XT, int BITS>
+hipError_t launch_had(const void* x, int64_t M, int K, int8_t* codes, float* scales,
+                      unsigned* clear, int n_clear, hipStream_t stream) {
+  switch (K) {
+    case 1 << 6: return launch_fwht_l<XT, BITS, 6>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 7: return launch_fwht_l<XT, BITS, 7>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 8: return launch_fwht_l<XT, BITS, 8>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 9: return launch_fwht_l<XT, BITS, 9>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 10: return launch_fwht_l<XT, BITS, 10>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 11: return launch_fwht_l<XT, BITS, 11>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 12: return launch_fwht_l<XT, BITS, 12>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 13: return launch_fwht_l<XT, BITS, 13>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 14: return launch_fwht_l<XT, BITS, 14>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 15: return launch_fwht_l<XT, BITS, 15>(x, M, codes, scales, clear, n_clear, stream);
+    default: return hipErrorInvalidValue;
   }
-  return hadamard ? launch_one<XT, 4, true>(x, M, K, logK, codes, scales, stream)
-                  : launch_one<XT, 4, false>(x, M, K, logK, codes, scales, stream);
+}
+
+template <typename XT, int BITS, int CH>
+hipError_t launch_rows_ch(const void* x, int64_t M, int K, int8_t* codes, float* scales,
+                          unsigned* clear, int n_clear, hipStream_t stream) {
+  quant_rows_kernel<XT, BITS, CH><<<dim3((unsigned)M), dim3(256), 0, stream>>>(
+      reinterpret_cast<const XT*>(x), K, codes, scales, clear, n_clear);
+  return hipGetLastError();
+}
+
+template <typename XT, int BITS>
+hipError_t launch_rows(const void* x, int64_t M, int K, int8_t* codes, float* scales,
+                       unsigned* clear, int n_clear, hipStream_t stream) {
+  const int ch = (K + 2047) / 2048;
+  if (ch <= 1) return launch_rows_ch<XT, BITS, 1>(x, M, K, codes, scales, clear, n_clear, stream);
+  if (ch <= 2) return launch_rows_ch<XT, BITS, 2>(x, M, K, codes, scales, clear, n_clear, stream);
+  if (ch <= 4) return launch_rows_ch<XT, BITS, 4>(x, M, K, codes, scales, clear, n_clear, stream);
+  if (ch <= 8) return launch_rows_ch<XT, BITS, 8>(x, M, K, codes, scales, clear, n_clear, stream);
+  return launch_rows_ch<XT, BITS, 16>(x, M, K, codes, scales, clear, n_clear, stream);
+}
+
+template <typename XT>
+hipError_t launch_dtype(const void* x, int64_t M, int K, int bits, int hadamard, int8_t* codes,
+                        float* scales, unsigned* clear, int n_clear, hipStream_t stream) {
+  if (hadamard) {
+    return bits == 8 ? launch_had<XT, 8>(x, M, K, codes, scales, clear, n_clear, stream)
+                     : launch_had<XT, 4>(x, M, K, codes, scales, clear, n_clear, stream);
+  }
+  return bits == 8 ? launch_rows<XT, 8>(x, M, K, codes, scales, clear, n_clear, stream)
+                   : launch_rows<XT, 4>(x, M, K, codes, scales, clear, n_clear, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
-                           int8_t* codes, float* scales, hipStream_t stream) {
-  int logK = 0;
-  while ((1 << logK) < K) ++logK;
+                           int8_t* codes, float* scales, unsigned* clear, int n_clear,
+                           hipStream_t stream) {
   if (x_dtype == 1)
-    return launch_dtype<uint16_t>(x, M, K, logK, bits, hadamard, codes, scales, stream);
-  return launch_dtype<float>(x, M, K, logK, bits, hadamard, codes, scales, stream);
+    return launch_dtype<uint16_t>(x, M, K, bits, hadamard, codes, scales, clear, n_clear, stream);
+  return launch_dtype<float>(x, M, K, bits, hadamard, codes, scales, clear, n_clear, stream);
 }
 
 }  // namespace bitnet

@@ -102,7 +102,10 @@ bitnet_status bitnet_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* W
 /* Forward                                                                   */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of workspace bitnet_hbitlinear_forward needs (codes, scales). */
+/* Bytes of workspace bitnet_hbitlinear_forward needs: the int8 codes and
+ * scales of the batch, plus split-K partials for long rows at M <= 16. It is
+ * 0 when the forward runs as a single fused kernel (M <= 16, hadamard = 0,
+ * M*K <= 16384, K <= 4096); ws may then be NULL. Returns 0 for invalid sizes. */
 size_t bitnet_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits, int hadamard);
 
 /* H-BitLinear forward (engine page, HBitLinear.forward after its RMSNorm;
@@ -115,7 +118,8 @@ size_t bitnet_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits,
  *   x        [M, K] in x_dtype (BITNET_F32 or BITNET_BF16).
  *   Wpacked  uint8 [N, K/4], block-64 layout; alpha: one fp32 on the device.
  *   y        fp32 [M, N]. Written.
- *   ws       workspace of at least bitnet_forward_workspace_bytes(...).
+ *   ws       workspace of at least bitnet_forward_workspace_bytes(...); its
+ *            contents on entry do not matter.
  * Requires K % 64 == 0, K <= BITNET_MAX_K, and a power-of-two K when
  * hadamard != 0. */
 bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int64_t M, int64_t K,
@@ -124,7 +128,9 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
                                         size_t ws_bytes, hipStream_t stream);
 
 /* The two stages of the forward, exposed for inspection and timing. They run
- * the same kernels as bitnet_hbitlinear_forward. */
+ * the kernels of the forward's two-launch path; where the forward fuses both
+ * stages into one kernel (see bitnet_forward_workspace_bytes) that kernel
+ * takes the same quantization and product steps in the same precision. */
 
 /* Transform + per-token quantization only (Eq. 3-6): writes int8 codes
  * [M, K] and fp32 scales s [M] (s = stat + eps, the value the dequantization
@@ -133,18 +139,27 @@ bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, i
                                           int64_t K, int bits, int hadamard, int8_t* codes,
                                           float* scales, hipStream_t stream);
 
-/* Exact integer product only: acc[m, n] = sum_k codes[m, k] * t[n, k], int32.
- * codes: int8 [M, K] with values in [-128, 127]. Requires K % 64 == 0. */
-bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
-                                      const uint8_t* Wpacked, int64_t N, int32_t* acc,
-                                      hipStream_t stream);
+/* Bytes of workspace the two product-only entry points below need (split-K
+ * partials and arrival counters at M <= 16 with long rows; often 0, and ws
+ * may then be NULL). This workspace must be zero-filled before its first use;
+ * every call leaves its counters zero again. Returns 0 for invalid sizes. */
+size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
-/* Integer product with the fused dequantization epilogue:
- * y = (codes . t^T) * alpha * scales[m] / c, c = 127 (bits 8) or sqrt 7 (bits 4). */
+/* Exact integer product only: acc[m, n] = sum_k codes[m, k] * t[n, k], int32.
+ * codes: int8 [M, K] with values in [-128, 127]. Requires K % 64 == 0 and
+ * K <= BITNET_MAX_K. */
+bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
+                                      const uint8_t* Wpacked, int64_t N, int32_t* acc, void* ws,
+                                      size_t ws_bytes, hipStream_t stream);
+
+/* Integer product with the fused dequantization epilogue (engine page,
+ * HBitLinear.forward's F.linear of the two dequantized operands, rewritten by
+ * linearity): y = (codes . t^T) * alpha * scales[m] / c, c = 127 (bits 8) or
+ * sqrt 7 (bits 4). */
 bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* scales, int64_t M,
                                             int64_t K, const uint8_t* Wpacked, int64_t N,
-                                            const float* alpha, int bits, float* y,
-                                            hipStream_t stream);
+                                            const float* alpha, int bits, float* y, void* ws,
+                                            size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

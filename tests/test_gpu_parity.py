@@ -63,8 +63,14 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     np.testing.assert_array_equal(acc_from_ref.cpu().numpy(), oracle.ternary_matmul_i64(ref["q"], t_gpu))
 
     assert_y_close(y.cpu().numpy(), ref["y64"])
-    # the forward is the two stages back to back
-    np.testing.assert_array_equal(y.cpu().numpy(), y2.cpu().numpy())
+    # The forward is the two stages back to back. Where it runs as one fused
+    # kernel the int4 absmean is summed in another order, so an ulp of the
+    # scale may move a code that sits on a rounding boundary.
+    fused = bl.forward_workspace_bytes(M, K, N, bits, had) == 0
+    if fused and bits == 4:
+        assert_y_close(y.cpu().numpy(), y2.cpu().numpy().astype(np.float64), what="fused vs staged")
+    else:
+        np.testing.assert_array_equal(y.cpu().numpy(), y2.cpu().numpy())
 
 
 # M <= 16: weight-streaming shape ------------------------------------------
@@ -75,8 +81,14 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     (16, 1024, 130, 4, 1, "bf16"),
     (7, 4096, 33, 8, 1, "fp32"),
     (16, 16384, 64, 4, 1, "bf16"),
-    (2, 192, 31, 8, 1 - 1, "bf16"),
+    (2, 192, 31, 8, 0, "bf16"),
     (5, 32768, 40, 8, 0, "fp32"),
+    (1, 32768, 100, 8, 0, "bf16"),     # K split over 8 workgroups
+    (2, 8192, 70, 4, 0, "bf16"),       # K split over 2, not fused
+    (4, 4096, 90, 4, 0, "bf16"),       # fused, int4
+    (16, 1024, 48, 4, 0, "fp32"),      # fused, full 16 rows
+    (16, 4096, 150, 8, 0, "bf16"),     # not fused (M*K too big), 4 column tiles
+    (9, 2048, 33, 4, 1, "fp32"),
 ])
 def test_parity_decode_shapes(M, K, N, bits, had, xdt):
     _run_case(M, K, N, bits, had, xdt, seed=M * 7 + K + N, n_out=max(1, K // 100), factor=30.0)
@@ -224,6 +236,60 @@ def test_bitwise_deterministic():
     np.testing.assert_array_equal(outs[0][0], outs[1][0])
     assert outs[0][1] == outs[1][1]
     np.testing.assert_array_equal(outs[0][2], outs[1][2])
+
+
+def test_split_k_counters_reset_between_calls():
+    _say("split-K counter reuse")
+    rng = np.random.default_rng(21)
+    M, K, N = 16, 16384, 200
+    q = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    Wp = bl.pack_2bit(torch.from_numpy(t).to(DEV))
+    codes = torch.from_numpy(q).to(DEV)
+    ws = bl.linear_workspace(M, K, N, DEV)
+    assert ws is not None
+    ref = oracle.ternary_matmul_i64(q, t)
+    for _ in range(3):
+        acc = bl.ternary_gemm_i32(codes, Wp, workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy(), ref)
+    # the arrival counters are back at zero after every call
+    counters_off = bl.linear_workspace_bytes(M, K, N) - 256
+    assert torch.count_nonzero(ws[counters_off:]).item() == 0
+
+
+@pytest.mark.parametrize("M,K,N,bits,had", [
+    (1, 2560, 700, 8, 0),      # one fused kernel
+    (16, 16384, 300, 4, 1),    # transform + split-K product
+    (200, 1024, 300, 4, 1),    # prefill tile
+])
+def test_graph_replay_matches_eager(M, K, N, bits, had):
+    _say(f"graph replay M={M} K={K} N={N}")
+    case = workloads.make_case(M, K, N, x_dtype="bf16", n_out=8, factor=30.0, seed=M + N)
+    x = _to_dev_x(case["x"], "bf16")
+    Wp, alpha = bl.ternarize_weights(torch.from_numpy(case["W"]).to(DEV))
+    need = bl.forward_workspace_bytes(M, K, N, bits, had)
+    ws = torch.empty((need,), dtype=torch.uint8, device=DEV) if need else None
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    bl.hbitlinear_forward(x, Wp, alpha, bits, had, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            bl.hbitlinear_forward(x, Wp, alpha, bits, had, out=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        y.fill_(float("nan"))
+        # unrelated eager work between replays
+        junk = torch.randn(64, 64, device=DEV) @ torch.randn(64, 64, device=DEV)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), eager.cpu().numpy())
+        del junk
 
 
 def test_module_wrapper():
