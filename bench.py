@@ -114,7 +114,6 @@ class Prepared:
         self.ws = torch.empty((bl.forward_workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.hadamard),),
                               dtype=torch.uint8, device=dev)
         self.codes, self.scales = bl.quantize_activations(self.x, wl.bits, wl.hadamard)
-        self.lin_ws = bl.linear_workspace(wl.M, wl.K, wl.N, dev)
         self.fused = bl.forward_workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.hadamard) == 0
         torch.cuda.synchronize()
 
@@ -125,7 +124,7 @@ class Prepared:
 
     def matmul_only(self, bl, i):
         bl.ternary_linear_dequant(self.codes, self.scales, self.Wp[i % self.copies], self.alpha,
-                                  self.wl.bits, out=self.y, workspace=self.lin_ws)
+                                  self.wl.bits, out=self.y)
 
     def free_latent(self):
         self.W = None

@@ -10,8 +10,6 @@ from .api import (  # noqa: F401
     HBitLinear,
     forward_workspace_bytes,
     hbitlinear_forward,
-    linear_workspace,
-    linear_workspace_bytes,
     pack_2bit,
     quantize_activations,
     ternarize_weights,

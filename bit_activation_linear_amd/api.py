@@ -97,26 +97,6 @@ def hbitlinear_forward(x: torch.Tensor, Wpacked: torch.Tensor, alpha: torch.Tens
     return out
 
 
-def linear_workspace_bytes(M: int, K: int, N: int) -> int:
-    return int(_lib.load().bitnet_linear_workspace_bytes(M, K, N))
-
-
-def linear_workspace(M: int, K: int, N: int, device) -> Optional[torch.Tensor]:
-    """Zero-filled workspace for ternary_gemm_i32 / ternary_linear_dequant
-    (None when the shape needs none). It can be reused by later calls of the
-    same shape: every call leaves it zeroed again."""
-    need = linear_workspace_bytes(M, K, N)
-    if need == 0:
-        return None
-    return torch.zeros((need,), dtype=torch.uint8, device=device)
-
-
-def _ws_args(workspace: Optional[torch.Tensor]):
-    if workspace is None:
-        return None, 0
-    return workspace.data_ptr(), workspace.numel()
-
-
 def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
                          codes: Optional[torch.Tensor] = None,
                          scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -133,8 +113,7 @@ def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
 
 
 def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
-                     out: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """acc int32 [M, N] = codes . t^T (exact)."""
     _require(codes, "codes", (torch.int8,), 2)
     _require(Wpacked, "Wpacked", (torch.uint8,), 2)
@@ -144,17 +123,14 @@ def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
         raise ValueError("Wpacked row length does not match K/4")
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=codes.device)
-    if workspace is None:
-        workspace = linear_workspace(M, K, N, codes.device)
     _lib.call("bitnet_ternary_gemm_i32", codes.data_ptr(), M, K, Wpacked.data_ptr(), N,
-              out.data_ptr(), *_ws_args(workspace), _stream_ptr(codes))
+              out.data_ptr(), _stream_ptr(codes))
     return out
 
 
 def ternary_linear_dequant(codes: torch.Tensor, scales: torch.Tensor, Wpacked: torch.Tensor,
                            alpha: torch.Tensor, bits: int,
-                           out: Optional[torch.Tensor] = None,
-                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y fp32 [M, N] = (codes . t^T) * alpha * scales / c."""
     _require(codes, "codes", (torch.int8,), 2)
     _require(scales, "scales", (torch.float32,), 1)
@@ -166,11 +142,9 @@ def ternary_linear_dequant(codes: torch.Tensor, scales: torch.Tensor, Wpacked: t
         raise ValueError("Wpacked row length does not match K/4")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
-    if workspace is None:
-        workspace = linear_workspace(M, K, N, codes.device)
     _lib.call("bitnet_ternary_linear_dequant", codes.data_ptr(), scales.data_ptr(), M, K,
               Wpacked.data_ptr(), N, alpha.data_ptr(), int(bits), out.data_ptr(),
-              *_ws_args(workspace), _stream_ptr(codes))
+              _stream_ptr(codes))
     return out
 
 

@@ -70,35 +70,12 @@ bitnet_status check_quant_args(const char* fn, int64_t K, int bits, int hadamard
   return BITNET_OK;
 }
 
-// Forward workspace: [codes M*K][scales 4M][split-K partials][split-K counters],
-// each part 256-B aligned. The fused decode kernel needs none of it.
+// Forward workspace: [codes M*K][scales 4M], each part 256-B aligned. The
+// fused decode kernel needs none of it.
 struct ForwardWorkspace {
   int8_t* codes;
   float* scales;
-  int32_t* partials;
-  unsigned* counters;
-  int n_counters;
 };
-
-size_t linear_ws_bytes(int64_t M, int64_t K, int64_t N) {
-  if (M > bitnet::kDecodeMaxM || M <= 0 || N <= 0) return 0;
-  const bitnet::GemvPlan p = bitnet::plan_gemv(M, K, N, false, false);
-  return bitnet::gemv_partials_bytes(p, M, N) + bitnet::gemv_counters_bytes(p);
-}
-
-void carve_linear(void* ws, int64_t M, int64_t K, int64_t N, int32_t** partials,
-                  unsigned** counters, int* n_counters) {
-  *partials = nullptr;
-  *counters = nullptr;
-  *n_counters = 0;
-  if (M > bitnet::kDecodeMaxM || M <= 0 || N <= 0) return;
-  const bitnet::GemvPlan p = bitnet::plan_gemv(M, K, N, false, false);
-  if (p.kz <= 1) return;
-  char* base = static_cast<char*>(ws);
-  *partials = reinterpret_cast<int32_t*>(base);
-  *counters = reinterpret_cast<unsigned*>(base + bitnet::gemv_partials_bytes(p, M, N));
-  *n_counters = p.col_groups;
-}
 
 bool forward_is_fused(int64_t M, int64_t K, int64_t N, int hadamard) {
   if (M > bitnet::kDecodeMaxM) return false;
@@ -108,29 +85,15 @@ bool forward_is_fused(int64_t M, int64_t K, int64_t N, int hadamard) {
 size_t forward_ws_bytes(int64_t M, int64_t K, int64_t N, int hadamard) {
   if (M <= 0 || N <= 0) return 0;
   if (forward_is_fused(M, K, N, hadamard)) return 0;
-  return round_up((size_t)M * (size_t)K) + round_up((size_t)M * sizeof(float)) +
-         linear_ws_bytes(M, K, N);
+  return round_up((size_t)M * (size_t)K) + round_up((size_t)M * sizeof(float));
 }
 
-ForwardWorkspace carve_forward(void* ws, int64_t M, int64_t K, int64_t N) {
+ForwardWorkspace carve_forward(void* ws, int64_t M, int64_t K) {
   char* base = static_cast<char*>(ws);
   ForwardWorkspace w;
   w.codes = reinterpret_cast<int8_t*>(base);
   w.scales = reinterpret_cast<float*>(base + round_up((size_t)M * (size_t)K));
-  char* rest = base + round_up((size_t)M * (size_t)K) + round_up((size_t)M * sizeof(float));
-  carve_linear(rest, M, K, N, &w.partials, &w.counters, &w.n_counters);
   return w;
-}
-
-bitnet_status check_linear_ws(const char* fn, int64_t M, int64_t K, int64_t N, void* ws,
-                              size_t ws_bytes) {
-  const size_t need = linear_ws_bytes(M, K, N);
-  if (need == 0) return BITNET_OK;
-  if (!ws || ws_bytes < need)
-    return fail(BITNET_ERR_INVALID_ARG, "%s: workspace %zu B < required %zu B", fn,
-                ws ? ws_bytes : (size_t)0, need);
-  if (!aligned(ws, 16)) return fail(BITNET_ERR_ALIGN, "%s: misaligned workspace", fn);
-  return BITNET_OK;
 }
 
 }  // namespace
@@ -185,11 +148,6 @@ size_t bitnet_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits,
   return forward_ws_bytes(M, K, N, hadamard);
 }
 
-size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
-  if (M < 0 || K <= 0 || N < 0 || K % 64 != 0) return 0;
-  return linear_ws_bytes(M, K, N);
-}
-
 bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, int64_t M,
                                           int64_t K, int bits, int hadamard, int8_t* codes,
                                           float* scales, hipStream_t stream) {
@@ -201,13 +159,13 @@ bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, i
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
   return hip_status(bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, codes,
-                                            scales, nullptr, 0, stream),
+                                            scales, stream),
                     fn);
 }
 
 bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
-                                      const uint8_t* Wpacked, int64_t N, int32_t* acc, void* ws,
-                                      size_t ws_bytes, hipStream_t stream) {
+                                      const uint8_t* Wpacked, int64_t N, int32_t* acc,
+                                      hipStream_t stream) {
   const char* fn = "bitnet_ternary_gemm_i32";
   if (bitnet_status st = check_dims(fn, M, K, N)) return st;
   if (K > BITNET_MAX_K)
@@ -217,20 +175,15 @@ bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
   if (!codes || !Wpacked || !acc) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(codes, 16) || !aligned(Wpacked, 16) || !aligned(acc, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
-  if (bitnet_status st = check_linear_ws(fn, M, K, N, ws, ws_bytes)) return st;
-  int32_t* partials;
-  unsigned* counters;
-  int n_counters;
-  carve_linear(ws, M, K, N, &partials, &counters, &n_counters);
   return hip_status(bitnet::launch_ternary_matmul(codes, nullptr, M, (int)K, Wpacked, N, nullptr,
-                                                  8, nullptr, acc, partials, counters, stream),
+                                                  8, nullptr, acc, stream),
                     fn);
 }
 
 bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* scales, int64_t M,
                                             int64_t K, const uint8_t* Wpacked, int64_t N,
-                                            const float* alpha, int bits, float* y, void* ws,
-                                            size_t ws_bytes, hipStream_t stream) {
+                                            const float* alpha, int bits, float* y,
+                                            hipStream_t stream) {
   const char* fn = "bitnet_ternary_linear_dequant";
   if (bitnet_status st = check_dims(fn, M, K, N)) return st;
   if (bits != 4 && bits != 8) return fail(BITNET_ERR_BAD_BITS, "%s: bits=%d must be 4 or 8", fn, bits);
@@ -243,13 +196,8 @@ bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* sc
   if (!aligned(codes, 16) || !aligned(Wpacked, 16) || !aligned(y, 4) || !aligned(scales, 4) ||
       !aligned(alpha, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
-  if (bitnet_status st = check_linear_ws(fn, M, K, N, ws, ws_bytes)) return st;
-  int32_t* partials;
-  unsigned* counters;
-  int n_counters;
-  carve_linear(ws, M, K, N, &partials, &counters, &n_counters);
   return hip_status(bitnet::launch_ternary_matmul(codes, scales, M, (int)K, Wpacked, N, alpha,
-                                                  bits, y, nullptr, partials, counters, stream),
+                                                  bits, y, nullptr, stream),
                     fn);
 }
 
@@ -275,12 +223,12 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
                                                   bits, y, stream),
                       fn);
   }
-  const ForwardWorkspace w = carve_forward(ws, M, K, N);
+  const ForwardWorkspace w = carve_forward(ws, M, K);
   hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
-                                         w.scales, w.counters, w.n_counters, stream);
+                                         w.scales, stream);
   if (e != hipSuccess) return hip_status(e, fn);
   e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
-                                    nullptr, w.partials, w.counters, stream);
+                                    nullptr, stream);
   return hip_status(e, fn);
 }
 

@@ -175,9 +175,7 @@ struct Min {
 template <typename XT, int BITS, int L, int LT>
 __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restrict__ x,
                                                              int8_t* __restrict__ codes,
-                                                             float* __restrict__ scales,
-                                                             unsigned* __restrict__ clear,
-                                                             int n_clear) {
+                                                             float* __restrict__ scales) {
   constexpr int K = 1 << L;
   constexpr int T = 1 << LT;
   constexpr int E = K / T;
@@ -187,9 +185,6 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restric
   __shared__ float red[(T + 63) / 64];
   const int t = threadIdx.x;
   const int row = blockIdx.x;
-  if (row == 0) {
-    for (int i = t; i < n_clear; i += T) clear[i] = 0u;
-  }
   const XT* xr = x + (size_t)row * K;
   int8_t* crow = codes + (size_t)row * K;
 
@@ -236,16 +231,11 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restric
 template <typename XT, int BITS, int CH>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ x, int K,
                                                          int8_t* __restrict__ codes,
-                                                         float* __restrict__ scales,
-                                                         unsigned* __restrict__ clear,
-                                                         int n_clear) {
+                                                         float* __restrict__ scales) {
   constexpr int T = 256;
   __shared__ float red[4];
   const int t = threadIdx.x;
   const int row = blockIdx.x;
-  if (row == 0) {
-    for (int i = t; i < n_clear; i += T) clear[i] = 0u;
-  }
   const XT* xr = x + (size_t)row * K;
   float v[CH][8];
   float s = 0.0f;
@@ -290,86 +280,80 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
 }
 
 template <typename XT, int BITS, int L, int LT>
-hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, unsigned* clear,
-                       int n_clear, hipStream_t stream) {
+hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, hipStream_t stream) {
   constexpr int K = 1 << L;
   const size_t lds = (size_t)(K + K / 32) * sizeof(float);
   auto kern = fwht_quant_kernel<XT, BITS, L, LT>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)M), dim3(1 << LT), lds, stream>>>(reinterpret_cast<const XT*>(x), codes,
-                                                          scales, clear, n_clear);
+                                                          scales);
   return hipGetLastError();
 }
 
 // Threads per row: 256 for batches (many rows in flight), 1024 for a
 // handful of long rows (decode), never fewer than 8 elements per thread.
 template <typename XT, int BITS, int L>
-hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales, unsigned* clear,
-                         int n_clear, hipStream_t stream) {
+hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales, hipStream_t stream) {
   constexpr int LT_BATCH = (L - 3 < 8) ? L - 3 : 8;
   constexpr int LT_FEW = (L - 3 < 10) ? L - 3 : 10;
   if (M <= 64 && LT_FEW != LT_BATCH)
-    return launch_fwht<XT, BITS, L, LT_FEW>(x, M, codes, scales, clear, n_clear, stream);
-  return launch_fwht<XT, BITS, L, LT_BATCH>(x, M, codes, scales, clear, n_clear, stream);
+    return launch_fwht<XT, BITS, L, LT_FEW>(x, M, codes, scales, stream);
+  return launch_fwht<XT, BITS, L, LT_BATCH>(x, M, codes, scales, stream);
 }
 
 template <typename XT, int BITS>
-hipError_t launch_had(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                      unsigned* clear, int n_clear, hipStream_t stream) {
+hipError_t launch_had(const void* x, int64_t M, int K, int8_t* codes, float* scales, hipStream_t stream) {
   switch (K) {
-    case 1 << 6: return launch_fwht_l<XT, BITS, 6>(x, M, codes, scales, clear, n_clear, stream);
-    case 1 << 7: return launch_fwht_l<XT, BITS, 7>(x, M, codes, scales, clear, n_clear, stream);
-    case 1 << 8: return launch_fwht_l<XT, BITS, 8>(x, M, codes, scales, clear, n_clear, stream);
-    case 1 << 9: return launch_fwht_l<XT, BITS, 9>(x, M, codes, scales, clear, n_clear, stream);
-    case 1 << 10: return launch_fwht_l<XT, BITS, 10>(x, M, codes, scales, clear, n_clear, stream);
-    case 1 << 11: return launch_fwht_l<XT, BITS, 11>(x, M, codes, scales, clear, n_clear, stream);
-    case 1 << 12: return launch_fwht_l<XT, BITS, 12>(x, M, codes, scales, clear, n_clear, stream);
-    case 1 << 13: return launch_fwht_l<XT, BITS, 13>(x, M, codes, scales, clear, n_clear, stream);
-    case 1 << 14: return launch_fwht_l<XT, BITS, 14>(x, M, codes, scales, clear, n_clear, stream);
-    case 1 << 15: return launch_fwht_l<XT, BITS, 15>(x, M, codes, scales, clear, n_clear, stream);
+    case 1 << 6: return launch_fwht_l<XT, BITS, 6>(x, M, codes, scales, stream);
+    case 1 << 7: return launch_fwht_l<XT, BITS, 7>(x, M, codes, scales, stream);
+    case 1 << 8: return launch_fwht_l<XT, BITS, 8>(x, M, codes, scales, stream);
+    case 1 << 9: return launch_fwht_l<XT, BITS, 9>(x, M, codes, scales, stream);
+    case 1 << 10: return launch_fwht_l<XT, BITS, 10>(x, M, codes, scales, stream);
+    case 1 << 11: return launch_fwht_l<XT, BITS, 11>(x, M, codes, scales, stream);
+    case 1 << 12: return launch_fwht_l<XT, BITS, 12>(x, M, codes, scales, stream);
+    case 1 << 13: return launch_fwht_l<XT, BITS, 13>(x, M, codes, scales, stream);
+    case 1 << 14: return launch_fwht_l<XT, BITS, 14>(x, M, codes, scales, stream);
+    case 1 << 15: return launch_fwht_l<XT, BITS, 15>(x, M, codes, scales, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename XT, int BITS, int CH>
-hipError_t launch_rows_ch(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                          unsigned* clear, int n_clear, hipStream_t stream) {
+hipError_t launch_rows_ch(const void* x, int64_t M, int K, int8_t* codes, float* scales, hipStream_t stream) {
   quant_rows_kernel<XT, BITS, CH><<<dim3((unsigned)M), dim3(256), 0, stream>>>(
-      reinterpret_cast<const XT*>(x), K, codes, scales, clear, n_clear);
+      reinterpret_cast<const XT*>(x), K, codes, scales);
   return hipGetLastError();
 }
 
 template <typename XT, int BITS>
-hipError_t launch_rows(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                       unsigned* clear, int n_clear, hipStream_t stream) {
+hipError_t launch_rows(const void* x, int64_t M, int K, int8_t* codes, float* scales, hipStream_t stream) {
   const int ch = (K + 2047) / 2048;
-  if (ch <= 1) return launch_rows_ch<XT, BITS, 1>(x, M, K, codes, scales, clear, n_clear, stream);
-  if (ch <= 2) return launch_rows_ch<XT, BITS, 2>(x, M, K, codes, scales, clear, n_clear, stream);
-  if (ch <= 4) return launch_rows_ch<XT, BITS, 4>(x, M, K, codes, scales, clear, n_clear, stream);
-  if (ch <= 8) return launch_rows_ch<XT, BITS, 8>(x, M, K, codes, scales, clear, n_clear, stream);
-  return launch_rows_ch<XT, BITS, 16>(x, M, K, codes, scales, clear, n_clear, stream);
+  if (ch <= 1) return launch_rows_ch<XT, BITS, 1>(x, M, K, codes, scales, stream);
+  if (ch <= 2) return launch_rows_ch<XT, BITS, 2>(x, M, K, codes, scales, stream);
+  if (ch <= 4) return launch_rows_ch<XT, BITS, 4>(x, M, K, codes, scales, stream);
+  if (ch <= 8) return launch_rows_ch<XT, BITS, 8>(x, M, K, codes, scales, stream);
+  return launch_rows_ch<XT, BITS, 16>(x, M, K, codes, scales, stream);
 }
 
 template <typename XT>
 hipError_t launch_dtype(const void* x, int64_t M, int K, int bits, int hadamard, int8_t* codes,
-                        float* scales, unsigned* clear, int n_clear, hipStream_t stream) {
+                        float* scales, hipStream_t stream) {
   if (hadamard) {
-    return bits == 8 ? launch_had<XT, 8>(x, M, K, codes, scales, clear, n_clear, stream)
-                     : launch_had<XT, 4>(x, M, K, codes, scales, clear, n_clear, stream);
+    return bits == 8 ? launch_had<XT, 8>(x, M, K, codes, scales, stream)
+                     : launch_had<XT, 4>(x, M, K, codes, scales, stream);
   }
-  return bits == 8 ? launch_rows<XT, 8>(x, M, K, codes, scales, clear, n_clear, stream)
-                   : launch_rows<XT, 4>(x, M, K, codes, scales, clear, n_clear, stream);
+  return bits == 8 ? launch_rows<XT, 8>(x, M, K, codes, scales, stream)
+                   : launch_rows<XT, 4>(x, M, K, codes, scales, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
-                           int8_t* codes, float* scales, unsigned* clear, int n_clear,
-                           hipStream_t stream) {
+                           int8_t* codes, float* scales, hipStream_t stream) {
   if (x_dtype == 1)
-    return launch_dtype<uint16_t>(x, M, K, bits, hadamard, codes, scales, clear, n_clear, stream);
-  return launch_dtype<float>(x, M, K, bits, hadamard, codes, scales, clear, n_clear, stream);
+    return launch_dtype<uint16_t>(x, M, K, bits, hadamard, codes, scales, stream);
+  return launch_dtype<float>(x, M, K, bits, hadamard, codes, scales, stream);
 }
 
 }  // namespace bitnet

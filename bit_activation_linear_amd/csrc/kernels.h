@@ -20,17 +20,13 @@ constexpr int64_t kDecodeMaxM = 16;
 // whole batch sit in the workgroup's LDS).
 constexpr int64_t kFusedMaxElems = 16384;
 
-// Work decomposition of the decode (M <= 16) product. One wave owns one
-// 256-k super-block (four 64-weight blocks, one per 16-lane group) of `ct`
-// 16-column tiles; the waves of a workgroup cover consecutive super-blocks
-// and combine through LDS; when K needs more super-blocks than one workgroup
-// has waves, `kz` workgroups split K and the last one to finish reduces their
-// int32 partials in a fixed order.
+// Work decomposition of the decode (M <= 16) product. A workgroup owns `ct`
+// 16-column tiles and all of K; `sb_waves` waves take interleaved 256-k
+// super-blocks (four 64-weight blocks, one per 16-lane group).
 struct GemvPlan {
   int ct;          // 16-column tiles per workgroup
-  int sb_waves;    // waves that own a super-block
+  int sb_waves;    // waves that own super-blocks
   int threads;     // workgroup size
-  int kz;          // K splits across workgroups
   int col_groups;  // workgroups along N
   bool fused;      // x is quantized inside the kernel
 };
@@ -40,14 +36,12 @@ inline GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, bool x_given, bool ha
   const int64_t nKB = K / 64;
   const int64_t nSB = (nKB + 3) / 4;
   p.sb_waves = (int)(nSB < 16 ? nSB : 16);
-  p.kz = (int)((nSB + p.sb_waves - 1) / p.sb_waves);
-  p.fused = x_given && !hadamard && M * K <= kFusedMaxElems && p.kz == 1;
-  // Several column tiles per wave reuse each code fragment when the codes
-  // are not negligible next to the weights.
-  p.ct = (!p.fused && M > 4) ? 4 : 1;
+  // Fusing keeps every token's codes in LDS and needs one 4-element chunk per
+  // thread and row: K <= 4 * 64 * sb_waves, i.e. a single round of waves.
+  p.fused = x_given && !hadamard && M * K <= kFusedMaxElems && nSB <= 16;
+  p.ct = 1;
   p.col_groups = (int)((N + 16 * p.ct - 1) / (16 * p.ct));
   int waves = p.sb_waves;
-  if (waves < p.ct) waves = p.ct;
   if (p.fused && waves < 4) waves = 4;
   p.threads = 64 * waves;
   return p;
@@ -55,13 +49,6 @@ inline GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, bool x_given, bool ha
 
 constexpr size_t kWsAlign = 256;
 inline size_t ws_round(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
-
-inline size_t gemv_partials_bytes(const GemvPlan& p, int64_t M, int64_t N) {
-  return p.kz > 1 ? ws_round((size_t)p.kz * (size_t)M * (size_t)N * sizeof(int32_t)) : 0;
-}
-inline size_t gemv_counters_bytes(const GemvPlan& p) {
-  return p.kz > 1 ? ws_round((size_t)p.col_groups * sizeof(unsigned)) : 0;
-}
 
 // Stage 1 of the absmean reduction: partials[i] = sum of |W| over a fixed
 // subset of the n elements (n % 4 == 0). Returns the number of partials used.
@@ -78,25 +65,20 @@ hipError_t launch_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* Wpac
                             hipStream_t stream);
 
 // Fused (optional) Walsh-Hadamard transform + per-token quantization.
-// x_dtype: 0 = fp32, 1 = bf16 bit patterns. Workgroup 0 also clears
-// `n_clear` words at `clear` (the decode kernel's split-K counters).
+// x_dtype: 0 = fp32, 1 = bf16 bit patterns.
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
-                           int8_t* codes, float* scales, unsigned* clear, int n_clear,
-                           hipStream_t stream);
+                           int8_t* codes, float* scales, hipStream_t stream);
 
 // Ternary product from codes. Exactly one of y (dequantized; needs scales,
-// alpha, bits) or acc (raw int32) is non-null. partials/counters come from
-// the workspace when the decode plan splits K (counters zero on entry; the
-// kernel leaves them zero).
+// alpha, bits) or acc (raw int32) is non-null.
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
                                  const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
-                                 float* y, int32_t* acc, int32_t* partials, unsigned* counters,
-                                 hipStream_t stream);
+                                 float* y, int32_t* acc, hipStream_t stream);
 
 // The two product shapes behind launch_ternary_matmul.
 hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, int32_t* partials, unsigned* counters, hipStream_t stream);
+                       int32_t* acc, hipStream_t stream);
 hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
                        int32_t* acc, hipStream_t stream);

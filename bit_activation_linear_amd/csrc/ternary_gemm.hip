@@ -171,11 +171,9 @@ hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int 
 
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
                                  const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
-                                 float* y, int32_t* acc, int32_t* partials, unsigned* counters,
-                                 hipStream_t stream) {
+                                 float* y, int32_t* acc, hipStream_t stream) {
   if (M <= kDecodeMaxM)
-    return launch_gemv(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, partials, counters,
-                       stream);
+    return launch_gemv(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream);
   return launch_gemm(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream);
 }
 

@@ -5,22 +5,26 @@
 // output F.linear(Q_act(x_r), alpha * t) equals (q . t^T) * alpha * s / c
 // with integer codes q (Eq. 5-6) and ternary t (Eq. 1).
 //
-// The kernel is bound by the packed weights streaming from HBM (N*K/4 bytes).
-// Every lane issues its 16-B weight loads before anything else, and the grid
-// holds enough waves that all of a decode layer's weights are in flight at
-// once: tokens are the 16-row side of the MFMA (rows >= M are zero), one
-// wave owns one 256-k super-block of `ct` 16-column tiles (its four 16-lane
-// groups take one 64-weight block each), the waves of a workgroup cover
-// consecutive super-blocks and add up through LDS, and when K has more
-// super-blocks than a workgroup has waves, `kz` workgroups split K: each
-// writes its int32 partial tile, and the last to arrive (an agent-scope
-// ticket counter) sums the partials in split order and applies the epilogue.
-// Integer sums are exact, so the result does not depend on the split.
+// The kernel is bound by the packed weights streaming from HBM (N*K/4 bytes)
+// and, at decode sizes, by the latency of that stream. Tokens are the 16-row
+// side of the MFMA (rows >= M are zero). A workgroup owns `ct` 16-column
+// tiles and the whole of K: its waves take interleaved 256-k super-blocks
+// (each 16-lane group one 64-weight block, so a lane loads one 16-B packed
+// vector per super-block and column tile), issue every load of up to four
+// super-blocks before the first MFMA, and add their tiles up through LDS.
+// Workgroups never exchange data: on this chip the eight XCD L2 caches are
+// not coherent with one another, so a cross-workgroup reduction inside one
+// kernel would need an L2 write-back per wave.
+//
+// Barriers between waves wait for LDS traffic only (s_waitcnt lgkmcnt(0) +
+// s_barrier); the default __syncthreads() would also wait for every global
+// load in flight, draining the weight stream at each barrier.
 //
 // With hadamard = 0 and a small batch the per-token quantization (Eq. 5-6)
-// runs inside the same kernel: every workgroup reads the whole (tiny) x,
-// reduces the per-token statistic, writes the codes to LDS and feeds the MFMA
-// from there, so the decode forward is a single launch.
+// runs in the same kernel: each workgroup reads the whole (tiny) x first,
+// reduces the per-token statistic with DPP, writes the codes to LDS and feeds
+// the MFMA from there, all while its weight loads are in flight, so the decode
+// forward is one launch.
 #include "kernels.h"
 #include "ternary_common.cuh"
 
@@ -28,6 +32,7 @@ namespace bitnet {
 namespace {
 
 constexpr float kEps = 1e-7f;
+constexpr int kRoundsInFlight = 4;  // super-blocks whose loads a lane issues together
 
 struct GemvArgs {
   const int8_t* codes;
@@ -37,29 +42,43 @@ struct GemvArgs {
   const float* alpha;
   float* y;
   int32_t* acc_out;
-  int32_t* partials;
-  unsigned* counters;
-  int M, K, N, sb_waves, kz;
+  int M, K, N, sb_waves;
   float c;
 };
 
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Weights and codes of one super-block for this lane (kb: its 64-weight
+// block). Loads are unconditional from clamped, always-valid addresses, so no
+// branch forces a wait between them. Out-of-range k is neutralized by zeroing
+// the codes with a bit mask (a branch that overwrote a loaded register would
+// have to wait for the load); out-of-range columns and token rows only feed
+// outputs that are never stored.
 template <int CT>
-__device__ __forceinline__ void load_weights(const GemvArgs& a, int kb, bool k_ok, int col,
-                                             uint4 (&p)[CT]) {
+__device__ __forceinline__ void load_round(const GemvArgs& a, const int8_t* codes_base, int kb,
+                                           bool k_ok, int col, uint4 (&p)[CT], v4i (&av)[4]) {
   const size_t row_bytes = (size_t)(a.K >> 2);
+  const int nKB = a.K >> 6;
+  const int kbc = kb < nKB ? kb : nKB - 1;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int n = (blockIdx.x * CT + ct) * 16 + col;
-    if (k_ok && n < a.N) {
-      p[ct] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)n * row_bytes + (size_t)kb * 16);
-    } else {
-      p[ct] = zero_weight_block();
-    }
+    const int nc = n < a.N ? n : a.N - 1;
+    p[ct] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
   }
+  const int mc = col < a.M ? col : a.M - 1;
+  const v4i* ap = reinterpret_cast<const v4i*>(codes_base + (size_t)mc * a.K + (size_t)kbc * 64);
+  const int kmask = k_ok ? -1 : 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) av[j] = ap[j] & kmask;
 }
 
 template <int CT>
-__device__ __forceinline__ void wave_mma(const v4i (&av)[4], const uint4 (&p)[CT], v4i (&acc)[CT]) {
+__device__ __forceinline__ void mma_round(const v4i (&av)[4], const uint4 (&p)[CT], v4i (&acc)[CT]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -68,63 +87,52 @@ __device__ __forceinline__ void wave_mma(const v4i (&av)[4], const uint4 (&p)[CT
                                                        0, 0);
 }
 
-// Combine the waves' 16x16 tiles, then (split K) the workgroups' partials,
-// then store. 16x16 MFMA layout: lane l holds rows 4*(l/16) + v, column l%16.
+// The wave's share of the product; codes_base is the [M, K] code matrix.
+template <int CT>
+__device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* codes_base,
+                                             v4i (&acc)[CT]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nKB = a.K >> 6, nSB = (nKB + 3) >> 2;
+  const int rounds = (nSB + a.sb_waves - 1) / a.sb_waves;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
+  if (wave >= a.sb_waves) return;
+  for (int r0 = 0; r0 < rounds; r0 += kRoundsInFlight) {
+    uint4 p[kRoundsInFlight][CT];
+    v4i av[kRoundsInFlight][4];
+#pragma unroll
+    for (int u = 0; u < kRoundsInFlight; ++u) {
+      const int sb = wave + a.sb_waves * (r0 + u);
+      const int kb = sb * 4 + grp;
+      const bool k_ok = (r0 + u < rounds) && sb < nSB && kb < nKB;
+      load_round<CT>(a, codes_base, kb, k_ok, col, p[u], av[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRoundsInFlight; ++u) {
+      if (r0 + u < rounds) mma_round<CT>(av[u], p[u], acc);
+    }
+  }
+}
+
+// Add the waves' 16x16 tiles and store. 16x16 MFMA layout: lane l holds rows
+// 4*(l/16) + v, column l%16.
 template <int CT, bool OUT_I32>
-__device__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[CT], v4i* red, int* flag,
-                            const float* s_rows) {
+__device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[CT], v4i* red,
+                                            const float* s_rows) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int nw = blockDim.x >> 6;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) red[(wave * CT + ct) * 64 + lane] = acc[ct];
-  __syncthreads();
-
-  const bool active = t < CT * 64;
+  lds_barrier();
+  if (t >= CT * 64) return;
   const int ct = t >> 6, l = t & 63;
   const int n = (blockIdx.x * CT + ct) * 16 + (l & 15);
+  if (n >= a.N) return;
+  v4i total = red[ct * 64 + l];
+  for (int w = 1; w < nw; ++w) total += red[(w * CT + ct) * 64 + l];
   const int m0 = 4 * (l >> 4);
-  v4i total = {0, 0, 0, 0};
-  if (active) {
-    for (int w = 0; w < nw; ++w) total += red[(w * CT + ct) * 64 + l];
-  }
-
-  if (a.kz > 1) {
-    if (active && n < a.N) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + v;
-        if (m < a.M) a.partials[((size_t)blockIdx.y * a.M + m) * a.N + n] = total[v];
-      }
-    }
-    __threadfence();
-    __syncthreads();
-    if (t == 0) {
-      const unsigned old = __hip_atomic_fetch_add(&a.counters[blockIdx.x], 1u, __ATOMIC_ACQ_REL,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-      *flag = (old == (unsigned)(a.kz - 1)) ? 1 : 0;
-    }
-    __syncthreads();
-    if (*flag == 0) return;
-    __threadfence();
-    if (active && n < a.N) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + v;
-        if (m < a.M) {
-          int s = 0;
-          for (int z = 0; z < a.kz; ++z)
-            s += __hip_atomic_load(&a.partials[((size_t)z * a.M + m) * a.N + n], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-          total[v] = s;
-        }
-      }
-    }
-    if (t == 0)
-      __hip_atomic_store(&a.counters[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  if (!active || n >= a.N) return;
   const float alpha = OUT_I32 ? 0.0f : *a.alpha;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -142,31 +150,9 @@ __device__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[CT], v4i* red, i
 template <int CT, bool OUT_I32>
 __global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a) {
   extern __shared__ v4i red[];
-  __shared__ int flag;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int nKB = a.K >> 6, nSB = (nKB + 3) >> 2;
-  const int sb = blockIdx.y * a.sb_waves + wave;
-  const bool wave_ok = wave < a.sb_waves && sb < nSB;
-  const int kb = sb * 4 + grp;
-  const bool k_ok = wave_ok && kb < nKB;
-
-  uint4 p[CT];
-  load_weights<CT>(a, kb, k_ok, col, p);
-  v4i av[4];
-  if (k_ok && col < a.M) {
-    const v4i* ap = reinterpret_cast<const v4i*>(a.codes + (size_t)col * a.K + (size_t)kb * 64);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) av[j] = ap[j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) av[j] = v4i{0, 0, 0, 0};
-  }
   v4i acc[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
-  if (wave_ok) wave_mma<CT>(av, p, acc);
-  gemv_finish<CT, OUT_I32>(a, acc, red, &flag, a.scales);
+  wave_product<CT>(a, a.codes, acc);
+  gemv_finish<CT, OUT_I32>(a, acc, red, a.scales);
 }
 
 __device__ __forceinline__ void load4(const float* x, size_t i, float (&v)[4]) {
@@ -181,80 +167,96 @@ __device__ __forceinline__ void load4(const uint16_t* x, size_t i, float (&v)[4]
   v[3] = __uint_as_float(u.y & 0xFFFF0000u);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// Wave-wide max or sum of non-negative values with DPP row shifts and row
+// broadcasts (zero is the identity of both); the fixed order keeps sums
+// bitwise reproducible. Every lane gets the result.
+template <bool IS_MAX>
+__device__ __forceinline__ float wave_reduce(float v) {
+#define BITNET_DPP_STEP(ctrl, rmask, bc)                                                      \
+  {                                                                                           \
+    const float o = __int_as_float(                                                           \
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rmask, 0xF, bc));             \
+    v = IS_MAX ? fmaxf(v, o) : v + o;                                                         \
+  }
+  BITNET_DPP_STEP(0x111, 0xF, true)   // row_shr:1
+  BITNET_DPP_STEP(0x112, 0xF, true)   // row_shr:2
+  BITNET_DPP_STEP(0x114, 0xF, true)   // row_shr:4
+  BITNET_DPP_STEP(0x118, 0xF, true)   // row_shr:8  -> lane 15 of each row: row total
+  BITNET_DPP_STEP(0x142, 0xA, false)  // row_bcast:15 -> lane 31 / 63: two rows
+  BITNET_DPP_STEP(0x143, 0xC, false)  // row_bcast:31 -> lane 63: whole wave
+#undef BITNET_DPP_STEP
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Decode forward with the quantization fused in. Requires K/4 <= blockDim.x
-// (each thread owns at most one 4-element chunk per token row) and kz == 1.
-template <typename XT, int BITS>
+// (each thread owns at most one 4-element chunk per token row) and M <= MG.
+template <typename XT, int BITS, int MG>
 __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int flag;
   const int nw = blockDim.x >> 6;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int col = lane & 15, grp = lane >> 4;
   v4i* red = reinterpret_cast<v4i*>(smem);
   int8_t* qlds = reinterpret_cast<int8_t*>(smem + (size_t)nw * 1024);
   const int mk16 = ((a.M * a.K) + 15) & ~15;
   float* part = reinterpret_cast<float*>(qlds + mk16);  // [nw][16]
   float* srow = part + nw * 16;                         // [16]
 
-  const int nKB = a.K >> 6, nSB = (nKB + 3) >> 2;
-  const int sb = wave;
-  const bool wave_ok = wave < a.sb_waves && sb < nSB;
-  const int kb = sb * 4 + grp;
-  const bool k_ok = wave_ok && kb < nKB;
-
-  // Weights first: their HBM latency overlaps the quantization below.
-  uint4 p[1];
-  load_weights<1>(a, kb, k_ok, col, p);
-
-  // x: thread t owns elements 4t .. 4t+3 of every token row.
+  // x first, unconditionally from clamped addresses: those loads return
+  // first, so the statistic below waits on them alone while the weight load
+  // issued right after is still in flight.
   const XT* x = reinterpret_cast<const XT*>(a.x);
   const int K4 = a.K >> 2;
   const bool own = t < K4;
-  float v[16][4];
+  const int tc = own ? t : 0;
+  float v[MG][4];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    if (m < a.M && own) {
-      load4(x, (size_t)m * a.K + 4 * t, v[m]);
-    } else {
-      v[m][0] = v[m][1] = v[m][2] = v[m][3] = 0.0f;
-    }
+  for (int m = 0; m < MG; ++m) {
+    const int mc = m < a.M ? m : a.M - 1;
+    load4(x, (size_t)mc * a.K + 4 * tc, v[m]);
+  }
+
+  const int col = lane & 15, grp = lane >> 4;
+  const int nKB = a.K >> 6, nSB = (nKB + 3) >> 2;
+  const int sb = wave;
+  const int kb = sb * 4 + grp;
+  const bool k_ok = wave < a.sb_waves && sb < nSB && kb < nKB;
+  uint4 p[1];
+  {
+    const size_t row_bytes = (size_t)(a.K >> 2);
+    const int n = blockIdx.x * 16 + col;
+    const int nc = n < a.N ? n : a.N - 1;
+    const int kbc = kb < nKB ? kb : nKB - 1;
+    // an out-of-range block meets all-zero codes below
+    p[0] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
   }
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
+  for (int m = 0; m < MG; ++m) {
     if (m < a.M) {
+      // threads past the row hold a clamped duplicate: they contribute 0
       float s;
       if (BITS == 8) {
         s = fmaxf(fmaxf(fabsf(v[m][0]), fabsf(v[m][1])), fmaxf(fabsf(v[m][2]), fabsf(v[m][3])));
-        s = wave_max(s);
+        s = wave_reduce<true>(own ? s : 0.0f);
       } else {
         s = (fabsf(v[m][0]) + fabsf(v[m][1])) + (fabsf(v[m][2]) + fabsf(v[m][3]));
-        s = wave_sum(s);
+        s = wave_reduce<false>(own ? s : 0.0f);
       }
       if (lane == 0) part[wave * 16 + m] = s;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (t < a.M) {
     float s = 0.0f;
     for (int w = 0; w < nw; ++w) s = (BITS == 8) ? fmaxf(s, part[w * 16 + t]) : s + part[w * 16 + t];
     if (BITS == 4) s = s / (float)a.K;
     srow[t] = s + kEps;
   }
-  __syncthreads();
+  lds_barrier();
   const float lo = (BITS == 8) ? -128.0f : -8.0f;
   const float hi = (BITS == 8) ? 127.0f : 7.0f;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
+  for (int m = 0; m < MG; ++m) {
     if (m < a.M && own) {
       const float mult = a.c / srow[m];
       unsigned word = 0;
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
       *reinterpret_cast<unsigned*>(qlds + (size_t)m * a.K + 4 * t) = word;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   v4i av[4];
   if (k_ok && col < a.M) {
@@ -279,8 +281,8 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
     for (int j = 0; j < 4; ++j) av[j] = v4i{0, 0, 0, 0};
   }
   v4i acc[1] = {v4i{0, 0, 0, 0}};
-  if (wave_ok) wave_mma<1>(av, p, acc);
-  gemv_finish<1, false>(a, acc, red, &flag, srow);
+  if (wave < a.sb_waves) mma_round<1>(av, p, acc);
+  gemv_finish<1, false>(a, acc, red, srow);
 }
 
 template <typename Kern>
@@ -296,18 +298,18 @@ hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stre
   auto kern = ternary_gemv_kernel<CT, OUT_I32>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)p.col_groups, (unsigned)p.kz), dim3(p.threads), lds, stream>>>(a);
+  kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a);
   return hipGetLastError();
 }
 
-template <typename XT, int BITS>
+template <typename XT, int BITS, int MG>
 hipError_t launch_fused_t(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   const int nw = p.threads / 64;
   const size_t lds = (size_t)nw * 1024 + (size_t)((a.M * a.K + 15) & ~15) + (size_t)nw * 16 * 4 + 64;
-  auto kern = fused_decode_kernel<XT, BITS>;
+  auto kern = fused_decode_kernel<XT, BITS, MG>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)p.col_groups, 1), dim3(p.threads), lds, stream>>>(a);
+  kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -315,7 +317,7 @@ hipError_t launch_fused_t(const GemvPlan& p, const GemvArgs& a, hipStream_t stre
 
 hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, int32_t* partials, unsigned* counters, hipStream_t stream) {
+                       int32_t* acc, hipStream_t stream) {
   const GemvPlan p = plan_gemv(M, K, N, false, false);
   GemvArgs a{};
   a.codes = codes;
@@ -324,15 +326,12 @@ hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int 
   a.alpha = alpha;
   a.y = y;
   a.acc_out = acc;
-  a.partials = partials;
-  a.counters = counters;
   a.M = (int)M;
   a.K = K;
   a.N = (int)N;
   a.sb_waves = p.sb_waves;
-  a.kz = p.kz;
   a.c = (bits == 8) ? kScaleInt8 : kScaleInt4;
-  if (p.ct == 4) return acc ? launch_gemv_ct<4, true>(p, a, stream) : launch_gemv_ct<4, false>(p, a, stream);
+  if (p.ct == 2) return acc ? launch_gemv_ct<2, true>(p, a, stream) : launch_gemv_ct<2, false>(p, a, stream);
   return acc ? launch_gemv_ct<1, true>(p, a, stream) : launch_gemv_ct<1, false>(p, a, stream);
 }
 
@@ -350,13 +349,19 @@ hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
   a.K = K;
   a.N = (int)N;
   a.sb_waves = p.sb_waves;
-  a.kz = 1;
   a.c = (bits == 8) ? kScaleInt8 : kScaleInt4;
-  if (x_dtype == 1) {
-    return bits == 8 ? launch_fused_t<uint16_t, 8>(p, a, stream)
-                     : launch_fused_t<uint16_t, 4>(p, a, stream);
+  if (M <= 4) {
+    if (x_dtype == 1)
+      return bits == 8 ? launch_fused_t<uint16_t, 8, 4>(p, a, stream)
+                       : launch_fused_t<uint16_t, 4, 4>(p, a, stream);
+    return bits == 8 ? launch_fused_t<float, 8, 4>(p, a, stream)
+                     : launch_fused_t<float, 4, 4>(p, a, stream);
   }
-  return bits == 8 ? launch_fused_t<float, 8>(p, a, stream) : launch_fused_t<float, 4>(p, a, stream);
+  if (x_dtype == 1)
+    return bits == 8 ? launch_fused_t<uint16_t, 8, 16>(p, a, stream)
+                     : launch_fused_t<uint16_t, 4, 16>(p, a, stream);
+  return bits == 8 ? launch_fused_t<float, 8, 16>(p, a, stream)
+                   : launch_fused_t<float, 4, 16>(p, a, stream);
 }
 
 }  // namespace bitnet

@@ -102,9 +102,9 @@ bitnet_status bitnet_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* W
 /* Forward                                                                   */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of workspace bitnet_hbitlinear_forward needs: the int8 codes and
- * scales of the batch, plus split-K partials for long rows at M <= 16. It is
- * 0 when the forward runs as a single fused kernel (M <= 16, hadamard = 0,
+/* Bytes of workspace bitnet_hbitlinear_forward needs: the int8 codes and fp32
+ * scales of the batch (M*K and 4*M bytes, each rounded up to 256). It is 0
+ * when the forward runs as a single fused kernel (M <= 16, hadamard = 0,
  * M*K <= 16384, K <= 4096); ws may then be NULL. Returns 0 for invalid sizes. */
 size_t bitnet_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits, int hadamard);
 
@@ -139,18 +139,12 @@ bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, i
                                           int64_t K, int bits, int hadamard, int8_t* codes,
                                           float* scales, hipStream_t stream);
 
-/* Bytes of workspace the two product-only entry points below need (split-K
- * partials and arrival counters at M <= 16 with long rows; often 0, and ws
- * may then be NULL). This workspace must be zero-filled before its first use;
- * every call leaves its counters zero again. Returns 0 for invalid sizes. */
-size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
-
 /* Exact integer product only: acc[m, n] = sum_k codes[m, k] * t[n, k], int32.
  * codes: int8 [M, K] with values in [-128, 127]. Requires K % 64 == 0 and
  * K <= BITNET_MAX_K. */
 bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
-                                      const uint8_t* Wpacked, int64_t N, int32_t* acc, void* ws,
-                                      size_t ws_bytes, hipStream_t stream);
+                                      const uint8_t* Wpacked, int64_t N, int32_t* acc,
+                                      hipStream_t stream);
 
 /* Integer product with the fused dequantization epilogue (engine page,
  * HBitLinear.forward's F.linear of the two dequantized operands, rewritten by
@@ -158,8 +152,8 @@ bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
  * sqrt 7 (bits 4). */
 bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* scales, int64_t M,
                                             int64_t K, const uint8_t* Wpacked, int64_t N,
-                                            const float* alpha, int bits, float* y, void* ws,
-                                            size_t ws_bytes, hipStream_t stream);
+                                            const float* alpha, int bits, float* y,
+                                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ import torch
 import oracle
 import bit_activation_linear_amd as bl
 from bit_activation_linear_amd import workloads
-from parity_util import assert_codes_match, assert_packed_match, assert_y_close
+from parity_util import assert_codes_match, assert_packed_match, assert_y_close, assert_y_parity
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -48,12 +48,12 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     torch.cuda.synchronize()
 
     t_ref, a_ref, p_w = oracle.ternarize(case["W"])
-    assert_packed_match(Wp.cpu().numpy(), t_ref, p_w)
+    w_flips = assert_packed_match(Wp.cpu().numpy(), t_ref, p_w)
     assert abs(alpha.item() - a_ref) <= 1e-6 * a_ref
 
     ref = oracle.forward(case["x"], x_dtype, t_ref, a_ref, bits, had)
     q_gpu = codes.cpu().numpy()
-    assert_codes_match(q_gpu, ref["q"], ref["p"])
+    q_flips = assert_codes_match(q_gpu, ref["q"], ref["p"])
     np.testing.assert_allclose(scales.cpu().numpy(), ref["s"], rtol=2e-6)
 
     # int32 accumulators exact on identical codes, both ways round.
@@ -62,13 +62,16 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     acc_from_ref = bl.ternary_gemm_i32(torch.from_numpy(ref["q"]).to(DEV), Wp)
     np.testing.assert_array_equal(acc_from_ref.cpu().numpy(), oracle.ternary_matmul_i64(ref["q"], t_gpu))
 
-    assert_y_close(y.cpu().numpy(), ref["y64"])
-    # The forward is the two stages back to back. Where it runs as one fused
-    # kernel the int4 absmean is summed in another order, so an ulp of the
-    # scale may move a code that sits on a rounding boundary.
+    # The staged product runs on exactly these codes.
+    assert_y_parity(y2.cpu().numpy(), q_gpu, t_gpu, ref, a_ref, bits, w_flips + q_flips)
+    # The forward is the two stages back to back, bit for bit, except where it
+    # runs as one fused kernel with int4: the absmean is then summed in another
+    # order, an ulp of the scale can move a code sitting on a rounding
+    # boundary, and one moved code shifts a whole output row by alpha*s/c.
     fused = bl.forward_workspace_bytes(M, K, N, bits, had) == 0
     if fused and bits == 4:
-        assert_y_close(y.cpu().numpy(), y2.cpu().numpy().astype(np.float64), what="fused vs staged")
+        assert_y_close(y.cpu().numpy(), y2.cpu().numpy().astype(np.float64), what="fused vs staged",
+                       tol=2e-3)
     else:
         np.testing.assert_array_equal(y.cpu().numpy(), y2.cpu().numpy())
 
@@ -83,8 +86,8 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     (16, 16384, 64, 4, 1, "bf16"),
     (2, 192, 31, 8, 0, "bf16"),
     (5, 32768, 40, 8, 0, "fp32"),
-    (1, 32768, 100, 8, 0, "bf16"),     # K split over 8 workgroups
-    (2, 8192, 70, 4, 0, "bf16"),       # K split over 2, not fused
+    (1, 32768, 100, 8, 0, "bf16"),     # eight rounds of super-blocks per wave
+    (2, 8192, 70, 4, 0, "bf16"),       # two rounds, not fused
     (4, 4096, 90, 4, 0, "bf16"),       # fused, int4
     (16, 1024, 48, 4, 0, "fp32"),      # fused, full 16 rows
     (16, 4096, 150, 8, 0, "bf16"),     # not fused (M*K too big), 4 column tiles
@@ -238,29 +241,9 @@ def test_bitwise_deterministic():
     np.testing.assert_array_equal(outs[0][2], outs[1][2])
 
 
-def test_split_k_counters_reset_between_calls():
-    _say("split-K counter reuse")
-    rng = np.random.default_rng(21)
-    M, K, N = 16, 16384, 200
-    q = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
-    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
-    Wp = bl.pack_2bit(torch.from_numpy(t).to(DEV))
-    codes = torch.from_numpy(q).to(DEV)
-    ws = bl.linear_workspace(M, K, N, DEV)
-    assert ws is not None
-    ref = oracle.ternary_matmul_i64(q, t)
-    for _ in range(3):
-        acc = bl.ternary_gemm_i32(codes, Wp, workspace=ws)
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(acc.cpu().numpy(), ref)
-    # the arrival counters are back at zero after every call
-    counters_off = bl.linear_workspace_bytes(M, K, N) - 256
-    assert torch.count_nonzero(ws[counters_off:]).item() == 0
-
-
 @pytest.mark.parametrize("M,K,N,bits,had", [
     (1, 2560, 700, 8, 0),      # one fused kernel
-    (16, 16384, 300, 4, 1),    # transform + split-K product
+    (16, 16384, 300, 4, 1),    # transform + streaming product
     (200, 1024, 300, 4, 1),    # prefill tile
 ])
 def test_graph_replay_matches_eager(M, K, N, bits, had):
