@@ -42,6 +42,15 @@ __device__ __forceinline__ uint4 zero_weight_block() {
   return make_uint4(kZeroWeights, kZeroWeights, kZeroWeights, kZeroWeights);
 }
 
+// Workgroup barrier that orders LDS traffic only (s_waitcnt lgkmcnt(0) +
+// s_barrier). __syncthreads() would also wait for every global load in
+// flight, which would drain the loads a kernel issues ahead of their use.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Dequantization factor alpha * s_m / c of output row m.
 __device__ __forceinline__ float dequant_factor(float alpha, float s, float c) {
   return (alpha * s) / c;

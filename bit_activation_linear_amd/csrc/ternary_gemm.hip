@@ -7,141 +7,208 @@
 // page's BitLinear_b158 takes the same integer-product-then-rescale form.
 // |q| <= 128 and K <= 32768 keep every int32 sum exact.
 //
-// 128x128 output tile per workgroup, four waves of 64x64, K step 128. Codes
-// go through a double-buffered LDS tile; packed weights go straight from HBM
-// to registers (a quarter of the bytes of an int8 tile) and are expanded
-// there.
+// Work decomposition. A workgroup of four waves (2 x 2) owns a
+// (64 RT) x (64 CT) output tile; each wave owns (32 RT) x (32 CT), i.e.
+// RT x CT accumulators of 32x32 int32 (AGPRs). K advances 128 per stage:
+// the stage's codes (BM x 128 B) and packed weights (BN x 32 B: two 16-B
+// blocks of 64 weights per column) are fetched with coalesced 16-B loads into
+// registers at the top of an iteration; halfway through the current stage's
+// MFMAs each thread expands its packed weights to int8 (a shift, a mask and
+// one v_perm_b32 per 4 weights, done once per workgroup rather than once per
+// wave) and writes codes and weights to the other half of a double-buffered
+// LDS tile. The MFMA loop itself then only reads LDS.
+//
+// MFMA operands. For the 32x32x32 instruction lane l supplies row (or column)
+// l % 32 and the 16 consecutive k of group g = l / 32. Sub-step h (k32) of a
+// stage uses k = 32h + 16g + [0, 16) for both operands, read as 16 bytes from
+// the LDS row of the code tile and of the expanded weight tile.
+//
+// Tile order. Workgroups are dispatched round-robin over the eight XCDs
+// (each with its own L2), so workgroup L runs on XCD L % 8. Each XCD gets a
+// contiguous range of tiles walked band by band (four M-tiles wide), so the
+// workgroups resident on one XCD at a time share code rows and weight columns
+// through its L2.
 #include "kernels.h"
 #include "ternary_common.cuh"
 
 namespace bitnet {
 namespace {
 
-// ------------------------------------------------------------------ GEMM --
+constexpr int BK = 128;
+constexpr int kAStride = BK + 16;  // bytes per LDS row (codes and expanded weights):
+                                   // the pad puts consecutive rows on distinct banks
+constexpr int kXcds = 8;
+constexpr int kBand = 4;
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kLdsStride = BK + 16;  // bytes per LDS row; the pad spreads rows over banks
+// A 16-B global load that stays where it is written: a volatile access is
+// neither sunk towards its use nor merged, so a prefetch issued before the
+// compute stays in flight during it.
+__device__ __forceinline__ uint4 ld_pinned(const void* p) {
+  const volatile uint4* vp = reinterpret_cast<const volatile uint4*>(p);
+  uint4 r;
+  r.x = vp->x;
+  r.y = vp->y;
+  r.z = vp->z;
+  r.w = vp->w;
+  return r;
+}
 
-template <bool OUT_I32>
-__global__ __launch_bounds__(256) void ternary_gemm_kernel(
+template <int RT, int CT, int WMW, int WNW, bool OUT_I32>
+__global__ __launch_bounds__(64 * WMW * WNW) void ternary_gemm_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ scales, int M, int K,
     const uint8_t* __restrict__ Wp, int N, const float* __restrict__ alpha_p, float c,
-    float* __restrict__ y, int32_t* __restrict__ acc_out) {
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLdsStride];
+    float* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_m, int tiles_n) {
+  constexpr int NT = 64 * WMW * WNW;              // threads
+  constexpr int BM = 32 * RT * WMW, BN = 32 * CT * WNW;
+  constexpr int A_CHUNKS = BM * (BK / 16) / NT;   // 16-B code chunks per thread per stage
+  constexpr int B_CHUNKS = BN * 2 / NT;           // 16-B weight chunks per thread per stage
+  static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small for the workgroup");
+  static_assert(A_CHUNKS * NT == BM * (BK / 16) && B_CHUNKS * NT == BN * 2, "uneven staging");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int8_t* As = reinterpret_cast<int8_t*>(smem);  // [2][BM][kAStride] codes
+  int8_t* Bs = As + 2 * BM * kAStride;           // [2][BN][kAStride] weights as int8
+
+  // XCD-aware tile order.
+  const int tiles = tiles_m * tiles_n;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int L = blockIdx.x;
+  const int tile = (L % kXcds) * per_xcd + L / kXcds;
+  if (tile >= tiles) return;
+  const int band = tile / (kBand * tiles_n);
+  const int band_m = (tiles_m - band * kBand) < kBand ? (tiles_m - band * kBand) : kBand;
+  const int in_band = tile - band * kBand * tiles_n;
+  const int tm = band * kBand + in_band % band_m;
+  const int tn = in_band / band_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
   const int nKB = K >> 6;
-  const int nks = (nKB + 1) >> 1;
-  const size_t wrow_bytes = (size_t)(K >> 2);
+  const int wrow_bytes = K >> 2;
 
-  // A tile loader: eight threads cover one 128-B row slice, 32 rows per round.
-  const int a_row = tid >> 3;
+  // Global -> register staging. Uniform tile bases plus 32-bit lane offsets;
+  // rows past M are clamped to a valid row (their outputs are not stored) and
+  // k past K is clamped: with an odd number of 64-weight blocks the last
+  // stage is a half stage whose second block is never read.
   const int a_col = (tid & 7) * 16;
-  // B loader: lane owns one column of each of the wave's two 32-column tiles
-  // and one of the two 64-k blocks of a K step.
-  const int b_grp = lane >> 5;
-  int b_col[2];
-  bool b_ok[2];
+  const int a_row0 = tid >> 3;
+  const int b_half = tid & 1;  // which 64-weight block of the stage this thread fetches
+  const int b_col0 = tid >> 1;
+  const int full = nKB >> 1;   // stages with both blocks
+  const int8_t* a_base = codes + (size_t)m0 * K;
+  const uint8_t* b_base = Wp + (size_t)n0 * wrow_bytes;
+  int a_off[A_CHUNKS];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    b_col[ct] = n0 + wn * 64 + ct * 32 + (lane & 31);
-    b_ok[ct] = b_col[ct] < N;
+  for (int i = 0; i < A_CHUNKS; ++i) {
+    const int r = a_row0 + (NT / 8) * i;
+    a_off[i] = (m0 + r < M ? r : M - 1 - m0) * K;
+  }
+  int b_off[B_CHUNKS];
+#pragma unroll
+  for (int i = 0; i < B_CHUNKS; ++i) {
+    const int cidx = b_col0 + (NT / 2) * i;
+    b_off[i] = (n0 + cidx < N ? cidx : N - 1 - n0) * wrow_bytes;
   }
 
-  auto load_a = [&](int ks, uint4 (&r)[4]) {
-    const int k = ks * BK + a_col;
+  v16i acc[RT][CT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + a_row + 32 * i;
-      if (m < M && k < K) {
-        r[i] = *reinterpret_cast<const uint4*>(codes + (size_t)m * K + k);
-      } else {
-        r[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_a = [&](int buf, const uint4 (&r)[4]) {
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(&As[buf][(a_row + 32 * i) * kLdsStride + a_col]) = r[i];
-    }
-  };
-  auto load_b = [&](int ks, uint4 (&r)[2]) {
-    const int kb = ks * 2 + b_grp;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      if (b_ok[ct] && kb < nKB) {
-        r[ct] = *reinterpret_cast<const uint4*>(Wp + (size_t)b_col[ct] * wrow_bytes + (size_t)kb * 16);
-      } else {
-        r[ct] = make_uint4(kZeroWeights, kZeroWeights, kZeroWeights, kZeroWeights);
-      }
-    }
-  };
-
-  v16i acc[2][2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0;
 
-  uint4 areg[4];
-  uint4 bcur[2], bnext[2];
-  load_a(0, areg);
-  load_b(0, bcur);
-  store_a(0, areg);
-  __syncthreads();
-
-  for (int ks = 0; ks < nks; ++ks) {
-    const bool more = ks + 1 < nks;
-    if (more) {
-      load_a(ks + 1, areg);
-      load_b(ks + 1, bnext);
-    }
-    v4i bx[2][4];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bx[ct][j] = expand_quarter(bcur[ct], j);
-    const int8_t* abuf = As[ks & 1];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int8_t* arow = abuf + (wm * 64 + rt * 32 + (lane & 31)) * kLdsStride + b_grp * 64;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4i af = *reinterpret_cast<const v4i*>(arow + 16 * j);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bx[ct][j], acc[rt][ct], 0, 0, 0);
-      }
-    }
-    if (more) {
-      store_a((ks + 1) & 1, areg);
-      bcur[0] = bnext[0];
-      bcur[1] = bnext[1];
-    }
-    __syncthreads();
+  uint4 ar[A_CHUNKS], br[B_CHUNKS];
+  // (Macros rather than lambdas: a lambda capturing these register arrays by
+  // reference makes the compiler keep them in scratch memory.)
+#define BITNET_FETCH(ks_)                                                                      \
+  {                                                                                            \
+    const int k_ = (ks_) * BK + a_col;                                                         \
+    const int kc_ = k_ < K ? k_ : K - 16;                                                      \
+    _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) ar[i] =                               \
+        ld_pinned(a_base + a_off[i] + kc_);                                                    \
+    const int kb_ = (ks_) * 2 + b_half;                                                        \
+    const int kbc_ = kb_ < nKB ? kb_ : nKB - 1;                                                \
+    _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) br[i] =                               \
+        ld_pinned(b_base + b_off[i] + kbc_ * 16);                                              \
+  }
+#define BITNET_STASH(buf_)                                                                     \
+  {                                                                                            \
+    int8_t* an_ = As + (buf_) * BM * kAStride;                                                 \
+    _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i)                                       \
+        *reinterpret_cast<uint4*>(an_ + (a_row0 + (NT / 8) * i) * kAStride + a_col) = ar[i];   \
+    int8_t* bn_ = Bs + (buf_) * BN * kAStride;                                                 \
+    _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) {                                     \
+      int8_t* row_ = bn_ + (b_col0 + (NT / 2) * i) * kAStride + b_half * 64;                   \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                            \
+          *reinterpret_cast<v4i*>(row_ + 16 * j) = expand_quarter(br[i], j);                   \
+    }                                                                                          \
   }
 
-  // 32x32 output layout: lane holds column lane % 32 and, for v = 0..15,
-  // row 8*(v/4) + 4*(lane/32) + v%4.
+  // MFMAs of k32 sub-steps [H0, H1) of the stage in LDS buffer buf_.
+#define BITNET_COMPUTE(buf_, H0, H1)                                                           \
+  {                                                                                            \
+    const int8_t* a_ = As + (buf_) * BM * kAStride + (wm * 32 * RT + l32) * kAStride + 16 * g; \
+    const int8_t* b_ = Bs + (buf_) * BN * kAStride + (wn * 32 * CT + l32) * kAStride + 16 * g; \
+    _Pragma("unroll") for (int h = (H0); h < (H1); ++h) {                                       \
+      v4i af[RT];                                                                              \
+      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) af[rt] =                               \
+          *reinterpret_cast<const v4i*>(a_ + rt * 32 * kAStride + 32 * h);                     \
+      v4i bf[CT];                                                                              \
+      _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) bf[ct] =                               \
+          *reinterpret_cast<const v4i*>(b_ + ct * 32 * kAStride + 32 * h);                     \
+      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                        \
+          _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) acc[rt][ct] =                      \
+              __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rt], bf[ct], acc[rt][ct], 0, 0, 0);     \
+    }                                                                                          \
+  }
+
+  BITNET_FETCH(0)
+  BITNET_STASH(0)
+  lds_barrier();
+
+  // Full stages (both blocks). Each iteration prefetches the next stage into
+  // registers (the last one re-reads a clamped stage into the idle buffer),
+  // runs half of the current stage's MFMAs, expands and stores the prefetch
+  // into the other buffer, then runs the second half. sched_barrier keeps the
+  // loads at the top, their first use in the middle, and the MFMA halves on
+  // either side.
+  for (int ks = 0; ks < full; ++ks) {
+    BITNET_FETCH(ks + 1)
+    __builtin_amdgcn_sched_barrier(0);
+    BITNET_COMPUTE(ks & 1, 0, 2)
+    __builtin_amdgcn_sched_barrier(0);
+    BITNET_STASH((ks + 1) & 1)
+    __builtin_amdgcn_sched_barrier(0);
+    BITNET_COMPUTE(ks & 1, 2, 4)
+    lds_barrier();
+  }
+  // With an odd number of blocks the last stage holds one block (two k32
+  // sub-steps).
+  if (nKB & 1) BITNET_COMPUTE(full & 1, 0, 2)
+#undef BITNET_FETCH
+#undef BITNET_STASH
+#undef BITNET_COMPUTE
+
+  // 32x32 output layout: lane holds column l32 and, for v = 0..15, row
+  // 8*(v/4) + 4*g + v%4 of its 32x32 block.
   const float alpha = OUT_I32 ? 0.0f : *alpha_p;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * 64 + rt * 32 + 8 * (v >> 2) + 4 * b_grp + (v & 3);
+      const int m = m0 + wm * 32 * RT + rt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
       if (m >= M) continue;
       const float f = OUT_I32 ? 0.0f : dequant_factor(alpha, scales[m], c);
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        if (!b_ok[ct]) continue;
-        const size_t o = (size_t)m * N + b_col[ct];
+      for (int ct = 0; ct < CT; ++ct) {
+        const int n = n0 + wn * 32 * CT + ct * 32 + l32;
+        if (n >= N) continue;
+        const size_t o = (size_t)m * N + n;
         if (OUT_I32) {
           acc_out[o] = acc[rt][ct][v];
         } else {
@@ -152,21 +219,42 @@ __global__ __launch_bounds__(256) void ternary_gemm_kernel(
   }
 }
 
+template <int RT, int CT, int WMW, int WNW, bool OUT_I32>
+hipError_t launch_tile(const int8_t* codes, const float* scales, int64_t M, int K,
+                       const uint8_t* Wpacked, int64_t N, const float* alpha, float c, float* y,
+                       int32_t* acc, hipStream_t stream) {
+  constexpr int BM = 32 * RT * WMW, BN = 32 * CT * WNW;
+  const int tiles_m = (int)((M + BM - 1) / BM);
+  const int tiles_n = (int)((N + BN - 1) / BN);
+  const int tiles = tiles_m * tiles_n;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const size_t lds = 2 * (size_t)(BM + BN) * kAStride;
+  auto kern = ternary_gemm_kernel<RT, CT, WMW, WNW, OUT_I32>;
+  if (lds > 48 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  kern<<<dim3((unsigned)(per_xcd * kXcds)), dim3(64 * WMW * WNW), lds, stream>>>(
+      codes, scales, (int)M, K, Wpacked, (int)N, alpha, c, y, acc, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
                        int32_t* acc, hipStream_t stream) {
   const float c = (bits == 8) ? kScaleInt8 : kScaleInt4;
-  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  if (acc) {
-    ternary_gemm_kernel<true><<<grid, dim3(256), 0, stream>>>(codes, scales, (int)M, K, Wpacked,
-                                                             (int)N, alpha, c, y, acc);
-  } else {
-    ternary_gemm_kernel<false><<<grid, dim3(256), 0, stream>>>(codes, scales, (int)M, K, Wpacked,
-                                                              (int)N, alpha, c, y, acc);
+  // 256 x 256 tiles when there are enough of them to fill every CU twice;
+  // 128 x 128 otherwise.
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 512) {
+    return acc ? launch_tile<4, 4, 2, 2, true>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream)
+               : launch_tile<4, 4, 2, 2, false>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
   }
-  return hipGetLastError();
+  return acc ? launch_tile<2, 2, 2, 2, true>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream)
+             : launch_tile<2, 2, 2, 2, false>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
 }
 
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,

@@ -46,12 +46,6 @@ struct GemvArgs {
   float c;
 };
 
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Weights and codes of one super-block for this lane (kb: its 64-weight
 // block). Loads are unconditional from clamped, always-valid addresses, so no
 // branch forces a wait between them. Out-of-range k is neutralized by zeroing
