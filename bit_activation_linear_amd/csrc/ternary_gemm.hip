@@ -7,6 +7,16 @@
 // page's BitLinear_b158 takes the same integer-product-then-rescale form.
 // |q| <= 128 and K <= 32768 keep every int32 sum exact.
 //
+// Weight operand. The MFMA multiplies the codes by the stored 2-bit field
+// u = t + 1 in {0, 1, 2} rather than by t itself, and the epilogue subtracts
+// the row sum of the codes: q . t = q . u - sum(q), exactly, in int32.
+// Unpacking u is a shift and a mask per four weights (no byte remap), and
+// the small non-negative operand toggles fewer MFMA input bits than
+// {-1, 0, +1} = {0xFF, 0x00, 0x01}, which matters because the matrix cores
+// of this chip lower their clock as operand switching activity rises. The
+// row sums come from the code fragments the MFMAs read anyway (v_dot4 with
+// a vector of ones).
+//
 // Work decomposition. A workgroup owns a BM x BN output tile and has
 // WMW x WNW x KS waves: each wave owns a (32 RT) x (32 CT) block of it
 // (RT x CT accumulators of 32x32 int32 in AGPRs) and one of KS interleaved
@@ -15,20 +25,22 @@
 //
 // Staging. Codes and packed weights go from global memory straight into LDS
 // (buffer_load_dwordx4 with the lds bit: each lane's 16 bytes land at
-// base + 16 * lane), so no register holds a tile in transit. LDS is a ring of three stage slots:
-// stage s + 2 is being fetched while stage s is multiplied, and one
-// workgroup barrier per stage both publishes a stage and frees the slot
-// after it. Codes keep their 128-byte k rows, with the 16-byte chunks of a
-// row permuted by a row-dependent XOR so that the 32 rows one MFMA operand
-// read touches fall on distinct LDS banks; the permutation is applied by
-// choosing which global chunk each lane fetches, so every fetch still reads
-// whole 128-byte rows. Packed weights keep their 16-byte blocks, laid out so
-// that lane l of an operand read takes the block of column l.
+// base + 16 * lane), so no register holds a tile in transit. LDS is a ring of
+// three stage slots: stage s + 3 is fetched while stage s + 1 and s + 2 are
+// in flight or waiting, and one workgroup barrier per stage both publishes
+// a stage and frees the slot of the one before it. The fetches are spread
+// between MFMAs, since a wave issuing ten of them back to back stalls for
+// hundreds of cycles. Codes keep their 128-byte k rows, with the 16-byte
+// chunks of a row permuted by a row-dependent XOR so that the rows one MFMA
+// operand read touches fall on distinct LDS banks; the permutation is
+// applied by choosing which global chunk each lane fetches, so every fetch
+// still reads whole 128-byte rows. Packed weights keep their 16-byte
+// blocks, laid out so that lane l of an operand read takes the block of
+// column l.
 //
-// Expansion. Each wave expands the packed weights it multiplies in
-// registers: a 16-byte block of one column holds 64 weights, of which a lane
-// needs the 16 of its k quarter; a shift, a mask and one v_perm_b32 per four
-// weights turn the 2-bit codes into int8 {-1, 0, +1}.
+// Pipeline. Work advances in 64-weight blocks (two k32 sub-steps): while the
+// MFMAs of one block run, the next block's operands are read from LDS, its
+// weights unpacked and its code row sums accumulated.
 //
 // MFMA operands. For the 32x32x32 instruction lane l supplies row (or column)
 // l % 32 and the 16 consecutive k of group g = l / 32. Sub-step h (k32) of a
@@ -45,8 +57,9 @@
 namespace bitnet {
 namespace {
 
-constexpr int BKW = 128;   // k per wave slice per stage
-constexpr int kSlots = 3;  // LDS ring depth
+constexpr int BKW = 128;     // k per wave slice per stage
+constexpr int kSlots = 3;    // LDS ring depth
+constexpr int kChunks = 8;   // MFMA groups per block in the interleaved schedule
 constexpr int kXcds = 8;
 constexpr int kBand = 4;
 
@@ -56,22 +69,26 @@ struct Shape {
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * RT * WMW;
   static constexpr int BN = 32 * CT * WNW;
-  static constexpr int SK = BKW * KS;        // k per stage
-  static constexpr int A_BYTES = BM * SK;    // codes of a stage
+  static constexpr int SK = BKW * KS;          // k per stage
+  static constexpr int A_BYTES = BM * SK;      // codes of a stage
   static constexpr int B_BYTES = BN * SK / 4;  // packed weights of a stage
   static constexpr int SLOT = A_BYTES + B_BYTES;
-  static constexpr int NA = A_BYTES / 1024;  // 1-KB direct loads per stage
+  static constexpr int NA = A_BYTES / 1024;    // 1-KB direct loads per stage
   static constexpr int NB = B_BYTES / 1024;
-  static constexpr int NA_W = NA / NW;       // ... per wave
+  static constexpr int NA_W = NA / NW;         // ... per wave
   static constexpr int NB_W = NB / NW;
-  static constexpr int LDS = kSlots * SLOT;
+  static constexpr int NL_W = NA_W + NB_W;
+  static constexpr int RING = kSlots * SLOT;
+  static constexpr int ROWSUM = RING;          // int32 row sums [KS][BM]
+  static constexpr int LDS = RING + KS * BM * 4;
   static constexpr int PART = RT * CT * 4096;  // one wave's accumulators in bytes
   static_assert(NA_W * NW == NA && NB_W * NW == NB && NB_W >= 1, "uneven staging");
-  static_assert(KS == 1 || (KS / 2) * WMW * WNW * PART <= LDS, "reduction does not fit");
+  static_assert(KS == 1 || (KS / 2) * WMW * WNW * PART <= RING, "reduction does not fit");
+  static_assert((2 * RT * CT) % kChunks == 0, "MFMA groups");
 };
 
 // Buffer resource over [base, base + bytes): raw (stride 0) dword access;
-// loads at or past `bytes` return zero.
+// loads at or past `bytes` return zero and touch no memory.
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u4 make_rsrc(const void* base, unsigned bytes) {
   const size_t a = reinterpret_cast<size_t>(base);
@@ -114,13 +131,22 @@ __device__ __forceinline__ int chunk_swizzle(int r) { return (r & 7) ^ ((r >> 3)
 #define BITNET_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-__device__ __forceinline__ v4i expand_shifted(const uint4 p, int sh) {
+// The 2-bit fields at bit offset sh of each byte: u = t + 1 for 16 weights.
+__device__ __forceinline__ v4i unpack_u(const uint4 p, int sh) {
   v4i r;
-  r.x = (int)__builtin_amdgcn_perm(0u, kCodeLut, (p.x >> sh) & 0x03030303u);
-  r.y = (int)__builtin_amdgcn_perm(0u, kCodeLut, (p.y >> sh) & 0x03030303u);
-  r.z = (int)__builtin_amdgcn_perm(0u, kCodeLut, (p.z >> sh) & 0x03030303u);
-  r.w = (int)__builtin_amdgcn_perm(0u, kCodeLut, (p.w >> sh) & 0x03030303u);
+  r.x = (int)((p.x >> sh) & 0x03030303u);
+  r.y = (int)((p.y >> sh) & 0x03030303u);
+  r.z = (int)((p.z >> sh) & 0x03030303u);
+  r.w = (int)((p.w >> sh) & 0x03030303u);
   return r;
+}
+
+// Sum of the 16 signed bytes of a code fragment, added to s.
+__device__ __forceinline__ int add_bytes(const v4i a, int s) {
+  s = __builtin_amdgcn_sdot4(a.x, 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(a.y, 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(a.z, 0x01010101, s, false);
+  return __builtin_amdgcn_sdot4(a.w, 0x01010101, s, false);
 }
 
 template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32>
@@ -158,38 +184,45 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
   // one slice for 32 columns. The loads go through buffer resources that end
   // at the tile's last valid row (column): rows past M and columns past N
   // read as zero, and k past K reads either the next row's bytes or zero --
-  // in both cases data that is never multiplied, and never a fault.
+  // in both cases data that is never multiplied, and never a fault. Fetches
+  // of stages past the last go through empty resources: they write zeros to
+  // a free slot and read no memory, which keeps every stage's load count,
+  // and so the vmcnt bookkeeping, uniform.
   const u4 a_rsrc = make_rsrc(codes + (size_t)m0 * K,
                               (unsigned)((M - m0 < S::BM ? M - m0 : S::BM) * K));
   const u4 b_rsrc = make_rsrc(Wp + (size_t)n0 * wrow,
                               (unsigned)((N - n0 < S::BN ? N - n0 : S::BN) * wrow));
+  u4 a_none = a_rsrc, b_none = b_rsrc;
+  a_none.z = 0;
+  b_none.z = 0;
   const unsigned lds0 = lds_address(smem);
-  int a_voff[S::NA_W], b_voff[S::NB_W];
-  unsigned a_lds[S::NA_W], b_lds[S::NB_W];
+  int voff[S::NL_W];
+  unsigned ldst[S::NL_W];
 #pragma unroll
   for (int i = 0; i < S::NA_W; ++i) {
     const int q = wave + S::NW * i;
     const int slice = q / (S::BM / 8), rb = q % (S::BM / 8);
     const int r = rb * 8 + (lane >> 3);
-    a_voff[i] = r * K + slice * BKW + 16 * ((lane & 7) ^ chunk_swizzle(r));
-    a_lds[i] = lds0 + slice * S::BM * BKW + rb * 1024;
+    voff[i] = r * K + slice * BKW + 16 * ((lane & 7) ^ chunk_swizzle(r));
+    ldst[i] = lds0 + slice * S::BM * BKW + rb * 1024;
   }
 #pragma unroll
   for (int i = 0; i < S::NB_W; ++i) {
     const int q = wave + S::NW * i;
     const int slice = q / (S::BN / 32), cg = q % (S::BN / 32);
-    b_voff[i] = (cg * 32 + l32) * wrow + (slice * 2 + g) * 16;
-    b_lds[i] = lds0 + S::A_BYTES + slice * (S::BN / 32) * 1024 + cg * 1024;
+    voff[S::NA_W + i] = (cg * 32 + l32) * wrow + (slice * 2 + g) * 16;
+    ldst[S::NA_W + i] = lds0 + S::A_BYTES + slice * (S::BN / 32) * 1024 + cg * 1024;
   }
-
-#define BITNET_ISSUE(ks_, slot_)                                                                \
+  // Load i of stage ks_ into slot slot_.
+#define BITNET_LOAD(ks_, slot_, i)                                                              \
   {                                                                                             \
-    const unsigned so_ = (unsigned)(slot_) * S::SLOT;                                           \
-    const int ka_ = (ks_) * S::SK, kb_ = (ks_) * S::SK / 4;                                     \
-    _Pragma("unroll") for (int i = 0; i < S::NA_W; ++i)                                         \
-        load_lds16(a_rsrc, a_voff[i] + ka_, a_lds[i] + so_);                                    \
-    _Pragma("unroll") for (int i = 0; i < S::NB_W; ++i)                                         \
-        load_lds16(b_rsrc, b_voff[i] + kb_, b_lds[i] + so_);                                    \
+    const bool live_ = (ks_) < nst;                                                             \
+    if ((i) < S::NA_W)                                                                          \
+      load_lds16(live_ ? a_rsrc : a_none, voff[i] + (ks_) * S::SK,                              \
+                 ldst[i] + (unsigned)(slot_) * S::SLOT);                                        \
+    else                                                                                        \
+      load_lds16(live_ ? b_rsrc : b_none, voff[i] + (ks_) * (S::SK / 4),                        \
+                 ldst[i] + (unsigned)(slot_) * S::SLOT);                                        \
   }
 
   // Operand reads. Codes: row wm*32RT + rt*32 + l32 of this wave's slice,
@@ -211,68 +244,154 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0;
+  int rsum[RT];  // this lane's share of the code row sums of its RT rows
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) rsum[rt] = 0;
 
-  // One 64-weight block (two k32 sub-steps) of the slice in slot slot_.
-#define BITNET_BLOCK(slot_, blk_)                                                               \
+  // Fragment sets X and Y alternate between the block being multiplied and
+  // the block being prepared.
+  v4i ax[2][RT], ay[2][RT];  // codes, per sub-step
+  v4i bx[2][CT], by[2][CT];  // weight fields u, per sub-step
+  uint4 pw[CT];              // packed weights of the block being prepared
+
+#define BITNET_READ(slot_, blk_, A_)                                                            \
   {                                                                                             \
     const char* sb_ = smem + (slot_) * S::SLOT;                                                 \
-    uint4 pw_[CT];                                                                              \
-    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) pw_[ct] =                                 \
+    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) pw[ct] =                                  \
         *reinterpret_cast<const uint4*>(sb_ + b_rd + ct * 1024 + (blk_) * 512);                 \
-    _Pragma("unroll") for (int hh = 0; hh < 2; ++hh) {                                          \
-      v4i af_[RT];                                                                              \
-      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) af_[rt] =                               \
-          *reinterpret_cast<const v4i*>(sb_ + a_rd[2 * (blk_) + hh] + rt * 32 * BKW);           \
-      v4i bf_[CT];                                                                              \
-      _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) bf_[ct] =                               \
-          expand_shifted(pw_[ct], 2 * g + 4 * hh);                                              \
-      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                         \
-          _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) acc[rt][ct] =                       \
-              __builtin_amdgcn_mfma_i32_32x32x32_i8(af_[rt], bf_[ct], acc[rt][ct], 0, 0, 0);    \
+    _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                            \
+        _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) A_[hh][rt] =                          \
+            *reinterpret_cast<const v4i*>(sb_ + a_rd[2 * (blk_) + hh] + rt * 32 * BKW);         \
+  }
+#define BITNET_UNPACK(B_)                                                                       \
+  _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                              \
+      _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) B_[hh][ct] =                            \
+          unpack_u(pw[ct], 2 * g + 4 * hh);
+#define BITNET_MMA(A_, B_)                                                                      \
+  _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                              \
+      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                       \
+    rsum[rt] = add_bytes(A_[hh][rt], rsum[rt]);                                                 \
+    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) acc[rt][ct] =                             \
+        __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct], acc[rt][ct], 0, 0, 0);    \
+  }
+  // The empty asm statements pin the next block's operands (codes read and
+  // weights unpacked) to the step that prepares them: otherwise the compiler
+  // sinks that work to its first use, past the MFMAs it is meant to overlap.
+#define BITNET_PIN(A_, B_)                                                                      \
+  _Pragma("unroll") for (int hh = 0; hh < 2; ++hh) {                                            \
+    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) asm volatile("" : "+v"(B_[hh][ct]));      \
+    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) asm volatile("" : "+v"(A_[hh][rt]));      \
+  }
+  // One block's MFMAs (operands A_, B_) cut into kChunks groups separated by
+  // scheduling barriers. Group 0 gives the next block's LDS reads (issued
+  // just before) time to land; the unpacking of its weights into NB_, the
+  // row sums of A_ and, when LD_ is set, this wave's share of the loads of
+  // stage lks_ into slot lslot_ are spread over the later groups, so the
+  // matrix pipe always has work queued.
+  constexpr int kMfmaPerBlock = 2 * RT * CT;
+  constexpr int kUnpackPerBlock = 2 * CT;
+  constexpr int kSumPerBlock = 2 * RT;
+#define BITNET_STEP(A_, B_, NB_, LD_, lks_, lslot_)                                             \
+  _Pragma("unroll") for (int ch = 0; ch < kChunks; ++ch) {                                      \
+    _Pragma("unroll") for (int e = 0; e < kUnpackPerBlock; ++e) {                               \
+      if (1 + e * (kChunks - 1) / kUnpackPerBlock == ch)                                        \
+        NB_[e / CT][e % CT] = unpack_u(pw[e % CT], 2 * g + 4 * (e / CT));                       \
     }                                                                                           \
+    _Pragma("unroll") for (int e = 0; e < kSumPerBlock; ++e) {                                  \
+      if (1 + e * (kChunks - 1) / kSumPerBlock == ch)                                           \
+        rsum[e % RT] = add_bytes(A_[e / RT][e % RT], rsum[e % RT]);                             \
+    }                                                                                           \
+    if (LD_) {                                                                                  \
+      _Pragma("unroll") for (int i = 0; i < S::NL_W; ++i) {                                     \
+        if (i * kChunks / S::NL_W == ch) BITNET_LOAD(lks_, lslot_, i)                           \
+      }                                                                                         \
+    }                                                                                           \
+    _Pragma("unroll") for (int f = ch * (kMfmaPerBlock / kChunks);                              \
+                           f < (ch + 1) * (kMfmaPerBlock / kChunks); ++f) {                     \
+      const int hh = f / (RT * CT), rt = (f / CT) % RT, ct = f % CT;                            \
+      acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct], acc[rt][ct],  \
+                                                          0, 0, 0);                             \
+    }                                                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
   }
 
-  constexpr int kLoadsPerStage = S::NA_W + S::NB_W;
   const int nst = (nKB + 2 * KS - 1) / (2 * KS);  // stages, the last possibly partial
   const int nfull = nKB / (2 * KS);               // stages whose every slice is whole
 
-  BITNET_ISSUE(0, 0)
-  if (nst > 1) BITNET_ISSUE(1, 1)
+  // Prologue: stages 0..2 in flight, stage 0 published, its block 0 read.
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int i = 0; i < S::NL_W; ++i) BITNET_LOAD(s, s, i)
+  BITNET_WAIT_VMCNT(2 * S::NL_W);
+  lds_barrier();
+  BITNET_READ(0, 0, ax)
+  BITNET_UNPACK(bx)
+
   int slot = 0;
   for (int ks = 0; ks < nfull; ++ks) {
-    // This wave's loads of stage ks are done once at most the next stage's
-    // are outstanding; the barrier then makes every wave's loads visible and
-    // guarantees that stage ks - 1's slot is no longer being read.
-    if (ks + 1 < nst) {
-      BITNET_WAIT_VMCNT(kLoadsPerStage);
-    } else {
-      BITNET_WAIT_VMCNT(0);
-    }
+    const int nslot = slot == 2 ? 0 : slot + 1;
+    // Block 0 of stage ks (set X) runs while block 1 (set Y) is prepared.
+    __builtin_amdgcn_sched_barrier(0);
+    BITNET_READ(slot, 1, ay)
+    BITNET_STEP(ax, bx, by, false, 0, 0)
+    BITNET_PIN(ay, by)
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage boundary. This wave's loads of stage ks + 1 are complete once at
+    // most those of stage ks + 2 are outstanding; after the barrier every
+    // wave's are visible and no wave reads stage ks any more, so its slot
+    // takes stage ks + 3.
+    BITNET_WAIT_VMCNT(S::NL_W);
     lds_barrier();
-    if (ks + 2 < nst) {
-      const int ns = slot == 0 ? 2 : slot - 1;  // (ks + 2) % 3
-      BITNET_ISSUE(ks + 2, ns)
-    }
-    BITNET_BLOCK(slot, 0)
-    BITNET_BLOCK(slot, 1)
-    slot = slot == 2 ? 0 : slot + 1;
+    // Block 1 of stage ks (set Y) runs while block 0 of stage ks + 1 (set X)
+    // is prepared (past the last stage this reads a stale slot, unused) and
+    // stage ks + 3 is fetched.
+    __builtin_amdgcn_sched_barrier(0);
+    BITNET_READ(nslot, 0, ax)
+    BITNET_STEP(ay, by, bx, true, ks + 3, slot)
+    BITNET_PIN(ax, bx)
+    __builtin_amdgcn_sched_barrier(0);
+    slot = nslot;
   }
   if (nst > nfull) {
-    // Partial last stage: this wave's slice holds vb whole blocks (0..2).
-    BITNET_WAIT_VMCNT(0);
-    lds_barrier();
+    // Partial last stage (published by the last boundary above, or by the
+    // prologue): this wave's slice holds vb whole blocks (0..2).
     const int vb = nKB - nfull * 2 * KS - 2 * kw;
-    if (vb >= 1) BITNET_BLOCK(slot, 0)
-    if (vb >= 2) BITNET_BLOCK(slot, 1)
+    if (vb >= 1) {
+      BITNET_READ(slot, 0, ax)
+      BITNET_UNPACK(bx)
+      BITNET_MMA(ax, bx)
+    }
+    if (vb >= 2) {
+      BITNET_READ(slot, 1, ay)
+      BITNET_UNPACK(by)
+      BITNET_MMA(ay, by)
+    }
   }
-#undef BITNET_ISSUE
-#undef BITNET_BLOCK
+#undef BITNET_READ
+#undef BITNET_UNPACK
+#undef BITNET_MMA
+#undef BITNET_STEP
+#undef BITNET_PIN
+#undef BITNET_LOAD
+
+  // No load may still be writing LDS past this point.
+  BITNET_WAIT_VMCNT(0);
+
+  // Row sums: add the two k halves (lane groups g = 0, 1) and publish the
+  // slice's sums per tile row; every wave of a (wm, kw) pair holds the same
+  // values, the one with wn = 0 writes them.
+  int* rowsum = reinterpret_cast<int*>(smem + S::ROWSUM);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int total = rsum[rt] + __shfl_xor(rsum[rt], 32);
+    if (wn == 0 && g == 0) rowsum[kw * S::BM + wm * 32 * RT + rt * 32 + l32] = total;
+  }
+  lds_barrier();
 
   if constexpr (KS > 1) {
-    // Add the k slices' partial sums through LDS, halving the number of
+    // Add the k slices' partial products through LDS, halving the number of
     // live slices per round; slice 0's waves end up with the full sums.
-    BITNET_WAIT_VMCNT(0);
-    lds_barrier();
 #pragma unroll
     for (int step = KS / 2; step >= 1; step >>= 1) {
       if (kw >= step && kw < 2 * step) {
@@ -310,30 +429,32 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
       lds_barrier();
     }
     if (kw != 0) return;
-  } else {
-    // No load may still be writing LDS when the workgroup retires.
-    BITNET_WAIT_VMCNT(0);
   }
 
   // 32x32 output layout: lane holds column l32 and, for v = 0..15, row
-  // 8*(v/4) + 4*g + v%4 of its 32x32 block.
+  // 8*(v/4) + 4*g + v%4 of its 32x32 block. q . t = q . u - sum(q).
   const float alpha = OUT_I32 ? 0.0f : *alpha_p;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * 32 * RT + rt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      const int r = wm * 32 * RT + rt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      const int m = m0 + r;
       if (m >= M) continue;
+      int rs = 0;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) rs += rowsum[s * S::BM + r];
       const float f = OUT_I32 ? 0.0f : dequant_factor(alpha, scales[m], c);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const int n = n0 + wn * 32 * CT + ct * 32 + l32;
         if (n >= N) continue;
         const size_t o = (size_t)m * N + n;
+        const int dot = acc[rt][ct][v] - rs;
         if (OUT_I32) {
-          acc_out[o] = acc[rt][ct][v];
+          acc_out[o] = dot;
         } else {
-          y[o] = (float)acc[rt][ct][v] * f;
+          y[o] = (float)dot * f;
         }
       }
     }
@@ -376,12 +497,14 @@ hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int 
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
                        int32_t* acc, hipStream_t stream) {
   const float c = (bits == 8) ? kScaleInt8 : kScaleInt4;
-  // 256 x 256 tiles (one k slice per stage) when there are enough of them to
-  // give every CU several; otherwise 128 x 128 tiles whose four waves split
-  // each 256-wide stage into two k slices.
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  // 128 x 512 tiles (four waves side by side along N, one k slice per stage)
+  // when there are enough of them to give every CU several: codes cost four
+  // times the bytes of packed weights per element, so a tile wide in N
+  // fetches the fewest bytes per MFMA. Otherwise 128 x 128 tiles whose four
+  // waves split each 256-wide stage into two k slices.
+  const int64_t big_tiles = ((M + 127) / 128) * ((N + 511) / 512);
   if (big_tiles >= 1024)
-    return launch_variant<4, 4, 2, 2, 1>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
+    return launch_variant<4, 4, 1, 4, 1>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
   return launch_variant<4, 2, 1, 2, 2>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
 }
 

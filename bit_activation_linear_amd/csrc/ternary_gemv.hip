@@ -21,10 +21,10 @@
 // load in flight, draining the weight stream at each barrier.
 //
 // With hadamard = 0 and a small batch the per-token quantization (Eq. 5-6)
-// runs in the same kernel: each workgroup reads the whole (tiny) x first,
-// reduces the per-token statistic with DPP, writes the codes to LDS and feeds
-// the MFMA from there, all while its weight loads are in flight, so the decode
-// forward is one launch.
+// runs in the same kernel: each wave quantizes the slice of the (tiny) x that
+// its own MFMAs consume, with one workgroup barrier to combine the per-token
+// statistic, all while its weight loads are in flight, so the decode forward
+// is one launch.
 #include "kernels.h"
 #include "ternary_common.cuh"
 
@@ -33,6 +33,7 @@ namespace {
 
 constexpr float kEps = 1e-7f;
 constexpr int kRoundsInFlight = 4;  // super-blocks whose loads a lane issues together
+constexpr int kFusedCt = 2;         // 16-column tiles per workgroup in the fused decode kernel
 
 struct GemvArgs {
   const int8_t* codes;
@@ -182,52 +183,72 @@ __device__ __forceinline__ float wave_reduce(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Decode forward with the quantization fused in. Requires K/4 <= blockDim.x
-// (each thread owns at most one 4-element chunk per token row) and M <= MG.
-template <typename XT, int BITS, int MG>
+// Decode forward with the quantization fused in. Requires M <= MG and
+// 256 * waves >= K (wave w owns the super-block k in [256 w, 256 w + 256),
+// for the statistic, for the codes and for the product).
+//
+// Each lane loads its packed weights, then 4 consecutive x values of every
+// token row in its wave's super-block; the per-row statistic (Eq. 5: absmax, or
+// Eq. 6: mean |x|) of the super-block is reduced in the wave with DPP, and a
+// single barrier publishes the waves' partial statistics. Every wave then
+// combines them in the same fixed order, quantizes its own values and hands
+// them to the lanes that feed them to the MFMA through a wave-private LDS
+// region (no further barrier), so little work separates the arrival of the
+// data from the product.
+template <typename XT, int BITS, int MG, int CT>
 __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nw = blockDim.x >> 6;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  v4i* red = reinterpret_cast<v4i*>(smem);
-  int8_t* qlds = reinterpret_cast<int8_t*>(smem + (size_t)nw * 1024);
-  const int mk16 = ((a.M * a.K) + 15) & ~15;
-  float* part = reinterpret_cast<float*>(qlds + mk16);  // [nw][16]
-  float* srow = part + nw * 16;                         // [16]
+  v4i* red = reinterpret_cast<v4i*>(smem);                                // [nw][CT][64]
+  float* part = reinterpret_cast<float*>(smem + (size_t)nw * CT * 1024);  // [nw][16]
+  float* srow = part + nw * 16;                                           // [16]
+  int8_t* qw = reinterpret_cast<int8_t*>(srow + 16) + (size_t)wave * a.M * 256;  // [M][256]
 
-  // x first, unconditionally from clamped addresses: those loads return
-  // first, so the statistic below waits on them alone while the weight load
-  // issued right after is still in flight.
+  const int col = lane & 15, grp = lane >> 4;
+  const int nKB = a.K >> 6;
+  const int kb = wave * 4 + grp;
+  const bool k_ok = kb < nKB;
+  // The weight load goes out first: it is the long pole (HBM), and a
+  // statistic that waited on x alone would let the x requests, which every
+  // workgroup sends to the same few lines, queue ahead of it. Loads are
+  // unconditional from clamped, always-valid addresses.
+  uint4 p[CT];
+  {
+    const size_t row_bytes = (size_t)(a.K >> 2);
+    const int kbc = kb < nKB ? kb : nKB - 1;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int n = (blockIdx.x * CT + ct) * 16 + col;
+      const int nc = n < a.N ? n : a.N - 1;
+      // an out-of-range block meets all-zero codes below
+      p[ct] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
+    }
+  }
+  // Then 4 consecutive x values of every token row in this wave's
+  // super-block.
   const XT* x = reinterpret_cast<const XT*>(a.x);
-  const int K4 = a.K >> 2;
-  const bool own = t < K4;
-  const int tc = own ? t : 0;
+  const int k0 = 256 * wave + 4 * lane;
+  const bool own = k0 < a.K;
+  const int kc = own ? k0 : 0;
+  // (Rows past M are not loaded: every workgroup reads this x, and
+  // redundant requests for the same lines queue at the L2.)
   float v[MG][4];
 #pragma unroll
   for (int m = 0; m < MG; ++m) {
-    const int mc = m < a.M ? m : a.M - 1;
-    load4(x, (size_t)mc * a.K + 4 * tc, v[m]);
+    if (m < a.M) {
+      load4(x, (size_t)m * a.K + kc, v[m]);
+    } else {
+      v[m][0] = v[m][1] = v[m][2] = v[m][3] = 0.0f;
+    }
   }
 
-  const int col = lane & 15, grp = lane >> 4;
-  const int nKB = a.K >> 6, nSB = (nKB + 3) >> 2;
-  const int sb = wave;
-  const int kb = sb * 4 + grp;
-  const bool k_ok = wave < a.sb_waves && sb < nSB && kb < nKB;
-  uint4 p[1];
-  {
-    const size_t row_bytes = (size_t)(a.K >> 2);
-    const int n = blockIdx.x * 16 + col;
-    const int nc = n < a.N ? n : a.N - 1;
-    const int kbc = kb < nKB ? kb : nKB - 1;
-    // an out-of-range block meets all-zero codes below
-    p[0] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
-  }
+
+  // Partial statistic of this wave's super-block, one per token row.
 #pragma unroll
   for (int m = 0; m < MG; ++m) {
     if (m < a.M) {
-      // threads past the row hold a clamped duplicate: they contribute 0
       float s;
       if (BITS == 8) {
         s = fmaxf(fmaxf(fabsf(v[m][0]), fabsf(v[m][1])), fmaxf(fabsf(v[m][2]), fabsf(v[m][3])));
@@ -240,19 +261,20 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
     }
   }
   lds_barrier();
-  if (t < a.M) {
-    float s = 0.0f;
-    for (int w = 0; w < nw; ++w) s = (BITS == 8) ? fmaxf(s, part[w * 16 + t]) : s + part[w * 16 + t];
-    if (BITS == 4) s = s / (float)a.K;
-    srow[t] = s + kEps;
-  }
-  lds_barrier();
+
+  // Whole-row statistic (every wave combines the partials in the same
+  // order, so all agree bit for bit) and this wave's codes.
   const float lo = (BITS == 8) ? -128.0f : -8.0f;
   const float hi = (BITS == 8) ? 127.0f : 7.0f;
 #pragma unroll
   for (int m = 0; m < MG; ++m) {
-    if (m < a.M && own) {
-      const float mult = a.c / srow[m];
+    if (m < a.M) {
+      float s = 0.0f;
+      for (int w = 0; w < nw; ++w) s = (BITS == 8) ? fmaxf(s, part[w * 16 + m]) : s + part[w * 16 + m];
+      if (BITS == 4) s = s / (float)a.K;
+      s += kEps;
+      if (wave == 0 && lane == m) srow[m] = s;
+      const float mult = a.c / s;
       unsigned word = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -260,23 +282,24 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
         q = fminf(fmaxf(q, lo), hi);
         word |= ((unsigned)(int)q & 0xFFu) << (8 * e);
       }
-      *reinterpret_cast<unsigned*>(qlds + (size_t)m * a.K + 4 * t) = word;
+      *reinterpret_cast<unsigned*>(qw + m * 256 + 4 * lane) = own ? word : 0u;
     }
   }
-  lds_barrier();
+  // The codes just written are read back by other lanes of the same wave;
+  // LDS serves a wave's accesses in order, so only the compiler needs fencing.
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
+  // MFMA operand: lane (col, grp) feeds token row col, block kb = 4 wave + grp.
+  const int kmask = (k_ok && col < a.M) ? -1 : 0;
+  const int8_t* qr = qw + (col < a.M ? col : 0) * 256 + grp * 64;
   v4i av[4];
-  if (k_ok && col < a.M) {
-    const v4i* ap = reinterpret_cast<const v4i*>(qlds + (size_t)col * a.K + (size_t)kb * 64);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) av[j] = ap[j];
-  } else {
+  for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const v4i*>(qr + 16 * j) & kmask;
+  v4i acc[CT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) av[j] = v4i{0, 0, 0, 0};
-  }
-  v4i acc[1] = {v4i{0, 0, 0, 0}};
-  if (wave < a.sb_waves) mma_round<1>(av, p, acc);
-  gemv_finish<1, false>(a, acc, red, srow);
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
+  mma_round<CT>(av, p, acc);
+  gemv_finish<CT, false>(a, acc, red, srow);
 }
 
 template <typename Kern>
@@ -296,15 +319,21 @@ hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stre
   return hipGetLastError();
 }
 
-template <typename XT, int BITS, int MG>
-hipError_t launch_fused_t(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+template <typename XT, int BITS, int MG, int CT>
+hipError_t launch_fused_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   const int nw = p.threads / 64;
-  const size_t lds = (size_t)nw * 1024 + (size_t)((a.M * a.K + 15) & ~15) + (size_t)nw * 16 * 4 + 64;
-  auto kern = fused_decode_kernel<XT, BITS, MG>;
+  const size_t lds = (size_t)nw * CT * 1024 + (size_t)nw * 16 * 4 + 64 + (size_t)nw * a.M * 256;
+  auto kern = fused_decode_kernel<XT, BITS, MG, CT>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a);
+  const unsigned groups = (unsigned)((a.N + 16 * CT - 1) / (16 * CT));
+  kern<<<dim3(groups), dim3(p.threads), lds, stream>>>(a);
   return hipGetLastError();
+}
+
+template <typename XT, int BITS, int MG>
+hipError_t launch_fused_t(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+  return launch_fused_ct<XT, BITS, MG, kFusedCt>(p, a, stream);
 }
 
 }  // namespace
@@ -344,6 +373,13 @@ hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
   a.N = (int)N;
   a.sb_waves = p.sb_waves;
   a.c = (bits == 8) ? kScaleInt8 : kScaleInt4;
+  if (M == 1) {  // single token: the smallest code, which a cold launch fetches fastest
+    if (x_dtype == 1)
+      return bits == 8 ? launch_fused_t<uint16_t, 8, 1>(p, a, stream)
+                       : launch_fused_t<uint16_t, 4, 1>(p, a, stream);
+    return bits == 8 ? launch_fused_t<float, 8, 1>(p, a, stream)
+                     : launch_fused_t<float, 4, 1>(p, a, stream);
+  }
   if (M <= 4) {
     if (x_dtype == 1)
       return bits == 8 ? launch_fused_t<uint16_t, 8, 4>(p, a, stream)
