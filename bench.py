@@ -14,6 +14,10 @@ The JSON line also carries:
   roofline      the dominant kernel (the ternary product) timed per launch with
                 HIP events on the launch stream, against the 8 TB/s HBM peak
                 (decode) or the 5.03 POP/s dense int8 MFMA peak (prefill);
+                `traffic` is the kernel's HBM bytes per launch from the
+                committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary under
+                profiles/ (copy-kernel calibrated), null once the kernel's
+                sources differ from the ones those counters were taken on;
   cpu_baseline  the fp64 CPU oracle on the host cores, on a bounded sample;
   per_workload  every measured workload at full size (prefill TOPS, decode
                 GB/s, the on-device ternarize+pack pass).
@@ -181,6 +185,32 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
     return p, res
 
 
+def _recorded_traffic(kernel, key):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of `kernel` on workload `key`, or None when there is none or when
+    the kernel's sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{key}.pmc_traffic.md")
+    if not os.path.exists(path):
+        return None, None
+    fields = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith((" ", "|", "#")):
+                k, v = ln.split(":", 1)
+                fields[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for rel in fields["source_files"].split():
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != fields["source_sha256"]:
+            return None, os.path.relpath(path, ROOT) + " (stale: kernel sources changed)"
+        return float(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    except (KeyError, OSError, ValueError):
+        return None, None
+
+
 def _cpu_baseline(key, budget_s):
     """fp64 oracle on a bounded number of whole forward calls of the workload."""
     import oracle
@@ -257,7 +287,10 @@ def main():
                            else "2*M*N*K int8 ops per launch")
     roof["launch_us_mean"] = head["matmul_kernel_us_mean"]
     roof["timing"] = "HIP events around one HIP-graph replay of back-to-back launches"
-    roof["traffic"] = None
+    traffic, source = _recorded_traffic(roof["kernel"], key)
+    roof["traffic"] = traffic
+    if source:
+        roof["traffic_source"] = source
     _log(f"[bench] {key}: forward {head['forward_us']:.2f} us, matmul {head['matmul_kernel_us_mean']:.2f} us")
     del p
 
