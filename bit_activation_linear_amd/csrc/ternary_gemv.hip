@@ -7,11 +7,10 @@
 //
 // The kernel is bound by the packed weights streaming from HBM (N*K/4 bytes)
 // and, at decode sizes, by the latency of that stream. Tokens are the 16-row
-// side of the MFMA (rows >= M are zero). A workgroup owns `ct` 16-column
-// tiles and the whole of K: its waves take interleaved 256-k super-blocks
-// (each 16-lane group one 64-weight block, so a lane loads one 16-B packed
-// vector per super-block and column tile), issue every load of up to four
-// super-blocks before the first MFMA, and add their tiles up through LDS.
+// side of the MFMA (rows >= M are zero). A workgroup owns 16-column tiles
+// and the whole of K: its waves take interleaved 256-k super-blocks (four
+// 64-weight blocks), issue every load of up to four super-blocks before the
+// first MFMA, and add their tiles up through LDS.
 // Workgroups never exchange data: on this chip the eight XCD L2 caches are
 // not coherent with one another, so a cross-workgroup reduction inside one
 // kernel would need an L2 write-back per wave.
@@ -47,31 +46,6 @@ struct GemvArgs {
   float c;
 };
 
-// Weights and codes of one super-block for this lane (kb: its 64-weight
-// block). Loads are unconditional from clamped, always-valid addresses, so no
-// branch forces a wait between them. Out-of-range k is neutralized by zeroing
-// the codes with a bit mask (a branch that overwrote a loaded register would
-// have to wait for the load); out-of-range columns and token rows only feed
-// outputs that are never stored.
-template <int CT>
-__device__ __forceinline__ void load_round(const GemvArgs& a, const int8_t* codes_base, int kb,
-                                           bool k_ok, int col, uint4 (&p)[CT], v4i (&av)[4]) {
-  const size_t row_bytes = (size_t)(a.K >> 2);
-  const int nKB = a.K >> 6;
-  const int kbc = kb < nKB ? kb : nKB - 1;
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int n = (blockIdx.x * CT + ct) * 16 + col;
-    const int nc = n < a.N ? n : a.N - 1;
-    p[ct] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
-  }
-  const int mc = col < a.M ? col : a.M - 1;
-  const v4i* ap = reinterpret_cast<const v4i*>(codes_base + (size_t)mc * a.K + (size_t)kbc * 64);
-  const int kmask = k_ok ? -1 : 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) av[j] = ap[j] & kmask;
-}
-
 template <int CT>
 __device__ __forceinline__ void mma_round(const v4i (&av)[4], const uint4 (&p)[CT], v4i (&acc)[CT]) {
 #pragma unroll
@@ -82,30 +56,77 @@ __device__ __forceinline__ void mma_round(const v4i (&av)[4], const uint4 (&p)[C
                                                        0, 0);
 }
 
+// Codes of one super-block are staged through a wave-private LDS area with
+// this row pitch (256 B of k plus 16 B of padding, so the 16 token rows an
+// MFMA operand read touches start on distinct banks).
+constexpr int kCodePitch = 272;
+
 // The wave's share of the product; codes_base is the [M, K] code matrix.
+//
+// Weights: lane (col, grp) loads the packed block 4 sb + grp of its column
+// (the four lanes of a column cover 64 contiguous bytes). Codes: the MFMA
+// wants row col, block 4 sb + grp, k-quarter j from that lane, a pattern that
+// touches 64 separate 16-byte pieces per load instruction; every workgroup
+// streams the whole code matrix, and at that rate the L2 -> CU path serves
+// such scattered loads at well under half the rate of contiguous ones. So
+// the codes are loaded as 4 rows x 256 contiguous bytes per instruction,
+// written to the wave's LDS area and read back in MFMA order (the same wave
+// writes and reads, so no barrier is needed).
 template <int CT>
 __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* codes_base,
-                                             v4i (&acc)[CT]) {
+                                             int8_t* stage, v4i (&acc)[CT]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int nKB = a.K >> 6, nSB = (nKB + 3) >> 2;
   const int rounds = (nSB + a.sb_waves - 1) / a.sb_waves;
+  const size_t row_bytes = (size_t)(a.K >> 2);
+  // contiguous code chunk i of this lane: token row 4 i + lane / 16, byte 16 (lane % 16) of the super-block
+  const int crow = lane >> 4, cbyte = 16 * (lane & 15);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
   if (wave >= a.sb_waves) return;
   for (int r0 = 0; r0 < rounds; r0 += kRoundsInFlight) {
     uint4 p[kRoundsInFlight][CT];
-    v4i av[kRoundsInFlight][4];
+    v4i cv[kRoundsInFlight][4];
 #pragma unroll
     for (int u = 0; u < kRoundsInFlight; ++u) {
       const int sb = wave + a.sb_waves * (r0 + u);
-      const int kb = sb * 4 + grp;
-      const bool k_ok = (r0 + u < rounds) && sb < nSB && kb < nKB;
-      load_round<CT>(a, codes_base, kb, k_ok, col, p[u], av[u]);
+      const int sbc = sb < nSB ? sb : nSB - 1;
+      const int kb = sbc * 4 + grp;
+      const int kbc = kb < nKB ? kb : nKB - 1;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int n = (blockIdx.x * CT + ct) * 16 + col;
+        const int nc = n < a.N ? n : a.N - 1;
+        p[u][ct] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
+      }
+      // Unconditional loads from clamped addresses; what is out of range is
+      // zeroed with a mask (a branch would force a wait on the load).
+      const int k = sbc * 256 + cbyte;
+      const bool k_ok = (r0 + u < rounds) && sb < nSB && k < a.K;
+      const int kc = k < a.K ? k : a.K - 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * i + crow;
+        const int mc = m < a.M ? m : a.M - 1;
+        const int mask = (k_ok && m < a.M) ? -1 : 0;
+        cv[u][i] = *reinterpret_cast<const v4i*>(codes_base + (size_t)mc * a.K + kc) & mask;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kRoundsInFlight; ++u) {
-      if (r0 + u < rounds) mma_round<CT>(av[u], p[u], acc);
+      if (r0 + u < rounds) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<v4i*>(stage + (4 * i + crow) * kCodePitch + cbyte) = cv[u][i];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        v4i av[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          av[j] = *reinterpret_cast<const v4i*>(stage + col * kCodePitch + 64 * grp + 16 * j);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        mma_round<CT>(av, p[u], acc);
+      }
     }
   }
 }
@@ -144,9 +165,13 @@ __device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[
 
 template <int CT, bool OUT_I32>
 __global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a) {
-  extern __shared__ v4i red[];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nw = blockDim.x >> 6;
+  v4i* red = reinterpret_cast<v4i*>(smem);  // [nw][CT][64]
+  int8_t* stage = reinterpret_cast<int8_t*>(smem + (size_t)nw * CT * 1024) +
+                  (size_t)(threadIdx.x >> 6) * 16 * kCodePitch;
   v4i acc[CT];
-  wave_product<CT>(a, a.codes, acc);
+  wave_product<CT>(a, a.codes, stage, acc);
   gemv_finish<CT, OUT_I32>(a, acc, red, a.scales);
 }
 
@@ -311,7 +336,7 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
 
 template <int CT, bool OUT_I32>
 hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
-  const size_t lds = (size_t)(p.threads / 64) * CT * 1024;
+  const size_t lds = (size_t)(p.threads / 64) * (CT * 1024 + 16 * kCodePitch);
   auto kern = ternary_gemv_kernel<CT, OUT_I32>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
@@ -354,7 +379,6 @@ hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int 
   a.N = (int)N;
   a.sb_waves = p.sb_waves;
   a.c = (bits == 8) ? kScaleInt8 : kScaleInt4;
-  if (p.ct == 2) return acc ? launch_gemv_ct<2, true>(p, a, stream) : launch_gemv_ct<2, false>(p, a, stream);
   return acc ? launch_gemv_ct<1, true>(p, a, stream) : launch_gemv_ct<1, false>(p, a, stream);
 }
 
