@@ -26,9 +26,10 @@
 // Staging. Codes and packed weights go from global memory straight into LDS
 // (buffer_load_dwordx4 with the lds bit: each lane's 16 bytes land at
 // base + 16 * lane), so no register holds a tile in transit. LDS is a ring of
-// three stage slots: stage s + 3 is fetched while stage s + 1 and s + 2 are
-// in flight or waiting, and one workgroup barrier per stage both publishes
-// a stage and frees the slot of the one before it. The fetches are spread
+// SL stage slots (three, or two when a stage is too big for three): stage
+// s + SL is fetched while the stages between are in flight or waiting, and
+// one workgroup barrier per stage both publishes a stage and frees the slot
+// of the one before it. The fetches are spread
 // between MFMAs, since a wave issuing ten of them back to back stalls for
 // hundreds of cycles. Codes keep their 128-byte k rows, with the 16-byte
 // chunks of a row permuted by a row-dependent XOR so that the rows one MFMA
@@ -58,7 +59,7 @@ namespace bitnet {
 namespace {
 
 constexpr int BKW = 128;     // k per wave slice per stage
-constexpr int kSlots = 3;    // LDS ring depth
+constexpr int kLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kChunks = 8;   // MFMA groups per block in the interleaved schedule
 constexpr int kXcds = 8;
 constexpr int kBand = 4;
@@ -78,12 +79,14 @@ struct Shape {
   static constexpr int NA_W = NA / NW;         // ... per wave
   static constexpr int NB_W = NB / NW;
   static constexpr int NL_W = NA_W + NB_W;
-  static constexpr int RING = kSlots * SLOT;
-  static constexpr int ROWSUM = RING;          // int32 row sums [KS][BM]
-  static constexpr int LDS = RING + KS * BM * 4;
+  static constexpr int SL = (3 * SLOT <= kLdsMax) ? 3 : 2;  // LDS ring depth (stage slots)
+  static constexpr int RING = SL * SLOT;
+  static constexpr int ROWSUM = RING - KS * BM * 4;  // int32 row sums [KS][BM], after the ring drains
+  static constexpr int LDS = RING;
   static constexpr int PART = RT * CT * 4096;  // one wave's accumulators in bytes
   static_assert(NA_W * NW == NA && NB_W * NW == NB && NB_W >= 1, "uneven staging");
-  static_assert(KS == 1 || (KS / 2) * WMW * WNW * PART <= RING, "reduction does not fit");
+  static_assert(SLOT * 2 <= kLdsMax, "two stage slots do not fit in LDS");
+  static_assert(KS == 1 || (KS / 2) * WMW * WNW * PART <= ROWSUM, "reduction does not fit");
   static_assert((2 * RT * CT) % kChunks == 0, "MFMA groups");
 };
 
@@ -196,33 +199,30 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
   a_none.z = 0;
   b_none.z = 0;
   const unsigned lds0 = lds_address(smem);
-  int voff[S::NL_W];
-  unsigned ldst[S::NL_W];
-#pragma unroll
-  for (int i = 0; i < S::NA_W; ++i) {
-    const int q = wave + S::NW * i;
-    const int slice = q / (S::BM / 8), rb = q % (S::BM / 8);
-    const int r = rb * 8 + (lane >> 3);
-    voff[i] = r * K + slice * BKW + 16 * ((lane & 7) ^ chunk_swizzle(r));
-    ldst[i] = lds0 + slice * S::BM * BKW + rb * 1024;
-  }
-#pragma unroll
-  for (int i = 0; i < S::NB_W; ++i) {
-    const int q = wave + S::NW * i;
-    const int slice = q / (S::BN / 32), cg = q % (S::BN / 32);
-    voff[S::NA_W + i] = (cg * 32 + l32) * wrow + (slice * 2 + g) * 16;
-    ldst[S::NA_W + i] = lds0 + S::A_BYTES + slice * (S::BN / 32) * 1024 + cg * 1024;
-  }
+  // Lane parts of the load offsets; everything else about load i of a stage
+  // is wave-uniform. Code row r = 8 rb + lane / 8 takes global chunk
+  // (lane % 8) ^ swizzle(r), and swizzle(r) = lane / 8 ^ (rb & 1).
+  const int a_lane0 = (lane >> 3) * K + 16 * ((lane & 7) ^ (lane >> 3));
+  const int a_lane1 = (lane >> 3) * K + 16 * ((lane & 7) ^ (lane >> 3) ^ 1);
+  const int b_lane = l32 * wrow + g * 16;
   // Load i of stage ks_ into slot slot_.
 #define BITNET_LOAD(ks_, slot_, i)                                                              \
   {                                                                                             \
     const bool live_ = (ks_) < nst;                                                             \
-    if ((i) < S::NA_W)                                                                          \
-      load_lds16(live_ ? a_rsrc : a_none, voff[i] + (ks_) * S::SK,                              \
-                 ldst[i] + (unsigned)(slot_) * S::SLOT);                                        \
-    else                                                                                        \
-      load_lds16(live_ ? b_rsrc : b_none, voff[i] + (ks_) * (S::SK / 4),                        \
-                 ldst[i] + (unsigned)(slot_) * S::SLOT);                                        \
+    if ((i) < S::NA_W) {                                                                        \
+      const int q_ = wave + S::NW * (i);                                                        \
+      const int slice_ = q_ / (S::BM / 8), rb_ = q_ % (S::BM / 8);                              \
+      load_lds16(live_ ? a_rsrc : a_none,                                                       \
+                 ((rb_ & 1) ? a_lane1 : a_lane0) + rb_ * 8 * K + slice_ * BKW + (ks_) * S::SK,  \
+                 lds0 + (unsigned)((slot_) * S::SLOT + slice_ * S::BM * BKW + rb_ * 1024));     \
+    } else {                                                                                    \
+      const int q_ = wave + S::NW * ((i) - S::NA_W);                                            \
+      const int slice_ = q_ / (S::BN / 32), cg_ = q_ % (S::BN / 32);                            \
+      load_lds16(live_ ? b_rsrc : b_none,                                                       \
+                 b_lane + cg_ * 32 * wrow + slice_ * 32 + (ks_) * (S::SK / 4),                  \
+                 lds0 + (unsigned)((slot_) * S::SLOT + S::A_BYTES +                             \
+                                   (slice_ * (S::BN / 32) + cg_) * 1024));                      \
+    }                                                                                           \
   }
 
   // Operand reads. Codes: row wm*32RT + rt*32 + l32 of this wave's slice,
@@ -320,17 +320,17 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
 
   // Prologue: stages 0..2 in flight, stage 0 published, its block 0 read.
 #pragma unroll
-  for (int s = 0; s < 3; ++s)
+  for (int s = 0; s < S::SL; ++s)
 #pragma unroll
     for (int i = 0; i < S::NL_W; ++i) BITNET_LOAD(s, s, i)
-  BITNET_WAIT_VMCNT(2 * S::NL_W);
+  BITNET_WAIT_VMCNT((S::SL - 1) * S::NL_W);
   lds_barrier();
   BITNET_READ(0, 0, ax)
   BITNET_UNPACK(bx)
 
   int slot = 0;
   for (int ks = 0; ks < nfull; ++ks) {
-    const int nslot = slot == 2 ? 0 : slot + 1;
+    const int nslot = slot + 1 == S::SL ? 0 : slot + 1;
     // Block 0 of stage ks (set X) runs while block 1 (set Y) is prepared.
     __builtin_amdgcn_sched_barrier(0);
     BITNET_READ(slot, 1, ay)
@@ -338,17 +338,17 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
     BITNET_PIN(ay, by)
     __builtin_amdgcn_sched_barrier(0);
     // Stage boundary. This wave's loads of stage ks + 1 are complete once at
-    // most those of stage ks + 2 are outstanding; after the barrier every
-    // wave's are visible and no wave reads stage ks any more, so its slot
-    // takes stage ks + 3.
-    BITNET_WAIT_VMCNT(S::NL_W);
+    // most those of the SL - 2 stages after it are outstanding; after the
+    // barrier every wave's are visible and no wave reads stage ks any more,
+    // so its slot takes stage ks + SL.
+    BITNET_WAIT_VMCNT((S::SL - 2) * S::NL_W);
     lds_barrier();
     // Block 1 of stage ks (set Y) runs while block 0 of stage ks + 1 (set X)
     // is prepared (past the last stage this reads a stale slot, unused) and
-    // stage ks + 3 is fetched.
+    // stage ks + SL is fetched.
     __builtin_amdgcn_sched_barrier(0);
     BITNET_READ(nslot, 0, ax)
-    BITNET_STEP(ay, by, bx, true, ks + 3, slot)
+    BITNET_STEP(ay, by, bx, true, ks + S::SL, slot)
     BITNET_PIN(ax, bx)
     __builtin_amdgcn_sched_barrier(0);
     slot = nslot;
@@ -375,8 +375,10 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
 #undef BITNET_PIN
 #undef BITNET_LOAD
 
-  // No load may still be writing LDS past this point.
+  // No load may still be writing LDS past this point, and no wave may still
+  // be reading the ring, whose tail now takes the row sums.
   BITNET_WAIT_VMCNT(0);
+  lds_barrier();
 
   // Row sums: add the two k halves (lane groups g = 0, 1) and publish the
   // slice's sums per tile row; every wave of a (wm, kw) pair holds the same

@@ -33,6 +33,7 @@ namespace {
 constexpr float kEps = 1e-7f;
 constexpr int kRoundsInFlight = 4;  // super-blocks whose loads a lane issues together
 constexpr int kFusedCt = 2;         // 16-column tiles per workgroup in the fused decode kernel
+constexpr int kFusedSbw = 1;        // 256-k super-blocks per wave in the fused decode kernel
 
 struct GemvArgs {
   const int8_t* codes;
@@ -209,18 +210,19 @@ __device__ __forceinline__ float wave_reduce(float v) {
 }
 
 // Decode forward with the quantization fused in. Requires M <= MG and
-// 256 * waves >= K (wave w owns the super-block k in [256 w, 256 w + 256),
-// for the statistic, for the codes and for the product).
+// 256 * SBW * waves >= K: wave w owns the SBW super-blocks w * SBW + r,
+// r < SBW (k in [256 (w SBW + r), +256)), for the statistic, for the codes
+// and for the product.
 //
-// Each lane loads its packed weights, then 4 consecutive x values of every
-// token row in its wave's super-block; the per-row statistic (Eq. 5: absmax, or
-// Eq. 6: mean |x|) of the super-block is reduced in the wave with DPP, and a
-// single barrier publishes the waves' partial statistics. Every wave then
-// combines them in the same fixed order, quantizes its own values and hands
-// them to the lanes that feed them to the MFMA through a wave-private LDS
-// region (no further barrier), so little work separates the arrival of the
-// data from the product.
-template <typename XT, int BITS, int MG, int CT>
+// Each lane loads its packed weights, then 4 consecutive x values per token
+// row and super-block; the per-row statistic (Eq. 5: absmax, or Eq. 6: mean
+// |x|) of the wave's share is reduced in the wave with DPP, and a single
+// barrier publishes the waves' partial statistics. Every wave then combines
+// them in the same fixed order, quantizes its own values and hands them to
+// the lanes that feed them to the MFMA through a wave-private LDS region (no
+// further barrier), so little work separates the arrival of the data from
+// the product.
+template <typename XT, int BITS, int MG, int CT, int SBW>
 __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nw = blockDim.x >> 6;
@@ -229,59 +231,70 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
   v4i* red = reinterpret_cast<v4i*>(smem);                                // [nw][CT][64]
   float* part = reinterpret_cast<float*>(smem + (size_t)nw * CT * 1024);  // [nw][16]
   float* srow = part + nw * 16;                                           // [16]
-  int8_t* qw = reinterpret_cast<int8_t*>(srow + 16) + (size_t)wave * a.M * 256;  // [M][256]
+  // this wave's codes: [SBW][M][256]
+  int8_t* qw = reinterpret_cast<int8_t*>(srow + 16) + (size_t)wave * SBW * a.M * 256;
 
   const int col = lane & 15, grp = lane >> 4;
   const int nKB = a.K >> 6;
-  const int kb = wave * 4 + grp;
-  const bool k_ok = kb < nKB;
-  // The weight load goes out first: it is the long pole (HBM), and a
+  // The weight loads go out first: they are the long pole (HBM), and a
   // statistic that waited on x alone would let the x requests, which every
-  // workgroup sends to the same few lines, queue ahead of it. Loads are
+  // workgroup sends to the same few lines, queue ahead of them. Loads are
   // unconditional from clamped, always-valid addresses.
-  uint4 p[CT];
+  uint4 p[SBW][CT];
   {
     const size_t row_bytes = (size_t)(a.K >> 2);
-    const int kbc = kb < nKB ? kb : nKB - 1;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int n = (blockIdx.x * CT + ct) * 16 + col;
-      const int nc = n < a.N ? n : a.N - 1;
-      // an out-of-range block meets all-zero codes below
-      p[ct] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
+    for (int r = 0; r < SBW; ++r) {
+      const int kb = (wave * SBW + r) * 4 + grp;
+      const int kbc = kb < nKB ? kb : nKB - 1;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int n = (blockIdx.x * CT + ct) * 16 + col;
+        const int nc = n < a.N ? n : a.N - 1;
+        // an out-of-range block meets all-zero codes below
+        p[r][ct] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
+      }
     }
   }
-  // Then 4 consecutive x values of every token row in this wave's
-  // super-block.
-  const XT* x = reinterpret_cast<const XT*>(a.x);
-  const int k0 = 256 * wave + 4 * lane;
-  const bool own = k0 < a.K;
-  const int kc = own ? k0 : 0;
+  // Then 4 consecutive x values of every token row in each super-block.
   // (Rows past M are not loaded: every workgroup reads this x, and
   // redundant requests for the same lines queue at the L2.)
-  float v[MG][4];
+  const XT* x = reinterpret_cast<const XT*>(a.x);
+  bool own[SBW];
+  float v[MG][SBW][4];
 #pragma unroll
-  for (int m = 0; m < MG; ++m) {
-    if (m < a.M) {
-      load4(x, (size_t)m * a.K + kc, v[m]);
-    } else {
-      v[m][0] = v[m][1] = v[m][2] = v[m][3] = 0.0f;
+  for (int r = 0; r < SBW; ++r) {
+    const int k0 = 256 * (wave * SBW + r) + 4 * lane;
+    own[r] = k0 < a.K;
+    const int kc = own[r] ? k0 : 0;
+#pragma unroll
+    for (int m = 0; m < MG; ++m) {
+      if (m < a.M) {
+        load4(x, (size_t)m * a.K + kc, v[m][r]);
+      } else {
+        v[m][r][0] = v[m][r][1] = v[m][r][2] = v[m][r][3] = 0.0f;
+      }
     }
   }
 
-
-  // Partial statistic of this wave's super-block, one per token row.
+  // Partial statistic of this wave's super-blocks, one per token row.
 #pragma unroll
   for (int m = 0; m < MG; ++m) {
     if (m < a.M) {
-      float s;
-      if (BITS == 8) {
-        s = fmaxf(fmaxf(fabsf(v[m][0]), fabsf(v[m][1])), fmaxf(fabsf(v[m][2]), fabsf(v[m][3])));
-        s = wave_reduce<true>(own ? s : 0.0f);
-      } else {
-        s = (fabsf(v[m][0]) + fabsf(v[m][1])) + (fabsf(v[m][2]) + fabsf(v[m][3]));
-        s = wave_reduce<false>(own ? s : 0.0f);
+      float s = 0.0f;
+#pragma unroll
+      for (int r = 0; r < SBW; ++r) {
+        float sr;
+        if (BITS == 8) {
+          sr = fmaxf(fmaxf(fabsf(v[m][r][0]), fabsf(v[m][r][1])),
+                     fmaxf(fabsf(v[m][r][2]), fabsf(v[m][r][3])));
+          s = fmaxf(s, own[r] ? sr : 0.0f);
+        } else {
+          sr = (fabsf(v[m][r][0]) + fabsf(v[m][r][1])) + (fabsf(v[m][r][2]) + fabsf(v[m][r][3]));
+          s += own[r] ? sr : 0.0f;
+        }
       }
+      s = (BITS == 8) ? wave_reduce<true>(s) : wave_reduce<false>(s);
       if (lane == 0) part[wave * 16 + m] = s;
     }
   }
@@ -300,30 +313,37 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
       s += kEps;
       if (wave == 0 && lane == m) srow[m] = s;
       const float mult = a.c / s;
-      unsigned word = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float q = __builtin_rintf(v[m][e] * mult);
-        q = fminf(fmaxf(q, lo), hi);
-        word |= ((unsigned)(int)q & 0xFFu) << (8 * e);
+      for (int r = 0; r < SBW; ++r) {
+        unsigned word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float q = __builtin_rintf(v[m][r][e] * mult);
+          q = fminf(fmaxf(q, lo), hi);
+          word |= ((unsigned)(int)q & 0xFFu) << (8 * e);
+        }
+        *reinterpret_cast<unsigned*>(qw + (r * a.M + m) * 256 + 4 * lane) = own[r] ? word : 0u;
       }
-      *reinterpret_cast<unsigned*>(qw + m * 256 + 4 * lane) = own ? word : 0u;
     }
   }
   // The codes just written are read back by other lanes of the same wave;
   // LDS serves a wave's accesses in order, so only the compiler needs fencing.
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-  // MFMA operand: lane (col, grp) feeds token row col, block kb = 4 wave + grp.
-  const int kmask = (k_ok && col < a.M) ? -1 : 0;
-  const int8_t* qr = qw + (col < a.M ? col : 0) * 256 + grp * 64;
-  v4i av[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const v4i*>(qr + 16 * j) & kmask;
+  // MFMA operand: lane (col, grp) feeds token row col, block 4 (w SBW + r) + grp.
   v4i acc[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
-  mma_round<CT>(av, p, acc);
+#pragma unroll
+  for (int r = 0; r < SBW; ++r) {
+    const int kb = (wave * SBW + r) * 4 + grp;
+    const int kmask = (kb < nKB && col < a.M) ? -1 : 0;
+    const int8_t* qr = qw + (r * a.M + (col < a.M ? col : 0)) * 256 + grp * 64;
+    v4i av[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const v4i*>(qr + 16 * j) & kmask;
+    mma_round<CT>(av, p[r], acc);
+  }
   gemv_finish<CT, false>(a, acc, red, srow);
 }
 
@@ -344,21 +364,23 @@ hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stre
   return hipGetLastError();
 }
 
-template <typename XT, int BITS, int MG, int CT>
-hipError_t launch_fused_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
-  const int nw = p.threads / 64;
-  const size_t lds = (size_t)nw * CT * 1024 + (size_t)nw * 16 * 4 + 64 + (size_t)nw * a.M * 256;
-  auto kern = fused_decode_kernel<XT, BITS, MG, CT>;
+template <typename XT, int BITS, int MG, int CT, int SBW>
+hipError_t launch_fused_ct(const GemvArgs& a, hipStream_t stream) {
+  const int nSB = ((a.K >> 6) + 3) >> 2;
+  // at least CT waves: the finish stores column tile ct from wave ct
+  const int nw = (nSB + SBW - 1) / SBW > CT ? (nSB + SBW - 1) / SBW : CT;
+  const size_t lds = (size_t)nw * CT * 1024 + (size_t)nw * 16 * 4 + 64 + (size_t)nw * SBW * a.M * 256;
+  auto kern = fused_decode_kernel<XT, BITS, MG, CT, SBW>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   const unsigned groups = (unsigned)((a.N + 16 * CT - 1) / (16 * CT));
-  kern<<<dim3(groups), dim3(p.threads), lds, stream>>>(a);
+  kern<<<dim3(groups), dim3(64 * nw), lds, stream>>>(a);
   return hipGetLastError();
 }
 
 template <typename XT, int BITS, int MG>
-hipError_t launch_fused_t(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
-  return launch_fused_ct<XT, BITS, MG, kFusedCt>(p, a, stream);
+hipError_t launch_fused_t(const GemvPlan&, const GemvArgs& a, hipStream_t stream) {
+  return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw>(a, stream);
 }
 
 }  // namespace
