@@ -20,6 +20,9 @@ Parity status per function (mirrors the design notes):
   quantize_activations pinned (hand values, torch per-channel quantizer)
   ternary_matmul_i64   pinned (int64 brute force)
   dequantize / forward pinned (fake-quant route of the engine page)
+  silu / swiglu        pinned (closed-form special values, torch.nn.functional.silu)
+  rmsnorm              pinned (torch.nn.RMSNorm, unit mean square, scale invariance)
+  forward_prologue     pinned (reduces to forward; torch module chain on small shapes)
 """
 
 from .hbitlinear import (  # noqa: F401
@@ -30,12 +33,16 @@ from .hbitlinear import (  # noqa: F401
     dequantize,
     forward,
     forward_from_codes,
+    forward_prologue,
     fwht,
     fwht_dense,
     hadamard_matrix,
     pack_2bit,
     quant_boundary_distance,
     quantize_activations,
+    rmsnorm,
+    silu,
+    swiglu,
     ternarize,
     ternary_matmul_i64,
     unpack_2bit,

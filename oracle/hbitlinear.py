@@ -251,3 +251,51 @@ def forward(x: np.ndarray, x_dtype: str, t: np.ndarray, alpha: float, bits: int,
     q, s, p = quantize_activations(xr, bits, eps)
     acc, y64 = forward_from_codes(q, s, t, alpha, bits)
     return {"y": y64.astype(np.float32), "y64": y64, "acc": acc, "q": q, "s": s, "p": p, "xr": xr}
+
+
+# ---------------------------------------------------------------------------
+# Prologue of the layer input — [engine] HBitLinear.forward step 1
+# (nn.RMSNorm(in_features, eps)) and BitNetV2FFN.forward (Swish(gate) * up,
+# the input of the H-BitLinear down projection).
+# ---------------------------------------------------------------------------
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """Swish / SiLU, g * sigmoid(g) = g / (1 + e^-g) (the FFN's F.silu)."""
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """[engine] BitNetV2FFN.forward: F.silu(gate_proj(x)) * up_proj(x)."""
+    return silu(gate) * np.asarray(up, dtype=np.float64)
+
+
+def rmsnorm(u: np.ndarray, weight=None, eps: float = EPS) -> np.ndarray:
+    """[engine] HBitLinear.forward step 1, nn.RMSNorm: per row,
+    u / sqrt(mean(u^2) + eps), times the elementwise weight (ones when None,
+    the module's initial value)."""
+    u = np.asarray(u, dtype=np.float64)
+    r = np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+    out = u / r
+    if weight is not None:
+        out = out * np.asarray(weight, dtype=np.float64)
+    return out
+
+
+def forward_prologue(x: np.ndarray, x_dtype: str, t: np.ndarray, alpha: float, bits: int,
+                     hadamard: int, up=None, rms: bool = False, norm_weight=None,
+                     norm_eps: float = EPS, eps: float = EPS) -> dict:
+    """The whole [engine] HBitLinear.forward with its input prologue: the
+    layer input is u = silu(x) * up when `up` is given (x is then the gate
+    projection), else x; RMSNorm when `rms`; then the transform, the
+    per-token quantization, the ternary product and the dequantization."""
+    u = widen_input(x, x_dtype)
+    if up is not None:
+        u = swiglu(u, widen_input(up, x_dtype))
+    if rms:
+        u = rmsnorm(u, norm_weight, norm_eps)
+    xr = fwht(u) if hadamard else u
+    q, s, p = quantize_activations(xr, bits, eps)
+    acc, y64 = forward_from_codes(q, s, t, alpha, bits)
+    return {"y": y64.astype(np.float32), "y64": y64, "acc": acc, "q": q, "s": s, "p": p, "xr": xr,
+            "u": u}
