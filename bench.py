@@ -162,6 +162,21 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
         res["matmul_hbm_frac"] = res["matmul_weight_GBs"] / HBM_PEAK_GBS
     else:
         res["matmul_mfma_frac"] = res["matmul_TOPS"] / INT8_MFMA_PEAK_TOPS
+    # The engine page's whole HBitLinear.forward: RMSNorm (unit weight plus a
+    # seeded elementwise weight) in front, and for the transform workloads
+    # (the FFN's Wdown) the SwiGLU product silu(gate) * up as the input.
+    gamma = torch.from_numpy((np.random.default_rng(1).standard_normal(wl.K) * 0.3 + 1.0)
+                             .astype(np.float32)).to(dev)
+    up = p.x.flip(0).contiguous() if wl.hadamard else None
+    pws = torch.empty((bl.forward_prologue_workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.hadamard),),
+                      dtype=torch.uint8, device=dev)
+
+    def with_prologue(i):
+        bl.hbitlinear_forward_prologue(p.x, p.Wp[i % p.copies], p.alpha, wl.bits, wl.hadamard, up=up,
+                                       rmsnorm=True, norm_weight=gamma, out=p.y, workspace=pws)
+    pro_ms = _time_steps(torch, with_prologue, steps, warmup)
+    res["forward_prologue_us"] = pro_ms * 1e3
+    res["prologue"] = ("silu(gate) * up, RMSNorm" if wl.hadamard else "RMSNorm") + " fused into the quantizer"
     if key == "prefill_int8_m8192_k4096_n14336" or key == "int4_hadamard_m4_k256_n256":
         # on-device ternarize + pack: two fp32 reads of W plus the packed write
         Wp = p.Wp[0]

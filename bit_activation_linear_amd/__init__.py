@@ -8,10 +8,13 @@ if it has not been built.
 
 from .api import (  # noqa: F401
     HBitLinear,
+    forward_prologue_workspace_bytes,
     forward_workspace_bytes,
     hbitlinear_forward,
+    hbitlinear_forward_prologue,
     pack_2bit,
     quantize_activations,
+    quantize_activations_prologue,
     ternarize_weights,
     ternary_gemm_i32,
     ternary_linear_dequant,

@@ -51,6 +51,13 @@ SIGNATURES = {
     "bitnet_ternary_gemm_i32": (_int, [_ptr, _i64, _i64, _ptr, _i64, _ptr, _ptr]),
     "bitnet_ternary_linear_dequant": (_int, [_ptr, _ptr, _i64, _i64, _ptr, _i64, _ptr, _int,
                                              _ptr, _ptr]),
+    "bitnet_forward_prologue_workspace_bytes": (_size, [_i64, _i64, _i64, _int, _int]),
+    "bitnet_hbitlinear_forward_prologue": (_int, [_ptr, _ptr, _int, _i64, _i64, _int, _ptr,
+                                                  ctypes.c_float, _ptr, _i64, _ptr, _int, _int,
+                                                  _ptr, _ptr, _size, _ptr]),
+    "bitnet_quantize_activations_prologue": (_int, [_ptr, _ptr, _int, _i64, _i64, _int, _ptr,
+                                                    ctypes.c_float, _int, _int, _ptr, _ptr,
+                                                    _ptr]),
 }
 
 _lock = threading.Lock()

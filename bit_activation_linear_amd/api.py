@@ -112,6 +112,68 @@ def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
     return codes, scales
 
 
+def _prologue_args(x: torch.Tensor, up: Optional[torch.Tensor], rmsnorm: bool,
+                   norm_weight: Optional[torch.Tensor]):
+    if up is not None:
+        _require(up, "up", (x.dtype,), 2)
+        if up.shape != x.shape:
+            raise ValueError(f"up must have x's shape {tuple(x.shape)}, got {tuple(up.shape)}")
+    if norm_weight is not None:
+        _require(norm_weight, "norm_weight", (torch.float32,), 1)
+        if norm_weight.shape[0] != x.shape[1]:
+            raise ValueError("norm_weight must have K elements")
+    return (up.data_ptr() if up is not None else None, int(bool(rmsnorm)),
+            norm_weight.data_ptr() if (rmsnorm and norm_weight is not None) else None)
+
+
+def forward_prologue_workspace_bytes(M: int, K: int, N: int, bits: int, hadamard: int) -> int:
+    return int(_lib.load().bitnet_forward_prologue_workspace_bytes(M, K, N, bits, int(hadamard)))
+
+
+def hbitlinear_forward_prologue(x: torch.Tensor, Wpacked: torch.Tensor, alpha: torch.Tensor,
+                                bits: int, hadamard: int, up: Optional[torch.Tensor] = None,
+                                rmsnorm: bool = True, norm_weight: Optional[torch.Tensor] = None,
+                                norm_eps: float = 1e-7, out: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The engine page's whole HBitLinear.forward: y = H-BitLinear of
+    RMSNorm(u) (when rmsnorm), with u = silu(x) * up when `up` is given (the
+    FFN's down projection: x is the gate projection) and u = x otherwise."""
+    _require(x, "x", (torch.float32, torch.bfloat16), 2)
+    _require(Wpacked, "Wpacked", (torch.uint8,), 2)
+    _require(alpha, "alpha", (torch.float32,), 1)
+    M, K = x.shape
+    N = Wpacked.shape[0]
+    if Wpacked.shape[1] * 4 != K:
+        raise ValueError(f"Wpacked has {Wpacked.shape[1]} bytes per row, expected K/4 = {K // 4}")
+    up_ptr, rms, g_ptr = _prologue_args(x, up, rmsnorm, norm_weight)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = forward_prologue_workspace_bytes(M, K, N, bits, hadamard)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _lib.call("bitnet_hbitlinear_forward_prologue", x.data_ptr(), up_ptr, _x_dtype(x), M, K, rms,
+              g_ptr, float(norm_eps), Wpacked.data_ptr(), N, alpha.data_ptr(), int(bits),
+              int(hadamard), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+              _stream_ptr(x))
+    return out
+
+
+def quantize_activations_prologue(x: torch.Tensor, bits: int, hadamard: int,
+                                  up: Optional[torch.Tensor] = None, rmsnorm: bool = True,
+                                  norm_weight: Optional[torch.Tensor] = None,
+                                  norm_eps: float = 1e-7) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(codes, scales) of the prologue + transform + quantization stage."""
+    _require(x, "x", (torch.float32, torch.bfloat16), 2)
+    M, K = x.shape
+    up_ptr, rms, g_ptr = _prologue_args(x, up, rmsnorm, norm_weight)
+    codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _lib.call("bitnet_quantize_activations_prologue", x.data_ptr(), up_ptr, _x_dtype(x), M, K, rms,
+              g_ptr, float(norm_eps), int(bits), int(hadamard), codes.data_ptr(),
+              scales.data_ptr(), _stream_ptr(x))
+    return codes, scales
+
+
 def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """acc int32 [M, N] = codes . t^T (exact)."""

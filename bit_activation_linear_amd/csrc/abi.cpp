@@ -232,4 +232,82 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
   return hip_status(e, fn);
 }
 
+size_t bitnet_forward_prologue_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits,
+                                               int hadamard) {
+  (void)bits;
+  (void)hadamard;
+  if (M <= 0 || K <= 0 || N <= 0 || K % 64 != 0) return 0;
+  return round_up((size_t)M * (size_t)K) + round_up((size_t)M * sizeof(float));
+}
+
+}  // extern "C"
+
+namespace {
+
+bitnet_status check_prologue(const char* fn, const void* up, int rmsnorm, const float* norm_weight,
+                             float norm_eps) {
+  if (rmsnorm != 0 && rmsnorm != 1)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: rmsnorm=%d must be 0 or 1", fn, rmsnorm);
+  if (rmsnorm && !(norm_eps > 0.0f && norm_eps < 3.0e38f))
+    return fail(BITNET_ERR_INVALID_ARG, "%s: norm_eps must be a positive finite value", fn);
+  if ((up && !aligned(up, 16)) || (rmsnorm && norm_weight && !aligned(norm_weight, 16)))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned prologue pointer", fn);
+  return BITNET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bitnet_status bitnet_quantize_activations_prologue(const void* x, const void* up,
+                                                   bitnet_dtype x_dtype, int64_t M, int64_t K,
+                                                   int rmsnorm, const float* norm_weight,
+                                                   float norm_eps, int bits, int hadamard,
+                                                   int8_t* codes, float* scales,
+                                                   hipStream_t stream) {
+  const char* fn = "bitnet_quantize_activations_prologue";
+  if (bitnet_status st = check_dims(fn, M, K, 0)) return st;
+  if (bitnet_status st = check_quant_args(fn, K, bits, hadamard, x_dtype)) return st;
+  if (bitnet_status st = check_prologue(fn, up, rmsnorm, norm_weight, norm_eps)) return st;
+  if (M == 0) return ok();
+  if (!x || !codes || !scales) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  const bitnet::Prologue pro{up, rmsnorm ? norm_weight : nullptr, norm_eps, rmsnorm};
+  return hip_status(bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, codes,
+                                            scales, stream, &pro),
+                    fn);
+}
+
+bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, bitnet_dtype x_dtype,
+                                                 int64_t M, int64_t K, int rmsnorm,
+                                                 const float* norm_weight, float norm_eps,
+                                                 const uint8_t* Wpacked, int64_t N,
+                                                 const float* alpha, int bits, int hadamard,
+                                                 float* y, void* ws, size_t ws_bytes,
+                                                 hipStream_t stream) {
+  const char* fn = "bitnet_hbitlinear_forward_prologue";
+  if (bitnet_status st = check_dims(fn, M, K, N)) return st;
+  if (bitnet_status st = check_quant_args(fn, K, bits, hadamard, x_dtype)) return st;
+  if (bitnet_status st = check_prologue(fn, up, rmsnorm, norm_weight, norm_eps)) return st;
+  if (M == 0 || N == 0) return ok();
+  if (!x || !Wpacked || !alpha || !y)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  const size_t need = bitnet_forward_prologue_workspace_bytes(M, K, N, bits, hadamard);
+  if (!ws || ws_bytes < need)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: workspace %zu B < required %zu B", fn,
+                ws ? ws_bytes : (size_t)0, need);
+  if (!aligned(x, 16) || !aligned(Wpacked, 16) || !aligned(ws, 16) || !aligned(y, 4) ||
+      !aligned(alpha, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  const ForwardWorkspace w = carve_forward(ws, M, K);
+  const bitnet::Prologue pro{up, rmsnorm ? norm_weight : nullptr, norm_eps, rmsnorm};
+  hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
+                                         w.scales, stream, &pro);
+  if (e != hipSuccess) return hip_status(e, fn);
+  e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
+                                    nullptr, stream);
+  return hip_status(e, fn);
+}
+
 }  // extern "C"

@@ -24,6 +24,12 @@
 // quantization scale. LDS layout: element i at float index i + i/32.
 //
 // Without the transform the row stays in registers end to end.
+//
+// Optional input prologue (PRO): the SwiGLU product silu(x) * up and the
+// RMSNorm of the engine page's HBitLinear.forward, applied as each vector is
+// loaded. The norm's 1/rms never touches the elements: its sum of squares is
+// reduced together with the statistic (one barrier), and it enters only the
+// scale and the code multiplier.
 #include "kernels.h"
 
 namespace bitnet {
@@ -101,6 +107,60 @@ __device__ __forceinline__ float block_stat(float s, float* red) {
   return r;
 }
 
+// Workgroup reduction of the statistic and of a sum of squares together
+// (one barrier), fixed order.
+template <int BITS, int T>
+__device__ __forceinline__ float2 block_stat2(float s, float q, float* red) {
+  constexpr int W = T < 64 ? T : 64;
+  s = (BITS == 8) ? group_max<W>(s) : group_sum<W>(s);
+  q = group_sum<W>(q);
+  constexpr int NW = (T + 63) / 64;
+  if (T >= 64) {
+    if ((threadIdx.x & 63) == 0) {
+      red[threadIdx.x >> 6] = s;
+      red[NW + (threadIdx.x >> 6)] = q;
+    }
+  } else if (threadIdx.x == 0) {
+    red[0] = s;
+    red[1] = q;
+  }
+  __syncthreads();
+  float r = red[0], rq = red[NW];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    r = (BITS == 8) ? fmaxf(r, red[w]) : r + red[w];
+    rq += red[NW + w];
+  }
+  return make_float2(r, rq);
+}
+
+// Input prologue on the 8 consecutive elements at idx of one row (v holds
+// x): SwiGLU product silu(x) * up (engine page BitNetV2FFN.forward), the
+// sum of squares RMSNorm needs (taken before its weight), then the RMSNorm
+// weight (engine page HBitLinear.forward step 1, nn.RMSNorm). The 1/rms
+// factor itself is applied through the quantization scale: per-token
+// quantization only sees x / stat(x).
+template <typename XT>
+__device__ __forceinline__ void apply_prologue8(const Prologue& pro, const XT* up_row, int idx,
+                                                float* v, float& sq) {
+  if (pro.up) {
+    float u[8];
+    load8(up_row + idx, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (v[e] / (1.0f + expf(-v[e]))) * u[e];
+  }
+  if (pro.rms) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq += v[e] * v[e];
+    if (pro.gamma) {
+      float g[8];
+      load8(pro.gamma + idx, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= g[e];
+    }
+  }
+}
+
 __device__ __forceinline__ float quant_clip(float v, float mult, float lo, float hi) {
   return fminf(fmaxf(__builtin_rintf(v * mult), lo), hi);
 }
@@ -115,9 +175,9 @@ struct QConst {
 // One middle chunk: butterflies over index bits [B0, B0 + NB). Thread t owns
 // the groups g = t + T*gi (gi < E >> NB); a group is the 2^NB elements
 // base(g) + (j << B0). LAST: quantize from registers and store the codes.
-template <int L, int LT, int B0, int NB, bool LAST, int BITS>
+template <int L, int LT, int B0, int NB, bool LAST, int BITS, bool PRO>
 __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_t* crow,
-                                         float* scale_out) {
+                                         float* scale_out, float sq, const Prologue& pro) {
   constexpr int T = 1 << LT;
   constexpr int E = 1 << (L - LT);
   constexpr int R = 1 << NB;
@@ -150,13 +210,31 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < E; ++i) s = (BITS == 8) ? fmaxf(s, fabsf(v[i])) : s + fabsf(v[i]);
-  float stat = block_stat<BITS, T>(s, red);
   // prod of L factors 1/sqrt2 = 2^(-L/2)
   float norm = __builtin_ldexpf(1.0f, -(L >> 1));
   if (L & 1) norm *= 0.70710678118654752f;
-  if (BITS == 4) stat = stat / (float)(1 << L);
-  const float sc = stat * norm + kEps;
-  const float mult = (QConst<BITS>::c * norm) / sc;
+  float sc, mult;
+  if constexpr (PRO) {
+    // stat of H(x) / rms + eps, and codes c H(x) / (stat of H(x) + eps rms):
+    // the same numbers as normalizing first (H is linear).
+    const float2 r = block_stat2<BITS, T>(s, sq, red);
+    float stat = r.x;
+    if (BITS == 4) stat = stat / (float)(1 << L);
+    if (pro.rms) {
+      const float sraw = stat * norm;
+      const float rms = sqrtf(r.y / (float)(1 << L) + pro.norm_eps);
+      sc = sraw / rms + kEps;
+      mult = (QConst<BITS>::c * norm) / (sraw + kEps * rms);
+    } else {  // the plain path's arithmetic, operation for operation
+      sc = stat * norm + kEps;
+      mult = (QConst<BITS>::c * norm) / sc;
+    }
+  } else {
+    float stat = block_stat<BITS, T>(s, red);
+    if (BITS == 4) stat = stat / (float)(1 << L);
+    sc = stat * norm + kEps;
+    mult = (QConst<BITS>::c * norm) / sc;
+  }
   if (t == 0) *scale_out = sc;
 #pragma unroll
   for (int gi = 0; gi < G; ++gi)
@@ -172,17 +250,18 @@ struct Min {
   static constexpr int value = A < B ? A : B;
 };
 
-template <typename XT, int BITS, int L, int LT>
+template <typename XT, int BITS, int L, int LT, bool PRO>
 __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restrict__ x,
                                                              int8_t* __restrict__ codes,
-                                                             float* __restrict__ scales) {
+                                                             float* __restrict__ scales,
+                                                             Prologue pro) {
   constexpr int K = 1 << L;
   constexpr int T = 1 << LT;
   constexpr int E = K / T;
   constexpr int e = L - LT;
   static_assert(E >= 8, "at least one 8-element vector per thread");
   extern __shared__ float lds[];
-  __shared__ float red[(T + 63) / 64];
+  __shared__ float red[2 * ((T + 63) / 64) + 2];
   const int t = threadIdx.x;
   const int row = blockIdx.x;
   const XT* xr = x + (size_t)row * K;
@@ -192,6 +271,12 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restric
   float v[E];
 #pragma unroll
   for (int rh = 0; rh < E / 8; ++rh) load8(xr + 8 * t + 8 * T * rh, v + 8 * rh);
+  float sq = 0.0f;
+  if constexpr (PRO) {
+    const XT* ur = pro.up ? reinterpret_cast<const XT*>(pro.up) + (size_t)row * K : nullptr;
+#pragma unroll
+    for (int rh = 0; rh < E / 8; ++rh) apply_prologue8(pro, ur, 8 * t + 8 * T * rh, v + 8 * rh, sq);
+  }
   fwht_regs<E>(v);
 #pragma unroll
   for (int rh = 0; rh < E / 8; ++rh)
@@ -210,40 +295,42 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restric
   static_assert(R3 <= NB3, "at most four middle chunks");
   float* sc = scales + row;
   if constexpr (R1 <= 0) {
-    mid_pass<L, LT, 3, NB0, true, BITS>(v, lds, red, crow, sc);
+    mid_pass<L, LT, 3, NB0, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
   } else {
-    mid_pass<L, LT, 3, NB0, false, BITS>(v, lds, red, crow, sc);
+    mid_pass<L, LT, 3, NB0, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
     if constexpr (R2 <= 0) {
-      mid_pass<L, LT, 3 + NB0, NB1, true, BITS>(v, lds, red, crow, sc);
+      mid_pass<L, LT, 3 + NB0, NB1, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
     } else {
-      mid_pass<L, LT, 3 + NB0, NB1, false, BITS>(v, lds, red, crow, sc);
+      mid_pass<L, LT, 3 + NB0, NB1, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
       if constexpr (R3 <= 0) {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS>(v, lds, red, crow, sc);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
       } else {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS>(v, lds, red, crow, sc);
-        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS>(v, lds, red, crow, sc);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
+        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
       }
     }
   }
 }
 
 // No transform: thread t owns the 8-element vectors at 8t + 2048c, c < CH.
-template <typename XT, int BITS, int CH>
+template <typename XT, int BITS, int CH, bool PRO>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ x, int K,
                                                          int8_t* __restrict__ codes,
-                                                         float* __restrict__ scales) {
+                                                         float* __restrict__ scales, Prologue pro) {
   constexpr int T = 256;
-  __shared__ float red[4];
+  __shared__ float red[8];
   const int t = threadIdx.x;
   const int row = blockIdx.x;
   const XT* xr = x + (size_t)row * K;
+  const XT* ur = (PRO && pro.up) ? reinterpret_cast<const XT*>(pro.up) + (size_t)row * K : nullptr;
   float v[CH][8];
-  float s = 0.0f;
+  float s = 0.0f, sq = 0.0f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int idx = 8 * t + 8 * T * c;
     if (idx < K) {
       load8(xr + idx, v[c]);
+      if constexpr (PRO) apply_prologue8(pro, ur, idx, v[c], sq);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
@@ -251,10 +338,26 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = (BITS == 8) ? fmaxf(s, fabsf(v[c][e])) : s + fabsf(v[c][e]);
   }
-  float stat = block_stat<BITS, T>(s, red);
-  if (BITS == 4) stat = stat / (float)K;
-  const float sc = stat + kEps;
-  const float mult = QConst<BITS>::c / sc;
+  float sc, mult;
+  if constexpr (PRO) {
+    // stat(x) / rms + eps, codes c x / (stat(x) + eps rms): the numbers of
+    // normalizing first.
+    const float2 r = block_stat2<BITS, T>(s, sq, red);
+    const float sraw = (BITS == 4) ? r.x / (float)K : r.x;
+    if (pro.rms) {
+      const float rms = sqrtf(r.y / (float)K + pro.norm_eps);
+      sc = sraw / rms + kEps;
+      mult = QConst<BITS>::c / (sraw + kEps * rms);
+    } else {  // the plain path's arithmetic, operation for operation
+      sc = sraw + kEps;
+      mult = QConst<BITS>::c / sc;
+    }
+  } else {
+    float stat = block_stat<BITS, T>(s, red);
+    if (BITS == 4) stat = stat / (float)K;
+    sc = stat + kEps;
+    mult = QConst<BITS>::c / sc;
+  }
   if (t == 0) scales[row] = sc;
   int8_t* crow = codes + (size_t)row * K;
 #pragma unroll
@@ -279,81 +382,92 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <typename XT, int BITS, int L, int LT>
-hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, hipStream_t stream) {
+template <typename XT, int BITS, int L, int LT, bool PRO>
+hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, const Prologue& pro,
+                       hipStream_t stream) {
   constexpr int K = 1 << L;
   const size_t lds = (size_t)(K + K / 32) * sizeof(float);
-  auto kern = fwht_quant_kernel<XT, BITS, L, LT>;
+  auto kern = fwht_quant_kernel<XT, BITS, L, LT, PRO>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)M), dim3(1 << LT), lds, stream>>>(reinterpret_cast<const XT*>(x), codes,
-                                                          scales);
+                                                          scales, pro);
   return hipGetLastError();
 }
 
 // Threads per row: 256 for batches (many rows in flight), 1024 for a
 // handful of long rows (decode), never fewer than 8 elements per thread.
-template <typename XT, int BITS, int L>
-hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales, hipStream_t stream) {
+template <typename XT, int BITS, int L, bool PRO>
+hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales,
+                         const Prologue& pro, hipStream_t stream) {
   constexpr int LT_BATCH = (L - 3 < 8) ? L - 3 : 8;
   constexpr int LT_FEW = (L - 3 < 10) ? L - 3 : 10;
   if (M <= 64 && LT_FEW != LT_BATCH)
-    return launch_fwht<XT, BITS, L, LT_FEW>(x, M, codes, scales, stream);
-  return launch_fwht<XT, BITS, L, LT_BATCH>(x, M, codes, scales, stream);
+    return launch_fwht<XT, BITS, L, LT_FEW, PRO>(x, M, codes, scales, pro, stream);
+  return launch_fwht<XT, BITS, L, LT_BATCH, PRO>(x, M, codes, scales, pro, stream);
 }
 
-template <typename XT, int BITS>
-hipError_t launch_had(const void* x, int64_t M, int K, int8_t* codes, float* scales, hipStream_t stream) {
+template <typename XT, int BITS, bool PRO>
+hipError_t launch_had(const void* x, int64_t M, int K, int8_t* codes, float* scales,
+                      const Prologue& pro, hipStream_t stream) {
   switch (K) {
-    case 1 << 6: return launch_fwht_l<XT, BITS, 6>(x, M, codes, scales, stream);
-    case 1 << 7: return launch_fwht_l<XT, BITS, 7>(x, M, codes, scales, stream);
-    case 1 << 8: return launch_fwht_l<XT, BITS, 8>(x, M, codes, scales, stream);
-    case 1 << 9: return launch_fwht_l<XT, BITS, 9>(x, M, codes, scales, stream);
-    case 1 << 10: return launch_fwht_l<XT, BITS, 10>(x, M, codes, scales, stream);
-    case 1 << 11: return launch_fwht_l<XT, BITS, 11>(x, M, codes, scales, stream);
-    case 1 << 12: return launch_fwht_l<XT, BITS, 12>(x, M, codes, scales, stream);
-    case 1 << 13: return launch_fwht_l<XT, BITS, 13>(x, M, codes, scales, stream);
-    case 1 << 14: return launch_fwht_l<XT, BITS, 14>(x, M, codes, scales, stream);
-    case 1 << 15: return launch_fwht_l<XT, BITS, 15>(x, M, codes, scales, stream);
+    case 1 << 6: return launch_fwht_l<XT, BITS, 6, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 7: return launch_fwht_l<XT, BITS, 7, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 8: return launch_fwht_l<XT, BITS, 8, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 9: return launch_fwht_l<XT, BITS, 9, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 10: return launch_fwht_l<XT, BITS, 10, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 11: return launch_fwht_l<XT, BITS, 11, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 12: return launch_fwht_l<XT, BITS, 12, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 13: return launch_fwht_l<XT, BITS, 13, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 14: return launch_fwht_l<XT, BITS, 14, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 15: return launch_fwht_l<XT, BITS, 15, PRO>(x, M, codes, scales, pro, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename XT, int BITS, int CH>
-hipError_t launch_rows_ch(const void* x, int64_t M, int K, int8_t* codes, float* scales, hipStream_t stream) {
-  quant_rows_kernel<XT, BITS, CH><<<dim3((unsigned)M), dim3(256), 0, stream>>>(
-      reinterpret_cast<const XT*>(x), K, codes, scales);
+template <typename XT, int BITS, int CH, bool PRO>
+hipError_t launch_rows_ch(const void* x, int64_t M, int K, int8_t* codes, float* scales,
+                          const Prologue& pro, hipStream_t stream) {
+  quant_rows_kernel<XT, BITS, CH, PRO><<<dim3((unsigned)M), dim3(256), 0, stream>>>(
+      reinterpret_cast<const XT*>(x), K, codes, scales, pro);
   return hipGetLastError();
 }
 
-template <typename XT, int BITS>
-hipError_t launch_rows(const void* x, int64_t M, int K, int8_t* codes, float* scales, hipStream_t stream) {
+template <typename XT, int BITS, bool PRO>
+hipError_t launch_rows(const void* x, int64_t M, int K, int8_t* codes, float* scales,
+                       const Prologue& pro, hipStream_t stream) {
   const int ch = (K + 2047) / 2048;
-  if (ch <= 1) return launch_rows_ch<XT, BITS, 1>(x, M, K, codes, scales, stream);
-  if (ch <= 2) return launch_rows_ch<XT, BITS, 2>(x, M, K, codes, scales, stream);
-  if (ch <= 4) return launch_rows_ch<XT, BITS, 4>(x, M, K, codes, scales, stream);
-  if (ch <= 8) return launch_rows_ch<XT, BITS, 8>(x, M, K, codes, scales, stream);
-  return launch_rows_ch<XT, BITS, 16>(x, M, K, codes, scales, stream);
+  if (ch <= 1) return launch_rows_ch<XT, BITS, 1, PRO>(x, M, K, codes, scales, pro, stream);
+  if (ch <= 2) return launch_rows_ch<XT, BITS, 2, PRO>(x, M, K, codes, scales, pro, stream);
+  if (ch <= 4) return launch_rows_ch<XT, BITS, 4, PRO>(x, M, K, codes, scales, pro, stream);
+  if (ch <= 8) return launch_rows_ch<XT, BITS, 8, PRO>(x, M, K, codes, scales, pro, stream);
+  return launch_rows_ch<XT, BITS, 16, PRO>(x, M, K, codes, scales, pro, stream);
 }
 
-template <typename XT>
+template <typename XT, bool PRO>
 hipError_t launch_dtype(const void* x, int64_t M, int K, int bits, int hadamard, int8_t* codes,
-                        float* scales, hipStream_t stream) {
+                        float* scales, const Prologue& pro, hipStream_t stream) {
   if (hadamard) {
-    return bits == 8 ? launch_had<XT, 8>(x, M, K, codes, scales, stream)
-                     : launch_had<XT, 4>(x, M, K, codes, scales, stream);
+    return bits == 8 ? launch_had<XT, 8, PRO>(x, M, K, codes, scales, pro, stream)
+                     : launch_had<XT, 4, PRO>(x, M, K, codes, scales, pro, stream);
   }
-  return bits == 8 ? launch_rows<XT, 8>(x, M, K, codes, scales, stream)
-                   : launch_rows<XT, 4>(x, M, K, codes, scales, stream);
+  return bits == 8 ? launch_rows<XT, 8, PRO>(x, M, K, codes, scales, pro, stream)
+                   : launch_rows<XT, 4, PRO>(x, M, K, codes, scales, pro, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
-                           int8_t* codes, float* scales, hipStream_t stream) {
+                           int8_t* codes, float* scales, hipStream_t stream, const Prologue* pro) {
+  const Prologue none{nullptr, nullptr, 0.0f, 0};
+  if (pro) {
+    if (x_dtype == 1)
+      return launch_dtype<uint16_t, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream);
+    return launch_dtype<float, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream);
+  }
   if (x_dtype == 1)
-    return launch_dtype<uint16_t>(x, M, K, bits, hadamard, codes, scales, stream);
-  return launch_dtype<float>(x, M, K, bits, hadamard, codes, scales, stream);
+    return launch_dtype<uint16_t, false>(x, M, K, bits, hadamard, codes, scales, none, stream);
+  return launch_dtype<float, false>(x, M, K, bits, hadamard, codes, scales, none, stream);
 }
 
 }  // namespace bitnet

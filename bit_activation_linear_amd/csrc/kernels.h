@@ -64,10 +64,22 @@ hipError_t launch_ternarize_pack(const float* W, int64_t N, int64_t K, const dou
 hipError_t launch_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* Wpacked,
                             hipStream_t stream);
 
-// Fused (optional) Walsh-Hadamard transform + per-token quantization.
-// x_dtype: 0 = fp32, 1 = bf16 bit patterns.
+// Optional input prologue of the quantizer: the layer input is
+// silu(x) * up when `up` is set (x is then the gate projection, `up` has x's
+// dtype and shape), followed by RMSNorm when `rms` is set (elementwise weight
+// `gamma`, ones when null, and `norm_eps`).
+struct Prologue {
+  const void* up;
+  const float* gamma;
+  float norm_eps;
+  int rms;
+};
+
+// Fused (optional) prologue + Walsh-Hadamard transform + per-token
+// quantization. x_dtype: 0 = fp32, 1 = bf16 bit patterns. pro may be null.
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
-                           int8_t* codes, float* scales, hipStream_t stream);
+                           int8_t* codes, float* scales, hipStream_t stream,
+                           const Prologue* pro = nullptr);
 
 // Ternary product from codes. Exactly one of y (dequantized; needs scales,
 // alpha, bits) or acc (raw int32) is non-null.

@@ -155,6 +155,51 @@ bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* sc
                                             const float* alpha, int bits, float* y,
                                             hipStream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* Forward with the layer-input prologue                                     */
+/* ------------------------------------------------------------------------ */
+
+/* The whole of the engine page's HBitLinear.forward, with the input
+ * prologue the plain forward leaves to the caller:
+ *   u   = up ? silu(x) * up : x      BitNetV2FFN.forward: Swish(gate) * up,
+ *                                    the input of the H-BitLinear down
+ *                                    projection (x is then the gate
+ *                                    projection; silu(g) = g / (1 + e^-g))
+ *   u   = rmsnorm ? u / sqrt(mean(u^2) + norm_eps) * norm_weight : u
+ *                                    HBitLinear.forward step 1, nn.RMSNorm
+ *   then exactly the steps of bitnet_hbitlinear_forward on u.
+ *   up           NULL, or [M, K] in x_dtype (same layout as x).
+ *   rmsnorm      0 or 1.
+ *   norm_weight  NULL (all ones, nn.RMSNorm's initial value) or fp32 [K];
+ *                read only when rmsnorm = 1.
+ *   norm_eps     > 0; the engine page passes the layer's eps (1e-7).
+ * The prologue is computed in fp32 as each vector is loaded and is never
+ * written to memory; 1/rms enters only the scale and the code multiplier
+ * (per-token quantization sees u / stat(u)). Same requirements, workspace
+ * rules and errors as bitnet_hbitlinear_forward, except that this forward
+ * always runs as two launches and so always needs its workspace
+ * (bitnet_forward_prologue_workspace_bytes); up and norm_weight must be
+ * 16-byte aligned; norm_eps <= 0 or rmsnorm not in {0, 1} is
+ * BITNET_ERR_INVALID_ARG. */
+size_t bitnet_forward_prologue_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits,
+                                               int hadamard);
+bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, bitnet_dtype x_dtype,
+                                                 int64_t M, int64_t K, int rmsnorm,
+                                                 const float* norm_weight, float norm_eps,
+                                                 const uint8_t* Wpacked, int64_t N,
+                                                 const float* alpha, int bits, int hadamard,
+                                                 float* y, void* ws, size_t ws_bytes,
+                                                 hipStream_t stream);
+
+/* Prologue + transform + per-token quantization only; writes the codes and
+ * scales bitnet_hbitlinear_forward_prologue multiplies with. */
+bitnet_status bitnet_quantize_activations_prologue(const void* x, const void* up,
+                                                   bitnet_dtype x_dtype, int64_t M, int64_t K,
+                                                   int rmsnorm, const float* norm_weight,
+                                                   float norm_eps, int bits, int hadamard,
+                                                   int8_t* codes, float* scales,
+                                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -151,3 +151,50 @@ def test_last_error_is_per_thread(lib):
     th.join()
     assert seen["msg"] == b""
     assert lib.bitnet_last_error() != b""
+
+
+def _fwd_pro(lib, x=FAKE, up=FAKE, xt=_lib.BF16, M=4, K=256, rms=1, g=FAKE, eps=1e-7, Wp=FAKE,
+             N=256, alpha=FAKE, bits=4, had=1, y=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.bitnet_hbitlinear_forward_prologue(x, up, xt, M, K, rms, g, eps, Wp, N, alpha, bits,
+                                                  had, y, ws, ws_bytes, None)
+
+
+def test_prologue_workspace_sizes(lib):
+    # always the two-launch path: codes + scales, even where the plain forward fuses
+    assert lib.bitnet_forward_prologue_workspace_bytes(1, 2560, 6912, 8, 0) == 2560 + 256
+    assert lib.bitnet_forward_prologue_workspace_bytes(2048, 8192, 2048, 4, 1) == 2048 * 8192 + 8192
+    assert lib.bitnet_forward_prologue_workspace_bytes(0, 64, 8, 8, 0) == 0
+    assert lib.bitnet_forward_prologue_workspace_bytes(4, 100, 8, 8, 0) == 0
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), _lib.ERR_INVALID_ARG),
+    (dict(ws=None), _lib.ERR_INVALID_ARG),
+    (dict(ws_bytes=100), _lib.ERR_INVALID_ARG),
+    (dict(rms=2), _lib.ERR_INVALID_ARG),
+    (dict(eps=0.0), _lib.ERR_INVALID_ARG),
+    (dict(eps=-1e-7), _lib.ERR_INVALID_ARG),
+    (dict(eps=float("inf")), _lib.ERR_INVALID_ARG),
+    (dict(eps=float("nan")), _lib.ERR_INVALID_ARG),
+    (dict(up=FAKE + 4), _lib.ERR_ALIGN),
+    (dict(g=FAKE + 8), _lib.ERR_ALIGN),
+    (dict(bits=3), _lib.ERR_BAD_BITS),
+    (dict(K=192, had=1), _lib.ERR_NOT_POW2),
+    (dict(K=100), _lib.ERR_ALIGN),
+])
+def test_prologue_forward_validation(lib, kwargs, status):
+    assert _fwd_pro(lib, **kwargs) == status
+    assert lib.bitnet_last_error() != b""
+
+
+def test_prologue_optional_parts_and_noop(lib):
+    # no RMSNorm: eps and the weight pointer are not inspected
+    assert _fwd_pro(lib, rms=0, eps=0.0, g=FAKE + 8, x=None) == _lib.ERR_INVALID_ARG
+    assert b"null pointer" in lib.bitnet_last_error()
+    # M = 0 / N = 0 are no-ops
+    assert _fwd_pro(lib, M=0, x=None, up=None, y=None, ws=None) == _lib.OK
+    assert _fwd_pro(lib, N=0, Wp=None, y=None, ws=None) == _lib.OK
+    q = lib.bitnet_quantize_activations_prologue
+    assert q(FAKE, None, _lib.F32, 2, 64, 1, None, 0.0, 8, 0, FAKE, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert q(FAKE, FAKE + 2, _lib.F32, 2, 64, 0, None, 1e-7, 8, 0, FAKE, FAKE, None) == _lib.ERR_ALIGN
+    assert q(None, None, _lib.F32, 0, 64, 1, None, 1e-7, 8, 0, None, None, None) == _lib.OK
