@@ -23,6 +23,8 @@ Parity status per function (mirrors the design notes):
   silu / swiglu        pinned (closed-form special values, torch.nn.functional.silu)
   rmsnorm              pinned (torch.nn.RMSNorm, unit mean square, scale invariance)
   forward_prologue     pinned (reduces to forward; torch module chain on small shapes)
+  kv_quantize          pinned (hand values per branch, the engine page's per-head
+                       fake-quant written with torch ops, brute-force BOS rule)
 """
 
 from .hbitlinear import (  # noqa: F401
@@ -37,6 +39,9 @@ from .hbitlinear import (  # noqa: F401
     fwht,
     fwht_dense,
     hadamard_matrix,
+    kv_code_params,
+    kv_dequantize,
+    kv_quantize,
     pack_2bit,
     quant_boundary_distance,
     quantize_activations,

@@ -299,3 +299,54 @@ def forward_prologue(x: np.ndarray, x_dtype: str, t: np.ndarray, alpha: float, b
     acc, y64 = forward_from_codes(q, s, t, alpha, bits)
     return {"y": y64.astype(np.float32), "y64": y64, "acc": acc, "q": q, "s": s, "p": p, "xr": xr,
             "u": u}
+
+
+# ---------------------------------------------------------------------------
+# Low-bit KV cache — [engine] module docstring item 5 (Section 3.1, Tables 2
+# and 3) and BitNetV2Attention._quantize_kv_head: post-RoPE keys/values
+# [B, H, S, D] quantized per token along the head dimension, the BOS token
+# (s = 0) always with the 8-bit absmax quantizer.
+# ---------------------------------------------------------------------------
+
+# bits -> (scale constant c, clip lo, clip hi, statistic); the 3-bit branch is
+# absmax with scale 3 and clip [-4, 3] (the page's own formula for it).
+_KV = {8: (127.0, -128, 127, "absmax"), 4: (math.sqrt(7.0), -8, 7, "absmean"),
+       3: (3.0, -4, 3, "absmax")}
+
+
+def kv_code_params(bits: int, token: int):
+    """(c, lo, hi, statistic) used for token index `token` of a head."""
+    return _KV[8] if token == 0 else _KV[bits]
+
+
+def kv_quantize(kv: np.ndarray, bits: int, eps: float = EPS):
+    """Codes q, scales s (s = stat + eps, so x ~ q * s / c) and pre-round p of
+    a [..., S, D] key or value tensor. Token 0 of every head uses the int8
+    absmax quantizer, the others `bits` (3, 4 or 8)."""
+    if bits not in _KV:
+        raise ValueError("KV cache bits must be 3, 4 or 8")
+    x = np.asarray(kv, dtype=np.float64)
+    S = x.shape[-2]
+    q = np.empty(x.shape, dtype=np.int8)
+    s = np.empty(x.shape[:-1], dtype=np.float64)
+    p = np.empty(x.shape, dtype=np.float64)
+    for tok in range(S):
+        c, lo, hi, stat = kv_code_params(bits, tok)
+        row = x[..., tok, :]
+        st = np.max(np.abs(row), axis=-1) if stat == "absmax" else np.mean(np.abs(row), axis=-1)
+        st = st + eps
+        pr = c * row / st[..., None]
+        q[..., tok, :] = np.clip(np.rint(pr), lo, hi).astype(np.int8)
+        s[..., tok] = st
+        p[..., tok, :] = pr
+    return q, s, p
+
+
+def kv_dequantize(q: np.ndarray, s: np.ndarray, bits: int) -> np.ndarray:
+    """x_hat = q * s / c with each token's own constant c."""
+    q = np.asarray(q, dtype=np.float64)
+    out = np.empty(q.shape, dtype=np.float64)
+    for tok in range(q.shape[-2]):
+        c = kv_code_params(bits, tok)[0]
+        out[..., tok, :] = q[..., tok, :] * np.asarray(s)[..., tok, None] / c
+    return out
