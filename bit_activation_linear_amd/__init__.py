@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     forward_workspace_bytes,
     hbitlinear_forward,
     hbitlinear_forward_prologue,
+    kv_quantize,
     pack_2bit,
     quantize_activations,
     quantize_activations_prologue,

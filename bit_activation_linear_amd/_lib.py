@@ -58,6 +58,7 @@ SIGNATURES = {
     "bitnet_quantize_activations_prologue": (_int, [_ptr, _ptr, _int, _i64, _i64, _int, _ptr,
                                                     ctypes.c_float, _int, _int, _ptr, _ptr,
                                                     _ptr]),
+    "bitnet_kv_quantize": (_int, [_ptr, _int, _i64, _i64, _i64, _int, _ptr, _ptr, _ptr]),
 }
 
 _lock = threading.Lock()

@@ -174,6 +174,20 @@ def quantize_activations_prologue(x: torch.Tensor, bits: int, hadamard: int,
     return codes, scales
 
 
+def kv_quantize(kv: torch.Tensor, bits: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Low-bit KV cache (engine page, BitNetV2Attention._quantize_kv_head):
+    kv [B, H, S, D] (fp32 or bf16, contiguous) -> (codes int8 [B, H, S, D],
+    scales fp32 [B, H, S]); token 0 of every head with the int8 absmax rule,
+    the others with `bits` in {3, 4, 8}."""
+    _require(kv, "kv", (torch.float32, torch.bfloat16), 4)
+    B, H, S, D = kv.shape
+    codes = torch.empty(kv.shape, dtype=torch.int8, device=kv.device)
+    scales = torch.empty((B, H, S), dtype=torch.float32, device=kv.device)
+    _lib.call("bitnet_kv_quantize", kv.data_ptr(), _x_dtype(kv), B * H * S, D, S, int(bits),
+              codes.data_ptr(), scales.data_ptr(), _stream_ptr(kv))
+    return codes, scales
+
+
 def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """acc int32 [M, N] = codes . t^T (exact)."""

@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libbitnet_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["abi.cpp", "ternarize.hip", "fwht_quant.hip", "ternary_gemv.hip", "ternary_gemm.hip"]
+SOURCES = ["abi.cpp", "ternarize.hip", "fwht_quant.hip", "ternary_gemv.hip", "ternary_gemm.hip",
+           "kv_quant.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -300,14 +300,48 @@ bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, 
   if (!aligned(x, 16) || !aligned(Wpacked, 16) || !aligned(ws, 16) || !aligned(y, 4) ||
       !aligned(alpha, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
-  const ForwardWorkspace w = carve_forward(ws, M, K);
   const bitnet::Prologue pro{up, rmsnorm ? norm_weight : nullptr, norm_eps, rmsnorm};
+  if (forward_is_fused(M, K, N, hadamard)) {
+    return hip_status(bitnet::launch_fused_decode(x, (int)x_dtype, M, (int)K, Wpacked, N, alpha,
+                                                  bits, y, stream, &pro),
+                      fn);
+  }
+  const ForwardWorkspace w = carve_forward(ws, M, K);
   hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
                                          w.scales, stream, &pro);
   if (e != hipSuccess) return hip_status(e, fn);
   e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
                                     nullptr, stream);
   return hip_status(e, fn);
+}
+
+bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R, int64_t D,
+                                 int64_t S, int bits, int8_t* codes, float* scales,
+                                 hipStream_t stream) {
+  const char* fn = "bitnet_kv_quantize";
+  if (R < 0 || D < 0 || S < 0)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: negative size (R=%lld D=%lld S=%lld)", fn,
+                (long long)R, (long long)D, (long long)S);
+  if (bits != 3 && bits != 4 && bits != 8)
+    return fail(BITNET_ERR_BAD_BITS, "%s: bits=%d must be 3, 4 or 8", fn, bits);
+  if (D % 8 != 0 || D < 8)
+    return fail(BITNET_ERR_ALIGN, "%s: D=%lld must be a positive multiple of 8", fn, (long long)D);
+  if (D > 512)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: D=%lld exceeds 512", fn, (long long)D);
+  if (S < 1 || R % S != 0)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: R=%lld must be a multiple of S=%lld >= 1", fn,
+                (long long)R, (long long)S);
+  if (x_dtype != BITNET_F32 && x_dtype != BITNET_BF16)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, x_dtype);
+  if (S > INT_MAX || R > (int64_t)INT_MAX * 64)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: R or S too large", fn);
+  if (R == 0) return ok();
+  if (!kv || !codes || !scales) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(kv, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bitnet::launch_kv_quantize(kv, (int)x_dtype, R, (int)D, (int)S, bits, codes,
+                                               scales, stream),
+                    fn);
 }
 
 }  // extern "C"

@@ -81,6 +81,11 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bit
                            int8_t* codes, float* scales, hipStream_t stream,
                            const Prologue* pro = nullptr);
 
+// Low-bit KV cache: rows of D elements, row r being token r % S of its head;
+// token 0 int8 absmax, the others bits = 3, 4 or 8.
+hipError_t launch_kv_quantize(const void* kv, int x_dtype, int64_t R, int D, int S, int bits,
+                              int8_t* codes, float* scales, hipStream_t stream);
+
 // Ternary product from codes. Exactly one of y (dequantized; needs scales,
 // alpha, bits) or acc (raw int32) is non-null.
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
@@ -98,6 +103,6 @@ hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int 
 // Decode forward with the quantization fused in (plan.fused must hold).
 hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
                                const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
-                               float* y, hipStream_t stream);
+                               float* y, hipStream_t stream, const Prologue* pro = nullptr);
 
 }  // namespace bitnet

@@ -222,8 +222,8 @@ __device__ __forceinline__ float wave_reduce(float v) {
 // the lanes that feed them to the MFMA through a wave-private LDS region (no
 // further barrier), so little work separates the arrival of the data from
 // the product.
-template <typename XT, int BITS, int MG, int CT, int SBW>
-__global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
+template <typename XT, int BITS, int MG, int CT, int SBW, bool PRO>
+__global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue pro) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nw = blockDim.x >> 6;
   const int t = threadIdx.x;
@@ -231,8 +231,10 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
   v4i* red = reinterpret_cast<v4i*>(smem);                                // [nw][CT][64]
   float* part = reinterpret_cast<float*>(smem + (size_t)nw * CT * 1024);  // [nw][16]
   float* srow = part + nw * 16;                                           // [16]
+  float* psq = srow + 16;  // [nw][16] partial sums of squares (prologue with RMSNorm)
   // this wave's codes: [SBW][M][256]
-  int8_t* qw = reinterpret_cast<int8_t*>(srow + 16) + (size_t)wave * SBW * a.M * 256;
+  int8_t* qw = reinterpret_cast<int8_t*>(psq + (PRO ? nw * 16 : 0)) +
+               (size_t)wave * SBW * a.M * 256;
 
   const int col = lane & 15, grp = lane >> 4;
   const int nKB = a.K >> 6;
@@ -276,6 +278,40 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
       }
     }
   }
+  // Input prologue (engine page: BitNetV2FFN's silu(gate) * up, then
+  // HBitLinear's RMSNorm weight); the norm's 1/rms enters only the scale and
+  // the code multiplier below, its sum of squares rides on the statistic's
+  // barrier.
+  float sq[MG];
+#pragma unroll
+  for (int m = 0; m < MG; ++m) sq[m] = 0.0f;
+  if constexpr (PRO) {
+#pragma unroll
+    for (int r = 0; r < SBW; ++r) {
+      const int k0 = 256 * (wave * SBW + r) + 4 * lane;
+      const int kc = own[r] ? k0 : 0;
+      float g[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (pro.rms && pro.gamma) load4(pro.gamma, (size_t)kc, g);
+#pragma unroll
+      for (int m = 0; m < MG; ++m) {
+        if (m < a.M) {
+          if (pro.up) {
+            float u[4];
+            load4(reinterpret_cast<const XT*>(pro.up), (size_t)m * a.K + kc, u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[m][r][e] = (v[m][r][e] / (1.0f + expf(-v[m][r][e]))) * u[e];
+          }
+          if (pro.rms) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sq[m] += own[r] ? v[m][r][e] * v[m][r][e] : 0.0f;
+              v[m][r][e] *= g[e];
+            }
+          }
+        }
+      }
+    }
+  }
 
   // Partial statistic of this wave's super-blocks, one per token row.
 #pragma unroll
@@ -296,6 +332,10 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
       }
       s = (BITS == 8) ? wave_reduce<true>(s) : wave_reduce<false>(s);
       if (lane == 0) part[wave * 16 + m] = s;
+      if (PRO && pro.rms) {
+        const float q = wave_reduce<false>(sq[m]);
+        if (lane == 0) psq[wave * 16 + m] = q;
+      }
     }
   }
   lds_barrier();
@@ -310,9 +350,18 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a) {
       float s = 0.0f;
       for (int w = 0; w < nw; ++w) s = (BITS == 8) ? fmaxf(s, part[w * 16 + m]) : s + part[w * 16 + m];
       if (BITS == 4) s = s / (float)a.K;
-      s += kEps;
+      float mult;
+      if (PRO && pro.rms) {
+        float q = 0.0f;
+        for (int w = 0; w < nw; ++w) q += psq[w * 16 + m];
+        const float rms = sqrtf(q / (float)a.K + pro.norm_eps);
+        mult = a.c / (s + kEps * rms);
+        s = s / rms + kEps;
+      } else {
+        s += kEps;
+        mult = a.c / s;
+      }
       if (wave == 0 && lane == m) srow[m] = s;
-      const float mult = a.c / s;
 #pragma unroll
       for (int r = 0; r < SBW; ++r) {
         unsigned word = 0;
@@ -364,23 +413,26 @@ hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stre
   return hipGetLastError();
 }
 
-template <typename XT, int BITS, int MG, int CT, int SBW>
-hipError_t launch_fused_ct(const GemvArgs& a, hipStream_t stream) {
+template <typename XT, int BITS, int MG, int CT, int SBW, bool PRO>
+hipError_t launch_fused_ct(const GemvArgs& a, const Prologue& pro, hipStream_t stream) {
   const int nSB = ((a.K >> 6) + 3) >> 2;
   // at least CT waves: the finish stores column tile ct from wave ct
   const int nw = (nSB + SBW - 1) / SBW > CT ? (nSB + SBW - 1) / SBW : CT;
-  const size_t lds = (size_t)nw * CT * 1024 + (size_t)nw * 16 * 4 + 64 + (size_t)nw * SBW * a.M * 256;
-  auto kern = fused_decode_kernel<XT, BITS, MG, CT, SBW>;
+  const size_t lds = (size_t)nw * CT * 1024 + (size_t)nw * 16 * 4 + 64 +
+                     (PRO ? (size_t)nw * 16 * 4 : 0) + (size_t)nw * SBW * a.M * 256;
+  auto kern = fused_decode_kernel<XT, BITS, MG, CT, SBW, PRO>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   const unsigned groups = (unsigned)((a.N + 16 * CT - 1) / (16 * CT));
-  kern<<<dim3(groups), dim3(64 * nw), lds, stream>>>(a);
+  kern<<<dim3(groups), dim3(64 * nw), lds, stream>>>(a, pro);
   return hipGetLastError();
 }
 
 template <typename XT, int BITS, int MG>
-hipError_t launch_fused_t(const GemvPlan&, const GemvArgs& a, hipStream_t stream) {
-  return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw>(a, stream);
+hipError_t launch_fused_t(const GemvArgs& a, const Prologue* pro, hipStream_t stream) {
+  if (pro) return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, true>(a, *pro, stream);
+  const Prologue none{nullptr, nullptr, 0.0f, 0};
+  return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, false>(a, none, stream);
 }
 
 }  // namespace
@@ -406,7 +458,7 @@ hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int 
 
 hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
                                const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
-                               float* y, hipStream_t stream) {
+                               float* y, hipStream_t stream, const Prologue* pro) {
   const GemvPlan p = plan_gemv(M, K, N, true, false);
   if (!p.fused) return hipErrorInvalidValue;
   GemvArgs a{};
@@ -421,23 +473,23 @@ hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
   a.c = (bits == 8) ? kScaleInt8 : kScaleInt4;
   if (M == 1) {  // single token: the smallest code, which a cold launch fetches fastest
     if (x_dtype == 1)
-      return bits == 8 ? launch_fused_t<uint16_t, 8, 1>(p, a, stream)
-                       : launch_fused_t<uint16_t, 4, 1>(p, a, stream);
-    return bits == 8 ? launch_fused_t<float, 8, 1>(p, a, stream)
-                     : launch_fused_t<float, 4, 1>(p, a, stream);
+      return bits == 8 ? launch_fused_t<uint16_t, 8, 1>(a, pro, stream)
+                       : launch_fused_t<uint16_t, 4, 1>(a, pro, stream);
+    return bits == 8 ? launch_fused_t<float, 8, 1>(a, pro, stream)
+                     : launch_fused_t<float, 4, 1>(a, pro, stream);
   }
   if (M <= 4) {
     if (x_dtype == 1)
-      return bits == 8 ? launch_fused_t<uint16_t, 8, 4>(p, a, stream)
-                       : launch_fused_t<uint16_t, 4, 4>(p, a, stream);
-    return bits == 8 ? launch_fused_t<float, 8, 4>(p, a, stream)
-                     : launch_fused_t<float, 4, 4>(p, a, stream);
+      return bits == 8 ? launch_fused_t<uint16_t, 8, 4>(a, pro, stream)
+                       : launch_fused_t<uint16_t, 4, 4>(a, pro, stream);
+    return bits == 8 ? launch_fused_t<float, 8, 4>(a, pro, stream)
+                     : launch_fused_t<float, 4, 4>(a, pro, stream);
   }
   if (x_dtype == 1)
-    return bits == 8 ? launch_fused_t<uint16_t, 8, 16>(p, a, stream)
-                     : launch_fused_t<uint16_t, 4, 16>(p, a, stream);
-  return bits == 8 ? launch_fused_t<float, 8, 16>(p, a, stream)
-                   : launch_fused_t<float, 4, 16>(p, a, stream);
+    return bits == 8 ? launch_fused_t<uint16_t, 8, 16>(a, pro, stream)
+                     : launch_fused_t<uint16_t, 4, 16>(a, pro, stream);
+  return bits == 8 ? launch_fused_t<float, 8, 16>(a, pro, stream)
+                   : launch_fused_t<float, 4, 16>(a, pro, stream);
 }
 
 }  // namespace bitnet

@@ -175,12 +175,12 @@ bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* sc
  *   norm_eps     > 0; the engine page passes the layer's eps (1e-7).
  * The prologue is computed in fp32 as each vector is loaded and is never
  * written to memory; 1/rms enters only the scale and the code multiplier
- * (per-token quantization sees u / stat(u)). Same requirements, workspace
- * rules and errors as bitnet_hbitlinear_forward, except that this forward
- * always runs as two launches and so always needs its workspace
- * (bitnet_forward_prologue_workspace_bytes); up and norm_weight must be
- * 16-byte aligned; norm_eps <= 0 or rmsnorm not in {0, 1} is
- * BITNET_ERR_INVALID_ARG. */
+ * (per-token quantization sees u / stat(u)). Same requirements and errors
+ * as bitnet_hbitlinear_forward, except that a workspace of
+ * bitnet_forward_prologue_workspace_bytes is always required (the decode
+ * shapes the plain forward runs as one kernel run as one kernel here too and
+ * leave it untouched); up and norm_weight must be 16-byte aligned;
+ * norm_eps <= 0 or rmsnorm not in {0, 1} is BITNET_ERR_INVALID_ARG. */
 size_t bitnet_forward_prologue_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits,
                                                int hadamard);
 bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, bitnet_dtype x_dtype,
@@ -199,6 +199,28 @@ bitnet_status bitnet_quantize_activations_prologue(const void* x, const void* up
                                                    float norm_eps, int bits, int hadamard,
                                                    int8_t* codes, float* scales,
                                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Low-bit KV cache                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Per-token quantization of post-RoPE keys or values (engine page, module
+ * docstring item 5 / Section 3.1, BitNetV2Attention._quantize_kv_head):
+ *   kv      [R, D] in x_dtype: the rows of a contiguous [B, H, S, D] tensor,
+ *           row r being token r % S of its head (R = B * H * S).
+ *   bits    3, 4 or 8 for tokens s >= 1; token 0 (BOS) of every head is
+ *           always quantized with the 8-bit absmax rule.
+ *             8 (and BOS): s = max|x| + eps,  q = RoundClip(127 x / s, -128, 127)
+ *             4:           s = mean|x| + eps, q = RoundClip(sqrt7 x / s, -8, 7)
+ *             3:           s = max|x| + eps,  q = RoundClip(3 x / s, -4, 3)
+ *   codes   int8 [R, D], written (one code per byte).
+ *   scales  fp32 [R], written: s, so that x ~ q * s / c with the token's c.
+ * Requires D % 8 == 0, 8 <= D <= 512, S >= 1 and R % S == 0; kv and codes
+ * 16-byte aligned. R = 0 is a no-op. bits outside {3, 4, 8} is
+ * BITNET_ERR_BAD_BITS. */
+bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R, int64_t D,
+                                 int64_t S, int bits, int8_t* codes, float* scales,
+                                 hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -198,3 +198,29 @@ def test_prologue_optional_parts_and_noop(lib):
     assert q(FAKE, None, _lib.F32, 2, 64, 1, None, 0.0, 8, 0, FAKE, FAKE, None) == _lib.ERR_INVALID_ARG
     assert q(FAKE, FAKE + 2, _lib.F32, 2, 64, 0, None, 1e-7, 8, 0, FAKE, FAKE, None) == _lib.ERR_ALIGN
     assert q(None, None, _lib.F32, 0, 64, 1, None, 1e-7, 8, 0, None, None, None) == _lib.OK
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(R=-1), _lib.ERR_INVALID_ARG),
+    (dict(bits=2), _lib.ERR_BAD_BITS),
+    (dict(bits=16), _lib.ERR_BAD_BITS),
+    (dict(D=12), _lib.ERR_ALIGN),
+    (dict(D=0), _lib.ERR_ALIGN),
+    (dict(D=520), _lib.ERR_UNSUPPORTED),
+    (dict(S=0), _lib.ERR_INVALID_ARG),
+    (dict(R=10, S=4), _lib.ERR_INVALID_ARG),
+    (dict(dt=5), _lib.ERR_UNSUPPORTED),
+    (dict(kv=None), _lib.ERR_INVALID_ARG),
+    (dict(codes=FAKE + 4), _lib.ERR_ALIGN),
+    (dict(kv=FAKE + 2), _lib.ERR_ALIGN),
+])
+def test_kv_quantize_validation(lib, args, status):
+    a = dict(kv=FAKE, dt=_lib.BF16, R=16, D=128, S=8, bits=3, codes=FAKE, scales=FAKE)
+    a.update(args)
+    assert lib.bitnet_kv_quantize(a["kv"], a["dt"], a["R"], a["D"], a["S"], a["bits"], a["codes"],
+                                  a["scales"], None) == status
+    assert lib.bitnet_last_error() != b""
+
+
+def test_kv_quantize_empty_is_noop(lib):
+    assert lib.bitnet_kv_quantize(None, _lib.BF16, 0, 64, 4, 4, None, None, None) == _lib.OK
