@@ -20,7 +20,9 @@ The JSON line also carries:
                 sources differ from the ones those counters were taken on;
   cpu_baseline  the fp64 CPU oracle on the host cores, on a bounded sample;
   per_workload  every measured workload at full size (prefill TOPS, decode
-                GB/s, the on-device ternarize+pack pass).
+                GB/s, the on-device ternarize+pack pass, and the whole layer
+                with its RMSNorm / SwiGLU input prologue);
+  kv_cache      the low-bit KV-cache quantizer (3- and 4-bit) in HBM GB/s.
 """
 
 from __future__ import annotations
@@ -200,6 +202,26 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
     return p, res
 
 
+def _measure_kv(torch, bl, dev, steps, warmup):
+    """Low-bit KV-cache quantizer on a 32-head, 4096-token, head_dim 128 bf16
+    cache (seeded N(0,1) values with a few x8 outlier channels): HBM bytes are
+    2 read + 1 written per element and 4 written per token."""
+    from bit_activation_linear_amd import workloads
+    B, H, S, D = 1, 32, 4096, 128
+    case = workloads.make_case(B * H * S, D, 1, x_dtype="bf16", n_out=4, factor=8.0, seed=0)
+    kv = _dev_x(torch, case["x"], "bf16", dev).view(B, H, S, D)
+    nbytes = B * H * S * (3 * D + 4)
+    res = {"shape": [B, H, S, D], "x_dtype": "bf16", "bytes_per_call": nbytes, "bits": {}}
+    codes = torch.empty(kv.shape, dtype=torch.int8, device=dev)
+    scales = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    for bits in (3, 4):
+        ms = _time_steps(torch, lambda i, b=bits: bl.kv_quantize(kv, b, codes=codes, scales=scales),
+                         steps, warmup)
+        res["bits"][bits] = {"us": ms * 1e3, "GBs": nbytes / (ms * 1e-3) / 1e9,
+                             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
 def _recorded_traffic(kernel, key):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary of `kernel` on workload `key`, or None when there is none or when
@@ -322,6 +344,11 @@ def main():
             per[other] = r
             _log(f"[bench] {other}: forward {r['forward_us']:.2f} us, matmul {r['matmul_kernel_us_mean']:.2f} us")
 
+    kv = None
+    if not args.no_extra:
+        kv = _measure_kv(torch, bl, dev, max(20, args.steps // 4), max(5, args.warmup // 2))
+        _log(f"[bench] kv cache: " + ", ".join(f"{b}-bit {r['us']:.2f} us" for b, r in kv["bits"].items()))
+
     cpu = None
     if not args.no_cpu:
         _log("[bench] CPU oracle baseline")
@@ -335,7 +362,7 @@ def main():
         "config": {"workload": key, "M": wl.M, "K": wl.K, "N": wl.N, "bits": wl.bits,
                    "hadamard": wl.hadamard, "x_dtype": wl.x_dtype,
                    "cold_weight_copies": head["cold_weight_copies"]},
-        "roofline": roof, "cpu_baseline": cpu, "per_workload": per,
+        "roofline": roof, "cpu_baseline": cpu, "per_workload": per, "kv_cache": kv,
     }
     print(json.dumps(line), flush=True)
 

@@ -174,15 +174,22 @@ def quantize_activations_prologue(x: torch.Tensor, bits: int, hadamard: int,
     return codes, scales
 
 
-def kv_quantize(kv: torch.Tensor, bits: int) -> Tuple[torch.Tensor, torch.Tensor]:
+def kv_quantize(kv: torch.Tensor, bits: int, codes: Optional[torch.Tensor] = None,
+                scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Low-bit KV cache (engine page, BitNetV2Attention._quantize_kv_head):
     kv [B, H, S, D] (fp32 or bf16, contiguous) -> (codes int8 [B, H, S, D],
     scales fp32 [B, H, S]); token 0 of every head with the int8 absmax rule,
     the others with `bits` in {3, 4, 8}."""
     _require(kv, "kv", (torch.float32, torch.bfloat16), 4)
     B, H, S, D = kv.shape
-    codes = torch.empty(kv.shape, dtype=torch.int8, device=kv.device)
-    scales = torch.empty((B, H, S), dtype=torch.float32, device=kv.device)
+    if codes is None:
+        codes = torch.empty(kv.shape, dtype=torch.int8, device=kv.device)
+    if scales is None:
+        scales = torch.empty((B, H, S), dtype=torch.float32, device=kv.device)
+    _require(codes, "codes", (torch.int8,), 4)
+    _require(scales, "scales", (torch.float32,), 3)
+    if tuple(codes.shape) != tuple(kv.shape) or tuple(scales.shape) != (B, H, S):
+        raise ValueError("codes must match kv's shape and scales be [B, H, S]")
     _lib.call("bitnet_kv_quantize", kv.data_ptr(), _x_dtype(kv), B * H * S, D, S, int(bits),
               codes.data_ptr(), scales.data_ptr(), _stream_ptr(kv))
     return codes, scales
@@ -229,10 +236,15 @@ class HBitLinear:
     device, then forward(x) many times (the prepare-once / forward-many split
     of the bitnet.cpp simulation page's edge linear layer).
 
-    The RMSNorm of the engine page's HBitLinear is not applied: x is taken to
-    be the normalized input."""
+    With rmsnorm=True the engine page's whole HBitLinear.forward runs,
+    RMSNorm (weight `norm_weight`, ones when None, and `norm_eps`) included;
+    forward(x, up=...) then also takes the FFN's SwiGLU product silu(x) * up
+    as the input. With rmsnorm=False (the default) x is taken to be the
+    normalized input."""
 
-    def __init__(self, weight: torch.Tensor, bits: int = 4, hadamard: bool = True):
+    def __init__(self, weight: torch.Tensor, bits: int = 4, hadamard: bool = True,
+                 rmsnorm: bool = False, norm_weight: Optional[torch.Tensor] = None,
+                 norm_eps: float = 1e-7):
         if bits not in (4, 8):
             raise ValueError("bits must be 4 or 8")
         K = weight.shape[1]
@@ -243,10 +255,22 @@ class HBitLinear:
         self.in_features = K
         self.out_features = weight.shape[0]
         self.Wpacked, self.alpha = ternarize_weights(weight.contiguous())
+        self.rmsnorm = bool(rmsnorm)
+        self.norm_weight = norm_weight
+        self.norm_eps = float(norm_eps)
         self._ws = None
 
-    def forward(self, x: torch.Tensor) -> torch.Tensor:
+    def forward(self, x: torch.Tensor, up: Optional[torch.Tensor] = None) -> torch.Tensor:
         M = x.shape[0]
+        if self.rmsnorm or up is not None:
+            need = forward_prologue_workspace_bytes(M, self.in_features, self.out_features,
+                                                    self.bits, self.hadamard)
+            if self._ws is None or self._ws.numel() < need or self._ws.device != x.device:
+                self._ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+            return hbitlinear_forward_prologue(x, self.Wpacked, self.alpha, self.bits,
+                                               self.hadamard, up=up, rmsnorm=self.rmsnorm,
+                                               norm_weight=self.norm_weight,
+                                               norm_eps=self.norm_eps, workspace=self._ws)
         need = forward_workspace_bytes(M, self.in_features, self.out_features, self.bits,
                                        self.hadamard)
         if need > 0 and (self._ws is None or self._ws.numel() < need or self._ws.device != x.device):

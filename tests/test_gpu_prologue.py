@@ -129,3 +129,22 @@ def test_prologue_zero_rows():
         s = scales.cpu().numpy()
         np.testing.assert_allclose(s[[0, 2, 3]], 1e-7, rtol=1e-6)
         assert np.all(y.cpu().numpy()[[0, 2, 3]] == 0.0)
+
+
+def test_module_wrapper_whole_layer():
+    """HBitLinear(rmsnorm=True) runs the engine page's whole HBitLinear.forward;
+    forward(x, up=...) the FFN's down projection of silu(x) * up."""
+    case = workloads.make_case(9, 512, 70, x_dtype="fp32", n_out=5, factor=40.0, seed=13)
+    up_np = workloads.make_case(9, 512, 1, x_dtype="fp32", seed=14)["x"]
+    g_np = (np.random.default_rng(15).standard_normal(512) * 0.2 + 1.0).astype(np.float32)
+    layer = bl.HBitLinear(torch.from_numpy(case["W"]).to(DEV), bits=4, hadamard=True, rmsnorm=True,
+                          norm_weight=torch.from_numpy(g_np).to(DEV))
+    x = torch.from_numpy(case["x"]).to(DEV)
+    y1 = layer(x)
+    y2 = layer(x, up=torch.from_numpy(up_np).to(DEV))
+    torch.cuda.synchronize()
+    t, a, _ = oracle.ternarize(case["W"])
+    r1 = oracle.forward_prologue(case["x"], "fp32", t, a, 4, 1, rms=True, norm_weight=g_np)
+    r2 = oracle.forward_prologue(case["x"], "fp32", t, a, 4, 1, up=up_np, rms=True, norm_weight=g_np)
+    assert_y_close(y1.cpu().numpy(), r1["y64"])
+    assert_y_close(y2.cpu().numpy(), r2["y64"])
