@@ -1,4 +1,4 @@
-"""CPU oracle for the H-BitLinear forward pass — TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the H-BitLinear forward and backward passes — TEST INFRASTRUCTURE ONLY.
 
 A plain, slow, fp64 NumPy restatement of what the method computes, written
 from the pages (see the citations on each function). It is the yardstick the
@@ -23,8 +23,10 @@ Parity status per function (mirrors the design notes):
   silu / swiglu        pinned (closed-form special values, torch.nn.functional.silu)
   rmsnorm              pinned (torch.nn.RMSNorm, unit mean square, scale invariance)
   forward_prologue     pinned (reduces to forward; torch module chain on small shapes)
-  kv_quantize          pinned (hand values per branch, the engine page's per-head
-                       fake-quant written with torch ops, brute-force BOS rule)
+  kv_quantize          pinned (hand values per branch, reduction to the pinned
+                       activation quantizers, 3-bit range and error bounds)
+  backward             pinned (torch autograd through the STE forward, adjoint
+                       identities, Eq. 8 via H*H = I, hand values, brute force)
 """
 
 from .hbitlinear import (  # noqa: F401
@@ -32,6 +34,7 @@ from .hbitlinear import (  # noqa: F401
     INT4_SCALE,
     INT8_SCALE,
     absmean_alpha,
+    backward,
     dequantize,
     forward,
     forward_from_codes,

@@ -1,4 +1,4 @@
-"""fp64 NumPy oracle of the H-BitLinear forward — TEST INFRASTRUCTURE ONLY.
+"""fp64 NumPy oracle of the H-BitLinear forward and backward — TEST INFRASTRUCTURE ONLY.
 
 Only tests/, the smoke check and the bench's CPU-baseline leg may call this.
 Nothing here is used by, or uses, the HIP library.
@@ -350,3 +350,36 @@ def kv_dequantize(q: np.ndarray, s: np.ndarray, bits: int) -> np.ndarray:
         c = kv_code_params(bits, tok)[0]
         out[..., tok, :] = q[..., tok, :] * np.asarray(s)[..., tok, None] / c
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward — [engine] Eq. 8 (HadamardTransformFunction: the gradient of the
+# transform is the transform of the gradient, H being symmetric and
+# orthonormal) and the straight-through estimators of WeightQuantTernarySTE,
+# ActQuantINT8STE and ActQuantINT4STE, whose backward passes hand the
+# incoming gradient through unchanged. HBitLinear.forward ends in
+# F.linear(x_q, w_q) with x_q = (s / c) q and w_q = alpha t.
+# ---------------------------------------------------------------------------
+
+def backward(dy: np.ndarray, q: np.ndarray, s: np.ndarray, t: np.ndarray, alpha: float,
+             bits: int, hadamard: int):
+    """Gradients of the H-BitLinear forward under the engine page's STE rules.
+
+    dy [M, N] is dL/dy; q [M, K], s [M] the per-token codes and scales the
+    forward quantized with; t [N, K] the ternary weights and alpha their
+    scale. Returns (dx [M, K], dw [N, K]), fp64:
+      dL/dx_q = dy . w_q              F.linear's input gradient
+      dL/dx_r = dL/dx_q               activation quantizer STE
+      dx      = H dL/dx_r (hadamard)  Eq. 8; else dL/dx_r
+      dL/dw_q = dy^T . x_q            F.linear's weight gradient
+      dw      = dL/dw_q               ternarizer STE (latent weights)
+    dx is the gradient with respect to the transform's input (the layer input
+    after its RMSNorm)."""
+    dy = np.asarray(dy, dtype=np.float64)
+    c = _QUANT[bits][0]
+    w_q = float(alpha) * np.asarray(t, dtype=np.float64)
+    x_q = np.asarray(q, dtype=np.float64) * (np.asarray(s, dtype=np.float64)[:, None] / c)
+    d_xr = dy @ w_q
+    dx = fwht(d_xr) if hadamard else d_xr
+    dw = dy.T @ x_q
+    return dx, dw
