@@ -20,8 +20,9 @@ The JSON line also carries:
                 sources differ from the ones those counters were taken on;
   cpu_baseline  the fp64 CPU oracle on the host cores, on a bounded sample;
   per_workload  every measured workload at full size (prefill TOPS, decode
-                GB/s, the on-device ternarize+pack pass, and the whole layer
-                with its RMSNorm / SwiGLU input prologue);
+                GB/s, the on-device ternarize+pack pass, the whole layer
+                with its RMSNorm / SwiGLU input prologue, and for the prefill
+                shapes the backward: dx and dw from a bf16 gradient);
   kv_cache      the low-bit KV-cache quantizer (3- and 4-bit) in HBM GB/s.
 """
 
@@ -44,6 +45,7 @@ METRIC = "H-BitLinear fwd: prefill int8-TOPS & decode weight-GB/s, % of MI355X r
 HEADLINE = "decode_int8_m1_k2560_n6912"
 HBM_PEAK_GBS = 8000.0
 INT8_MFMA_PEAK_TOPS = 5033.2  # 256 CU x 2.4 GHz x 8192 int8 ops/clk/CU (dense)
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 bf16 flops/clk/CU (dense)
 COLD_BYTES = 512 * 2 ** 20
 
 
@@ -179,6 +181,29 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
     pro_ms = _time_steps(torch, with_prologue, steps, warmup)
     res["forward_prologue_us"] = pro_ms * 1e3
     res["prologue"] = ("silu(gate) * up, RMSNorm" if wl.hadamard else "RMSNorm") + " fused into the quantizer"
+    if wl.M > 16:
+        # Backward (engine page Eq. 8, STE quantizer gradients): dx and dw from
+        # a seeded bf16 gradient dy and the forward's codes and scales.
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        dy = (torch.randn((wl.M, wl.N), generator=gen, device=dev) * 1e-3).to(torch.bfloat16)
+        dx = torch.empty((wl.M, wl.K), dtype=torch.float32, device=dev)
+        dw = torch.empty((wl.N, wl.K), dtype=torch.float32, device=dev)
+        bws = torch.empty((bl.backward_workspace_bytes(wl.M, wl.K, wl.N, torch.bfloat16),),
+                          dtype=torch.uint8, device=dev)
+
+        def bwd(i):
+            bl.hbitlinear_backward(dy, p.codes, p.scales, p.Wp[i % p.copies], p.alpha, wl.bits,
+                                   wl.hadamard, dx=dx, dw=dw, workspace=bws)
+        b_ms = _time_steps(torch, bwd, max(5, steps // 4), 2)
+        bflops = 4 * wl.M * wl.N * wl.K  # dx and dw, 2MNK each
+        res["backward_us"] = b_ms * 1e3
+        res["backward_TFLOPs"] = bflops / (b_ms * 1e-3) / 1e12
+        res["backward_bf16_mfma_frac"] = res["backward_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
+        res["backward"] = ("dx = H(alpha dy . t) and dw = dy^T . x_q from a bf16 dy; 4*M*N*K "
+                           "algorithmic flops on bf16 MFMA (dw runs two passes: hi and lo parts "
+                           "of dy*s/c)")
+        del dy, dx, dw, bws
     if key == "prefill_int8_m8192_k4096_n14336" or key == "int4_hadamard_m4_k256_n256":
         # on-device ternarize + pack: two fp32 reads of W plus the packed write
         Wp = p.Wp[0]
@@ -342,7 +367,8 @@ def main():
             del po
             torch.cuda.empty_cache()
             per[other] = r
-            _log(f"[bench] {other}: forward {r['forward_us']:.2f} us, matmul {r['matmul_kernel_us_mean']:.2f} us")
+            _log(f"[bench] {other}: forward {r['forward_us']:.2f} us, matmul {r['matmul_kernel_us_mean']:.2f} us"
+                 + (f", backward {r['backward_us']:.1f} us" if "backward_us" in r else ""))
 
     kv = None
     if not args.no_extra:

@@ -1,4 +1,4 @@
-"""H-BitLinear forward (BitNet v2) on AMD MI355X.
+"""H-BitLinear forward and backward (BitNet v2) on AMD MI355X.
 
 The compute path is the HIP library libbitnet_mi355x.so (C ABI in
 include/bitnet_mi355x.h); this package is its thin torch binding. Importing
@@ -8,8 +8,10 @@ if it has not been built.
 
 from .api import (  # noqa: F401
     HBitLinear,
+    backward_workspace_bytes,
     forward_prologue_workspace_bytes,
     forward_workspace_bytes,
+    hbitlinear_backward,
     hbitlinear_forward,
     hbitlinear_forward_prologue,
     kv_quantize,

@@ -195,6 +195,49 @@ def kv_quantize(kv: torch.Tensor, bits: int, codes: Optional[torch.Tensor] = Non
     return codes, scales
 
 
+def backward_workspace_bytes(M: int, K: int, N: int, dy_dtype: torch.dtype, want_dx: bool = True,
+                             want_dw: bool = True) -> int:
+    code = _lib.BF16 if dy_dtype == torch.bfloat16 else _lib.F32
+    return int(_lib.load().bitnet_backward_workspace_bytes(M, K, N, code, int(want_dx),
+                                                           int(want_dw)))
+
+
+def hbitlinear_backward(dy: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                        Wpacked: torch.Tensor, alpha: torch.Tensor, bits: int, hadamard: int,
+                        want_dx: bool = True, want_dw: bool = True,
+                        dx: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None):
+    """Gradients of the H-BitLinear forward (engine page Eq. 8 and the STE
+    quantizer gradients): dx fp32 [M, K] with respect to the transform's input
+    and dw fp32 [N, K] of the latent weights, from dy [M, N] (bf16 or fp32)
+    and the forward's codes / scales (bitnet quantize_activations). Returns
+    (dx or None, dw or None)."""
+    _require(dy, "dy", (torch.float32, torch.bfloat16), 2)
+    _require(codes, "codes", (torch.int8,), 2)
+    _require(scales, "scales", (torch.float32,), 1)
+    _require(Wpacked, "Wpacked", (torch.uint8,), 2)
+    _require(alpha, "alpha", (torch.float32,), 1)
+    M, N = dy.shape
+    K = codes.shape[1]
+    if codes.shape[0] != M or scales.shape[0] != M:
+        raise ValueError("codes and scales must have one row per row of dy")
+    if Wpacked.shape[0] != N or Wpacked.shape[1] * 4 != K:
+        raise ValueError(f"Wpacked must be [N, K/4] = [{N}, {K // 4}], got {tuple(Wpacked.shape)}")
+    if want_dx and dx is None:
+        dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
+    if want_dw and dw is None:
+        dw = torch.empty((N, K), dtype=torch.float32, device=dy.device)
+    need = backward_workspace_bytes(M, K, N, dy.dtype, want_dx, want_dw)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dy.device)
+    ws_ptr, ws_len = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
+    _lib.call("bitnet_hbitlinear_backward", dy.data_ptr(), _x_dtype(dy), M, N, codes.data_ptr(),
+              scales.data_ptr(), K, Wpacked.data_ptr(), alpha.data_ptr(), int(bits), int(hadamard),
+              dx.data_ptr() if want_dx else None, dw.data_ptr() if want_dw else None, ws_ptr,
+              ws_len, _stream_ptr(dy))
+    return (dx if want_dx else None), (dw if want_dw else None)
+
+
 def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """acc int32 [M, N] = codes . t^T (exact)."""

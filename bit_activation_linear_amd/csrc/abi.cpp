@@ -244,6 +244,148 @@ size_t bitnet_forward_prologue_workspace_bytes(int64_t M, int64_t K, int64_t N, 
 
 namespace {
 
+// Backward workspace. The dx parts (t^T in bf16; the hi/lo halves of an
+// fp32 dy) and the dw parts (hi/lo of dy * s / c transposed; the codes
+// transposed) are used one after the other on the stream, so they share the
+// same bytes.
+constexpr int64_t kMaxGradDim = (int64_t)1 << 22;
+
+struct BackwardWorkspace {
+  uint16_t* wt;
+  uint16_t* dy_hi;
+  uint16_t* dy_lo;
+  uint16_t* p_hi;
+  uint16_t* p_lo;
+  uint16_t* qt;
+};
+
+int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
+
+size_t backward_dx_bytes(int64_t M, int64_t K, int64_t N, int dy_dtype) {
+  size_t b = round_up((size_t)K * N * 2);
+  if (dy_dtype == BITNET_F32) b += 2 * round_up((size_t)M * N * 2);
+  return b;
+}
+
+size_t backward_dw_bytes(int64_t M, int64_t K, int64_t N) {
+  const size_t Mp = (size_t)pad64(M);
+  return 2 * round_up((size_t)N * Mp * 2) + round_up((size_t)K * Mp * 2);
+}
+
+BackwardWorkspace carve_backward(void* ws, int64_t M, int64_t K, int64_t N) {
+  BackwardWorkspace w{};
+  char* b = static_cast<char*>(ws);
+  w.wt = reinterpret_cast<uint16_t*>(b);
+  w.dy_hi = reinterpret_cast<uint16_t*>(b + round_up((size_t)K * N * 2));
+  w.dy_lo = reinterpret_cast<uint16_t*>(b + round_up((size_t)K * N * 2) + round_up((size_t)M * N * 2));
+  const size_t Mp = (size_t)pad64(M);
+  w.p_hi = reinterpret_cast<uint16_t*>(b);
+  w.p_lo = reinterpret_cast<uint16_t*>(b + round_up((size_t)N * Mp * 2));
+  w.qt = reinterpret_cast<uint16_t*>(b + 2 * round_up((size_t)N * Mp * 2));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitnet_backward_workspace_bytes(int64_t M, int64_t K, int64_t N, bitnet_dtype dy_dtype,
+                                       int want_dx, int want_dw) {
+  if (M < 0 || K <= 0 || N < 0 || K % 64 != 0 || N % 64 != 0) return 0;
+  size_t b = 0;
+  if (want_dx) b = backward_dx_bytes(M, K, N, dy_dtype);
+  if (want_dw) {
+    const size_t d = backward_dw_bytes(M, K, N);
+    if (d > b) b = d;
+  }
+  return b;
+}
+
+bitnet_status bitnet_hbitlinear_backward(const void* dy, bitnet_dtype dy_dtype, int64_t M,
+                                         int64_t N, const int8_t* codes, const float* scales,
+                                         int64_t K, const uint8_t* Wpacked, const float* alpha,
+                                         int bits, int hadamard, float* dx, float* dw, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "bitnet_hbitlinear_backward";
+  if (M < 0 || K < 0 || N < 0)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: negative size (M=%lld K=%lld N=%lld)", fn,
+                (long long)M, (long long)K, (long long)N);
+  if (K == 0 || K % 64 != 0 || N % 64 != 0)
+    return fail(BITNET_ERR_ALIGN, "%s: K=%lld must be a positive multiple of 64 and N=%lld a "
+                "multiple of 64", fn, (long long)K, (long long)N);
+  if (M >= kMaxGradDim || N >= kMaxGradDim)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: M=%lld or N=%lld not below 2^22", fn, (long long)M,
+                (long long)N);
+  if (bits != 4 && bits != 8)
+    return fail(BITNET_ERR_BAD_BITS, "%s: bits=%d must be 4 or 8", fn, bits);
+  if (hadamard != 0 && hadamard != 1)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: hadamard=%d must be 0 or 1", fn, hadamard);
+  if (hadamard && (!is_pow2(K) || K > BITNET_MAX_K))
+    return fail(BITNET_ERR_NOT_POW2, "%s: K=%lld must be a power of two <= %d with hadamard=1",
+                fn, (long long)K, BITNET_MAX_K);
+  if (dy_dtype != BITNET_F32 && dy_dtype != BITNET_BF16)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: unknown dy dtype %d", fn, dy_dtype);
+  if (!dx && !dw) return ok();
+  if (M == 0 && !dw) return ok();  // dx has no elements
+  if ((M > 0 && N > 0 && !dy) || (dx && (!Wpacked || !alpha)) || (dw && M > 0 && (!codes || !scales)))
+    return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  const size_t need = bitnet_backward_workspace_bytes(M, K, N, dy_dtype, dx != nullptr,
+                                                      dw != nullptr);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(BITNET_ERR_INVALID_ARG, "%s: workspace %zu B < required %zu B", fn,
+                ws ? ws_bytes : (size_t)0, need);
+  if (!aligned(dy, 16) || !aligned(codes, 16) || !aligned(Wpacked, 16) || !aligned(ws, 256) ||
+      !aligned(dx, 4) || !aligned(dw, 4) || !aligned(scales, 4) || !aligned(alpha, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+
+  const BackwardWorkspace w = carve_backward(ws, M, K, N);
+  hipError_t e = hipSuccess;
+  if (dx && M > 0) {
+    // dx = H (alpha dy . t): t^T expanded to bf16, one product per bf16 part
+    // of dy, then the transform of each row.
+    e = bitnet::launch_expand_transpose(Wpacked, N, K, w.wt, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dy_dtype == BITNET_BF16) {
+      e = bitnet::launch_bf16_gemm_nt(static_cast<const uint16_t*>(dy), N, w.wt, N, M, K, N, dx, K,
+                                      alpha, 1.0f, false, stream);
+    } else {
+      e = bitnet::launch_split_rows(static_cast<const float*>(dy), M * N, w.dy_hi, w.dy_lo, stream);
+      if (e == hipSuccess)
+        e = bitnet::launch_bf16_gemm_nt(w.dy_hi, N, w.wt, N, M, K, N, dx, K, alpha, 1.0f, false,
+                                        stream);
+      if (e == hipSuccess)
+        e = bitnet::launch_bf16_gemm_nt(w.dy_lo, N, w.wt, N, M, K, N, dx, K, alpha, 1.0f, true,
+                                        stream);
+    }
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (hadamard) {
+      e = bitnet::launch_fwht_f32(dx, M, (int)K, dx, stream);
+      if (e != hipSuccess) return hip_status(e, fn);
+    }
+  }
+  if (dw) {
+    // dw = dy^T x_q = (dy s / c)^T q: both operands transposed so that the
+    // tokens are contiguous, dy s / c in two bf16 parts.
+    const int64_t Mp = pad64(M);
+    const float inv_c = 1.0f / (bits == 8 ? 127.0f : 2.6457513110645906f);
+    e = bitnet::launch_scale_transpose_split(dy, (int)dy_dtype, scales, inv_c, M, N, Mp, w.p_hi,
+                                             w.p_lo, stream);
+    if (e == hipSuccess) e = bitnet::launch_codes_transpose(codes, M, K, Mp, w.qt, stream);
+    if (e == hipSuccess)
+      e = bitnet::launch_bf16_gemm_nt(w.p_hi, Mp, w.qt, Mp, N, K, Mp, dw, K, nullptr, 1.0f, false,
+                                      stream);
+    if (e == hipSuccess && Mp > 0)
+      e = bitnet::launch_bf16_gemm_nt(w.p_lo, Mp, w.qt, Mp, N, K, Mp, dw, K, nullptr, 1.0f, true,
+                                      stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
 bitnet_status check_prologue(const char* fn, const void* up, int rmsnorm, const float* norm_weight,
                              float norm_eps) {
   if (rmsnorm != 0 && rmsnorm != 1)

@@ -174,10 +174,12 @@ struct QConst {
 
 // One middle chunk: butterflies over index bits [B0, B0 + NB). Thread t owns
 // the groups g = t + T*gi (gi < E >> NB); a group is the 2^NB elements
-// base(g) + (j << B0). LAST: quantize from registers and store the codes.
+// base(g) + (j << B0). LAST: quantize from registers and store the codes,
+// or, with BITS = 0 (transform only), store the normalized fp32 values to frow.
 template <int L, int LT, int B0, int NB, bool LAST, int BITS, bool PRO>
 __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_t* crow,
-                                         float* scale_out, float sq, const Prologue& pro) {
+                                         float* scale_out, float sq, const Prologue& pro,
+                                         float* frow = nullptr) {
   constexpr int T = 1 << LT;
   constexpr int E = 1 << (L - LT);
   constexpr int R = 1 << NB;
@@ -207,12 +209,19 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
     return;
   }
 
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < E; ++i) s = (BITS == 8) ? fmaxf(s, fabsf(v[i])) : s + fabsf(v[i]);
   // prod of L factors 1/sqrt2 = 2^(-L/2)
   float norm = __builtin_ldexpf(1.0f, -(L >> 1));
   if (L & 1) norm *= 0.70710678118654752f;
+  if constexpr (BITS == 0) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int j = 0; j < R; ++j) frow[base[gi] + (j << B0)] = v[gi * R + j] * norm;
+    return;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) s = (BITS == 8) ? fmaxf(s, fabsf(v[i])) : s + fabsf(v[i]);
   float sc, mult;
   if constexpr (PRO) {
     // stat of H(x) / rms + eps, and codes c H(x) / (stat of H(x) + eps rms):
@@ -250,11 +259,12 @@ struct Min {
   static constexpr int value = A < B ? A : B;
 };
 
+// BITS = 0: transform only, the normalized fp32 row written to fout (which
+// may alias x: a row is read whole before any of it is written).
 template <typename XT, int BITS, int L, int LT, bool PRO>
-__global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restrict__ x,
-                                                             int8_t* __restrict__ codes,
+__global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t* __restrict__ codes,
                                                              float* __restrict__ scales,
-                                                             Prologue pro) {
+                                                             Prologue pro, float* fout) {
   constexpr int K = 1 << L;
   constexpr int T = 1 << LT;
   constexpr int E = K / T;
@@ -265,7 +275,8 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restric
   const int t = threadIdx.x;
   const int row = blockIdx.x;
   const XT* xr = x + (size_t)row * K;
-  int8_t* crow = codes + (size_t)row * K;
+  int8_t* crow = BITS ? codes + (size_t)row * K : nullptr;
+  float* frow = BITS ? nullptr : fout + (size_t)row * K;
 
   // Phase A: vectors of 8 from E/8 places, butterflies of the register bits.
   float v[E];
@@ -293,20 +304,20 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* __restric
   constexpr int R3 = R2 - NB2;
   constexpr int NB3 = Min<e, (R3 > 0 ? R3 : 1)>::value;
   static_assert(R3 <= NB3, "at most four middle chunks");
-  float* sc = scales + row;
+  float* sc = BITS ? scales + row : nullptr;
   if constexpr (R1 <= 0) {
-    mid_pass<L, LT, 3, NB0, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
+    mid_pass<L, LT, 3, NB0, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
   } else {
-    mid_pass<L, LT, 3, NB0, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
+    mid_pass<L, LT, 3, NB0, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
     if constexpr (R2 <= 0) {
-      mid_pass<L, LT, 3 + NB0, NB1, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
+      mid_pass<L, LT, 3 + NB0, NB1, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
     } else {
-      mid_pass<L, LT, 3 + NB0, NB1, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
+      mid_pass<L, LT, 3 + NB0, NB1, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
       if constexpr (R3 <= 0) {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
       } else {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
-        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
+        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
       }
     }
   }
@@ -384,14 +395,14 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
 
 template <typename XT, int BITS, int L, int LT, bool PRO>
 hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, const Prologue& pro,
-                       hipStream_t stream) {
+                       hipStream_t stream, float* fout = nullptr) {
   constexpr int K = 1 << L;
   const size_t lds = (size_t)(K + K / 32) * sizeof(float);
   auto kern = fwht_quant_kernel<XT, BITS, L, LT, PRO>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)M), dim3(1 << LT), lds, stream>>>(reinterpret_cast<const XT*>(x), codes,
-                                                          scales, pro);
+                                                          scales, pro, fout);
   return hipGetLastError();
 }
 
@@ -399,12 +410,19 @@ hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, c
 // handful of long rows (decode), never fewer than 8 elements per thread.
 template <typename XT, int BITS, int L, bool PRO>
 hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales,
-                         const Prologue& pro, hipStream_t stream) {
+                         const Prologue& pro, hipStream_t stream, float* fout = nullptr) {
   constexpr int LT_BATCH = (L - 3 < 8) ? L - 3 : 8;
   constexpr int LT_FEW = (L - 3 < 10) ? L - 3 : 10;
   if (M <= 64 && LT_FEW != LT_BATCH)
-    return launch_fwht<XT, BITS, L, LT_FEW, PRO>(x, M, codes, scales, pro, stream);
-  return launch_fwht<XT, BITS, L, LT_BATCH, PRO>(x, M, codes, scales, pro, stream);
+    return launch_fwht<XT, BITS, L, LT_FEW, PRO>(x, M, codes, scales, pro, stream, fout);
+  return launch_fwht<XT, BITS, L, LT_BATCH, PRO>(x, M, codes, scales, pro, stream, fout);
+}
+
+// Transform only (fp32 rows in and out, in place allowed).
+template <int L>
+hipError_t launch_fwht_f32_l(const float* x, int64_t M, float* out, hipStream_t stream) {
+  const Prologue none{nullptr, nullptr, 0.0f, 0};
+  return launch_fwht_l<float, 0, L, false>(x, M, nullptr, nullptr, none, stream, out);
 }
 
 template <typename XT, int BITS, bool PRO>
@@ -456,6 +474,23 @@ hipError_t launch_dtype(const void* x, int64_t M, int K, int bits, int hadamard,
 }
 
 }  // namespace
+
+hipError_t launch_fwht_f32(const float* x, int64_t M, int K, float* out, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  switch (K) {
+    case 1 << 6: return launch_fwht_f32_l<6>(x, M, out, stream);
+    case 1 << 7: return launch_fwht_f32_l<7>(x, M, out, stream);
+    case 1 << 8: return launch_fwht_f32_l<8>(x, M, out, stream);
+    case 1 << 9: return launch_fwht_f32_l<9>(x, M, out, stream);
+    case 1 << 10: return launch_fwht_f32_l<10>(x, M, out, stream);
+    case 1 << 11: return launch_fwht_f32_l<11>(x, M, out, stream);
+    case 1 << 12: return launch_fwht_f32_l<12>(x, M, out, stream);
+    case 1 << 13: return launch_fwht_f32_l<13>(x, M, out, stream);
+    case 1 << 14: return launch_fwht_f32_l<14>(x, M, out, stream);
+    case 1 << 15: return launch_fwht_f32_l<15>(x, M, out, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
                            int8_t* codes, float* scales, hipStream_t stream, const Prologue* pro) {

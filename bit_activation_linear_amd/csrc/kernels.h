@@ -105,4 +105,36 @@ hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
                                const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
                                float* y, hipStream_t stream, const Prologue* pro = nullptr);
 
+// ---- Backward -------------------------------------------------------------
+
+// C[R, Cn] (+)= scale * A[R, Kc] . B[Cn, Kc]^T on bf16 operands (uint16 bit
+// patterns, row pitches lda / ldb elements), fp32 out with pitch ldc;
+// scale = scale_h * *scale_p (scale_p may be null). Kc % 64 == 0.
+hipError_t launch_bf16_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                               int64_t R, int64_t Cn, int64_t Kc, float* C, int64_t ldc,
+                               const float* scale_p, float scale_h, bool accumulate,
+                               hipStream_t stream);
+
+// Wt [K, N] bf16 = t^T from the packed weights (N % 64 == 0, K % 64 == 0).
+hipError_t launch_expand_transpose(const uint8_t* Wpacked, int64_t N, int64_t K, uint16_t* Wt,
+                                   hipStream_t stream);
+
+// fp32 -> hi, lo bf16 (hi + lo equals x to 16 significant bits); n % 8 == 0.
+hipError_t launch_split_rows(const float* x, int64_t n, uint16_t* hi, uint16_t* lo,
+                             hipStream_t stream);
+
+// phi / plo [N, Mp] = split of dy[m][n] * scales[m] * inv_c, transposed,
+// zero for m >= M (Mp % 64 == 0, N % 64 == 0).
+hipError_t launch_scale_transpose_split(const void* dy, int dy_dtype, const float* scales,
+                                        float inv_c, int64_t M, int64_t N, int64_t Mp,
+                                        uint16_t* phi, uint16_t* plo, hipStream_t stream);
+
+// Qt [K, Mp] bf16 = codes^T, zero for m >= M.
+hipError_t launch_codes_transpose(const int8_t* codes, int64_t M, int64_t K, int64_t Mp,
+                                  uint16_t* Qt, hipStream_t stream);
+
+// Orthonormal Walsh-Hadamard transform of fp32 rows of length K (a power of
+// two, 64 .. 32768); out may equal x.
+hipError_t launch_fwht_f32(const float* x, int64_t M, int K, float* out, hipStream_t stream);
+
 }  // namespace bitnet

@@ -59,10 +59,7 @@ namespace bitnet {
 namespace {
 
 constexpr int BKW = 128;     // k per wave slice per stage
-constexpr int kLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kChunks = 8;   // MFMA groups per block in the interleaved schedule
-constexpr int kXcds = 8;
-constexpr int kBand = 4;
 
 template <int RT, int CT, int WMW, int WNW, int KS>
 struct Shape {
@@ -89,50 +86,6 @@ struct Shape {
   static_assert(KS == 1 || (KS / 2) * WMW * WNW * PART <= ROWSUM, "reduction does not fit");
   static_assert((2 * RT * CT) % kChunks == 0, "MFMA groups");
 };
-
-// Buffer resource over [base, base + bytes): raw (stride 0) dword access;
-// loads at or past `bytes` return zero and touch no memory.
-typedef unsigned u4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u4 make_rsrc(const void* base, unsigned bytes) {
-  const size_t a = reinterpret_cast<size_t>(base);
-  u4 r;
-  r.x = (unsigned)a;
-  r.y = (unsigned)(a >> 32) & 0xFFFFu;
-  r.z = bytes;
-  r.w = 0x00020000u;
-  return r;
-}
-
-// LDS byte address of a pointer into the dynamic shared array.
-__device__ __forceinline__ unsigned lds_address(const char* p) {
-  typedef const __attribute__((address_space(3))) char lds_char;
-  return (unsigned)(size_t)(lds_char*)p;
-}
-
-// 16 bytes per lane from buffer offset voff straight into LDS at
-// lds + 16 * lane (lds is wave-uniform; the instruction takes it from M0,
-// which is saved and restored around it). Written as inline assembly so that
-// the compiler, which cannot tell which LDS bytes such a load writes, does not
-// wait for it before every LDS read: completion is tracked by hand with
-// s_waitcnt vmcnt before the workgroup barrier that publishes a stage.
-__device__ __forceinline__ void load_lds16(const u4 rsrc, int voff, unsigned lds) {
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(rsrc), "s"(lds)
-      : "memory");
-}
-
-// XOR applied to the 16-byte chunk index of code row r in LDS.
-__device__ __forceinline__ int chunk_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-#define BITNET_WAIT_VMCNT(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // The 2-bit fields at bit offset sh of each byte: u = t + 1 for 16 weights.
 __device__ __forceinline__ v4i unpack_u(const uint4 p, int sh) {

@@ -222,6 +222,42 @@ bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R
                                  int64_t S, int bits, int8_t* codes, float* scales,
                                  hipStream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* Backward                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Gradients of the H-BitLinear forward under the engine page's training
+ * rules: HadamardTransformFunction's backward applies the transform to the
+ * gradient (Eq. 8), and the STE autograd functions of the weight and
+ * activation quantizers pass the gradient through unchanged. With the
+ * forward's y = F.linear(x_q, w_q), x_q = (scales[m] / c) q, w_q = alpha t:
+ *   dx = H (alpha * dy . t)   [M, K] fp32, the gradient with respect to the
+ *                             transform's input (H only when hadamard = 1)
+ *   dw = dy^T . x_q           [N, K] fp32, the gradient of the latent
+ *                             weights
+ *   dy       [M, N] in dy_dtype (BITNET_BF16 or BITNET_F32), row-major.
+ *   codes    int8 [M, K], scales fp32 [M]: what bitnet_quantize_activations
+ *            wrote for the forward's input (read only when dw is set).
+ *   Wpacked, alpha: the forward's packed weights [N, K/4] and alpha (read
+ *            only when dx is set).
+ *   bits     4 or 8 (c = sqrt 7 or 127); hadamard 0 or 1.
+ *   dx, dw   outputs, written (not accumulated); either may be NULL to skip
+ *            that gradient.
+ * Arithmetic: products on bf16 matrix cores with fp32 accumulation; a bf16
+ * dy and the ternary weights are exact there; an fp32 dy (for dx) and
+ * dy * scales / c (for dw) are split into two bf16 parts (16 significant
+ * bits). Workspace: bitnet_backward_workspace_bytes (256-B aligned).
+ * Requires K % 64 == 0, N % 64 == 0, M and N below 2^22, and for
+ * hadamard = 1 a power-of-two K <= BITNET_MAX_K; dy, codes and ws 16-byte
+ * aligned. M = 0 writes dw = 0; N = 0 writes dx = 0. */
+size_t bitnet_backward_workspace_bytes(int64_t M, int64_t K, int64_t N, bitnet_dtype dy_dtype,
+                                       int want_dx, int want_dw);
+bitnet_status bitnet_hbitlinear_backward(const void* dy, bitnet_dtype dy_dtype, int64_t M,
+                                         int64_t N, const int8_t* codes, const float* scales,
+                                         int64_t K, const uint8_t* Wpacked, const float* alpha,
+                                         int bits, int hadamard, float* dx, float* dw, void* ws,
+                                         size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -224,3 +224,63 @@ def test_kv_quantize_validation(lib, args, status):
 
 def test_kv_quantize_empty_is_noop(lib):
     assert lib.bitnet_kv_quantize(None, _lib.BF16, 0, 64, 4, 4, None, None, None) == _lib.OK
+
+
+def test_backward_workspace_sizes(lib):
+    # dx: t^T in bf16 (K*N*2); an fp32 dy adds its two bf16 halves (2*M*N*2)
+    assert lib.bitnet_backward_workspace_bytes(128, 256, 192, _lib.BF16, 1, 0) == 256 * 192 * 2
+    assert lib.bitnet_backward_workspace_bytes(128, 256, 192, _lib.F32, 1, 0) == \
+        256 * 192 * 2 + 2 * 128 * 192 * 2
+    # dw: hi/lo of dy*s/c transposed (2*N*Mp*2) + codes transposed (K*Mp*2), Mp = M padded to 64
+    assert lib.bitnet_backward_workspace_bytes(100, 256, 192, _lib.BF16, 0, 1) == \
+        2 * 192 * 128 * 2 + 256 * 128 * 2
+    # both: the two parts share the bytes
+    dx_part = 256 * 192 * 2 + 2 * 100 * 192 * 2        # every part a multiple of 256 here
+    dw_part = 2 * 192 * 128 * 2 + 256 * 128 * 2
+    assert lib.bitnet_backward_workspace_bytes(100, 256, 192, _lib.F32, 1, 1) == max(dx_part, dw_part)
+    assert lib.bitnet_backward_workspace_bytes(100, 256, 192, _lib.BF16, 1, 1) == dw_part
+    assert lib.bitnet_backward_workspace_bytes(4, 100, 64, _lib.BF16, 1, 1) == 0  # invalid K
+    assert lib.bitnet_backward_workspace_bytes(4, 128, 96, _lib.BF16, 1, 1) == 0  # invalid N
+
+
+def _bwd(lib, dy=FAKE, dt=_lib.BF16, M=128, N=192, codes=FAKE, scales=FAKE, K=256, Wp=FAKE,
+         alpha=FAKE, bits=8, had=1, dx=FAKE, dw=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.bitnet_hbitlinear_backward(dy, dt, M, N, codes, scales, K, Wp, alpha, bits, had, dx,
+                                          dw, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dy=None), _lib.ERR_INVALID_ARG),
+    (dict(codes=None), _lib.ERR_INVALID_ARG),
+    (dict(scales=None), _lib.ERR_INVALID_ARG),
+    (dict(Wp=None), _lib.ERR_INVALID_ARG),
+    (dict(alpha=None), _lib.ERR_INVALID_ARG),
+    (dict(ws=None), _lib.ERR_INVALID_ARG),
+    (dict(ws_bytes=100), _lib.ERR_INVALID_ARG),
+    (dict(M=-1), _lib.ERR_INVALID_ARG),
+    (dict(had=2), _lib.ERR_INVALID_ARG),
+    (dict(bits=3), _lib.ERR_BAD_BITS),
+    (dict(K=100), _lib.ERR_ALIGN),
+    (dict(N=100), _lib.ERR_ALIGN),
+    (dict(K=192, had=1), _lib.ERR_NOT_POW2),
+    (dict(K=65536, had=1), _lib.ERR_NOT_POW2),
+    (dict(M=1 << 22), _lib.ERR_UNSUPPORTED),
+    (dict(dt=9), _lib.ERR_UNSUPPORTED),
+    (dict(dy=FAKE + 2), _lib.ERR_ALIGN),
+    (dict(codes=FAKE + 8), _lib.ERR_ALIGN),
+    (dict(ws=FAKE + 16), _lib.ERR_ALIGN),
+    (dict(dx=FAKE + 1), _lib.ERR_ALIGN),
+])
+def test_backward_validation(lib, kwargs, status):
+    assert _bwd(lib, **kwargs) == status
+    assert lib.bitnet_last_error() != b""
+
+
+def test_backward_optional_outputs(lib):
+    # neither gradient wanted: nothing to do, nothing read
+    assert _bwd(lib, dx=None, dw=None, dy=None, ws=None) == _lib.OK
+    # dx only: codes and scales are not needed; dw only: the weights are not
+    assert _bwd(lib, dw=None, codes=None, scales=None, Wp=None) == _lib.ERR_INVALID_ARG
+    assert _bwd(lib, dx=None, Wp=None, alpha=None, codes=None) == _lib.ERR_INVALID_ARG
+    # no tokens and no weight gradient: dx has no elements
+    assert _bwd(lib, M=0, dw=None, dy=None, ws=None) == _lib.OK

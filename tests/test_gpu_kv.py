@@ -55,3 +55,20 @@ def test_kv_quantize_parity(B, H, S, D, xdt, bits):
     if S > 1:
         lo, hi = {3: (-4, 3), 4: (-8, 7), 8: (-128, 127)}[bits]
         assert c[..., 1:, :].min() >= lo and c[..., 1:, :].max() <= hi
+
+
+@pytest.mark.parametrize("B,H,S,D,xdt,bits", [
+    (1, 32, 4096, 128, "bf16", 3),   # the timed cache: four rows per lane group, no tail
+    (1, 33, 4001, 128, "bf16", 4),   # four rows per lane group with a ragged last workgroup
+    (2, 32, 4099, 64, "bf16", 8),
+    (1, 128, 4097, 32, "fp32", 3),
+])
+def test_kv_quantize_parity_large(B, H, S, D, xdt, bits):
+    print(f"kv large case B={B} H={H} S={S} D={D} x={xdt} bits={bits}", flush=True)
+    x_np, kv = _kv(B, H, S, D, xdt, seed=7 + S + D + bits)
+    codes, scales = bl.kv_quantize(kv, bits)
+    torch.cuda.synchronize()
+    ref_in = oracle.widen_input(x_np, xdt).reshape(B, H, S, D)
+    q, s, p = oracle.kv_quantize(ref_in, bits)
+    assert_codes_match(codes.cpu().numpy(), q, p)
+    np.testing.assert_allclose(scales.cpu().numpy(), s, rtol=2e-6)

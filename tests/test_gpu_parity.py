@@ -16,7 +16,8 @@ import torch
 import oracle
 import bit_activation_linear_amd as bl
 from bit_activation_linear_amd import workloads
-from parity_util import assert_codes_match, assert_packed_match, assert_y_close, assert_y_parity
+from parity_util import (EPILOGUE_TOL, assert_codes_match, assert_packed_match, assert_y_close,
+                         assert_y_with_flips, decode_packed)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -43,27 +44,37 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     Wp, alpha = bl.ternarize_weights(W)
     codes, scales = bl.quantize_activations(x, bits, had)
     y = bl.hbitlinear_forward(x, Wp, alpha, bits, had)
-    acc = bl.ternary_gemm_i32(codes, Wp)
     y2 = bl.ternary_linear_dequant(codes, scales, Wp, alpha, bits)
     torch.cuda.synchronize()
 
     t_ref, a_ref, p_w = oracle.ternarize(case["W"])
-    w_flips = assert_packed_match(Wp.cpu().numpy(), t_ref, p_w)
+    assert_packed_match(Wp.cpu().numpy(), t_ref, p_w)
     assert abs(alpha.item() - a_ref) <= 1e-6 * a_ref
 
     ref = oracle.forward(case["x"], x_dtype, t_ref, a_ref, bits, had)
     q_gpu = codes.cpu().numpy()
-    q_flips = assert_codes_match(q_gpu, ref["q"], ref["p"])
+    assert_codes_match(q_gpu, ref["q"], ref["p"])
     np.testing.assert_allclose(scales.cpu().numpy(), ref["s"], rtol=2e-6)
 
-    # int32 accumulators exact on identical codes, both ways round.
-    t_gpu = oracle.unpack_2bit(Wp.cpu().numpy())
-    np.testing.assert_array_equal(acc.cpu().numpy(), oracle.ternary_matmul_i64(q_gpu, t_gpu))
-    acc_from_ref = bl.ternary_gemm_i32(torch.from_numpy(ref["q"]).to(DEV), Wp)
-    np.testing.assert_array_equal(acc_from_ref.cpu().numpy(), oracle.ternary_matmul_i64(ref["q"], t_gpu))
+    # The product stages on the oracle's own codes, weights, scales and alpha:
+    # int32 accumulators bit-exact, the dequantized output to fp32 rounding.
+    q_ref_d = torch.from_numpy(ref["q"]).to(DEV)
+    Wp_ref = torch.from_numpy(oracle.pack_2bit(t_ref)).to(DEV)
+    s32 = ref["s"].astype(np.float32)
+    a32 = np.float32(a_ref)
+    acc_ref_gpu = bl.ternary_gemm_i32(q_ref_d, Wp_ref)
+    y_ep = bl.ternary_linear_dequant(q_ref_d, torch.from_numpy(s32).to(DEV), Wp_ref,
+                                     torch.tensor([a32], device=DEV), bits)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc_ref_gpu.cpu().numpy(), ref["acc"])
+    assert_y_close(y_ep.cpu().numpy(),
+                   oracle.dequantize(ref["acc"], float(a32), s32.astype(np.float64), bits),
+                   what="epilogue on the oracle's codes", tol=EPILOGUE_TOL)
 
-    # The staged product runs on exactly these codes.
-    assert_y_parity(y2.cpu().numpy(), q_gpu, t_gpu, ref, a_ref, bits, w_flips + q_flips)
+    # End to end on the GPU's own codes and weights; a flip inside the
+    # rounding band is allowed its bounded effect on y.
+    assert_y_with_flips(y2.cpu().numpy(), q_gpu, decode_packed(Wp.cpu().numpy()), ref["q"], t_ref,
+                        ref["s"], a_ref, bits, ref["y64"])
     # The forward is the two stages back to back, bit for bit, except where it
     # runs as one fused kernel with int4: the absmean is then summed in another
     # order, an ulp of the scale can move a code sitting on a rounding
@@ -154,10 +165,10 @@ def test_parity_full_workload(key):
         rows = np.unique(np.concatenate([[0, wl.M - 1], rng.choice(wl.M, SAMPLE_ROWS - 2, replace=False)]))
     acc_ref, y_ref = oracle.forward_from_codes(q_ref[rows], s_ref[rows], t_ref, a_ref, wl.bits)
     assert_y_close(y.cpu().numpy()[rows], y_ref)
-    # exact integer product of the GPU's own codes on the sampled rows
-    acc = bl.ternary_gemm_i32(codes[torch.from_numpy(rows).to(DEV)].contiguous(), Wp)
-    t_gpu = oracle.unpack_2bit(Wp.cpu().numpy())
-    np.testing.assert_array_equal(acc.cpu().numpy(), oracle.ternary_matmul_i64(q_gpu[rows], t_gpu))
+    # exact integer product of the oracle's codes and weights on the sampled rows
+    acc = bl.ternary_gemm_i32(torch.from_numpy(np.ascontiguousarray(q_ref[rows])).to(DEV),
+                              torch.from_numpy(oracle.pack_2bit(t_ref)).to(DEV))
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
 
 
 # Edge and degenerate cases ------------------------------------------------
@@ -184,7 +195,7 @@ def test_zero_rows_and_constant_weights():
     y = bl.hbitlinear_forward(x, Wp, alpha, 8, 1)
     torch.cuda.synchronize()
     assert alpha.item() == pytest.approx(0.25)
-    assert np.all(oracle.unpack_2bit(Wp.cpu().numpy()) == -1)
+    assert np.all(decode_packed(Wp.cpu().numpy()) == -1)
     assert torch.count_nonzero(codes[3]).item() == 0 and torch.count_nonzero(y[17]).item() == 0
     assert scales[3].item() == pytest.approx(1e-7)
 
@@ -211,18 +222,18 @@ def test_pack_2bit_matches_oracle():
 def test_integer_extremes_exact():
     _say("integer extremes")
     K = 32768
-    codes = torch.full((18, K), 127, dtype=torch.int8, device=DEV)
-    codes[1] = -128
-    codes[5, ::3] = -128
+    q = np.full((18, K), 127, dtype=np.int8)
+    q[1] = -128
+    q[5, ::3] = -128
     t = np.ones((33, K), dtype=np.int8)
     t[2] = -1
     t[7, ::2] = 0
+    codes = torch.from_numpy(q).to(DEV)
     Wp = bl.pack_2bit(torch.from_numpy(t).to(DEV))
     for m in (18, 2):  # prefill tile and the streaming shape
         acc = bl.ternary_gemm_i32(codes[:m].contiguous(), Wp)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(acc.cpu().numpy(),
-                                      oracle.ternary_matmul_i64(codes[:m].cpu().numpy(), t))
+        np.testing.assert_array_equal(acc.cpu().numpy(), oracle.ternary_matmul_i64(q[:m], t))
 
 
 def test_bitwise_deterministic():

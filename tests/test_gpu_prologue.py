@@ -16,7 +16,7 @@ import torch
 import oracle
 import bit_activation_linear_amd as bl
 from bit_activation_linear_amd import workloads
-from parity_util import assert_codes_match, assert_packed_match, assert_y_close, assert_y_parity
+from parity_util import assert_codes_match, assert_packed_match, assert_y_close, assert_y_with_flips, decode_packed
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -57,15 +57,16 @@ def _run(M, K, N, bits, had, x_dtype, swiglu, rms, gamma, seed):
     torch.cuda.synchronize()
 
     t_ref, a_ref, p_w = oracle.ternarize(case["W"])
-    w_flips = assert_packed_match(Wp.cpu().numpy(), t_ref, p_w)
+    assert_packed_match(Wp.cpu().numpy(), t_ref, p_w)
     ref = oracle.forward_prologue(case["x"], x_dtype, t_ref, a_ref, bits, had, up=up_np, rms=rms,
                                   norm_weight=None if g_np is None else g_np.astype(np.float64))
     q_gpu = codes.cpu().numpy()
-    q_flips = assert_codes_match(q_gpu, ref["q"], ref["p"])
+    assert_codes_match(q_gpu, ref["q"], ref["p"])
     np.testing.assert_allclose(scales.cpu().numpy(), ref["s"], rtol=1e-5)
-    t_gpu = oracle.unpack_2bit(Wp.cpu().numpy())
-    # the staged product runs on exactly the inspected codes
-    assert_y_parity(y2.cpu().numpy(), q_gpu, t_gpu, ref, a_ref, bits, w_flips + q_flips)
+    # the staged product on the inspected codes; a flip inside the rounding
+    # band is allowed its bounded effect on y
+    assert_y_with_flips(y2.cpu().numpy(), q_gpu, decode_packed(Wp.cpu().numpy()), ref["q"], t_ref,
+                        ref["s"], a_ref, bits, ref["y64"])
     # The forward is those two stages, bit for bit, except for the decode
     # shapes it runs as one fused kernel: there the statistic and the sum of
     # squares are reduced in another order, an ulp of a scale can move a code

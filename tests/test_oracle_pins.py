@@ -325,3 +325,14 @@ def test_generator_bf16_rounding_matches_torch():
     ours = workloads.fp32_to_bf16_bits(x)
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(ours, ref)
+
+
+def test_test_side_decoder_agrees_with_the_oracle():
+    """The GPU parity tests decode packed weights with their own decoder
+    (no GPU output is ever passed to the oracle); it must read the layout
+    the oracle packs."""
+    from parity_util import decode_packed
+
+    rng = np.random.default_rng(12)
+    t = rng.integers(-1, 2, size=(9, 320)).astype(np.int8)
+    np.testing.assert_array_equal(decode_packed(oracle.pack_2bit(t)), t)
