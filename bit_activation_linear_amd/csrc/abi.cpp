@@ -346,15 +346,12 @@ bitnet_status bitnet_hbitlinear_backward(const void* dy, bitnet_dtype dy_dtype, 
     e = bitnet::launch_expand_transpose(Wpacked, N, K, w.wt, stream);
     if (e != hipSuccess) return hip_status(e, fn);
     if (dy_dtype == BITNET_BF16) {
-      e = bitnet::launch_bf16_gemm_nt(static_cast<const uint16_t*>(dy), N, w.wt, N, M, K, N, dx, K,
-                                      alpha, 1.0f, false, stream);
+      e = bitnet::launch_bf16_gemm_nt(static_cast<const uint16_t*>(dy), nullptr, N, w.wt, N, M, K,
+                                      N, dx, K, alpha, 1.0f, stream);
     } else {
       e = bitnet::launch_split_rows(static_cast<const float*>(dy), M * N, w.dy_hi, w.dy_lo, stream);
       if (e == hipSuccess)
-        e = bitnet::launch_bf16_gemm_nt(w.dy_hi, N, w.wt, N, M, K, N, dx, K, alpha, 1.0f, false,
-                                        stream);
-      if (e == hipSuccess)
-        e = bitnet::launch_bf16_gemm_nt(w.dy_lo, N, w.wt, N, M, K, N, dx, K, alpha, 1.0f, true,
+        e = bitnet::launch_bf16_gemm_nt(w.dy_hi, w.dy_lo, N, w.wt, N, M, K, N, dx, K, alpha, 1.0f,
                                         stream);
     }
     if (e != hipSuccess) return hip_status(e, fn);
@@ -372,10 +369,7 @@ bitnet_status bitnet_hbitlinear_backward(const void* dy, bitnet_dtype dy_dtype, 
                                              w.p_lo, stream);
     if (e == hipSuccess) e = bitnet::launch_codes_transpose(codes, M, K, Mp, w.qt, stream);
     if (e == hipSuccess)
-      e = bitnet::launch_bf16_gemm_nt(w.p_hi, Mp, w.qt, Mp, N, K, Mp, dw, K, nullptr, 1.0f, false,
-                                      stream);
-    if (e == hipSuccess && Mp > 0)
-      e = bitnet::launch_bf16_gemm_nt(w.p_lo, Mp, w.qt, Mp, N, K, Mp, dw, K, nullptr, 1.0f, true,
+      e = bitnet::launch_bf16_gemm_nt(w.p_hi, w.p_lo, Mp, w.qt, Mp, N, K, Mp, dw, K, nullptr, 1.0f,
                                       stream);
     if (e != hipSuccess) return hip_status(e, fn);
   }

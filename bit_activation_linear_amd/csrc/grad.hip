@@ -11,7 +11,7 @@
 // Both products are dense floating-point contractions and run on
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
 //   - dx: dy in bf16 (exact when the caller's gradient is bf16; an fp32
-//     gradient is split into hi + lo bf16 parts, two passes) times t, which
+//     gradient is split into hi + lo bf16 parts) times t, which
 //     bf16 holds exactly. The packed weights are expanded once per call into
 //     a bf16 copy of t^T [K, N] so that both operands have the contraction
 //     (N) contiguous.
@@ -21,12 +21,15 @@
 // Every product in the MFMA is exact; only the fp32 accumulation and the
 // 2^-17 relative residual of the hi/lo split round.
 //
-// GEMM kernel: C[R, Cn] (+)= scale * A[R, Kc] . B[Cn, Kc]^T, bf16 row-major
-// operands with Kc % 64 == 0. Direct-to-LDS staging as in the forward
-// prefill kernel: a ring of SL stage slots, each holding 64 k (128 bytes) of
-// the tile's A and B rows, 16-byte chunks of every row XOR-permuted so that
-// operand reads are bank-conflict-free; one barrier per stage; the next
-// 32-k block's operands are read while the current block's MFMAs run.
+// GEMM kernel: C[R, Cn] = scale * (A + A2)[R, Kc] . B[Cn, Kc]^T, bf16
+// row-major operands with Kc % 64 == 0; with SPLIT the hi and lo parts A and
+// A2 are staged side by side and multiplied into the same accumulators, so
+// a split operand costs twice the MFMAs but no second pass over C.
+// Direct-to-LDS staging as in the forward prefill kernel: a ring of SL stage
+// slots, each holding 64 k (128 bytes) of the tile's A (and A2) and B rows,
+// 16-byte chunks of every row XOR-permuted so that operand reads are
+// bank-conflict-free; one barrier per stage; the next 32-k block's operands
+// are read while the current block's MFMAs run.
 #include "kernels.h"
 #include "ternary_common.cuh"
 
@@ -39,13 +42,14 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kRow = 128;        // bytes of one operand row per stage (64 bf16)
 constexpr int kGradChunks = 8;   // MFMA groups per block in the interleaved schedule
 
-template <int RT, int CT, int WM, int WN>
+template <int RT, int CT, int WM, int WN, bool SPLIT>
 struct GShape {
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * RT * WM;
   static constexpr int BN = 32 * CT * WN;
-  static constexpr int A_BYTES = BM * kRow;
+  static constexpr int NAP = SPLIT ? 2 : 1;      // A parts (hi, lo)
+  static constexpr int A_BYTES = NAP * BM * kRow;  // part p's rows at p * BM
   static constexpr int B_BYTES = BN * kRow;
   static constexpr int SLOT = A_BYTES + B_BYTES;
   static constexpr int NA = A_BYTES / 1024;  // 1-KB direct loads per stage (8 rows each)
@@ -55,19 +59,20 @@ struct GShape {
   static constexpr int LDS = SL * SLOT;
   static_assert(NL_W * NW == NA + NB, "uneven staging");
   static_assert(2 * SLOT <= kLdsMax, "two stage slots do not fit in LDS");
-  static_assert((2 * RT * CT) % kGradChunks == 0, "MFMA groups");
+  static_assert((2 * NAP * RT * CT) % kGradChunks == 0, "MFMA groups");
+  static_assert(BM % 16 == 0, "the parts' rows must keep the swizzle");
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const v4i v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int RT, int CT, int WM, int WN, bool ACCUM>
+template <int RT, int CT, int WM, int WN, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void bf16_gemm_nt_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-    int R, int Cn, int Kc, float* __restrict__ C, int64_t ldc, const float* __restrict__ scale_p,
-    float scale_h, int tiles_m, int tiles_n) {
-  using S = GShape<RT, CT, WM, WN>;
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2, int64_t lda,
+    const uint16_t* __restrict__ B, int64_t ldb, int R, int Cn, int Kc, float* __restrict__ C,
+    int64_t ldc, const float* __restrict__ scale_p, float scale_h, int tiles_m, int tiles_n) {
+  using S = GShape<RT, CT, WM, WN, SPLIT>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   // XCD-aware tile order (workgroup L runs on XCD L % 8; each XCD walks a
@@ -97,6 +102,7 @@ __global__ __launch_bounds__(64 * WM * WN) void bf16_gemm_nt_kernel(
   const unsigned a_bytes = (unsigned)((R - r0 < S::BM ? R - r0 : S::BM) * arow);
   const unsigned b_bytes = (unsigned)((Cn - c0 < S::BN ? Cn - c0 : S::BN) * brow);
   const u4 a_rsrc = make_rsrc(A + (size_t)r0 * lda, a_bytes);
+  const u4 a2_rsrc = make_rsrc((SPLIT ? A2 : A) + (size_t)r0 * lda, a_bytes);
   const u4 b_rsrc = make_rsrc(B + (size_t)c0 * ldb, b_bytes);
   u4 a_none = a_rsrc, b_none = b_rsrc;
   a_none.z = 0;
@@ -115,8 +121,10 @@ __global__ __launch_bounds__(64 * WM * WN) void bf16_gemm_nt_kernel(
     const bool live_ = (ks_) < nst;                                                             \
     const int q_ = wave + S::NW * (i);                                                          \
     if (q_ < S::NA) {                                                                           \
-      load_lds16(live_ ? a_rsrc : a_none,                                                       \
-                 ((q_ & 1) ? a_lane1 : a_lane0) + (int)(q_ * 8 * arow) + (ks_) * kRow,          \
+      const bool lo_ = SPLIT && q_ >= S::BM / 8;                                                \
+      const int qa_ = lo_ ? q_ - S::BM / 8 : q_;                                                \
+      load_lds16(live_ ? (lo_ ? a2_rsrc : a_rsrc) : a_none,                                     \
+                 ((qa_ & 1) ? a_lane1 : a_lane0) + (int)(qa_ * 8 * arow) + (ks_) * kRow,        \
                  lds0 + (unsigned)((slot_) * S::SLOT + q_ * 1024));                             \
     } else {                                                                                    \
       const int qb_ = q_ - S::NA;                                                               \
@@ -148,15 +156,18 @@ __global__ __launch_bounds__(64 * WM * WN) void bf16_gemm_nt_kernel(
       for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0.0f;
 
   // Fragment sets X and Y alternate between the 32-k block being multiplied
-  // and the block being read.
-  v4i ax[2][RT], ay[2][RT], bx[2][CT], by[2][CT];
+  // and the block being read. A fragment i < RT is part hi's row block i,
+  // i >= RT part lo's row block i - RT (same accumulator).
+  constexpr int RA = S::NAP * RT;
+  v4i ax[2][RA], ay[2][RA], bx[2][CT], by[2][CT];
 
 #define GRAD_READ(slot_, blk_, A_, B_)                                                          \
   {                                                                                             \
     const char* sb_ = smem + (slot_) * S::SLOT;                                                 \
     _Pragma("unroll") for (int hh = 0; hh < 2; ++hh) {                                          \
-      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) A_[hh][rt] =                            \
-          *reinterpret_cast<const v4i*>(sb_ + a_rd[2 * (blk_) + hh] + rt * 32 * kRow);          \
+      _Pragma("unroll") for (int ra = 0; ra < RA; ++ra) A_[hh][ra] =                            \
+          *reinterpret_cast<const v4i*>(sb_ + a_rd[2 * (blk_) + hh] +                           \
+                                        ((ra / RT) * S::BM + (ra % RT) * 32) * kRow);           \
       _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) B_[hh][ct] =                            \
           *reinterpret_cast<const v4i*>(sb_ + b_rd[2 * (blk_) + hh] + ct * 32 * kRow);          \
     }                                                                                           \
@@ -164,12 +175,12 @@ __global__ __launch_bounds__(64 * WM * WN) void bf16_gemm_nt_kernel(
 #define GRAD_PIN(A_, B_)                                                                        \
   _Pragma("unroll") for (int hh = 0; hh < 2; ++hh) {                                            \
     _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) asm volatile("" : "+v"(B_[hh][ct]));      \
-    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) asm volatile("" : "+v"(A_[hh][rt]));      \
+    _Pragma("unroll") for (int ra = 0; ra < RA; ++ra) asm volatile("" : "+v"(A_[hh][ra]));      \
   }
   // One block's MFMAs in kGradChunks groups separated by scheduling barriers;
   // with LD_ set, this wave's loads of stage lks_ into slot lslot_ are spread
   // over the groups.
-  constexpr int kMfmaPerBlock = 2 * RT * CT;
+  constexpr int kMfmaPerBlock = 2 * RA * CT;
 #define GRAD_STEP(A_, B_, LD_, lks_, lslot_)                                                    \
   _Pragma("unroll") for (int ch = 0; ch < kGradChunks; ++ch) {                                  \
     if (LD_) {                                                                                  \
@@ -179,9 +190,9 @@ __global__ __launch_bounds__(64 * WM * WN) void bf16_gemm_nt_kernel(
     }                                                                                           \
     _Pragma("unroll") for (int f = ch * (kMfmaPerBlock / kGradChunks);                          \
                            f < (ch + 1) * (kMfmaPerBlock / kGradChunks); ++f) {                 \
-      const int hh = f / (RT * CT), rt = (f / CT) % RT, ct = f % CT;                            \
-      acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                                    \
-          as_bf16x8(A_[hh][rt]), as_bf16x8(B_[hh][ct]), acc[rt][ct], 0, 0, 0);                  \
+      const int hh = f / (RA * CT), ra = (f / CT) % RA, ct = f % CT;                            \
+      acc[ra % RT][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                               \
+          as_bf16x8(A_[hh][ra]), as_bf16x8(B_[hh][ct]), acc[ra % RT][ct], 0, 0, 0);             \
     }                                                                                           \
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
@@ -239,13 +250,7 @@ __global__ __launch_bounds__(64 * WM * WN) void bf16_gemm_nt_kernel(
       for (int ct = 0; ct < CT; ++ct) {
         const int cc = c0 + wn * 32 * CT + ct * 32 + l32;
         if (cc >= Cn) continue;
-        float* o = C + (size_t)r * ldc + cc;
-        const float val = acc[rt][ct][v] * scale;
-        if (ACCUM) {
-          *o += val;
-        } else {
-          *o = val;
-        }
+        C[(size_t)r * ldc + cc] = acc[rt][ct][v] * scale;
       }
     }
   }
@@ -415,36 +420,38 @@ __global__ __launch_bounds__(256) void codes_transpose_kernel(const int8_t* __re
   dst[1] = src[1];
 }
 
-template <int RT, int CT, int WM, int WN, bool ACCUM>
-hipError_t launch_gemm_t(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t R,
-                         int64_t Cn, int64_t Kc, float* C, int64_t ldc, const float* scale_p,
-                         float scale_h, hipStream_t stream) {
-  using S = GShape<RT, CT, WM, WN>;
+template <int RT, int CT, int WM, int WN, bool SPLIT>
+hipError_t launch_gemm_t(const uint16_t* A, const uint16_t* A2, int64_t lda, const uint16_t* B,
+                         int64_t ldb, int64_t R, int64_t Cn, int64_t Kc, float* C, int64_t ldc,
+                         const float* scale_p, float scale_h, hipStream_t stream) {
+  using S = GShape<RT, CT, WM, WN, SPLIT>;
   const int tiles_m = (int)((R + S::BM - 1) / S::BM);
   const int tiles_n = (int)((Cn + S::BN - 1) / S::BN);
   const int tiles = tiles_m * tiles_n;
   if (tiles == 0) return hipSuccess;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  auto kern = bf16_gemm_nt_kernel<RT, CT, WM, WN, ACCUM>;
+  auto kern = bf16_gemm_nt_kernel<RT, CT, WM, WN, SPLIT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)(per_xcd * kXcds)), dim3(S::NT), S::LDS, stream>>>(
-      A, lda, B, ldb, (int)R, (int)Cn, (int)Kc, C, ldc, scale_p, scale_h, tiles_m, tiles_n);
+      A, A2, lda, B, ldb, (int)R, (int)Cn, (int)Kc, C, ldc, scale_p, scale_h, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bf16_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                               int64_t R, int64_t Cn, int64_t Kc, float* C, int64_t ldc,
-                               const float* scale_p, float scale_h, bool accumulate,
+// 256 x 256 tiles for one A part; 128 x 256 tiles (the two parts' rows side
+// by side in LDS, same MFMA count per stage) for a split A.
+hipError_t launch_bf16_gemm_nt(const uint16_t* A, const uint16_t* A_lo, int64_t lda,
+                               const uint16_t* B, int64_t ldb, int64_t R, int64_t Cn, int64_t Kc,
+                               float* C, int64_t ldc, const float* scale_p, float scale_h,
                                hipStream_t stream) {
-  if (accumulate)
-    return launch_gemm_t<4, 4, 2, 2, true>(A, lda, B, ldb, R, Cn, Kc, C, ldc, scale_p, scale_h,
-                                           stream);
-  return launch_gemm_t<4, 4, 2, 2, false>(A, lda, B, ldb, R, Cn, Kc, C, ldc, scale_p, scale_h,
-                                          stream);
+  if (A_lo)
+    return launch_gemm_t<2, 4, 2, 2, true>(A, A_lo, lda, B, ldb, R, Cn, Kc, C, ldc, scale_p,
+                                           scale_h, stream);
+  return launch_gemm_t<4, 4, 2, 2, false>(A, nullptr, lda, B, ldb, R, Cn, Kc, C, ldc, scale_p,
+                                          scale_h, stream);
 }
 
 hipError_t launch_expand_transpose(const uint8_t* Wpacked, int64_t N, int64_t K, uint16_t* Wt,

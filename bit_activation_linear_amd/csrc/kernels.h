@@ -107,12 +107,13 @@ hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
 
 // ---- Backward -------------------------------------------------------------
 
-// C[R, Cn] (+)= scale * A[R, Kc] . B[Cn, Kc]^T on bf16 operands (uint16 bit
-// patterns, row pitches lda / ldb elements), fp32 out with pitch ldc;
-// scale = scale_h * *scale_p (scale_p may be null). Kc % 64 == 0.
-hipError_t launch_bf16_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                               int64_t R, int64_t Cn, int64_t Kc, float* C, int64_t ldc,
-                               const float* scale_p, float scale_h, bool accumulate,
+// C[R, Cn] = scale * (A + A_lo)[R, Kc] . B[Cn, Kc]^T on bf16 operands
+// (uint16 bit patterns, row pitches lda / ldb elements; A_lo may be null),
+// fp32 out with pitch ldc; scale = scale_h * *scale_p (scale_p may be null).
+// Kc % 64 == 0.
+hipError_t launch_bf16_gemm_nt(const uint16_t* A, const uint16_t* A_lo, int64_t lda,
+                               const uint16_t* B, int64_t ldb, int64_t R, int64_t Cn, int64_t Kc,
+                               float* C, int64_t ldc, const float* scale_p, float scale_h,
                                hipStream_t stream);
 
 // Wt [K, N] bf16 = t^T from the packed weights (N % 64 == 0, K % 64 == 0).
