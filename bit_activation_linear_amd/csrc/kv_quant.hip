@@ -53,78 +53,60 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// RPT token rows per group of G lanes, kRowsPerPass = 256 / G rows apart;
-// lane j of a group owns elements 8j .. 8j+7 (j < D / 8) of each. All RPT
-// loads are issued before any arithmetic so that every lane keeps RPT
-// 16-byte requests in flight.
-template <typename XT, int BITS, int G, int RPT>
+// One token row per group of G lanes; lane j of a group owns elements
+// 8j .. 8j+7 (j < D / 8).
+template <typename XT, int BITS, int G>
 __global__ __launch_bounds__(256) void kv_quant_kernel(const XT* __restrict__ kv, int64_t R, int D,
                                                        int S, int8_t* __restrict__ codes,
                                                        float* __restrict__ scales) {
-  constexpr int kRowsPerPass = 256 / G;
+  constexpr int kRowsPerBlock = 256 / G;
   const int t = threadIdx.x;
   const int j = t % G;
-  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerPass * RPT + t / G;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + t / G;
+  const bool row_ok = row < R;
+  const int64_t rc = row_ok ? row : R - 1;
   const bool own = j * 8 < D;
   const int jc = own ? j : 0;
-  float v[RPT][8];
+  float v[8];
+  load8v(kv + rc * D + 8 * jc, v);
+
+  const bool bos = (rc % S) == 0;
+  float st_max = 0.0f, st_sum = 0.0f;
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int64_t row = row0 + (int64_t)r * kRowsPerPass;
-    const int64_t rc = row < R ? row : R - 1;
-    load8v(kv + rc * D + 8 * jc, v[r]);
+  for (int e = 0; e < 8; ++e) {
+    st_max = fmaxf(st_max, fabsf(v[e]));
+    st_sum += fabsf(v[e]);
   }
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int64_t row = row0 + (int64_t)r * kRowsPerPass;
-    const bool row_ok = row < R;
-    const int64_t rc = row_ok ? row : R - 1;
-    const bool bos = (rc % S) == 0;
-    float st_max = 0.0f, st_sum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      st_max = fmaxf(st_max, fabsf(v[r][e]));
-      st_sum += fabsf(v[r][e]);
-    }
-    st_max = group_max<G>(own ? st_max : 0.0f);
-    st_sum = group_sum<G>(own ? st_sum : 0.0f);
-    // BOS tokens, and every token at 8 bits, use absmax with c = 127.
-    float c, lo, hi, st;
-    if (bos || BITS == 8) {
-      c = 127.0f; lo = -128.0f; hi = 127.0f; st = st_max;
-    } else if (BITS == 4) {
-      c = 2.6457513110645906f; lo = -8.0f; hi = 7.0f; st = st_sum / (float)D;
-    } else {
-      c = 3.0f; lo = -4.0f; hi = 3.0f; st = st_max;
-    }
-    const float s = st + kEps;
-    const float mult = c / s;
-    unsigned w[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float q = fminf(fmaxf(__builtin_rintf(v[r][e] * mult), lo), hi);
-      w[e >> 2] |= ((unsigned)(int)q & 0xFFu) << (8 * (e & 3));
-    }
-    if (row_ok && own) *reinterpret_cast<uint2*>(codes + row * D + 8 * j) = make_uint2(w[0], w[1]);
-    if (row_ok && j == 0) scales[row] = s;
+  st_max = group_max<G>(own ? st_max : 0.0f);
+  st_sum = group_sum<G>(own ? st_sum : 0.0f);
+  // BOS tokens, and every token at 8 bits, use absmax with c = 127.
+  float c, lo, hi, st;
+  if (bos || BITS == 8) {
+    c = 127.0f; lo = -128.0f; hi = 127.0f; st = st_max;
+  } else if (BITS == 4) {
+    c = 2.6457513110645906f; lo = -8.0f; hi = 7.0f; st = st_sum / (float)D;
+  } else {
+    c = 3.0f; lo = -4.0f; hi = 3.0f; st = st_max;
   }
+  const float s = st + kEps;
+  const float mult = c / s;
+  unsigned w[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float q = fminf(fmaxf(__builtin_rintf(v[e] * mult), lo), hi);
+    w[e >> 2] |= ((unsigned)(int)q & 0xFFu) << (8 * (e & 3));
+  }
+  if (row_ok && own) *reinterpret_cast<uint2*>(codes + row * D + 8 * j) = make_uint2(w[0], w[1]);
+  if (row_ok && j == 0) scales[row] = s;
 }
 
 template <typename XT, int BITS, int G>
 hipError_t launch_kv_g(const void* kv, int64_t R, int D, int S, int8_t* codes, float* scales,
                        hipStream_t stream) {
-  constexpr int kRowsPerPass = 256 / G;
-  // Four rows per lane group once the grid would still hold several
-  // workgroups per CU; one row otherwise.
-  if (R >= (int64_t)kRowsPerPass * 4 * 2048) {
-    const int64_t blocks = (R + kRowsPerPass * 4 - 1) / (kRowsPerPass * 4);
-    kv_quant_kernel<XT, BITS, G, 4><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        reinterpret_cast<const XT*>(kv), R, D, S, codes, scales);
-  } else {
-    const int64_t blocks = (R + kRowsPerPass - 1) / kRowsPerPass;
-    kv_quant_kernel<XT, BITS, G, 1><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        reinterpret_cast<const XT*>(kv), R, D, S, codes, scales);
-  }
+  constexpr int kRowsPerBlock = 256 / G;
+  const int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
+  kv_quant_kernel<XT, BITS, G><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      reinterpret_cast<const XT*>(kv), R, D, S, codes, scales);
   return hipGetLastError();
 }
 

@@ -58,8 +58,8 @@ def test_kv_quantize_parity(B, H, S, D, xdt, bits):
 
 
 @pytest.mark.parametrize("B,H,S,D,xdt,bits", [
-    (1, 32, 4096, 128, "bf16", 3),   # the timed cache: four rows per lane group, no tail
-    (1, 33, 4001, 128, "bf16", 4),   # four rows per lane group with a ragged last workgroup
+    (1, 32, 4096, 128, "bf16", 3),   # the timed cache
+    (1, 33, 4001, 128, "bf16", 4),   # a ragged last workgroup
     (2, 32, 4099, 64, "bf16", 8),
     (1, 128, 4097, 32, "fp32", 3),
 ])
