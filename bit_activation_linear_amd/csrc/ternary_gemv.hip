@@ -136,10 +136,9 @@ __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* co
 // 4*(l/16) + v, column l%16.
 template <int CT, bool OUT_I32>
 __device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[CT], v4i* red,
-                                            const float* s_rows) {
+                                            const float* s_rows, int nw, float alpha) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int nw = blockDim.x >> 6;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) red[(wave * CT + ct) * 64 + lane] = acc[ct];
   lds_barrier();
@@ -150,7 +149,6 @@ __device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[
   v4i total = red[ct * 64 + l];
   for (int w = 1; w < nw; ++w) total += red[(w * CT + ct) * 64 + l];
   const int m0 = 4 * (l >> 4);
-  const float alpha = OUT_I32 ? 0.0f : *a.alpha;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int m = m0 + v;
@@ -171,9 +169,10 @@ __global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a) {
   v4i* red = reinterpret_cast<v4i*>(smem);  // [nw][CT][64]
   int8_t* stage = reinterpret_cast<int8_t*>(smem + (size_t)nw * CT * 1024) +
                   (size_t)(threadIdx.x >> 6) * 16 * kCodePitch;
+  const float alpha = OUT_I32 ? 0.0f : *a.alpha;
   v4i acc[CT];
   wave_product<CT>(a, a.codes, stage, acc);
-  gemv_finish<CT, OUT_I32>(a, acc, red, a.scales);
+  gemv_finish<CT, OUT_I32>(a, acc, red, a.scales, nw, alpha);
 }
 
 __device__ __forceinline__ void load4(const float* x, size_t i, float (&v)[4]) {
@@ -186,6 +185,34 @@ __device__ __forceinline__ void load4(const uint16_t* x, size_t i, float (&v)[4]
   v[1] = __uint_as_float(u.x & 0xFFFF0000u);
   v[2] = __uint_as_float(u.y << 16);
   v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+
+// The same four values loaded raw and widened later, so that the load can be
+// issued well before its first use.
+template <typename XT>
+struct Raw4;
+template <>
+struct Raw4<float> {
+  float4 d;
+};
+template <>
+struct Raw4<uint16_t> {
+  uint2 d;
+};
+__device__ __forceinline__ void raw_load4(const float* x, size_t i, Raw4<float>& r) {
+  r.d = *reinterpret_cast<const float4*>(x + i);
+}
+__device__ __forceinline__ void raw_load4(const uint16_t* x, size_t i, Raw4<uint16_t>& r) {
+  r.d = *reinterpret_cast<const uint2*>(x + i);
+}
+__device__ __forceinline__ void widen4(const Raw4<float>& r, float (&v)[4]) {
+  v[0] = r.d.x; v[1] = r.d.y; v[2] = r.d.z; v[3] = r.d.w;
+}
+__device__ __forceinline__ void widen4(const Raw4<uint16_t>& r, float (&v)[4]) {
+  v[0] = __uint_as_float(r.d.x << 16);
+  v[1] = __uint_as_float(r.d.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(r.d.y << 16);
+  v[3] = __uint_as_float(r.d.y & 0xFFFF0000u);
 }
 
 // Wave-wide max or sum of non-negative values with DPP row shifts and row
@@ -214,8 +241,8 @@ __device__ __forceinline__ float wave_reduce(float v) {
 // r < SBW (k in [256 (w SBW + r), +256)), for the statistic, for the codes
 // and for the product.
 //
-// Each lane loads its packed weights, then 4 consecutive x values per token
-// row and super-block; the per-row statistic (Eq. 5: absmax, or Eq. 6: mean
+// Each lane loads 4 consecutive x values per token row and super-block, then
+// its packed weights; the per-row statistic (Eq. 5: absmax, or Eq. 6: mean
 // |x|) of the wave's share is reduced in the wave with DPP, and a single
 // barrier publishes the waves' partial statistics. Every wave then combines
 // them in the same fixed order, quantizes its own values and hands them to
@@ -225,7 +252,17 @@ __device__ __forceinline__ float wave_reduce(float v) {
 template <typename XT, int BITS, int MG, int CT, int SBW, bool PRO>
 __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue pro) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int nw = blockDim.x >> 6;
+  // The scalars the kernel needs (kernel arguments and alpha) are fetched
+  // before the weight stream goes out, and pinned there: a small load issued
+  // once the stream is in flight waits behind it, about a microsecond, on
+  // the path from the statistic to the store. The wave count follows from K
+  // as in the launcher, with no read of the dispatch packet.
+  asm volatile("" ::"s"(a.M), "s"(a.K), "s"(a.N), "s"(a.c), "s"(a.y), "s"(a.x), "s"(a.Wp));
+  if constexpr (PRO)
+    asm volatile("" ::"s"(pro.up), "s"(pro.gamma), "s"(pro.norm_eps), "s"(pro.rms));
+  const float alpha = *a.alpha;
+  const int nsb = ((a.K >> 6) + 3) >> 2;
+  const int nw = (nsb + SBW - 1) / SBW > CT ? (nsb + SBW - 1) / SBW : CT;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   v4i* red = reinterpret_cast<v4i*>(smem);                                // [nw][CT][64]
@@ -238,10 +275,36 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
 
   const int col = lane & 15, grp = lane >> 4;
   const int nKB = a.K >> 6;
-  // The weight loads go out first: they are the long pole (HBM), and a
-  // statistic that waited on x alone would let the x requests, which every
-  // workgroup sends to the same few lines, queue ahead of them. Loads are
-  // unconditional from clamped, always-valid addresses.
+  // x (and the prologue's inputs) first, then the packed weights. Vector
+  // loads complete in issue order, so with this order the statistic, the
+  // barrier and the quantization wait for x alone and run while the weight
+  // stream (the long pole, HBM) is still arriving. The loads are
+  // unconditional from clamped, always-valid addresses (a load inside a
+  // branch would be waited for inside it) and are widened only after the
+  // weight loads have gone out. Each lane takes 4 consecutive x values of
+  // every token row in each super-block.
+  const XT* x = reinterpret_cast<const XT*>(a.x);
+  const XT* upp = (PRO && pro.up) ? reinterpret_cast<const XT*>(pro.up) : x;
+  const bool use_g = PRO && pro.rms && pro.gamma;
+  const float* gp = use_g ? pro.gamma : reinterpret_cast<const float*>(a.x);
+  bool own[SBW];
+  Raw4<XT> xraw[MG][SBW];
+  Raw4<XT> uraw[PRO ? MG : 1][SBW];
+  float4 graw[SBW];
+#pragma unroll
+  for (int r = 0; r < SBW; ++r) {
+    const int k0 = 256 * (wave * SBW + r) + 4 * lane;
+    own[r] = k0 < a.K;
+    const int kc = own[r] ? k0 : 0;
+#pragma unroll
+    for (int m = 0; m < MG; ++m) {
+      const size_t i = (size_t)(m < a.M ? m : 0) * a.K + kc;
+      raw_load4(x, i, xraw[m][r]);
+      if (PRO) raw_load4(upp, i, uraw[PRO ? m : 0][r]);
+    }
+    if (PRO) graw[r] = *reinterpret_cast<const float4*>(gp + (use_g ? kc : 0));
+  }
+  // Packed weights; unconditional loads from clamped, always-valid addresses.
   uint4 p[SBW][CT];
   {
     const size_t row_bytes = (size_t)(a.K >> 2);
@@ -258,25 +321,22 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
       }
     }
   }
-  // Then 4 consecutive x values of every token row in each super-block.
-  // (Rows past M are not loaded: every workgroup reads this x, and
-  // redundant requests for the same lines queue at the L2.)
-  const XT* x = reinterpret_cast<const XT*>(a.x);
-  bool own[SBW];
+  __builtin_amdgcn_sched_barrier(0);
+  // Rows past M hold row 0's values and are never used.
   float v[MG][SBW][4];
+  float u[PRO ? MG : 1][SBW][4];
+  float g[SBW][4];
 #pragma unroll
   for (int r = 0; r < SBW; ++r) {
-    const int k0 = 256 * (wave * SBW + r) + 4 * lane;
-    own[r] = k0 < a.K;
-    const int kc = own[r] ? k0 : 0;
 #pragma unroll
     for (int m = 0; m < MG; ++m) {
-      if (m < a.M) {
-        load4(x, (size_t)m * a.K + kc, v[m][r]);
-      } else {
-        v[m][r][0] = v[m][r][1] = v[m][r][2] = v[m][r][3] = 0.0f;
-      }
+      widen4(xraw[m][r], v[m][r]);
+      if (PRO) widen4(uraw[PRO ? m : 0][r], u[PRO ? m : 0][r]);
     }
+    g[r][0] = use_g ? graw[r].x : 1.0f;
+    g[r][1] = use_g ? graw[r].y : 1.0f;
+    g[r][2] = use_g ? graw[r].z : 1.0f;
+    g[r][3] = use_g ? graw[r].w : 1.0f;
   }
   // Input prologue (engine page: BitNetV2FFN's silu(gate) * up, then
   // HBitLinear's RMSNorm weight); the norm's 1/rms enters only the scale and
@@ -288,24 +348,19 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
   if constexpr (PRO) {
 #pragma unroll
     for (int r = 0; r < SBW; ++r) {
-      const int k0 = 256 * (wave * SBW + r) + 4 * lane;
-      const int kc = own[r] ? k0 : 0;
-      float g[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (pro.rms && pro.gamma) load4(pro.gamma, (size_t)kc, g);
 #pragma unroll
       for (int m = 0; m < MG; ++m) {
         if (m < a.M) {
           if (pro.up) {
-            float u[4];
-            load4(reinterpret_cast<const XT*>(pro.up), (size_t)m * a.K + kc, u);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[m][r][e] = (v[m][r][e] / (1.0f + expf(-v[m][r][e]))) * u[e];
+            for (int e = 0; e < 4; ++e)
+              v[m][r][e] = (v[m][r][e] / (1.0f + expf(-v[m][r][e]))) * u[m][r][e];
           }
           if (pro.rms) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               sq[m] += own[r] ? v[m][r][e] * v[m][r][e] : 0.0f;
-              v[m][r][e] *= g[e];
+              v[m][r][e] *= g[r][e];
             }
           }
         }
@@ -393,7 +448,7 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
     for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const v4i*>(qr + 16 * j) & kmask;
     mma_round<CT>(av, p[r], acc);
   }
-  gemv_finish<CT, false>(a, acc, red, srow);
+  gemv_finish<CT, false>(a, acc, red, srow, nw, alpha);
 }
 
 template <typename Kern>
