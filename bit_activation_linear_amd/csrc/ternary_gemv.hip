@@ -134,9 +134,11 @@ __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* co
 
 // Add the waves' 16x16 tiles and store. 16x16 MFMA layout: lane l holds rows
 // 4*(l/16) + v, column l%16.
+// s_row[v] is the scale of output row 4 (l / 16) + v of the finishing lane
+// (loaded ahead by the caller, like alpha).
 template <int CT, bool OUT_I32>
 __device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[CT], v4i* red,
-                                            const float* s_rows, int nw, float alpha) {
+                                            const float (&s_row)[4], int nw, float alpha) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
 #pragma unroll
@@ -157,7 +159,7 @@ __device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[
     if (OUT_I32) {
       a.acc_out[o] = total[v];
     } else {
-      a.y[o] = (float)total[v] * dequant_factor(alpha, s_rows[m], a.c);
+      a.y[o] = (float)total[v] * dequant_factor(alpha, s_row[v], a.c);
     }
   }
 }
@@ -169,10 +171,22 @@ __global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a) {
   v4i* red = reinterpret_cast<v4i*>(smem);  // [nw][CT][64]
   int8_t* stage = reinterpret_cast<int8_t*>(smem + (size_t)nw * CT * 1024) +
                   (size_t)(threadIdx.x >> 6) * 16 * kCodePitch;
-  const float alpha = OUT_I32 ? 0.0f : *a.alpha;
+  // Scalars, alpha and the finishing lanes' row scales are fetched before
+  // the weight stream: a small load issued behind it waits about a
+  // microsecond.
+  asm volatile("" ::"s"(a.M), "s"(a.K), "s"(a.N), "s"(a.c), "s"(a.y), "s"(a.sb_waves), "s"(a.Wp),
+               "s"(a.codes), "s"(nw));
+  float alpha = 0.0f;
+  float s_row[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (!OUT_I32) {
+    alpha = *a.alpha;
+    const int m0 = 4 * ((threadIdx.x & 63) >> 4);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s_row[v] = a.scales[m0 + v < a.M ? m0 + v : a.M - 1];
+  }
   v4i acc[CT];
   wave_product<CT>(a, a.codes, stage, acc);
-  gemv_finish<CT, OUT_I32>(a, acc, red, a.scales, nw, alpha);
+  gemv_finish<CT, OUT_I32>(a, acc, red, s_row, nw, alpha);
 }
 
 __device__ __forceinline__ void load4(const float* x, size_t i, float (&v)[4]) {
@@ -448,7 +462,13 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
     for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const v4i*>(qr + 16 * j) & kmask;
     mma_round<CT>(av, p[r], acc);
   }
-  gemv_finish<CT, false>(a, acc, red, srow, nw, alpha);
+  float s_row[4];
+  {
+    const int m0 = 4 * (lane >> 4);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s_row[v] = srow[m0 + v < a.M ? m0 + v : 0];
+  }
+  gemv_finish<CT, false>(a, acc, red, s_row, nw, alpha);
 }
 
 template <typename Kern>
