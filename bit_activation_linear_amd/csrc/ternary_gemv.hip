@@ -471,6 +471,105 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
   gemv_finish<CT, false>(a, acc, red, s_row, nw, alpha);
 }
 
+// Single-token decode forward, one wave per 16 output columns and all of K
+// (NSB 256-k super-blocks, NSB <= 16). Every x value the wave needs fits in
+// its registers, so it computes the whole-row statistic itself (DPP),
+// quantizes, runs the MFMAs over all of K into one accumulator and stores:
+// no workgroup barrier and no cross-wave reduction on the path, which is
+// then the latency of the x and weight loads plus this wave's arithmetic.
+// Each workgroup is one wave (several independent waves per workgroup
+// measured slower). NSB is exact and every load unconditional: a load count
+// that depends on a branch makes the compiler wait for every load in
+// flight, the weights included, before the first use of x, and padding the
+// count with re-read blocks costs ~0.2 us per super-block.
+template <typename XT, int BITS, int NSB>
+__global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
+  __shared__ __attribute__((aligned(16))) int8_t qw[NSB * 256];  // [sb][256] codes
+  asm volatile("" ::"s"(a.K), "s"(a.N), "s"(a.c), "s"(a.y), "s"(a.x), "s"(a.Wp));
+  const float alpha = *a.alpha;
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nKB = a.K >> 6;
+  // x first (4 consecutive values per super-block), then the weights.
+  const XT* x = reinterpret_cast<const XT*>(a.x);
+  Raw4<XT> xraw[NSB];
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    const int k0 = 256 * sb + 4 * lane;
+    raw_load4(x, (size_t)(k0 < a.K ? k0 : 0), xraw[sb]);
+  }
+  uint4 p[NSB];
+  {
+    const size_t row_bytes = (size_t)(a.K >> 2);
+    const int n = blockIdx.x * 16 + col;
+    const int nc = n < a.N ? n : a.N - 1;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      const int kb = sb * 4 + grp;
+      const int kbc = kb < nKB ? kb : nKB - 1;
+      // an out-of-range block meets all-zero codes below
+      p[sb] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float v[NSB][4];
+  float st = 0.0f;
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    const bool own = 256 * sb + 4 * lane < a.K;
+    widen4(xraw[sb], v[sb]);
+    float sr;
+    if (BITS == 8) {
+      sr = fmaxf(fmaxf(fabsf(v[sb][0]), fabsf(v[sb][1])), fmaxf(fabsf(v[sb][2]), fabsf(v[sb][3])));
+      st = fmaxf(st, own ? sr : 0.0f);
+    } else {
+      sr = (fabsf(v[sb][0]) + fabsf(v[sb][1])) + (fabsf(v[sb][2]) + fabsf(v[sb][3]));
+      st += own ? sr : 0.0f;
+    }
+  }
+  st = (BITS == 8) ? wave_reduce<true>(st) : wave_reduce<false>(st);
+  if (BITS == 4) st = st / (float)a.K;
+  st += kEps;
+  const float mult = a.c / st;
+  const float lo = (BITS == 8) ? -128.0f : -8.0f;
+  const float hi = (BITS == 8) ? 127.0f : 7.0f;
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    const bool own = 256 * sb + 4 * lane < a.K;
+    unsigned word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float q = __builtin_rintf(v[sb][e] * mult);
+      q = fminf(fmaxf(q, lo), hi);
+      word |= ((unsigned)(int)q & 0xFFu) << (8 * e);
+    }
+    *reinterpret_cast<unsigned*>(qw + sb * 256 + 4 * lane) = own ? word : 0u;
+  }
+  // Codes written by this wave are read back by other lanes of it; LDS serves
+  // a wave's accesses in order, so only the compiler needs fencing.
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // MFMA operand: lane (col, grp) feeds token row col (only row 0 is live),
+  // block 4 sb + grp.
+  v4i acc[1] = {v4i{0, 0, 0, 0}};
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    const int kb = sb * 4 + grp;
+    const int kmask = (kb < nKB && col == 0) ? -1 : 0;
+    const int8_t* qr = qw + sb * 256 + grp * 64;
+    v4i av[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const v4i*>(qr + 16 * j) & kmask;
+    const uint4 pb[1] = {p[sb]};
+    mma_round<1>(av, pb, acc);
+  }
+  // 16x16 layout: lane holds rows 4 (lane / 16) + v, column lane % 16; row 0
+  // sits in element 0 of the lanes of group 0.
+  const int n = blockIdx.x * 16 + col;
+  if (grp == 0 && n < a.N) a.y[n] = (float)acc[0][0] * dequant_factor(alpha, st, a.c);
+}
+
 template <typename Kern>
 hipError_t ensure_lds(Kern kern, size_t bytes) {
   if (bytes <= 48 * 1024) return hipSuccess;
@@ -503,8 +602,35 @@ hipError_t launch_fused_ct(const GemvArgs& a, const Prologue& pro, hipStream_t s
   return hipGetLastError();
 }
 
+template <typename XT, int BITS, int NSB>
+hipError_t launch_wave_nsb(const GemvArgs& a, hipStream_t stream) {
+  wave_decode_kernel<XT, BITS, NSB><<<dim3((unsigned)((a.N + 15) / 16)), dim3(64), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// The one-wave kernel for a single token without the prologue (whose
+// per-element work is better spread over the multi-wave kernel's waves).
+template <typename XT, int BITS>
+bool try_launch_wave(const GemvArgs& a, const Prologue* pro, hipStream_t stream, hipError_t* err) {
+  const int nsb = ((a.K >> 6) + 3) >> 2;
+  if (a.M != 1 || pro || nsb > 16) return false;
+  switch (nsb) {
+#define BITNET_WAVE_CASE(n) \
+  case n: *err = launch_wave_nsb<XT, BITS, n>(a, stream); break;
+    BITNET_WAVE_CASE(1) BITNET_WAVE_CASE(2) BITNET_WAVE_CASE(3) BITNET_WAVE_CASE(4)
+    BITNET_WAVE_CASE(5) BITNET_WAVE_CASE(6) BITNET_WAVE_CASE(7) BITNET_WAVE_CASE(8)
+    BITNET_WAVE_CASE(9) BITNET_WAVE_CASE(10) BITNET_WAVE_CASE(11) BITNET_WAVE_CASE(12)
+    BITNET_WAVE_CASE(13) BITNET_WAVE_CASE(14) BITNET_WAVE_CASE(15) BITNET_WAVE_CASE(16)
+#undef BITNET_WAVE_CASE
+    default: return false;
+  }
+  return true;
+}
+
 template <typename XT, int BITS, int MG>
 hipError_t launch_fused_t(const GemvArgs& a, const Prologue* pro, hipStream_t stream) {
+  hipError_t err = hipSuccess;
+  if (try_launch_wave<XT, BITS>(a, pro, stream, &err)) return err;
   if (pro) return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, true>(a, *pro, stream);
   const Prologue none{nullptr, nullptr, 0.0f, 0};
   return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, false>(a, none, stream);

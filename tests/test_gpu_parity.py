@@ -103,6 +103,11 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     (16, 1024, 48, 4, 0, "fp32"),      # fused, full 16 rows
     (16, 4096, 150, 8, 0, "bf16"),     # not fused (M*K too big), 4 column tiles
     (9, 2048, 33, 4, 1, "fp32"),
+    (2, 2048, 100, 4, 0, "bf16"),      # multi-wave fused kernel, two rows
+    (4, 1024, 70, 8, 0, "fp32"),       # multi-wave fused kernel, four rows
+    (1, 4096, 50, 4, 0, "fp32"),       # one-wave kernel (single token), sixteen super-blocks
+    (1, 1344, 77, 8, 0, "bf16"),       # one-wave kernel, 21 blocks: a partial last super-block
+    (3, 1344, 40, 8, 0, "bf16"),       # multi-wave fused kernel, partial last super-block
 ])
 def test_parity_decode_shapes(M, K, N, bits, had, xdt):
     _run_case(M, K, N, bits, had, xdt, seed=M * 7 + K + N, n_out=max(1, K // 100), factor=30.0)

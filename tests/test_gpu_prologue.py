@@ -89,6 +89,8 @@ def _run(M, K, N, bits, had, x_dtype, swiglu, rms, gamma, seed):
     (4, 4096, 90, 4, 0, "bf16", True, True, True),       # fused decode kernel, whole prologue
     (16, 1024, 48, 8, 0, "fp32", True, False, False),    # fused decode kernel, SwiGLU only
     (1, 2048, 200, 8, 0, "bf16", False, True, False),    # fused decode kernel, unit-weight norm
+    (2, 2048, 70, 4, 0, "bf16", True, True, True),       # fused decode kernel, two rows, whole prologue
+    (1, 4096, 64, 8, 0, "fp32", True, True, True),       # fused decode kernel, fp32, longest fused row
 ])
 def test_prologue_parity(M, K, N, bits, had, xdt, swiglu, rms, gamma):
     _run(M, K, N, bits, had, xdt, swiglu, rms, gamma, seed=M + K + N + 7 * bits + had)
