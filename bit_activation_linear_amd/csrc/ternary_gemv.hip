@@ -532,42 +532,76 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
   if (BITS == 4) st = st / (float)a.K;
   st += kEps;
   const float mult = a.c / st;
-  const float lo = (BITS == 8) ? -128.0f : -8.0f;
-  const float hi = (BITS == 8) ? 127.0f : 7.0f;
+  // Codes: adding 1.5 * 2^23 to the rounded product p leaves rint(p) (ties to
+  // even, |p| < 2^22) in the low bits of the sum, so one add replaces round
+  // and convert, med3 clamps, and the code is the sum's low byte. The product
+  // is rounded first (no fused multiply-add), as in the quantizer kernels.
+  constexpr float kMagic = 12582912.0f;
+  const float lo = kMagic + ((BITS == 8) ? -128.0f : -8.0f);
+  const float hi = kMagic + ((BITS == 8) ? 127.0f : 7.0f);
+  int qsum = 0;  // this lane's share of the code row sum
 #pragma unroll
   for (int sb = 0; sb < NSB; ++sb) {
     const bool own = 256 * sb + 4 * lane < a.K;
-    unsigned word = 0;
+    unsigned b[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float q = __builtin_rintf(v[sb][e] * mult);
-      q = fminf(fmaxf(q, lo), hi);
-      word |= ((unsigned)(int)q & 0xFFu) << (8 * e);
+      const float f = __fadd_rn(__fmul_rn(v[sb][e], mult), kMagic);
+      b[e] = __float_as_uint(__builtin_amdgcn_fmed3f(f, lo, hi));
     }
-    *reinterpret_cast<unsigned*>(qw + sb * 256 + 4 * lane) = own ? word : 0u;
+    // low bytes of b[0..3] -> one word (byte e = code e)
+    const unsigned w01 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
+    const unsigned w23 = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+    const unsigned word = own ? (w01 | w23) : 0u;
+    qsum = __builtin_amdgcn_sdot4((int)word, 0x01010101, qsum, false);
+    *reinterpret_cast<unsigned*>(qw + sb * 256 + 4 * lane) = word;
   }
   // Codes written by this wave are read back by other lanes of it; LDS serves
   // a wave's accesses in order, so only the compiler needs fencing.
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
+  // Wave-wide code row sum (exact int32 in float-free DPP steps).
+  {
+    float fs = __int_as_float(qsum);
+#define BITNET_ISUM(ctrl, rmask, bc)                                                            \
+  {                                                                                             \
+    const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(fs), ctrl, rmask, 0xF, bc);     \
+    fs = __int_as_float(__float_as_int(fs) + o);                                                \
+  }
+    BITNET_ISUM(0x111, 0xF, true)
+    BITNET_ISUM(0x112, 0xF, true)
+    BITNET_ISUM(0x114, 0xF, true)
+    BITNET_ISUM(0x118, 0xF, true)
+    BITNET_ISUM(0x142, 0xA, false)
+    BITNET_ISUM(0x143, 0xC, false)
+#undef BITNET_ISUM
+    qsum = __builtin_amdgcn_readlane(__float_as_int(fs), 63);
+  }
+
   // MFMA operand: lane (col, grp) feeds token row col (only row 0 is live),
-  // block 4 sb + grp.
-  v4i acc[1] = {v4i{0, 0, 0, 0}};
+  // block 4 sb + grp, times the stored field u = t + 1 in {0, 1, 2}
+  // (a shift and a mask per four weights); q . t = q . u - sum(q).
+  v4i acc = v4i{0, 0, 0, 0};
 #pragma unroll
   for (int sb = 0; sb < NSB; ++sb) {
     const int kb = sb * 4 + grp;
     const int kmask = (kb < nKB && col == 0) ? -1 : 0;
     const int8_t* qr = qw + sb * 256 + grp * 64;
-    v4i av[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const v4i*>(qr + 16 * j) & kmask;
-    const uint4 pb[1] = {p[sb]};
-    mma_round<1>(av, pb, acc);
+    for (int j = 0; j < 4; ++j) {
+      const v4i av = *reinterpret_cast<const v4i*>(qr + 16 * j) & kmask;
+      v4i u;
+      u.x = (int)((p[sb].x >> (2 * j)) & 0x03030303u);
+      u.y = (int)((p[sb].y >> (2 * j)) & 0x03030303u);
+      u.z = (int)((p[sb].z >> (2 * j)) & 0x03030303u);
+      u.w = (int)((p[sb].w >> (2 * j)) & 0x03030303u);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, u, acc, 0, 0, 0);
+    }
   }
   // 16x16 layout: lane holds rows 4 (lane / 16) + v, column lane % 16; row 0
   // sits in element 0 of the lanes of group 0.
   const int n = blockIdx.x * 16 + col;
-  if (grp == 0 && n < a.N) a.y[n] = (float)acc[0][0] * dequant_factor(alpha, st, a.c);
+  if (grp == 0 && n < a.N) a.y[n] = (float)(acc[0] - qsum) * dequant_factor(alpha, st, a.c);
 }
 
 template <typename Kern>
