@@ -484,7 +484,9 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
 // count with re-read blocks costs ~0.2 us per super-block.
 template <typename XT, int BITS, int NSB>
 __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
-  __shared__ __attribute__((aligned(16))) int8_t qw[NSB * 256];  // [sb][256] codes
+  // [sb][256] codes, then 64 zero bytes that the lanes feeding dead MFMA rows
+  // (and blocks past K) read instead of masking their operands
+  __shared__ __attribute__((aligned(16))) int8_t qw[NSB * 256 + 64];
   asm volatile("" ::"s"(a.K), "s"(a.N), "s"(a.c), "s"(a.y), "s"(a.x), "s"(a.Wp));
   const float alpha = *a.alpha;
   const int lane = threadIdx.x;
@@ -535,7 +537,8 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
   // Codes: adding 1.5 * 2^23 to the rounded product p leaves rint(p) (ties to
   // even, |p| < 2^22) in the low bits of the sum, so one add replaces round
   // and convert, med3 clamps, and the code is the sum's low byte. The product
-  // is rounded first (no fused multiply-add), as in the quantizer kernels.
+  // is rounded first, as in the quantizer kernels: the empty asm keeps the
+  // compiler from fusing the multiply into the add.
   constexpr float kMagic = 12582912.0f;
   const float lo = kMagic + ((BITS == 8) ? -128.0f : -8.0f);
   const float hi = kMagic + ((BITS == 8) ? 127.0f : 7.0f);
@@ -546,8 +549,9 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
     unsigned b[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float f = __fadd_rn(__fmul_rn(v[sb][e], mult), kMagic);
-      b[e] = __float_as_uint(__builtin_amdgcn_fmed3f(f, lo, hi));
+      float pr = v[sb][e] * mult;
+      asm volatile("" : "+v"(pr));
+      b[e] = __float_as_uint(__builtin_amdgcn_fmed3f(pr + kMagic, lo, hi));
     }
     // low bytes of b[0..3] -> one word (byte e = code e)
     const unsigned w01 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
@@ -556,6 +560,7 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
     qsum = __builtin_amdgcn_sdot4((int)word, 0x01010101, qsum, false);
     *reinterpret_cast<unsigned*>(qw + sb * 256 + 4 * lane) = word;
   }
+  if (lane < 16) *reinterpret_cast<unsigned*>(qw + NSB * 256 + 4 * lane) = 0u;
   // Codes written by this wave are read back by other lanes of it; LDS serves
   // a wave's accesses in order, so only the compiler needs fencing.
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -585,11 +590,10 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
 #pragma unroll
   for (int sb = 0; sb < NSB; ++sb) {
     const int kb = sb * 4 + grp;
-    const int kmask = (kb < nKB && col == 0) ? -1 : 0;
-    const int8_t* qr = qw + sb * 256 + grp * 64;
+    const int8_t* qr = (kb < nKB && col == 0) ? qw + sb * 256 + grp * 64 : qw + NSB * 256;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const v4i av = *reinterpret_cast<const v4i*>(qr + 16 * j) & kmask;
+      const v4i av = *reinterpret_cast<const v4i*>(qr + 16 * j);
       v4i u;
       u.x = (int)((p[sb].x >> (2 * j)) & 0x03030303u);
       u.y = (int)((p[sb].y >> (2 * j)) & 0x03030303u);
