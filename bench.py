@@ -342,7 +342,10 @@ def main():
         roof = {"bound": "mfma", "achieved": head["matmul_TOPS"], "peak": INT8_MFMA_PEAK_TOPS,
                 "unit": "TFLOP/s", "frac": head["matmul_TOPS"] / INT8_MFMA_PEAK_TOPS}
     if decode:
-        roof["kernel"] = "fused_decode_kernel" if head["fused_single_kernel"] else "ternary_gemv_kernel"
+        if not head["fused_single_kernel"]:
+            roof["kernel"] = "ternary_gemv_kernel"
+        else:  # a single token runs the one-wave kernel, a few tokens the multi-wave one
+            roof["kernel"] = "wave_decode_kernel" if wl.M == 1 else "fused_decode_kernel"
     else:
         roof["kernel"] = "ternary_gemm_kernel"
     roof["algorithmic"] = ("N*K/4 packed weight bytes per launch" if decode
