@@ -482,12 +482,18 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
 // that depends on a branch makes the compiler wait for every load in
 // flight, the weights included, before the first use of x, and padding the
 // count with re-read blocks costs ~0.2 us per super-block.
-template <typename XT, int BITS, int NSB>
-__global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
+// With RMS, the layer input is RMSNorm'd first (engine page HBitLinear.forward
+// step 1; gamma may be null for unit weight): the sum of squares is one more
+// DPP reduction and 1/rms enters only the scale and the code multiplier, as
+// in the other quantizer kernels.
+template <typename XT, int BITS, int NSB, bool RMS>
+__global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a, const float* gamma,
+                                                         float norm_eps) {
   // [sb][256] codes, then 64 zero bytes that the lanes feeding dead MFMA rows
   // (and blocks past K) read instead of masking their operands
   __shared__ __attribute__((aligned(16))) int8_t qw[NSB * 256 + 64];
   asm volatile("" ::"s"(a.K), "s"(a.N), "s"(a.c), "s"(a.y), "s"(a.x), "s"(a.Wp));
+  if constexpr (RMS) asm volatile("" ::"s"(gamma), "s"(norm_eps));
   const float alpha = *a.alpha;
   const int lane = threadIdx.x;
   const int col = lane & 15, grp = lane >> 4;
@@ -495,10 +501,15 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
   // x first (4 consecutive values per super-block), then the weights.
   const XT* x = reinterpret_cast<const XT*>(a.x);
   Raw4<XT> xraw[NSB];
+  const bool use_g = RMS && gamma;
+  const float* gp = use_g ? gamma : reinterpret_cast<const float*>(a.x);
+  float4 graw[RMS ? NSB : 1];
 #pragma unroll
   for (int sb = 0; sb < NSB; ++sb) {
     const int k0 = 256 * sb + 4 * lane;
-    raw_load4(x, (size_t)(k0 < a.K ? k0 : 0), xraw[sb]);
+    const int kc = k0 < a.K ? k0 : 0;
+    raw_load4(x, (size_t)kc, xraw[sb]);
+    if (RMS) graw[RMS ? sb : 0] = *reinterpret_cast<const float4*>(gp + (use_g ? kc : 0));
   }
   uint4 p[NSB];
   {
@@ -516,11 +527,20 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 
   float v[NSB][4];
-  float st = 0.0f;
+  float st = 0.0f, sq = 0.0f;
 #pragma unroll
   for (int sb = 0; sb < NSB; ++sb) {
     const bool own = 256 * sb + 4 * lane < a.K;
     widen4(xraw[sb], v[sb]);
+    if constexpr (RMS) {
+      const float g[4] = {use_g ? graw[sb].x : 1.0f, use_g ? graw[sb].y : 1.0f,
+                          use_g ? graw[sb].z : 1.0f, use_g ? graw[sb].w : 1.0f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sq += own ? v[sb][e] * v[sb][e] : 0.0f;
+        v[sb][e] *= g[e];
+      }
+    }
     float sr;
     if (BITS == 8) {
       sr = fmaxf(fmaxf(fabsf(v[sb][0]), fabsf(v[sb][1])), fmaxf(fabsf(v[sb][2]), fabsf(v[sb][3])));
@@ -532,8 +552,15 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
   }
   st = (BITS == 8) ? wave_reduce<true>(st) : wave_reduce<false>(st);
   if (BITS == 4) st = st / (float)a.K;
-  st += kEps;
-  const float mult = a.c / st;
+  float mult;
+  if constexpr (RMS) {
+    const float rms = sqrtf(wave_reduce<false>(sq) / (float)a.K + norm_eps);
+    mult = a.c / (st + kEps * rms);
+    st = st / rms + kEps;
+  } else {
+    st += kEps;
+    mult = a.c / st;
+  }
   // Codes: adding 1.5 * 2^23 to the rounded product p leaves rint(p) (ties to
   // even, |p| < 2^22) in the low bits of the sum, so one add replaces round
   // and convert, med3 clamps, and the code is the sum's low byte. The product
@@ -641,20 +668,25 @@ hipError_t launch_fused_ct(const GemvArgs& a, const Prologue& pro, hipStream_t s
 }
 
 template <typename XT, int BITS, int NSB>
-hipError_t launch_wave_nsb(const GemvArgs& a, hipStream_t stream) {
-  wave_decode_kernel<XT, BITS, NSB><<<dim3((unsigned)((a.N + 15) / 16)), dim3(64), 0, stream>>>(a);
+hipError_t launch_wave_nsb(const GemvArgs& a, const Prologue* pro, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.N + 15) / 16));
+  if (pro && pro->rms)
+    wave_decode_kernel<XT, BITS, NSB, true><<<grid, dim3(64), 0, stream>>>(a, pro->gamma, pro->norm_eps);
+  else
+    wave_decode_kernel<XT, BITS, NSB, false><<<grid, dim3(64), 0, stream>>>(a, nullptr, 0.0f);
   return hipGetLastError();
 }
 
-// The one-wave kernel for a single token without the prologue (whose
-// per-element work is better spread over the multi-wave kernel's waves).
+// The one-wave kernel for a single token, with or without RMSNorm; the
+// SwiGLU product (an exponential per element) is better spread over the
+// multi-wave kernel's waves.
 template <typename XT, int BITS>
 bool try_launch_wave(const GemvArgs& a, const Prologue* pro, hipStream_t stream, hipError_t* err) {
   const int nsb = ((a.K >> 6) + 3) >> 2;
-  if (a.M != 1 || pro || nsb > 16) return false;
+  if (a.M != 1 || (pro && pro->up) || nsb > 16) return false;
   switch (nsb) {
 #define BITNET_WAVE_CASE(n) \
-  case n: *err = launch_wave_nsb<XT, BITS, n>(a, stream); break;
+  case n: *err = launch_wave_nsb<XT, BITS, n>(a, pro, stream); break;
     BITNET_WAVE_CASE(1) BITNET_WAVE_CASE(2) BITNET_WAVE_CASE(3) BITNET_WAVE_CASE(4)
     BITNET_WAVE_CASE(5) BITNET_WAVE_CASE(6) BITNET_WAVE_CASE(7) BITNET_WAVE_CASE(8)
     BITNET_WAVE_CASE(9) BITNET_WAVE_CASE(10) BITNET_WAVE_CASE(11) BITNET_WAVE_CASE(12)
