@@ -219,6 +219,13 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
       for (int j = 0; j < R; ++j) frow[base[gi] + (j << B0)] = v[gi * R + j] * norm;
     return;
   }
+  // The transformed row goes back to LDS (the statistic's barrier below
+  // publishes it), so that each thread then quantizes E contiguous elements
+  // and writes them with 16-byte stores instead of E single-byte stores.
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int j = 0; j < R; ++j) lds[pad_idx(base[gi] + (j << B0))] = v[gi * R + j];
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < E; ++i) s = (BITS == 8) ? fmaxf(s, fabsf(v[i])) : s + fabsf(v[i]);
@@ -245,13 +252,17 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
     mult = (QConst<BITS>::c * norm) / sc;
   }
   if (t == 0) *scale_out = sc;
+  const int e0 = t * E;
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi)
+  for (int c = 0; c < E; c += 8) {
+    unsigned w[2] = {0u, 0u};
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const float q = quant_clip(v[gi * R + j], mult, QConst<BITS>::lo, QConst<BITS>::hi);
-      crow[base[gi] + (j << B0)] = (int8_t)(int)q;
+    for (int i = 0; i < 8; ++i) {
+      const float q = quant_clip(lds[pad_idx(e0 + c + i)], mult, QConst<BITS>::lo, QConst<BITS>::hi);
+      w[i >> 2] |= ((unsigned)(int)q & 0xFFu) << (8 * (i & 3));
     }
+    *reinterpret_cast<uint2*>(crow + e0 + c) = make_uint2(w[0], w[1]);
+  }
 }
 
 template <int A, int B>
