@@ -611,28 +611,37 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a, const float
   }
 
   // MFMA operand: lane (col, grp) feeds token row col (only row 0 is live),
-  // block 4 sb + grp, times the stored field u = t + 1 in {0, 1, 2}
-  // (a shift and a mask per four weights); q . t = q . u - sum(q).
-  v4i acc = v4i{0, 0, 0, 0};
+  // block 4 sb + grp, times the stored field u = t + 1 in {0, 1, 2};
+  // q . t = q . u - sum(q). The fields of quarters 0, 1 and 2 are masked in
+  // place, worth u, 4u and 16u, and quarter 3's is shifted down to the
+  // 16u position; three accumulators keep the scales apart and are shifted
+  // back (exactly: each holds a multiple of its scale) at the end. One
+  // operation per four weights for three quarters of the weights.
+  v4i acc1 = v4i{0, 0, 0, 0}, acc4 = v4i{0, 0, 0, 0}, acc16 = v4i{0, 0, 0, 0};
 #pragma unroll
   for (int sb = 0; sb < NSB; ++sb) {
     const int kb = sb * 4 + grp;
     const int8_t* qr = (kb < nKB && col == 0) ? qw + sb * 256 + grp * 64 : qw + NSB * 256;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i av = *reinterpret_cast<const v4i*>(qr + 16 * j);
-      v4i u;
-      u.x = (int)((p[sb].x >> (2 * j)) & 0x03030303u);
-      u.y = (int)((p[sb].y >> (2 * j)) & 0x03030303u);
-      u.z = (int)((p[sb].z >> (2 * j)) & 0x03030303u);
-      u.w = (int)((p[sb].w >> (2 * j)) & 0x03030303u);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, u, acc, 0, 0, 0);
-    }
+    const uint4 pw = p[sb];
+    v4i u;
+    u.x = (int)(pw.x & 0x03030303u); u.y = (int)(pw.y & 0x03030303u);
+    u.z = (int)(pw.z & 0x03030303u); u.w = (int)(pw.w & 0x03030303u);
+    acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i*>(qr), u, acc1, 0, 0, 0);
+    u.x = (int)(pw.x & 0x0C0C0C0Cu); u.y = (int)(pw.y & 0x0C0C0C0Cu);
+    u.z = (int)(pw.z & 0x0C0C0C0Cu); u.w = (int)(pw.w & 0x0C0C0C0Cu);
+    acc4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i*>(qr + 16), u, acc4, 0, 0, 0);
+    u.x = (int)(pw.x & 0x30303030u); u.y = (int)(pw.y & 0x30303030u);
+    u.z = (int)(pw.z & 0x30303030u); u.w = (int)(pw.w & 0x30303030u);
+    acc16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i*>(qr + 32), u, acc16, 0, 0, 0);
+    u.x = (int)((pw.x >> 2) & 0x30303030u); u.y = (int)((pw.y >> 2) & 0x30303030u);
+    u.z = (int)((pw.z >> 2) & 0x30303030u); u.w = (int)((pw.w >> 2) & 0x30303030u);
+    acc16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i*>(qr + 48), u, acc16, 0, 0, 0);
   }
+  const int dot = acc1[0] + (acc4[0] >> 2) + (acc16[0] >> 4) - qsum;
   // 16x16 layout: lane holds rows 4 (lane / 16) + v, column lane % 16; row 0
   // sits in element 0 of the lanes of group 0.
   const int n = blockIdx.x * 16 + col;
-  if (grp == 0 && n < a.N) a.y[n] = (float)(acc[0] - qsum) * dequant_factor(alpha, st, a.c);
+  if (grp == 0 && n < a.N) a.y[n] = (float)dot * dequant_factor(alpha, st, a.c);
 }
 
 template <typename Kern>
