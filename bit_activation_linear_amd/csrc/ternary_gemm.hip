@@ -19,7 +19,7 @@
 //
 // Work decomposition. A workgroup owns a BM x BN output tile and has
 // WMW x WNW x KS waves: each wave owns a (32 RT) x (32 CT) block of it
-// (RT x CT accumulators of 32x32 int32 in AGPRs) and one of KS interleaved
+// (RT x CT accumulators of 32x32 int32) and one of KS interleaved
 // 128-wide k slices of every stage; with KS > 1 the slices' partial sums are
 // added through LDS at the end.
 //
@@ -452,15 +452,16 @@ hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int 
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
                        int32_t* acc, hipStream_t stream) {
   const float c = (bits == 8) ? kScaleInt8 : kScaleInt4;
-  // 128 x 512 tiles (four waves side by side along N, one k slice per stage)
-  // when there are enough of them to give every CU several: codes cost four
-  // times the bytes of packed weights per element, so a tile wide in N
-  // fetches the fewest bytes per MFMA. Otherwise 128 x 128 tiles whose four
-  // waves split each 256-wide stage into two k slices.
-  const int64_t big_tiles = ((M + 127) / 128) * ((N + 511) / 512);
+  // Two waves per SIMD (eight per workgroup, 64 x 128 or 128 x 64 per wave,
+  // accumulators in VGPRs): while one wave waits on LDS or the stage barrier
+  // the other issues MFMAs, which measured 13-18% faster than one wave of
+  // 128 x 128 per SIMD. 256 x 256 tiles when there are enough of them to give
+  // every CU several; otherwise 128 x 128 tiles whose waves split each
+  // 256-wide stage into two k slices.
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles >= 1024)
-    return launch_variant<4, 4, 1, 4, 1>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
-  return launch_variant<4, 2, 1, 2, 2>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
+    return launch_variant<2, 4, 4, 2, 1>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
+  return launch_variant<2, 2, 2, 2, 2>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
 }
 
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
