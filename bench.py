@@ -77,6 +77,25 @@ def _capture(torch, fn, calls):
     return g
 
 
+def _time_replays(torch, fn, steps, reps):
+    """Per-call ms of `reps` separate replays of one graph of `steps` calls
+    (the spread of the timed figure, not of single calls)."""
+    g = _capture(torch, fn, steps)
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end) / steps)
+    del g
+    return out
+
+
 def _time_steps(torch, fn, steps, warmup):
     """ms per call over exactly `steps` calls replayed from one HIP graph.
 
@@ -164,6 +183,9 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
     }
     if wl.M <= 16:
         res["matmul_hbm_frac"] = res["matmul_weight_GBs"] / HBM_PEAK_GBS
+        if p.copies > 1:
+            # the same forward on one weight copy, served from the caches
+            res["forward_us_warm"] = _time_steps(torch, lambda i: p.forward(bl, 0), steps, warmup) * 1e3
     else:
         res["matmul_mfma_frac"] = res["matmul_TOPS"] / INT8_MFMA_PEAK_TOPS
     # The engine page's whole HBitLinear.forward: RMSNorm (unit weight plus a
@@ -333,6 +355,17 @@ def main():
     p, head = _measure_workload(torch, bl, key, dev, args.steps, args.warmup)
     ms = head["forward_us"] / 1e3
     decode = wl.M <= 16
+    # Spread of the timed figure over separate replays, and, as context, a
+    # plain device copy of the same (cold) weight bytes.
+    reps = _time_replays(torch, lambda i: p.forward(bl, i), args.steps, 7)
+    reps_us = sorted(r * 1e3 for r in reps)
+    head["forward_us_replays_p10_p50_p90"] = [reps_us[0], reps_us[3], reps_us[-1]]
+    if decode and p.copies > 1:
+        dst = torch.empty_like(p.Wp[0])
+        cp_ms = _time_steps(torch, lambda i: dst.copy_(p.Wp[i % p.copies]), args.steps, 5)
+        head["copy_same_bytes_us"] = cp_ms * 1e3
+        head["copy_same_bytes_read_GBs"] = p.Wp[0].numel() / (cp_ms * 1e-3) / 1e9
+        del dst
     if decode:
         value, unit = head["forward_weight_GBs"], "GB/s"
         roof = {"bound": "hbm", "achieved": head["matmul_weight_GBs"], "peak": HBM_PEAK_GBS,
