@@ -70,12 +70,19 @@ bitnet_status check_quant_args(const char* fn, int64_t K, int bits, int hadamard
   return BITNET_OK;
 }
 
-// Forward workspace: [codes M*K][scales 4M], each part 256-B aligned. The
-// fused decode kernel needs none of it.
+// Forward workspace: [codes M*K][scales 4M][code row sums 4M], each part
+// 256-B aligned. The fused decode kernel needs none of it. The quantizer
+// writes each token's code sum so that the GEMM's epilogue can subtract it
+// without summing the codes again.
 struct ForwardWorkspace {
   int8_t* codes;
   float* scales;
+  int32_t* rowsum;
 };
+
+size_t forward_parts_bytes(int64_t M, int64_t K) {
+  return round_up((size_t)M * (size_t)K) + 2 * round_up((size_t)M * sizeof(float));
+}
 
 bool forward_is_fused(int64_t M, int64_t K, int64_t N, int hadamard) {
   if (M > bitnet::kDecodeMaxM) return false;
@@ -85,7 +92,7 @@ bool forward_is_fused(int64_t M, int64_t K, int64_t N, int hadamard) {
 size_t forward_ws_bytes(int64_t M, int64_t K, int64_t N, int hadamard) {
   if (M <= 0 || N <= 0) return 0;
   if (forward_is_fused(M, K, N, hadamard)) return 0;
-  return round_up((size_t)M * (size_t)K) + round_up((size_t)M * sizeof(float));
+  return forward_parts_bytes(M, K);
 }
 
 ForwardWorkspace carve_forward(void* ws, int64_t M, int64_t K) {
@@ -93,6 +100,8 @@ ForwardWorkspace carve_forward(void* ws, int64_t M, int64_t K) {
   ForwardWorkspace w;
   w.codes = reinterpret_cast<int8_t*>(base);
   w.scales = reinterpret_cast<float*>(base + round_up((size_t)M * (size_t)K));
+  w.rowsum = reinterpret_cast<int32_t*>(base + round_up((size_t)M * (size_t)K) +
+                                        round_up((size_t)M * sizeof(float)));
   return w;
 }
 
@@ -225,10 +234,10 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
   }
   const ForwardWorkspace w = carve_forward(ws, M, K);
   hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
-                                         w.scales, stream);
+                                         w.scales, stream, nullptr, w.rowsum);
   if (e != hipSuccess) return hip_status(e, fn);
   e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
-                                    nullptr, stream);
+                                    nullptr, stream, w.rowsum);
   return hip_status(e, fn);
 }
 
@@ -237,7 +246,7 @@ size_t bitnet_forward_prologue_workspace_bytes(int64_t M, int64_t K, int64_t N, 
   (void)bits;
   (void)hadamard;
   if (M <= 0 || K <= 0 || N <= 0 || K % 64 != 0) return 0;
-  return round_up((size_t)M * (size_t)K) + round_up((size_t)M * sizeof(float));
+  return forward_parts_bytes(M, K);
 }
 
 }  // extern "C"
@@ -444,10 +453,10 @@ bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, 
   }
   const ForwardWorkspace w = carve_forward(ws, M, K);
   hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
-                                         w.scales, stream, &pro);
+                                         w.scales, stream, &pro, w.rowsum);
   if (e != hipSuccess) return hip_status(e, fn);
   e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
-                                    nullptr, stream);
+                                    nullptr, stream, w.rowsum);
   return hip_status(e, fn);
 }
 

@@ -196,10 +196,27 @@ struct QConst {
 // the groups g = t + T*gi (gi < E >> NB); a group is the 2^NB elements
 // base(g) + (j << B0). LAST: quantize from registers and store the codes,
 // or, with BITS = 0 (transform only), store the normalized fp32 values to frow.
+// Workgroup sum of one int per thread (fixed order), T threads; every
+// thread gets the total. ired holds one int per wave.
+template <int T>
+__device__ __forceinline__ int block_isum(int v, int* ired) {
+  constexpr int W = T < 64 ? T : 64;
+#pragma unroll
+  for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, W);
+  constexpr int NW = (T + 63) / 64;
+  if ((threadIdx.x & 63) == 0) ired[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) r += ired[w];
+  return r;
+}
+
 template <int L, int LT, int B0, int NB, bool LAST, int BITS, bool PRO>
 __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_t* crow,
                                          float* scale_out, float sq, const Prologue& pro,
-                                         float* frow = nullptr) {
+                                         float* frow = nullptr, int* ired = nullptr,
+                                         int32_t* rs_out = nullptr) {
   constexpr int T = 1 << LT;
   constexpr int E = 1 << (L - LT);
   constexpr int R = 1 << NB;
@@ -273,12 +290,19 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
   }
   if (t == 0) *scale_out = sc;
   const int e0 = t * E;
+  int qs = 0;  // this thread's share of the code sum
 #pragma unroll
   for (int c = 0; c < E; c += 8) {
     float u[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[i] = lds[pad_idx(e0 + c + i)];
-    *reinterpret_cast<uint2*>(crow + e0 + c) = quant_pack8<BITS>(u, mult);
+    const uint2 w = quant_pack8<BITS>(u, mult);
+    *reinterpret_cast<uint2*>(crow + e0 + c) = w;
+    qs = __builtin_amdgcn_sdot4((int)w.y, 0x01010101, __builtin_amdgcn_sdot4((int)w.x, 0x01010101, qs, false), false);
+  }
+  if (rs_out) {
+    const int total = block_isum<T>(qs, ired);
+    if (t == 0) *rs_out = total;
   }
 }
 
@@ -292,7 +316,8 @@ struct Min {
 template <typename XT, int BITS, int L, int LT, bool PRO>
 __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t* __restrict__ codes,
                                                              float* __restrict__ scales,
-                                                             Prologue pro, float* fout) {
+                                                             Prologue pro, float* fout,
+                                                             int32_t* __restrict__ rowsum) {
   constexpr int K = 1 << L;
   constexpr int T = 1 << LT;
   constexpr int E = K / T;
@@ -300,11 +325,13 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t
   static_assert(E >= 8, "at least one 8-element vector per thread");
   extern __shared__ float lds[];
   __shared__ float red[2 * ((T + 63) / 64) + 2];
+  __shared__ int ired[(T + 63) / 64];
   const int t = threadIdx.x;
   const int row = blockIdx.x;
   const XT* xr = x + (size_t)row * K;
   int8_t* crow = BITS ? codes + (size_t)row * K : nullptr;
   float* frow = BITS ? nullptr : fout + (size_t)row * K;
+  int32_t* rso = (BITS && rowsum) ? rowsum + row : nullptr;
 
   // Phase A: vectors of 8 from E/8 places, butterflies of the register bits.
   float v[E];
@@ -334,18 +361,18 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t
   static_assert(R3 <= NB3, "at most four middle chunks");
   float* sc = BITS ? scales + row : nullptr;
   if constexpr (R1 <= 0) {
-    mid_pass<L, LT, 3, NB0, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
+    mid_pass<L, LT, 3, NB0, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
   } else {
-    mid_pass<L, LT, 3, NB0, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
+    mid_pass<L, LT, 3, NB0, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
     if constexpr (R2 <= 0) {
-      mid_pass<L, LT, 3 + NB0, NB1, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
+      mid_pass<L, LT, 3 + NB0, NB1, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
     } else {
-      mid_pass<L, LT, 3 + NB0, NB1, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
+      mid_pass<L, LT, 3 + NB0, NB1, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
       if constexpr (R3 <= 0) {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
       } else {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
-        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
+        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
       }
     }
   }
@@ -355,9 +382,11 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t
 template <typename XT, int BITS, int CH, bool PRO>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ x, int K,
                                                          int8_t* __restrict__ codes,
-                                                         float* __restrict__ scales, Prologue pro) {
+                                                         float* __restrict__ scales, Prologue pro,
+                                                         int32_t* __restrict__ rowsum) {
   constexpr int T = 256;
   __shared__ float red[8];
+  __shared__ int ired[4];
   const int t = threadIdx.x;
   const int row = blockIdx.x;
   const XT* xr = x + (size_t)row * K;
@@ -399,10 +428,20 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ 
   }
   if (t == 0) scales[row] = sc;
   int8_t* crow = codes + (size_t)row * K;
+  int qs = 0;  // this thread's share of the code sum
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int idx = 8 * t + 8 * T * c;
-    if (idx < K) *reinterpret_cast<uint2*>(crow + idx) = quant_pack8<BITS>(v[c], mult);
+    if (idx < K) {
+      const uint2 w = quant_pack8<BITS>(v[c], mult);
+      *reinterpret_cast<uint2*>(crow + idx) = w;
+      qs = __builtin_amdgcn_sdot4((int)w.y, 0x01010101,
+                                  __builtin_amdgcn_sdot4((int)w.x, 0x01010101, qs, false), false);
+    }
+  }
+  if (rowsum) {
+    const int total = block_isum<T>(qs, ired);
+    if (t == 0) rowsum[row] = total;
   }
 }
 
@@ -415,14 +454,14 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
 
 template <typename XT, int BITS, int L, int LT, bool PRO>
 hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, const Prologue& pro,
-                       hipStream_t stream, float* fout = nullptr) {
+                       hipStream_t stream, float* fout = nullptr, int32_t* rowsum = nullptr) {
   constexpr int K = 1 << L;
   const size_t lds = (size_t)(K + K / 32) * sizeof(float);
   auto kern = fwht_quant_kernel<XT, BITS, L, LT, PRO>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)M), dim3(1 << LT), lds, stream>>>(reinterpret_cast<const XT*>(x), codes,
-                                                          scales, pro, fout);
+                                                          scales, pro, fout, rowsum);
   return hipGetLastError();
 }
 
@@ -430,12 +469,13 @@ hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, c
 // handful of long rows (decode), never fewer than 8 elements per thread.
 template <typename XT, int BITS, int L, bool PRO>
 hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales,
-                         const Prologue& pro, hipStream_t stream, float* fout = nullptr) {
+                         const Prologue& pro, hipStream_t stream, float* fout = nullptr,
+                         int32_t* rowsum = nullptr) {
   constexpr int LT_BATCH = (L - 3 < 8) ? L - 3 : 8;
   constexpr int LT_FEW = (L - 3 < 10) ? L - 3 : 10;
   if (M <= 64 && LT_FEW != LT_BATCH)
-    return launch_fwht<XT, BITS, L, LT_FEW, PRO>(x, M, codes, scales, pro, stream, fout);
-  return launch_fwht<XT, BITS, L, LT_BATCH, PRO>(x, M, codes, scales, pro, stream, fout);
+    return launch_fwht<XT, BITS, L, LT_FEW, PRO>(x, M, codes, scales, pro, stream, fout, rowsum);
+  return launch_fwht<XT, BITS, L, LT_BATCH, PRO>(x, M, codes, scales, pro, stream, fout, rowsum);
 }
 
 // Transform only (fp32 rows in and out, in place allowed).
@@ -447,50 +487,50 @@ hipError_t launch_fwht_f32_l(const float* x, int64_t M, float* out, hipStream_t 
 
 template <typename XT, int BITS, bool PRO>
 hipError_t launch_had(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                      const Prologue& pro, hipStream_t stream) {
+                      const Prologue& pro, hipStream_t stream, int32_t* rowsum) {
   switch (K) {
-    case 1 << 6: return launch_fwht_l<XT, BITS, 6, PRO>(x, M, codes, scales, pro, stream);
-    case 1 << 7: return launch_fwht_l<XT, BITS, 7, PRO>(x, M, codes, scales, pro, stream);
-    case 1 << 8: return launch_fwht_l<XT, BITS, 8, PRO>(x, M, codes, scales, pro, stream);
-    case 1 << 9: return launch_fwht_l<XT, BITS, 9, PRO>(x, M, codes, scales, pro, stream);
-    case 1 << 10: return launch_fwht_l<XT, BITS, 10, PRO>(x, M, codes, scales, pro, stream);
-    case 1 << 11: return launch_fwht_l<XT, BITS, 11, PRO>(x, M, codes, scales, pro, stream);
-    case 1 << 12: return launch_fwht_l<XT, BITS, 12, PRO>(x, M, codes, scales, pro, stream);
-    case 1 << 13: return launch_fwht_l<XT, BITS, 13, PRO>(x, M, codes, scales, pro, stream);
-    case 1 << 14: return launch_fwht_l<XT, BITS, 14, PRO>(x, M, codes, scales, pro, stream);
-    case 1 << 15: return launch_fwht_l<XT, BITS, 15, PRO>(x, M, codes, scales, pro, stream);
+    case 1 << 6: return launch_fwht_l<XT, BITS, 6, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 7: return launch_fwht_l<XT, BITS, 7, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 8: return launch_fwht_l<XT, BITS, 8, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 9: return launch_fwht_l<XT, BITS, 9, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 10: return launch_fwht_l<XT, BITS, 10, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 11: return launch_fwht_l<XT, BITS, 11, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 12: return launch_fwht_l<XT, BITS, 12, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 13: return launch_fwht_l<XT, BITS, 13, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 14: return launch_fwht_l<XT, BITS, 14, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 15: return launch_fwht_l<XT, BITS, 15, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename XT, int BITS, int CH, bool PRO>
 hipError_t launch_rows_ch(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                          const Prologue& pro, hipStream_t stream) {
+                          const Prologue& pro, hipStream_t stream, int32_t* rowsum) {
   quant_rows_kernel<XT, BITS, CH, PRO><<<dim3((unsigned)M), dim3(256), 0, stream>>>(
-      reinterpret_cast<const XT*>(x), K, codes, scales, pro);
+      reinterpret_cast<const XT*>(x), K, codes, scales, pro, rowsum);
   return hipGetLastError();
 }
 
 template <typename XT, int BITS, bool PRO>
 hipError_t launch_rows(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                       const Prologue& pro, hipStream_t stream) {
+                       const Prologue& pro, hipStream_t stream, int32_t* rowsum) {
   const int ch = (K + 2047) / 2048;
-  if (ch <= 1) return launch_rows_ch<XT, BITS, 1, PRO>(x, M, K, codes, scales, pro, stream);
-  if (ch <= 2) return launch_rows_ch<XT, BITS, 2, PRO>(x, M, K, codes, scales, pro, stream);
-  if (ch <= 4) return launch_rows_ch<XT, BITS, 4, PRO>(x, M, K, codes, scales, pro, stream);
-  if (ch <= 8) return launch_rows_ch<XT, BITS, 8, PRO>(x, M, K, codes, scales, pro, stream);
-  return launch_rows_ch<XT, BITS, 16, PRO>(x, M, K, codes, scales, pro, stream);
+  if (ch <= 1) return launch_rows_ch<XT, BITS, 1, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
+  if (ch <= 2) return launch_rows_ch<XT, BITS, 2, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
+  if (ch <= 4) return launch_rows_ch<XT, BITS, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
+  if (ch <= 8) return launch_rows_ch<XT, BITS, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
+  return launch_rows_ch<XT, BITS, 16, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
 }
 
 template <typename XT, bool PRO>
 hipError_t launch_dtype(const void* x, int64_t M, int K, int bits, int hadamard, int8_t* codes,
-                        float* scales, const Prologue& pro, hipStream_t stream) {
+                        float* scales, const Prologue& pro, hipStream_t stream, int32_t* rowsum) {
   if (hadamard) {
-    return bits == 8 ? launch_had<XT, 8, PRO>(x, M, K, codes, scales, pro, stream)
-                     : launch_had<XT, 4, PRO>(x, M, K, codes, scales, pro, stream);
+    return bits == 8 ? launch_had<XT, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum)
+                     : launch_had<XT, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
   }
-  return bits == 8 ? launch_rows<XT, 8, PRO>(x, M, K, codes, scales, pro, stream)
-                   : launch_rows<XT, 4, PRO>(x, M, K, codes, scales, pro, stream);
+  return bits == 8 ? launch_rows<XT, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum)
+                   : launch_rows<XT, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
 }
 
 }  // namespace
@@ -513,16 +553,17 @@ hipError_t launch_fwht_f32(const float* x, int64_t M, int K, float* out, hipStre
 }
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
-                           int8_t* codes, float* scales, hipStream_t stream, const Prologue* pro) {
+                           int8_t* codes, float* scales, hipStream_t stream, const Prologue* pro,
+                           int32_t* rowsum) {
   const Prologue none{nullptr, nullptr, 0.0f, 0};
   if (pro) {
     if (x_dtype == 1)
-      return launch_dtype<uint16_t, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream);
-    return launch_dtype<float, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream);
+      return launch_dtype<uint16_t, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum);
+    return launch_dtype<float, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum);
   }
   if (x_dtype == 1)
-    return launch_dtype<uint16_t, false>(x, M, K, bits, hadamard, codes, scales, none, stream);
-  return launch_dtype<float, false>(x, M, K, bits, hadamard, codes, scales, none, stream);
+    return launch_dtype<uint16_t, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum);
+  return launch_dtype<float, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum);
 }
 
 }  // namespace bitnet

@@ -77,9 +77,11 @@ struct Prologue {
 
 // Fused (optional) prologue + Walsh-Hadamard transform + per-token
 // quantization. x_dtype: 0 = fp32, 1 = bf16 bit patterns. pro may be null.
+// rowsum, when not null, receives each token's code sum (int32 [M]), which
+// the prefill product then needs not compute.
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
                            int8_t* codes, float* scales, hipStream_t stream,
-                           const Prologue* pro = nullptr);
+                           const Prologue* pro = nullptr, int32_t* rowsum = nullptr);
 
 // Low-bit KV cache: rows of D elements, row r being token r % S of its head;
 // token 0 int8 absmax, the others bits = 3, 4 or 8.
@@ -87,10 +89,12 @@ hipError_t launch_kv_quantize(const void* kv, int x_dtype, int64_t R, int D, int
                               int8_t* codes, float* scales, hipStream_t stream);
 
 // Ternary product from codes. Exactly one of y (dequantized; needs scales,
-// alpha, bits) or acc (raw int32) is non-null.
+// alpha, bits) or acc (raw int32) is non-null. rowsum (optional, with y):
+// the codes' per-token sums from launch_quantize.
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
                                  const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
-                                 float* y, int32_t* acc, hipStream_t stream);
+                                 float* y, int32_t* acc, hipStream_t stream,
+                                 const int32_t* rowsum = nullptr);
 
 // The two product shapes behind launch_ternary_matmul.
 hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int K,
@@ -98,7 +102,7 @@ hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int 
                        int32_t* acc, hipStream_t stream);
 hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, hipStream_t stream);
+                       int32_t* acc, hipStream_t stream, const int32_t* rowsum = nullptr);
 
 // Decode forward with the quantization fused in (plan.fused must hold).
 hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,

@@ -14,8 +14,10 @@
 // the small non-negative operand toggles fewer MFMA input bits than
 // {-1, 0, +1} = {0xFF, 0x00, 0x01}, which matters because the matrix cores
 // of this chip lower their clock as operand switching activity rises. The
-// row sums come from the code fragments the MFMAs read anyway (v_dot4 with
-// a vector of ones).
+// forward passes the row sums the quantizer computed with the codes (RSG);
+// given bare codes, the kernel sums the code fragments the MFMAs read
+// anyway (v_dot4 with a vector of ones), which measured 10-19% of the
+// kernel's time.
 //
 // Work decomposition. A workgroup owns a BM x BN output tile and has
 // WMW x WNW x KS waves: each wave owns a (32 RT) x (32 CT) block of it
@@ -105,11 +107,12 @@ __device__ __forceinline__ int add_bytes(const v4i a, int s) {
   return __builtin_amdgcn_sdot4(a.w, 0x01010101, s, false);
 }
 
-template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32>
+template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG>
 __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ scales, int M, int K,
     const uint8_t* __restrict__ Wp, int N, const float* __restrict__ alpha_p, float c,
-    float* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_m, int tiles_n) {
+    float* __restrict__ y, int32_t* __restrict__ acc_out, const int32_t* __restrict__ rowsum_g,
+    int tiles_m, int tiles_n) {
   using S = Shape<RT, CT, WMW, WNW, KS>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
 #define BITNET_MMA(A_, B_)                                                                      \
   _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                              \
       _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                       \
-    rsum[rt] = add_bytes(A_[hh][rt], rsum[rt]);                                                 \
+    if (!RSG) rsum[rt] = add_bytes(A_[hh][rt], rsum[rt]);                                       \
     _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) acc[rt][ct] =                             \
         __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct], acc[rt][ct], 0, 0, 0);    \
   }
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
         NB_[e / CT][e % CT] = unpack_u(pw[e % CT], 2 * g + 4 * (e / CT));                       \
     }                                                                                           \
     _Pragma("unroll") for (int e = 0; e < kSumPerBlock; ++e) {                                  \
-      if (1 + e * (kChunks - 1) / kSumPerBlock == ch)                                           \
+      if (!RSG && 1 + e * (kChunks - 1) / kSumPerBlock == ch)                                   \
         rsum[e % RT] = add_bytes(A_[e / RT][e % RT], rsum[e % RT]);                             \
     }                                                                                           \
     if (LD_) {                                                                                  \
@@ -337,12 +340,14 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
   // slice's sums per tile row; every wave of a (wm, kw) pair holds the same
   // values, the one with wn = 0 writes them.
   int* rowsum = reinterpret_cast<int*>(smem + S::ROWSUM);
+  if constexpr (!RSG) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int total = rsum[rt] + __shfl_xor(rsum[rt], 32);
-    if (wn == 0 && g == 0) rowsum[kw * S::BM + wm * 32 * RT + rt * 32 + l32] = total;
+    for (int rt = 0; rt < RT; ++rt) {
+      const int total = rsum[rt] + __shfl_xor(rsum[rt], 32);
+      if (wn == 0 && g == 0) rowsum[kw * S::BM + wm * 32 * RT + rt * 32 + l32] = total;
+    }
+    lds_barrier();
   }
-  lds_barrier();
 
   if constexpr (KS > 1) {
     // Add the k slices' partial products through LDS, halving the number of
@@ -397,8 +402,12 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
       const int m = m0 + r;
       if (m >= M) continue;
       int rs = 0;
+      if constexpr (RSG) {
+        rs = rowsum_g[m];
+      } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) rs += rowsum[s * S::BM + r];
+        for (int s = 0; s < KS; ++s) rs += rowsum[s * S::BM + r];
+      }
       const float f = OUT_I32 ? 0.0f : dequant_factor(alpha, scales[m], c);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -416,41 +425,45 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
   }
 }
 
-template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32>
+template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG>
 hipError_t launch_tile(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, float c, float* y,
-                       int32_t* acc, hipStream_t stream) {
+                       int32_t* acc, const int32_t* rowsum, hipStream_t stream) {
   using S = Shape<RT, CT, WMW, WNW, KS>;
   const int tiles_m = (int)((M + S::BM - 1) / S::BM);
   const int tiles_n = (int)((N + S::BN - 1) / S::BN);
   const int tiles = tiles_m * tiles_n;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  auto kern = ternary_gemm_kernel<RT, CT, WMW, WNW, KS, OUT_I32>;
+  auto kern = ternary_gemm_kernel<RT, CT, WMW, WNW, KS, OUT_I32, RSG>;
   if (S::LDS > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
     if (e != hipSuccess) return e;
   }
   kern<<<dim3((unsigned)(per_xcd * kXcds)), dim3(S::NT), S::LDS, stream>>>(
-      codes, scales, (int)M, K, Wpacked, (int)N, alpha, c, y, acc, tiles_m, tiles_n);
+      codes, scales, (int)M, K, Wpacked, (int)N, alpha, c, y, acc, rowsum, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 template <int RT, int CT, int WMW, int WNW, int KS>
 hipError_t launch_variant(const int8_t* codes, const float* scales, int64_t M, int K,
                           const uint8_t* Wpacked, int64_t N, const float* alpha, float c, float* y,
-                          int32_t* acc, hipStream_t stream) {
-  return acc ? launch_tile<RT, CT, WMW, WNW, KS, true>(codes, scales, M, K, Wpacked, N, alpha, c,
-                                                       y, acc, stream)
-             : launch_tile<RT, CT, WMW, WNW, KS, false>(codes, scales, M, K, Wpacked, N, alpha, c,
-                                                        y, acc, stream);
+                          int32_t* acc, const int32_t* rowsum, hipStream_t stream) {
+  if (acc)
+    return launch_tile<RT, CT, WMW, WNW, KS, true, false>(codes, scales, M, K, Wpacked, N, alpha,
+                                                          c, y, acc, nullptr, stream);
+  if (rowsum)
+    return launch_tile<RT, CT, WMW, WNW, KS, false, true>(codes, scales, M, K, Wpacked, N, alpha,
+                                                          c, y, nullptr, rowsum, stream);
+  return launch_tile<RT, CT, WMW, WNW, KS, false, false>(codes, scales, M, K, Wpacked, N, alpha, c,
+                                                         y, nullptr, nullptr, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, hipStream_t stream) {
+                       int32_t* acc, hipStream_t stream, const int32_t* rowsum) {
   const float c = (bits == 8) ? kScaleInt8 : kScaleInt4;
   // Two waves per SIMD (eight per workgroup, 64 x 128 or 128 x 64 per wave,
   // accumulators in VGPRs): while one wave waits on LDS or the stage barrier
@@ -460,16 +473,19 @@ hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int 
   // 256-wide stage into two k slices.
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles >= 1024)
-    return launch_variant<2, 4, 4, 2, 1>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
-  return launch_variant<2, 2, 2, 2, 2>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, stream);
+    return launch_variant<2, 4, 4, 2, 1>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, rowsum,
+                                         stream);
+  return launch_variant<2, 2, 2, 2, 2>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, rowsum,
+                                       stream);
 }
 
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
                                  const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
-                                 float* y, int32_t* acc, hipStream_t stream) {
+                                 float* y, int32_t* acc, hipStream_t stream,
+                                 const int32_t* rowsum) {
   if (M <= kDecodeMaxM)
     return launch_gemv(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream);
-  return launch_gemm(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream);
+  return launch_gemm(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream, rowsum);
 }
 
 }  // namespace bitnet

@@ -33,8 +33,8 @@ def test_version_and_empty_error(lib):
 
 def test_workspace_sizes(lib):
     # codes M*K bytes + scales 4*M bytes, each rounded up to 256 B
-    assert lib.bitnet_forward_workspace_bytes(4, 256, 256, 4, 1) == 1024 + 256
-    assert lib.bitnet_forward_workspace_bytes(2048, 8192, 2048, 4, 1) == 2048 * 8192 + 8192
+    assert lib.bitnet_forward_workspace_bytes(4, 256, 256, 4, 1) == 1024 + 2 * 256
+    assert lib.bitnet_forward_workspace_bytes(2048, 8192, 2048, 4, 1) == 2048 * 8192 + 2 * 8192
     assert lib.bitnet_forward_workspace_bytes(0, 64, 8, 8, 0) == 0
     assert lib.bitnet_forward_workspace_bytes(4, 100, 8, 8, 0) == 0  # invalid K
     assert lib.bitnet_ternarize_workspace_bytes(14336, 4096) >= 8 * 1024
@@ -42,10 +42,10 @@ def test_workspace_sizes(lib):
     assert lib.bitnet_forward_workspace_bytes(1, 2560, 6912, 8, 0) == 0
     assert lib.bitnet_forward_workspace_bytes(16, 1024, 64, 4, 0) == 0
     # with the transform the same shape needs codes + scales
-    assert lib.bitnet_forward_workspace_bytes(1, 2048, 6912, 8, 1) == 2048 + 256
+    assert lib.bitnet_forward_workspace_bytes(1, 2048, 6912, 8, 1) == 2048 + 2 * 256
     # decode with long rows or the transform: codes + scales
-    assert lib.bitnet_forward_workspace_bytes(16, 16384, 4096, 4, 1) == 16 * 16384 + 256
-    assert lib.bitnet_forward_workspace_bytes(1, 8192, 4096, 8, 0) == 8192 + 256
+    assert lib.bitnet_forward_workspace_bytes(16, 16384, 4096, 4, 1) == 16 * 16384 + 2 * 256
+    assert lib.bitnet_forward_workspace_bytes(1, 8192, 4096, 8, 0) == 8192 + 2 * 256
 
 
 def _fwd(lib, x=FAKE, xt=_lib.BF16, M=4, K=256, Wp=FAKE, N=256, alpha=FAKE, bits=4, had=1,
@@ -161,8 +161,8 @@ def _fwd_pro(lib, x=FAKE, up=FAKE, xt=_lib.BF16, M=4, K=256, rms=1, g=FAKE, eps=
 
 def test_prologue_workspace_sizes(lib):
     # always the two-launch path: codes + scales, even where the plain forward fuses
-    assert lib.bitnet_forward_prologue_workspace_bytes(1, 2560, 6912, 8, 0) == 2560 + 256
-    assert lib.bitnet_forward_prologue_workspace_bytes(2048, 8192, 2048, 4, 1) == 2048 * 8192 + 8192
+    assert lib.bitnet_forward_prologue_workspace_bytes(1, 2560, 6912, 8, 0) == 2560 + 2 * 256
+    assert lib.bitnet_forward_prologue_workspace_bytes(2048, 8192, 2048, 4, 1) == 2048 * 8192 + 2 * 8192
     assert lib.bitnet_forward_prologue_workspace_bytes(0, 64, 8, 8, 0) == 0
     assert lib.bitnet_forward_prologue_workspace_bytes(4, 100, 8, 8, 0) == 0
 
