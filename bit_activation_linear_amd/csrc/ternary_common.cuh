@@ -102,6 +102,20 @@ __device__ __forceinline__ void load_lds16(const u4 rsrc, int voff, unsigned lds
       : "memory");
 }
 
+// 4 bytes per lane from buffer offset voff into LDS at lds + 4 * lane (same
+// conventions as load_lds16).
+__device__ __forceinline__ void load_lds4(const u4 rsrc, int voff, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds)
+      : "memory");
+}
+
 // XOR applied to the 16-byte chunk index of code row r in LDS.
 __device__ __forceinline__ int chunk_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 

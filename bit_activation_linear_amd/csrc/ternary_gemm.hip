@@ -425,6 +425,322 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streamed tiles: the large-product variant given the quantizer's row sums.
+//
+// With one workgroup per CU and several 256 x 256 tiles per CU, every CU
+// finishes its tile at about the same time, and the fp32 outputs of all of
+// them (64 MB at M=8192 N=14336) then go to HBM in one burst while the matrix
+// cores idle: measured, the stores cost about a fifth of the kernel. Here one
+// workgroup per CU walks its tiles in sequence with one continuous stage
+// pipeline: the first stages of tile i + 1 are fetched while tile i is still
+// multiplied, and tile i's outputs are stored (without waiting for them)
+// while those fetches are in flight and the next tile's MFMAs start.
+//
+// Output stores. The vector-memory counter covers loads and stores alike and
+// drains in issue order, so the stage waits of the next tile's first two
+// stages allow for the tile's stores; that needs few, wide stores. The
+// accumulators are therefore turned around through a small per-wave LDS
+// buffer (16 rows of a 32 x 32 block at a time) so that each lane stores 16
+// contiguous bytes of one row: RT * CT * 4 buffer_store_dwordx4 per wave and
+// tile. Rows past M fall outside the store resource and columns past N get an
+// out-of-range offset, so every store instruction issues (the count stays
+// exact) and nothing lands outside y.
+//
+// Scales and code row sums of a tile travel with its first stage: one more
+// direct-to-LDS dword load per wave (waves 0..3 scales, 4..7 row sums) into a
+// double-buffered area; every other stage's extra load reads nothing and
+// writes zeros to a sink, so every stage has the same load count.
+template <int RT, int CT, int WMW, int WNW>
+struct StreamShape {
+  using S = Shape<RT, CT, WMW, WNW, 1>;
+  static constexpr int TPITCH = 40;                   // floats per transpose row (bank offset 32 between row r and r + 4)
+  static constexpr int TBUF = 16 * TPITCH * 4;        // one wave's transpose buffer
+  static constexpr int TRANS = S::RING;
+  static constexpr int META = TRANS + S::NW * TBUF;   // [2][scales BM | row sums BM]
+  static constexpr int META_BYTES = 2 * S::BM * 4;
+  static constexpr int SINK = META + 2 * META_BYTES;  // 256 B per wave
+  static constexpr int LDS = SINK + S::NW * 256;
+  static constexpr int NLG = S::NL_W + 1;             // loads per wave and stage
+  static constexpr int STORES = RT * CT * 4;          // dwordx4 stores per wave and tile
+  static_assert(S::NW * 64 == 2 * S::BM, "one scale or row sum per lane");
+  static_assert(LDS <= kLdsMax, "LDS");
+  static_assert((S::SL - 1) * NLG + STORES <= 63, "vmcnt range");
+};
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+template <int RT, int CT, int WMW, int WNW>
+__global__ __launch_bounds__(64 * WMW * WNW) void ternary_gemm_stream_kernel(
+    const int8_t* __restrict__ codes, const float* __restrict__ scales,
+    const int32_t* __restrict__ rowsum_g, int M, int K, const uint8_t* __restrict__ Wp, int N,
+    const float* __restrict__ alpha_p, float c, float* __restrict__ y, int tiles_m, int tiles_n) {
+  using S = Shape<RT, CT, WMW, WNW, 1>;
+  using T = StreamShape<RT, CT, WMW, WNW>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int wrow = K >> 2;
+  const int nst = K / (2 * 64);  // 128-k stages per tile, all whole
+
+  // This workgroup's tiles. XCD x = blockIdx.x % 8 owns the contiguous range
+  // [x per_xcd, (x + 1) per_xcd) of the band-ordered tile walk, which its
+  // workgroups take in turn, so the tiles resident on one XCD at a time are
+  // neighbours in the walk and share codes and weights in its L2.
+  const int tiles = tiles_m * tiles_n;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int wg_step = gridDim.x / kXcds;
+  const int first = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int t_end = min(tiles, (blockIdx.x % kXcds + 1) * per_xcd);
+  const int ntiles = first < t_end ? (t_end - first + wg_step - 1) / wg_step : 0;
+  if (ntiles == 0) return;
+  const int total = ntiles * nst;
+
+  // alpha is used here so that its load completes before the stage loads go
+  // out (a later first use would wait for them too).
+  const float alpha = *alpha_p;
+  asm volatile("" ::"v"(alpha));
+
+  const unsigned lds0 = lds_address(smem);
+  const int a_lane0 = (lane >> 3) * K + 16 * ((lane & 7) ^ (lane >> 3));
+  const int a_lane1 = (lane >> 3) * K + 16 * ((lane & 7) ^ (lane >> 3) ^ 1);
+  const int b_lane = l32 * wrow + g * 16;
+  const int meta_lane = 4 * (lane + 64 * (wave & 3));  // row 64 (wave % 4) + lane of the tile
+
+  // Load cursor: stage ld_ks of tile ld_i, and that tile's resources.
+  int ld_i = 0, ld_ks = 0;
+  u4 a_rsrc, b_rsrc, m_rsrc;
+  auto set_load_tile = [&]() {
+    if (ld_i < ntiles) {
+      const int tile = first + ld_i * wg_step;
+      const int band = tile / (kBand * tiles_n);
+      const int band_m = min(tiles_m - band * kBand, kBand);
+      const int in_band = tile - band * kBand * tiles_n;
+      const int m0 = (band * kBand + in_band % band_m) * S::BM;
+      const int n0 = (in_band / band_m) * S::BN;
+      const int rows = min(M - m0, S::BM);
+      a_rsrc = make_rsrc(codes + (size_t)m0 * K, (unsigned)(rows * K));
+      b_rsrc = make_rsrc(Wp + (size_t)n0 * wrow, (unsigned)(min(N - n0, S::BN) * wrow));
+      m_rsrc = (wave < 4) ? make_rsrc(scales + m0, (unsigned)(rows * 4))
+                          : make_rsrc(rowsum_g + m0, (unsigned)(rows * 4));
+    } else {
+      a_rsrc.z = 0;
+      b_rsrc.z = 0;
+      m_rsrc.z = 0;
+    }
+  };
+  set_load_tile();
+  u4 none = a_rsrc;
+  none.z = 0;
+
+  // Load q of the current load stage into slot lslot_ (q < NL_W: codes or
+  // weights, as in the per-tile kernel; q == NL_W: the tile's scales or row
+  // sums when the stage is its first, else nothing, into the sink).
+#define BITNET_SLOAD(lslot_, q)                                                                 \
+  {                                                                                             \
+    if ((q) < S::NA_W) {                                                                        \
+      const int q_ = wave + S::NW * (q);                                                        \
+      const int rb_ = q_ % (S::BM / 8);                                                         \
+      load_lds16(a_rsrc, ((rb_ & 1) ? a_lane1 : a_lane0) + rb_ * 8 * K + ld_ks * S::SK,         \
+                 lds0 + (unsigned)((lslot_) * S::SLOT + rb_ * 1024));                           \
+    } else if ((q) < S::NL_W) {                                                                 \
+      const int cg_ = wave + S::NW * ((q) - S::NA_W);                                           \
+      load_lds16(b_rsrc, b_lane + cg_ * 32 * wrow + ld_ks * (S::SK / 4),                        \
+                 lds0 + (unsigned)((lslot_) * S::SLOT + S::A_BYTES + cg_ * 1024));              \
+    } else {                                                                                    \
+      const bool first_ = ld_ks == 0; /* a select, not a branch */                              \
+      load_lds4(first_ ? m_rsrc : none, meta_lane,                                              \
+                lds0 + (unsigned)(first_ ? T::META + (ld_i & 1) * T::META_BYTES + 256 * wave    \
+                                         : T::SINK + 256 * wave));                              \
+    }                                                                                           \
+  }
+#define BITNET_SADVANCE()                                                                       \
+  {                                                                                             \
+    if (++ld_ks == nst) {                                                                       \
+      ld_ks = 0;                                                                                \
+      ++ld_i;                                                                                   \
+      set_load_tile();                                                                          \
+    }                                                                                           \
+  }
+
+  int a_rd[4];
+  {
+    const int r = wm * 32 * RT + l32;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) a_rd[h] = r * BKW + 16 * ((2 * h + g) ^ chunk_swizzle(r));
+  }
+  const int b_rd = S::A_BYTES + wn * CT * 1024 + 16 * l32;
+
+  v16i acc[RT][CT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0;
+  v4i ax[2][RT], ay[2][RT];
+  v4i bx[2][CT], by[2][CT];
+  uint4 pw[CT];
+
+#define BITNET_SREAD(slot_, blk_, A_)                                                           \
+  {                                                                                             \
+    const char* sb_ = smem + (slot_) * S::SLOT;                                                 \
+    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) pw[ct] =                                  \
+        *reinterpret_cast<const uint4*>(sb_ + b_rd + ct * 1024 + (blk_) * 512);                 \
+    _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                            \
+        _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) A_[hh][rt] =                          \
+            *reinterpret_cast<const v4i*>(sb_ + a_rd[2 * (blk_) + hh] + rt * 32 * BKW);         \
+  }
+#define BITNET_SUNPACK(B_)                                                                      \
+  _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                              \
+      _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) B_[hh][ct] =                            \
+          unpack_u(pw[ct], 2 * g + 4 * hh);
+#define BITNET_SPIN(A_, B_)                                                                     \
+  _Pragma("unroll") for (int hh = 0; hh < 2; ++hh) {                                            \
+    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) asm volatile("" : "+v"(B_[hh][ct]));      \
+    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) asm volatile("" : "+v"(A_[hh][rt]));      \
+  }
+  constexpr int kMfmaPerBlock = 2 * RT * CT;
+  constexpr int kUnpackPerBlock = 2 * CT;
+#define BITNET_SSTEP(A_, B_, NB_, LD_, lslot_)                                                  \
+  _Pragma("unroll") for (int ch = 0; ch < kChunks; ++ch) {                                      \
+    _Pragma("unroll") for (int e = 0; e < kUnpackPerBlock; ++e) {                               \
+      if (1 + e * (kChunks - 1) / kUnpackPerBlock == ch)                                        \
+        NB_[e / CT][e % CT] = unpack_u(pw[e % CT], 2 * g + 4 * (e / CT));                       \
+    }                                                                                           \
+    if (LD_) {                                                                                  \
+      _Pragma("unroll") for (int q = 0; q < T::NLG; ++q) {                                      \
+        if (q * kChunks / T::NLG == ch) BITNET_SLOAD(lslot_, q)                                 \
+      }                                                                                         \
+    }                                                                                           \
+    _Pragma("unroll") for (int f = ch * (kMfmaPerBlock / kChunks);                              \
+                           f < (ch + 1) * (kMfmaPerBlock / kChunks); ++f) {                     \
+      const int hh = f / (RT * CT), rt = (f / CT) % RT, ct = f % CT;                            \
+      acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct], acc[rt][ct],  \
+                                                          0, 0, 0);                             \
+    }                                                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+  }
+
+  // Epilogue of tile ti: y = (q . u - sum(q)) * alpha * s / c for its rows,
+  // turned around 16 rows at a time through this wave's LDS buffer and
+  // stored as 16-byte row pieces.
+  float* tb = reinterpret_cast<float*>(smem + T::TRANS + wave * T::TBUF);
+  auto epilogue = [&](int ti) {
+    const int tile = first + ti * wg_step;
+    const int band = tile / (kBand * tiles_n);
+    const int band_m = min(tiles_m - band * kBand, kBand);
+    const int in_band = tile - band * kBand * tiles_n;
+    const int m0 = (band * kBand + in_band % band_m) * S::BM;
+    const int n0 = (in_band / band_m) * S::BN;
+    const int rows = min(M - m0, S::BM);
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc(y + (size_t)m0 * N, (short)0, rows * N * 4, 0x00020000);
+    const float* msc = reinterpret_cast<const float*>(smem + T::META + (ti & 1) * T::META_BYTES);
+    const int* mrs = reinterpret_cast<const int*>(msc + S::BM);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      // this lane's rows: rb + 8 q + 4 g + e (q, e = 0..3), the 32x32 MFMA layout
+      const int rb = wm * 32 * RT + rt * 32;
+      v4f f[4];
+      v4i rs[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f sv = *reinterpret_cast<const v4f*>(msc + rb + 8 * q + 4 * g);
+        rs[q] = *reinterpret_cast<const v4i*>(mrs + rb + 8 * q + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[q][e] = dequant_factor(alpha, sv[e], c);
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int nc = n0 + wn * 32 * CT + ct * 32 + 4 * (lane & 7);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int q = 2 * h + qq, v = 4 * q + e;
+              tb[(8 * qq + 4 * g + e) * T::TPITCH + l32] =
+                  (float)(acc[rt][ct][v] - rs[q][e]) * f[q][e];
+            }
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int r = 8 * jj + (lane >> 3);
+            const v4f o = *reinterpret_cast<const v4f*>(tb + r * T::TPITCH + 4 * (lane & 7));
+            const int off = nc < N ? ((rb + 16 * h + r) * N + nc) * 4 : (int)0x80000000;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, o), yr, off, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  // Prologue: stages 0 .. SL - 1 in flight, stage 0 published, its block 0 read.
+#pragma unroll
+  for (int s = 0; s < S::SL; ++s) {
+#pragma unroll
+    for (int q = 0; q < T::NLG; ++q) BITNET_SLOAD(s, q)
+    BITNET_SADVANCE()
+  }
+  BITNET_WAIT_VMCNT((S::SL - 1) * T::NLG);
+  lds_barrier();
+  BITNET_SREAD(0, 0, ax)
+  BITNET_SUNPACK(bx)
+
+  int slot = 0, ks = 0, ti = 0;
+  for (int gs = 0; gs < total; ++gs) {
+    const int nslot = slot + 1 == S::SL ? 0 : slot + 1;
+    __builtin_amdgcn_sched_barrier(0);
+    BITNET_SREAD(slot, 1, ay)
+    BITNET_SSTEP(ax, bx, by, false, 0)
+    BITNET_SPIN(ay, by)
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage boundary: this wave's loads of stage gs + 1 are complete once at
+    // most the loads of stage gs + 2 -- and, in a tile's first two stages, the
+    // previous tile's stores, issued after or between them -- are
+    // outstanding.
+    if (ti > 0 && ks <= 1) {
+      BITNET_WAIT_VMCNT((S::SL - 2) * T::NLG + T::STORES);
+    } else {
+      BITNET_WAIT_VMCNT((S::SL - 2) * T::NLG);
+    }
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    BITNET_SREAD(nslot, 0, ax)
+    BITNET_SSTEP(ay, by, bx, true, slot)
+    BITNET_SPIN(ax, bx)
+    __builtin_amdgcn_sched_barrier(0);
+    BITNET_SADVANCE()
+    slot = nslot;
+    if (++ks == nst) {
+      epilogue(ti);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0;
+      ks = 0;
+      ++ti;
+    }
+  }
+  // The fetches past the last stage write zeros into free LDS; let them land
+  // before the workgroup ends.
+  BITNET_WAIT_VMCNT(0);
+#undef BITNET_SLOAD
+#undef BITNET_SADVANCE
+#undef BITNET_SREAD
+#undef BITNET_SUNPACK
+#undef BITNET_SPIN
+#undef BITNET_SSTEP
+}
+
 template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG>
 hipError_t launch_tile(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, float c, float* y,
@@ -459,6 +775,33 @@ hipError_t launch_variant(const int8_t* codes, const float* scales, int64_t M, i
                                                          y, nullptr, nullptr, stream);
 }
 
+template <int RT, int CT, int WMW, int WNW>
+hipError_t launch_stream(const int8_t* codes, const float* scales, const int32_t* rowsum,
+                         int64_t M, int K, const uint8_t* Wpacked, int64_t N, const float* alpha,
+                         float c, float* y, hipStream_t stream) {
+  using S = Shape<RT, CT, WMW, WNW, 1>;
+  using T = StreamShape<RT, CT, WMW, WNW>;
+  const int tiles_m = (int)((M + S::BM - 1) / S::BM);
+  const int tiles_n = (int)((N + S::BN - 1) / S::BN);
+  const int tiles = tiles_m * tiles_n;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // one workgroup per CU (the LDS footprint admits no second), the same
+  // number on every XCD
+  int grid = (tiles < cus ? tiles : cus) / kXcds * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  auto kern = ternary_gemm_stream_kernel<RT, CT, WMW, WNW>;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+  if (e != hipSuccess) return e;
+  kern<<<dim3((unsigned)grid), dim3(S::NT), T::LDS, stream>>>(
+      codes, scales, rowsum, (int)M, K, Wpacked, (int)N, alpha, c, y, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int K,
@@ -472,6 +815,11 @@ hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int 
   // every CU several; otherwise 128 x 128 tiles whose waves split each
   // 256-wide stage into two k slices.
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  // Many tiles, row sums given: one workgroup per CU streams its tiles, the
+  // stores of one overlapping the next one's fetches and products.
+  if (big_tiles >= 1024 && rowsum && !acc && K % 128 == 0 && K >= 512 && N % 4 == 0 &&
+      N <= (1 << 20) && (reinterpret_cast<uintptr_t>(y) & 15) == 0)
+    return launch_stream<2, 4, 4, 2>(codes, scales, rowsum, M, K, Wpacked, N, alpha, c, y, stream);
   if (big_tiles >= 1024)
     return launch_variant<2, 4, 4, 2, 1>(codes, scales, M, K, Wpacked, N, alpha, c, y, acc, rowsum,
                                          stream);

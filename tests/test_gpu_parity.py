@@ -176,6 +176,47 @@ def test_parity_full_workload(key):
     np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
 
 
+# Many tiles per CU --------------------------------------------------------
+# Large products where the forward has the quantizer's row sums run one
+# workgroup per CU that walks its tiles with one stage pipeline across tile
+# boundaries, storing each tile's outputs while the next one is fetched and
+# multiplied; other shapes fall back to the per-tile kernel. The forward is
+# compared bit for bit with the per-tile product of the same codes (which
+# sums the codes itself), and on sampled rows with the oracle.
+@pytest.mark.parametrize("M,K,N,bits,had", [
+    (8293, 512, 8228, 8, 0),    # ragged rows and columns, 4-5 tiles per workgroup, 4 stages each
+    (4200, 640, 16384, 4, 0),   # 5 stages per tile
+    (4100, 1024, 16384, 4, 1),  # transform, 8 stages per tile
+    (8200, 576, 8196, 8, 0),    # K not a multiple of 128: per-tile kernel
+    (8200, 512, 8190, 4, 0),    # N not a multiple of 4: per-tile kernel
+])
+def test_parity_many_tiles(M, K, N, bits, had):
+    _say(f"many tiles M={M} K={K} N={N} bits={bits} hadamard={had}")
+    case = workloads.make_case(M, K, N, x_dtype="bf16", n_out=max(1, K // 100), factor=20.0,
+                               seed=M + N)
+    x = _to_dev_x(case["x"], "bf16")
+    W = torch.from_numpy(case["W"]).to(DEV)
+    Wp, alpha = bl.ternarize_weights(W)
+    y = bl.hbitlinear_forward(x, Wp, alpha, bits, had)
+    codes, scales = bl.quantize_activations(x, bits, had)
+    y2 = bl.ternary_linear_dequant(codes, scales, Wp, alpha, bits)
+    torch.cuda.synchronize()
+    del W
+    y_np = y.cpu().numpy()
+    np.testing.assert_array_equal(y_np, y2.cpu().numpy())
+    del y2
+
+    t_ref, a_ref, _ = oracle.ternarize(case["W"])
+    x64 = oracle.widen_input(case["x"], "bf16")
+    q_ref, s_ref, p_ref = oracle.quantize_activations(oracle.fwht(x64) if had else x64, bits)
+    assert_codes_match(codes.cpu().numpy(), q_ref, p_ref)
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, M - 1], np.arange(M - (M % 256), M)[:8],
+                                     rng.choice(M, 40, replace=False)]))
+    _, y_ref = oracle.forward_from_codes(q_ref[rows], s_ref[rows], t_ref, a_ref, bits)
+    assert_y_close(y_np[rows], y_ref)
+
+
 # Edge and degenerate cases ------------------------------------------------
 def test_zero_weights_give_zero_output():
     _say("zero weights")
