@@ -140,7 +140,9 @@ class Prepared:
         self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
         self.ws = torch.empty((bl.forward_workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.hadamard),),
                               dtype=torch.uint8, device=dev)
-        self.codes, self.scales = bl.quantize_activations(self.x, wl.bits, wl.hadamard)
+        self.rowsum = torch.empty((wl.M,), dtype=torch.int32, device=dev)
+        self.codes, self.scales = bl.quantize_activations(self.x, wl.bits, wl.hadamard,
+                                                          rowsum=self.rowsum)
         self.fused = bl.forward_workspace_bytes(wl.M, wl.K, wl.N, wl.bits, wl.hadamard) == 0
         torch.cuda.synchronize()
 
@@ -151,7 +153,7 @@ class Prepared:
 
     def matmul_only(self, bl, i):
         bl.ternary_linear_dequant(self.codes, self.scales, self.Wp[i % self.copies], self.alpha,
-                                  self.wl.bits, out=self.y)
+                                  self.wl.bits, out=self.y, rowsum=self.rowsum)
 
     def free_latent(self):
         self.W = None

@@ -47,10 +47,11 @@ SIGNATURES = {
     "bitnet_forward_workspace_bytes": (_size, [_i64, _i64, _i64, _int, _int]),
     "bitnet_hbitlinear_forward": (_int, [_ptr, _int, _i64, _i64, _ptr, _i64, _ptr, _int, _int,
                                          _ptr, _ptr, _size, _ptr]),
-    "bitnet_quantize_activations": (_int, [_ptr, _int, _i64, _i64, _int, _int, _ptr, _ptr, _ptr]),
+    "bitnet_quantize_activations": (_int, [_ptr, _int, _i64, _i64, _int, _int, _ptr, _ptr, _ptr,
+                                           _ptr]),
     "bitnet_ternary_gemm_i32": (_int, [_ptr, _i64, _i64, _ptr, _i64, _ptr, _ptr]),
-    "bitnet_ternary_linear_dequant": (_int, [_ptr, _ptr, _i64, _i64, _ptr, _i64, _ptr, _int,
-                                             _ptr, _ptr]),
+    "bitnet_ternary_linear_dequant": (_int, [_ptr, _ptr, _ptr, _i64, _i64, _ptr, _i64, _ptr,
+                                             _int, _ptr, _ptr]),
     "bitnet_forward_prologue_workspace_bytes": (_size, [_i64, _i64, _i64, _int, _int]),
     "bitnet_hbitlinear_forward_prologue": (_int, [_ptr, _ptr, _int, _i64, _i64, _int, _ptr,
                                                   ctypes.c_float, _ptr, _i64, _ptr, _int, _int,

@@ -99,16 +99,23 @@ def hbitlinear_forward(x: torch.Tensor, Wpacked: torch.Tensor, alpha: torch.Tens
 
 def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
                          codes: Optional[torch.Tensor] = None,
-                         scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """(codes int8 [M, K], scales fp32 [M]) of the transform + quantization stage."""
+                         scales: Optional[torch.Tensor] = None,
+                         rowsum: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(codes int8 [M, K], scales fp32 [M]) of the transform + quantization
+    stage; `rowsum` (int32 [M]), when given, receives each token's code sum."""
     _require(x, "x", (torch.float32, torch.bfloat16), 2)
     M, K = x.shape
     if codes is None:
         codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if scales is None:
         scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if rowsum is not None:
+        _require(rowsum, "rowsum", (torch.int32,), 1)
+        if rowsum.shape[0] != M:
+            raise ValueError("rowsum must have one entry per token")
     _lib.call("bitnet_quantize_activations", x.data_ptr(), _x_dtype(x), M, K, int(bits),
-              int(hadamard), codes.data_ptr(), scales.data_ptr(), _stream_ptr(x))
+              int(hadamard), codes.data_ptr(), scales.data_ptr(),
+              rowsum.data_ptr() if rowsum is not None else None, _stream_ptr(x))
     return codes, scales
 
 
@@ -255,9 +262,10 @@ def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
 
 
 def ternary_linear_dequant(codes: torch.Tensor, scales: torch.Tensor, Wpacked: torch.Tensor,
-                           alpha: torch.Tensor, bits: int,
-                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y fp32 [M, N] = (codes . t^T) * alpha * scales / c."""
+                           alpha: torch.Tensor, bits: int, out: Optional[torch.Tensor] = None,
+                           rowsum: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y fp32 [M, N] = (codes . t^T) * alpha * scales / c. `rowsum`: the
+    codes' per-token sums from quantize_activations, or None."""
     _require(codes, "codes", (torch.int8,), 2)
     _require(scales, "scales", (torch.float32,), 1)
     _require(Wpacked, "Wpacked", (torch.uint8,), 2)
@@ -268,9 +276,13 @@ def ternary_linear_dequant(codes: torch.Tensor, scales: torch.Tensor, Wpacked: t
         raise ValueError("Wpacked row length does not match K/4")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
-    _lib.call("bitnet_ternary_linear_dequant", codes.data_ptr(), scales.data_ptr(), M, K,
-              Wpacked.data_ptr(), N, alpha.data_ptr(), int(bits), out.data_ptr(),
-              _stream_ptr(codes))
+    if rowsum is not None:
+        _require(rowsum, "rowsum", (torch.int32,), 1)
+        if rowsum.shape[0] != M:
+            raise ValueError("rowsum must have one entry per token")
+    _lib.call("bitnet_ternary_linear_dequant", codes.data_ptr(), scales.data_ptr(),
+              rowsum.data_ptr() if rowsum is not None else None, M, K, Wpacked.data_ptr(), N,
+              alpha.data_ptr(), int(bits), out.data_ptr(), _stream_ptr(codes))
     return out
 
 

@@ -159,16 +159,16 @@ size_t bitnet_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits,
 
 bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, int64_t M,
                                           int64_t K, int bits, int hadamard, int8_t* codes,
-                                          float* scales, hipStream_t stream) {
+                                          float* scales, int32_t* rowsum, hipStream_t stream) {
   const char* fn = "bitnet_quantize_activations";
   if (bitnet_status st = check_dims(fn, M, K, 0)) return st;
   if (bitnet_status st = check_quant_args(fn, K, bits, hadamard, x_dtype)) return st;
   if (M == 0) return ok();
   if (!x || !codes || !scales) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(rowsum, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
   return hip_status(bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, codes,
-                                            scales, stream),
+                                            scales, stream, nullptr, rowsum),
                     fn);
 }
 
@@ -189,10 +189,10 @@ bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
                     fn);
 }
 
-bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* scales, int64_t M,
-                                            int64_t K, const uint8_t* Wpacked, int64_t N,
-                                            const float* alpha, int bits, float* y,
-                                            hipStream_t stream) {
+bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* scales,
+                                            const int32_t* rowsum, int64_t M, int64_t K,
+                                            const uint8_t* Wpacked, int64_t N, const float* alpha,
+                                            int bits, float* y, hipStream_t stream) {
   const char* fn = "bitnet_ternary_linear_dequant";
   if (bitnet_status st = check_dims(fn, M, K, N)) return st;
   if (bits != 4 && bits != 8) return fail(BITNET_ERR_BAD_BITS, "%s: bits=%d must be 4 or 8", fn, bits);
@@ -203,10 +203,10 @@ bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* sc
   if (!codes || !scales || !Wpacked || !alpha || !y)
     return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(codes, 16) || !aligned(Wpacked, 16) || !aligned(y, 4) || !aligned(scales, 4) ||
-      !aligned(alpha, 4))
+      !aligned(alpha, 4) || !aligned(rowsum, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
   return hip_status(bitnet::launch_ternary_matmul(codes, scales, M, (int)K, Wpacked, N, alpha,
-                                                  bits, y, nullptr, stream),
+                                                  bits, y, nullptr, stream, rowsum),
                     fn);
 }
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define BITNET_ABI_VERSION 1
+#define BITNET_ABI_VERSION 2
 #define BITNET_EPS 1e-7f
 /* Largest K the fused transform + quantizer stages in one CU's LDS (fp32). */
 #define BITNET_MAX_K 32768
@@ -135,10 +135,13 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
 
 /* Transform + per-token quantization only (Eq. 3-6): writes int8 codes
  * [M, K] and fp32 scales s [M] (s = stat + eps, the value the dequantization
- * multiplies by). Same requirements as the forward. */
+ * multiplies by), and, when rowsum is not NULL, each token's code sum
+ * rowsum[m] = sum_k codes[m, k] (int32 [M], exact), which
+ * bitnet_ternary_linear_dequant can take instead of summing the codes again.
+ * Same requirements as the forward; rowsum 4-byte aligned. */
 bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, int64_t M,
                                           int64_t K, int bits, int hadamard, int8_t* codes,
-                                          float* scales, hipStream_t stream);
+                                          float* scales, int32_t* rowsum, hipStream_t stream);
 
 /* Exact integer product only: acc[m, n] = sum_k codes[m, k] * t[n, k], int32.
  * codes: int8 [M, K] with values in [-128, 127]. Requires K % 64 == 0 and
@@ -150,11 +153,14 @@ bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
 /* Integer product with the fused dequantization epilogue (engine page,
  * HBitLinear.forward's F.linear of the two dequantized operands, rewritten by
  * linearity): y = (codes . t^T) * alpha * scales[m] / c, c = 127 (bits 8) or
- * sqrt 7 (bits 4). */
-bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* scales, int64_t M,
-                                            int64_t K, const uint8_t* Wpacked, int64_t N,
-                                            const float* alpha, int bits, float* y,
-                                            hipStream_t stream);
+ * sqrt 7 (bits 4). rowsum: NULL, or the codes' per-token sums as
+ * bitnet_quantize_activations wrote them (int32 [M]); the prefill product
+ * then skips summing the codes, which is how the forward runs it. A rowsum
+ * that is not the codes' sum gives wrong outputs (it is not checked). */
+bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* scales,
+                                            const int32_t* rowsum, int64_t M, int64_t K,
+                                            const uint8_t* Wpacked, int64_t N, const float* alpha,
+                                            int bits, float* y, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Forward with the layer-input prologue                                     */

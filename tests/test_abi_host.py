@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_empty_error(lib):
-    assert lib.bitnet_abi_version() == 1
+    assert lib.bitnet_abi_version() == 2
 
 
 def test_workspace_sizes(lib):
@@ -117,9 +117,10 @@ def test_pack_validation(lib):
 
 def test_stage_entry_points_validation(lib):
     q = lib.bitnet_quantize_activations
-    assert q(FAKE, _lib.F32, 2, 64, 5, 0, FAKE, FAKE, None) == _lib.ERR_BAD_BITS
-    assert q(FAKE, _lib.F32, 2, 320, 8, 1, FAKE, FAKE, None) == _lib.ERR_NOT_POW2
-    assert q(None, _lib.F32, 2, 64, 8, 0, FAKE, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert q(FAKE, _lib.F32, 2, 64, 5, 0, FAKE, FAKE, None, None) == _lib.ERR_BAD_BITS
+    assert q(FAKE, _lib.F32, 2, 320, 8, 1, FAKE, FAKE, None, None) == _lib.ERR_NOT_POW2
+    assert q(None, _lib.F32, 2, 64, 8, 0, FAKE, FAKE, None, None) == _lib.ERR_INVALID_ARG
+    assert q(FAKE, _lib.F32, 2, 64, 8, 0, FAKE, FAKE, FAKE + 2, None) == _lib.ERR_ALIGN
     g = lib.bitnet_ternary_gemm_i32
     assert g(FAKE, 2, 70, FAKE, 3, FAKE, None) == _lib.ERR_ALIGN
     assert g(None, 2, 64, FAKE, 3, FAKE, None) == _lib.ERR_INVALID_ARG
@@ -127,8 +128,9 @@ def test_stage_entry_points_validation(lib):
     assert g(FAKE, 2, 65536, FAKE, 3, FAKE, None) == _lib.ERR_UNSUPPORTED
     assert g(FAKE + 8, 2, 64, FAKE, 3, FAKE, None) == _lib.ERR_ALIGN
     d = lib.bitnet_ternary_linear_dequant
-    assert d(FAKE, FAKE, 2, 64, FAKE, 3, FAKE, 3, FAKE, None) == _lib.ERR_BAD_BITS
-    assert d(FAKE, None, 2, 64, FAKE, 3, FAKE, 8, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert d(FAKE, FAKE, None, 2, 64, FAKE, 3, FAKE, 3, FAKE, None) == _lib.ERR_BAD_BITS
+    assert d(FAKE, None, None, 2, 64, FAKE, 3, FAKE, 8, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert d(FAKE, FAKE, FAKE + 2, 2, 64, FAKE, 3, FAKE, 8, FAKE, None) == _lib.ERR_ALIGN
 
 
 def test_binding_raises_typed_error(lib):

@@ -42,10 +42,16 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     W = torch.from_numpy(case["W"]).to(DEV)
 
     Wp, alpha = bl.ternarize_weights(W)
-    codes, scales = bl.quantize_activations(x, bits, had)
+    rowsum = torch.empty((M,), dtype=torch.int32, device=DEV)
+    codes, scales = bl.quantize_activations(x, bits, had, rowsum=rowsum)
     y = bl.hbitlinear_forward(x, Wp, alpha, bits, had)
     y2 = bl.ternary_linear_dequant(codes, scales, Wp, alpha, bits)
+    y3 = bl.ternary_linear_dequant(codes, scales, Wp, alpha, bits, rowsum=rowsum)
     torch.cuda.synchronize()
+    # the quantizer's code sums are exact, and the product given them is the
+    # product that sums the codes itself, bit for bit
+    np.testing.assert_array_equal(rowsum.cpu().numpy(), codes.cpu().numpy().astype(np.int64).sum(1))
+    np.testing.assert_array_equal(y3.cpu().numpy(), y2.cpu().numpy())
 
     t_ref, a_ref, p_w = oracle.ternarize(case["W"])
     assert_packed_match(Wp.cpu().numpy(), t_ref, p_w)
@@ -198,13 +204,17 @@ def test_parity_many_tiles(M, K, N, bits, had):
     W = torch.from_numpy(case["W"]).to(DEV)
     Wp, alpha = bl.ternarize_weights(W)
     y = bl.hbitlinear_forward(x, Wp, alpha, bits, had)
-    codes, scales = bl.quantize_activations(x, bits, had)
+    rowsum = torch.empty((M,), dtype=torch.int32, device=DEV)
+    codes, scales = bl.quantize_activations(x, bits, had, rowsum=rowsum)
     y2 = bl.ternary_linear_dequant(codes, scales, Wp, alpha, bits)
+    y3 = bl.ternary_linear_dequant(codes, scales, Wp, alpha, bits, rowsum=rowsum)
     torch.cuda.synchronize()
     del W
     y_np = y.cpu().numpy()
     np.testing.assert_array_equal(y_np, y2.cpu().numpy())
-    del y2
+    np.testing.assert_array_equal(y3.cpu().numpy(), y_np)
+    np.testing.assert_array_equal(rowsum.cpu().numpy(), codes.cpu().numpy().astype(np.int64).sum(1))
+    del y2, y3
 
     t_ref, a_ref, _ = oracle.ternarize(case["W"])
     x64 = oracle.widen_input(case["x"], "bf16")
