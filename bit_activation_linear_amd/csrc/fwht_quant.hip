@@ -38,6 +38,9 @@ namespace {
 constexpr float kEps = 1e-7f;
 
 __device__ __forceinline__ int pad_idx(int i) { return i + (i >> 5); }
+// For a and b with no set bit in common (a + b == a | b),
+// pad_idx(a + b) == pad_idx(a) + pad_idx(b): with b a compile-time constant
+// the second term becomes an immediate LDS offset.
 
 __device__ __forceinline__ void load8(const float* p, float* v) {
   const float4 a = reinterpret_cast<const float4*>(p)[0];
@@ -222,16 +225,20 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
   constexpr int R = 1 << NB;
   constexpr int G = E / R;
   const int t = threadIdx.x;
-  int base[G];
+  // group base: the bits [B0, B0 + NB) are clear, so base + (j << B0) is
+  // base | (j << B0) and its padded index is pad_idx(base) + pad_idx(j << B0)
+  int base[G], pbase[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     const int g = t + T * gi;
     base[gi] = (g & ((1 << B0) - 1)) | ((g >> B0) << (B0 + NB));
+    pbase[gi] = pad_idx(base[gi]);
   }
+#define BITNET_PJ(j) ((j << B0) + ((j << B0) >> 5))
 #pragma unroll
   for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-    for (int j = 0; j < R; ++j) v[gi * R + j] = lds[pad_idx(base[gi] + (j << B0))];
+    for (int j = 0; j < R; ++j) v[gi * R + j] = lds[pbase[gi] + BITNET_PJ(j)];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) fwht_regs<R>(v + gi * R);
 
@@ -241,7 +248,7 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
 #pragma unroll
     for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-      for (int j = 0; j < R; ++j) lds[pad_idx(base[gi] + (j << B0))] = v[gi * R + j];
+      for (int j = 0; j < R; ++j) lds[pbase[gi] + BITNET_PJ(j)] = v[gi * R + j];
     __syncthreads();
     return;
   }
@@ -262,7 +269,8 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
 #pragma unroll
   for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-    for (int j = 0; j < R; ++j) lds[pad_idx(base[gi] + (j << B0))] = v[gi * R + j];
+    for (int j = 0; j < R; ++j) lds[pbase[gi] + BITNET_PJ(j)] = v[gi * R + j];
+#undef BITNET_PJ
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < E; ++i) s = (BITS == 8) ? fmaxf(s, fabsf(v[i])) : s + fabsf(v[i]);
@@ -290,12 +298,13 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
   }
   if (t == 0) *scale_out = sc;
   const int e0 = t * E;
+  const int pe0 = pad_idx(e0);  // e0 is a multiple of E, c + i < E
   int qs = 0;  // this thread's share of the code sum
 #pragma unroll
   for (int c = 0; c < E; c += 8) {
     float u[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = lds[pad_idx(e0 + c + i)];
+    for (int i = 0; i < 8; ++i) u[i] = lds[pe0 + (c + i) + ((c + i) >> 5)];
     const uint2 w = quant_pack8<BITS>(u, mult);
     *reinterpret_cast<uint2*>(crow + e0 + c) = w;
     qs = __builtin_amdgcn_sdot4((int)w.y, 0x01010101, __builtin_amdgcn_sdot4((int)w.x, 0x01010101, qs, false), false);
@@ -347,7 +356,8 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t
 #pragma unroll
   for (int rh = 0; rh < E / 8; ++rh)
 #pragma unroll
-    for (int lo = 0; lo < 8; ++lo) lds[pad_idx(8 * t + 8 * T * rh + lo)] = v[8 * rh + lo];
+    for (int lo = 0; lo < 8; ++lo)
+      lds[pad_idx(8 * t) + 8 * T * rh + ((8 * T * rh) >> 5) + lo] = v[8 * rh + lo];
   __syncthreads();
 
   // Middle bits [3, 3 + LT) in chunks of up to e bits.
