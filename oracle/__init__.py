@@ -27,6 +27,9 @@ Parity status per function (mirrors the design notes):
                        activation quantizers, 3-bit range and error bounds)
   backward             pinned (torch autograd through the STE forward, adjoint
                        identities, Eq. 8 via H*H = I, hand values, brute force)
+  tl2 (module)         pinned (tests/test_oracle_tl2.py: the mirror table against
+                       all 27 states, the index's closed form, round trips, hand
+                       built bytes, 5/3 bits per weight)
 """
 
 from .hbitlinear import (  # noqa: F401
@@ -56,3 +59,5 @@ from .hbitlinear import (  # noqa: F401
     unpack_2bit,
     widen_input,
 )
+
+from . import tl2  # noqa: F401,E402
