@@ -14,12 +14,15 @@ from .api import (  # noqa: F401
     hbitlinear_backward,
     hbitlinear_forward,
     hbitlinear_forward_prologue,
+    hbitlinear_forward_tl2,
     kv_quantize,
     pack_2bit,
+    pack_tl2,
     quantize_activations,
     quantize_activations_prologue,
     ternarize_weights,
     ternary_gemm_i32,
     ternary_linear_dequant,
+    tl2_bytes,
 )
 from ._lib import BitNetError  # noqa: F401

@@ -60,6 +60,10 @@ SIGNATURES = {
                                                     ctypes.c_float, _int, _int, _ptr, _ptr,
                                                     _ptr]),
     "bitnet_kv_quantize": (_int, [_ptr, _int, _i64, _i64, _i64, _int, _ptr, _ptr, _ptr]),
+    "bitnet_tl2_bytes": (_size, [_i64, _i64]),
+    "bitnet_pack_tl2": (_int, [_ptr, _i64, _i64, _ptr, _ptr]),
+    "bitnet_hbitlinear_forward_tl2": (_int, [_ptr, _int, _i64, _i64, _ptr, _i64, _ptr, _int, _ptr,
+                                             _ptr]),
     "bitnet_backward_workspace_bytes": (_size, [_i64, _i64, _i64, _int, _int, _int]),
     "bitnet_hbitlinear_backward": (_int, [_ptr, _int, _i64, _i64, _ptr, _ptr, _i64, _ptr, _ptr,
                                           _int, _int, _ptr, _ptr, _ptr, _size, _ptr]),

@@ -70,6 +70,41 @@ def pack_2bit(T: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tens
     return out
 
 
+def tl2_bytes(N: int, K: int) -> int:
+    """Bytes of the TL2 (1.67 bits per weight) encoding of [N, K] weights."""
+    return int(_lib.load().bitnet_tl2_bytes(N, K))
+
+
+def pack_tl2(Wpacked: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """TL2 encoding uint8 [N, tl2_bytes(N, K) / N] of 2-bit packed weights [N, K/4]."""
+    _require(Wpacked, "Wpacked", (torch.uint8,), 2)
+    N, K = Wpacked.shape[0], Wpacked.shape[1] * 4
+    nbytes = tl2_bytes(N, K)
+    if out is None:
+        out = torch.empty((N, nbytes // max(N, 1)), dtype=torch.uint8, device=Wpacked.device)
+    elif out.numel() < nbytes:
+        raise ValueError("out is smaller than the TL2 encoding")
+    _lib.call("bitnet_pack_tl2", Wpacked.data_ptr(), N, K, out.data_ptr(), _stream_ptr(Wpacked))
+    return out
+
+
+def hbitlinear_forward_tl2(x: torch.Tensor, Wtl2: torch.Tensor, alpha: torch.Tensor, bits: int,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y fp32 [1, N]: the single-token forward (no transform) on TL2 weights."""
+    _require(x, "x", (torch.float32, torch.bfloat16), 2)
+    _require(Wtl2, "Wtl2", (torch.uint8,), 2)
+    _require(alpha, "alpha", (torch.float32,), 1)
+    M, K = x.shape
+    N = Wtl2.shape[0]
+    if Wtl2.numel() != tl2_bytes(N, K):
+        raise ValueError("Wtl2 does not hold the TL2 encoding of [N, K] weights")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _lib.call("bitnet_hbitlinear_forward_tl2", x.data_ptr(), _x_dtype(x), M, K, Wtl2.data_ptr(), N,
+              alpha.data_ptr(), int(bits), out.data_ptr(), _stream_ptr(x))
+    return out
+
+
 def forward_workspace_bytes(M: int, K: int, N: int, bits: int, hadamard: int) -> int:
     return int(_lib.load().bitnet_forward_workspace_bytes(M, K, N, bits, int(hadamard)))
 

@@ -489,4 +489,42 @@ bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R
                     fn);
 }
 
+size_t bitnet_tl2_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K <= 0 || K % 64 != 0) return 0;
+  return bitnet::tl2_bytes(N, K);
+}
+
+bitnet_status bitnet_pack_tl2(const uint8_t* Wpacked, int64_t N, int64_t K, uint8_t* Wtl2,
+                              hipStream_t stream) {
+  const char* fn = "bitnet_pack_tl2";
+  if (bitnet_status st = check_dims(fn, 0, K, N)) return st;
+  if (N == 0) return ok();
+  if (!Wpacked || !Wtl2) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(Wpacked, 16) || !aligned(Wtl2, 16))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bitnet::launch_repack_tl2(Wpacked, N, (int)K, Wtl2, stream), fn);
+}
+
+bitnet_status bitnet_hbitlinear_forward_tl2(const void* x, bitnet_dtype x_dtype, int64_t M,
+                                            int64_t K, const uint8_t* Wtl2, int64_t N,
+                                            const float* alpha, int bits, float* y,
+                                            hipStream_t stream) {
+  const char* fn = "bitnet_hbitlinear_forward_tl2";
+  if (bitnet_status st = check_dims(fn, M, K, N)) return st;
+  if (bitnet_status st = check_quant_args(fn, K, bits, 0, x_dtype)) return st;
+  if (M > 1)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: M=%lld, the TL2 decode takes one token", fn,
+                (long long)M);
+  if (K > bitnet::kTl2MaxK)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: K=%lld exceeds %d", fn, (long long)K,
+                bitnet::kTl2MaxK);
+  if (M == 0 || N == 0) return ok();
+  if (!x || !Wtl2 || !alpha || !y) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(x, 16) || !aligned(Wtl2, 16) || !aligned(y, 4) || !aligned(alpha, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bitnet::launch_tl2_decode(x, (int)x_dtype, (int)K, Wtl2, N, alpha, bits, y,
+                                              stream),
+                    fn);
+}
+
 }  // extern "C"

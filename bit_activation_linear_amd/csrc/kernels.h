@@ -142,4 +142,15 @@ hipError_t launch_codes_transpose(const int8_t* codes, int64_t M, int64_t K, int
 // two, 64 .. 32768); out may equal x.
 hipError_t launch_fwht_f32(const float* x, int64_t M, int K, float* out, hipStream_t stream);
 
+// TL2 weight code (edge page mirror consolidation, 5 bits per 3 weights):
+// blocks of 128 triplets per column (64 index bytes, 16 sign bytes).
+constexpr int kTl2MaxK = 6 * 768;  // single-token TL2 decode: six 768-weight super-blocks
+size_t tl2_bytes(int64_t N, int64_t K);
+// 2-bit packed weights [N, K/4] -> TL2 [N, tl2_bytes / N].
+hipError_t launch_repack_tl2(const uint8_t* Wpacked, int64_t N, int K, uint8_t* Wtl2,
+                             hipStream_t stream);
+// Single-token decode forward (M = 1, no transform, K <= kTl2MaxK) on TL2 weights.
+hipError_t launch_tl2_decode(const void* x, int x_dtype, int K, const uint8_t* Wtl2, int64_t N,
+                             const float* alpha, int bits, float* y, hipStream_t stream);
+
 }  // namespace bitnet

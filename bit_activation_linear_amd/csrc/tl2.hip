@@ -1,0 +1,309 @@
+// TL2 ternary weight code (1.67 bits per weight) for single-token decode.
+//
+// Edge page (Quillan-Ronin bitnet_cpp_edge.py), module docstring item 2 and
+// class SignedUnsignedWeightPacker: the 27 states of a ternary triplet
+// (w0, w1, w2) fold onto 14 base triplets (all zero, or first non-zero
+// element +1) and a sign, stored as a 4-bit index and one bit: 5 bits per
+// 3 weights. In the page's table the index of a base triplet equals its
+// balanced-ternary value 9 w0 + 3 w1 + w2, so a triplet of value v has index
+// |v| and sign v < 0.
+//
+// Device layout, per output column, in blocks of 128 triplets (384 weights;
+// the row is padded with zero weights to whole blocks): 64 bytes of 4-bit
+// indices, then 16 bytes of sign bits. Triplet j = 32 g + 4 i + tt (group g,
+// slot i, position tt) keeps its index in nibble i % 2 of byte
+// 16 g + 4 (i / 2) + tt and its sign in bit i of byte 64 + 4 g + tt. So the
+// four triplets of one slot sit in the four bytes of one index word (one mask
+// spreads them to byte lanes) and in bit i of the four bytes of one sign
+// word.
+//
+// Decode product. As in the 2-bit single-token kernel, one wave owns 16
+// output columns and all of K, quantizes the token itself and runs
+// v_mfma_i32_16x16x64_i8 with the token as row 0. A weight byte lane carries
+// the stored field u = t + 1 in {0, 1, 2} and q . t = q . u - sum(q). A
+// slot's four triplet indices become, through two v_perm byte-table lookups
+// (entries 0-7 and 8-13), a byte holding the three fields u0 | u1 << 2 |
+// u2 << 4 of the base triplet; a set sign bit mirrors the byte to
+// 0x2A - byte (each field u -> 2 - u). Fields 0, 1 and 2 are then masked in
+// place (worth u, 4u and 16u) and meet the codes of the triplets' first,
+// second and third weights in three MFMAs with three accumulators, which
+// are scaled back exactly at the end. The codes are written to LDS in that
+// order: lane l owns triplets 4 l .. 4 l + 3 of each 768-weight super-block
+// and writes the codes of their first, second and third weights as three
+// words.
+#include "kernels.h"
+#include "ternary_common.cuh"
+#include "decode_common.cuh"
+
+namespace bitnet {
+namespace {
+
+constexpr float kEps = 1e-7f;
+constexpr int kTl2BlockK = 384;       // weights per block
+constexpr int kTl2BlockBytes = 80;    // 64 index bytes + 16 sign bytes
+constexpr int kTl2SuperK = 768;       // weights per super-block (two blocks)
+
+// One thread per (column, block, group): 32 triplets = 96 weights read from
+// the 2-bit layout (weight k of a row: field k / 16 % 4 of byte k % 16 of
+// 16-byte block k / 64, holding t + 1), 16 index bytes and 4 sign bytes
+// written.
+__global__ __launch_bounds__(256) void repack_tl2_kernel(const uint8_t* __restrict__ Wp,
+                                                         int64_t N, int K, int nblk,
+                                                         uint8_t* __restrict__ Wt) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = N * nblk * 4;
+  if (tid >= total) return;
+  const int g = (int)(tid & 3);
+  const int b = (int)((tid >> 2) % nblk);
+  const int64_t n = (tid >> 2) / nblk;
+  const uint8_t* row = Wp + n * (int64_t)(K >> 2);
+  unsigned idxw[4] = {0u, 0u, 0u, 0u};
+  unsigned signw = 0u;
+#pragma unroll 4
+  for (int jj = 0; jj < 32; ++jj) {
+    const int i = jj >> 2, tt = jj & 3;
+    const int k0 = kTl2BlockK * b + 3 * (32 * g + jj);
+    int t[3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const int k = k0 + p;
+      if (k < K) {
+        const uint8_t byte = row[(k >> 6) * 16 + (k & 15)];
+        t[p] = (int)((byte >> (2 * ((k >> 4) & 3))) & 3u) - 1;
+      } else {
+        t[p] = 0;
+      }
+    }
+    const int v = 9 * t[0] + 3 * t[1] + t[2];
+    const unsigned idx = (unsigned)(v < 0 ? -v : v);
+    idxw[i >> 1] |= idx << (8 * tt + 4 * (i & 1));
+    signw |= (v < 0 ? 1u : 0u) << (8 * tt + i);
+  }
+  uint8_t* out = Wt + n * (int64_t)nblk * kTl2BlockBytes + (int64_t)b * kTl2BlockBytes;
+  *reinterpret_cast<uint4*>(out + 16 * g) = make_uint4(idxw[0], idxw[1], idxw[2], idxw[3]);
+  *reinterpret_cast<unsigned*>(out + 64 + 4 * g) = signw;
+}
+
+// Field byte u0 | u1 << 2 | u2 << 4 (u = w + 1) of base triplets 0-7 and
+// 8-13, four entries per word (the edge page's table, in its order).
+constexpr unsigned kLut0 = 0x19092515u;  // (0,0,0) (0,0,1) (0,1,-1) (0,1,0)
+constexpr unsigned kLut1 = 0x22120229u;  // (0,1,1) (1,-1,-1) (1,-1,0) (1,-1,1)
+constexpr unsigned kLut2 = 0x0A261606u;  // (1,0,-1) (1,0,0) (1,0,1) (1,1,-1)
+constexpr unsigned kLut3 = 0x00002A1Au;  // (1,1,0) (1,1,1)
+
+// 0xFF in each byte of x whose bit `bit` is set.
+__device__ __forceinline__ unsigned byte_mask(unsigned x, int bit) {
+  const unsigned b = (x >> bit) & 0x01010101u;
+  return (b << 8) - b;
+}
+
+// Field bytes of the four triplets of one slot: idx4 holds their indices
+// (0..13) in its bytes, sign4 their signs in bit `bit` of its bytes.
+__device__ __forceinline__ unsigned slot_fields(unsigned idx4, unsigned sign4, int bit) {
+  const unsigned sel = idx4 & 0x07070707u;
+  const unsigned lo = __builtin_amdgcn_perm(kLut1, kLut0, sel);
+  const unsigned hi = __builtin_amdgcn_perm(kLut3, kLut2, sel);
+  const unsigned f = (byte_mask(idx4, 3) & hi) | (~byte_mask(idx4, 3) & lo);
+  const unsigned neg = byte_mask(sign4, bit);
+  return (neg & (0x2A2A2A2Au - f)) | (~neg & f);
+}
+
+// Single-token decode forward on TL2 weights: one wave per 16 columns and
+// all of K (NS 768-weight super-blocks, K <= 768 NS). Quantization as in the
+// 2-bit single-token kernel (Eq. 5 / Eq. 6), with each lane owning 12
+// consecutive values per super-block.
+template <typename XT, int BITS, int NS>
+__global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__ xv,
+                                                        const uint8_t* __restrict__ Wt,
+                                                        const float* __restrict__ alpha_p,
+                                                        float* __restrict__ y, int K, int N,
+                                                        float c) {
+  // codes per super-block: [bb][g][h][p] 16-byte words (768 B), then 64 zero
+  // bytes read by the lanes that feed the dead MFMA rows
+  __shared__ __attribute__((aligned(16))) int8_t qw[NS * 768 + 64];
+  asm volatile("" ::"s"(K), "s"(N), "s"(c), "s"(y), "s"(xv), "s"(Wt));
+  const float alpha = *alpha_p;
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nblk = (K + kTl2BlockK - 1) / kTl2BlockK;
+  // x first: 12 consecutive values per super-block, then the weights
+  const XT* x = reinterpret_cast<const XT*>(xv);
+  Raw4<XT> xraw[NS][3];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int k0 = kTl2SuperK * s + 12 * lane + 4 * r;
+      raw_load4(x, (size_t)(k0 < K ? k0 : 0), xraw[s][r]);
+    }
+  uint4 widx[2 * NS];
+  unsigned wsign[2 * NS];
+  {
+    const int n = blockIdx.x * 16 + col;
+    const int nc = n < N ? n : N - 1;
+    const uint8_t* wrow = Wt + (size_t)nc * nblk * kTl2BlockBytes;
+#pragma unroll
+    for (int b = 0; b < 2 * NS; ++b) {
+      // a block past the row's end meets all-zero codes below
+      const uint8_t* blk = wrow + (b < nblk ? b : nblk - 1) * kTl2BlockBytes;
+      widx[b] = *reinterpret_cast<const uint4*>(blk + 16 * grp);
+      wsign[b] = *reinterpret_cast<const unsigned*>(blk + 64 + 4 * grp);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float v[NS][12];
+  float st = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const bool own = kTl2SuperK * s + 12 * lane + 4 * r < K;
+      float w4[4];
+      widen4(xraw[s][r], w4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[s][4 * r + e] = w4[e];
+      if (BITS == 8) {
+        const float m = fmaxf(fmaxf(fabsf(w4[0]), fabsf(w4[1])), fmaxf(fabsf(w4[2]), fabsf(w4[3])));
+        st = fmaxf(st, own ? m : 0.0f);
+      } else {
+        const float m = (fabsf(w4[0]) + fabsf(w4[1])) + (fabsf(w4[2]) + fabsf(w4[3]));
+        st += own ? m : 0.0f;
+      }
+    }
+  st = (BITS == 8) ? wave_reduce<true>(st) : wave_reduce<false>(st);
+  if (BITS == 4) st = st / (float)K;
+  st += kEps;
+  const float mult = c / st;
+  // Codes as in the 2-bit single-token kernel (magic-number rounding, med3
+  // clamp, the code in the sum's low byte).
+  constexpr float kMagic = 12582912.0f;
+  const float lo = kMagic + ((BITS == 8) ? -128.0f : -8.0f);
+  const float hi = kMagic + ((BITS == 8) ? 127.0f : 7.0f);
+  int qsum = 0;
+  // this lane's triplets in the super-block: block half bb, group g, slot i
+  const int bb = lane >> 5, g = (lane >> 3) & 3, i = lane & 7;
+  const int wbase = ((bb * 4 + g) * 2 + (i >> 2)) * 48 + 4 * (i & 3);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    unsigned b[12];
+#pragma unroll
+    for (int e = 0; e < 12; ++e) {
+      const bool own = kTl2SuperK * s + 12 * lane + e < K;
+      float pr = v[s][e] * mult;
+      asm volatile("" : "+v"(pr));
+      b[e] = own ? __float_as_uint(__builtin_amdgcn_fmed3f(pr + kMagic, lo, hi)) : 0u;
+    }
+    // word p: codes of the triplets' weights p (values p, p + 3, p + 6, p + 9)
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const unsigned word = __builtin_amdgcn_perm(b[p + 3], b[p], 0x0C0C0400u) |
+                            __builtin_amdgcn_perm(b[p + 9], b[p + 6], 0x04000C0Cu);
+      qsum = __builtin_amdgcn_sdot4((int)word, 0x01010101, qsum, false);
+      *reinterpret_cast<unsigned*>(qw + s * 768 + wbase + 16 * p) = word;
+    }
+  }
+  if (lane < 16) *reinterpret_cast<unsigned*>(qw + NS * 768 + 4 * lane) = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  {
+    float fs = __int_as_float(qsum);
+#define BITNET_ISUM(ctrl, rmask, bc)                                                            \
+  {                                                                                             \
+    const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(fs), ctrl, rmask, 0xF, bc);     \
+    fs = __int_as_float(__float_as_int(fs) + o);                                                \
+  }
+    BITNET_ISUM(0x111, 0xF, true)
+    BITNET_ISUM(0x112, 0xF, true)
+    BITNET_ISUM(0x114, 0xF, true)
+    BITNET_ISUM(0x118, 0xF, true)
+    BITNET_ISUM(0x142, 0xA, false)
+    BITNET_ISUM(0x143, 0xC, false)
+#undef BITNET_ISUM
+    qsum = __builtin_amdgcn_readlane(__float_as_int(fs), 63);
+  }
+
+  // MFMA operands: lane (col, grp) feeds column col's slots 4 h .. 4 h + 3 of
+  // group grp of each block; lanes of token row 0 (col == 0) feed the codes.
+  v4i acc1 = v4i{0, 0, 0, 0}, acc4 = v4i{0, 0, 0, 0}, acc16 = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int b = 0; b < 2 * NS; ++b) {
+    const unsigned iw[4] = {widx[b].x, widx[b].y, widx[b].z, widx[b].w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int8_t* qa = col == 0
+                             ? qw + (b >> 1) * 768 + (((b & 1) * 4 + grp) * 2 + h) * 48
+                             : qw + NS * 768;
+      const int step = col == 0 ? 16 : 0;
+      v4i u1, u4, u16;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int slot = 4 * h + sl;
+        const unsigned idx4 = (iw[slot >> 1] >> (4 * (slot & 1))) & 0x0F0F0F0Fu;
+        const unsigned f = slot_fields(idx4, wsign[b], slot);
+        u1[sl] = (int)(f & 0x03030303u);
+        u4[sl] = (int)(f & 0x0C0C0C0Cu);
+        u16[sl] = (int)(f & 0x30303030u);
+      }
+      acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i*>(qa), u1, acc1,
+                                                   0, 0, 0);
+      acc4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i*>(qa + step), u4,
+                                                   acc4, 0, 0, 0);
+      acc16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          *reinterpret_cast<const v4i*>(qa + 2 * step), u16, acc16, 0, 0, 0);
+    }
+  }
+  const int dot = acc1[0] + (acc4[0] >> 2) + (acc16[0] >> 4) - qsum;
+  const int n = blockIdx.x * 16 + col;
+  if (grp == 0 && n < N) y[n] = (float)dot * dequant_factor(alpha, st, c);
+}
+
+template <typename XT, int BITS, int NS>
+hipError_t launch_tl2_ns(const void* x, const uint8_t* Wt, const float* alpha, float* y, int K,
+                         int64_t N, hipStream_t stream) {
+  const float c = (BITS == 8) ? kScaleInt8 : kScaleInt4;
+  tl2_decode_kernel<XT, BITS, NS><<<dim3((unsigned)((N + 15) / 16)), dim3(64), 0, stream>>>(
+      x, Wt, alpha, y, K, (int)N, c);
+  return hipGetLastError();
+}
+
+template <typename XT, int BITS>
+hipError_t launch_tl2_t(const void* x, const uint8_t* Wt, const float* alpha, float* y, int K,
+                        int64_t N, hipStream_t stream) {
+  switch ((K + kTl2SuperK - 1) / kTl2SuperK) {
+    case 1: return launch_tl2_ns<XT, BITS, 1>(x, Wt, alpha, y, K, N, stream);
+    case 2: return launch_tl2_ns<XT, BITS, 2>(x, Wt, alpha, y, K, N, stream);
+    case 3: return launch_tl2_ns<XT, BITS, 3>(x, Wt, alpha, y, K, N, stream);
+    case 4: return launch_tl2_ns<XT, BITS, 4>(x, Wt, alpha, y, K, N, stream);
+    case 5: return launch_tl2_ns<XT, BITS, 5>(x, Wt, alpha, y, K, N, stream);
+    case 6: return launch_tl2_ns<XT, BITS, 6>(x, Wt, alpha, y, K, N, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t tl2_bytes(int64_t N, int64_t K) {
+  return (size_t)N * (size_t)((K + kTl2BlockK - 1) / kTl2BlockK) * kTl2BlockBytes;
+}
+
+hipError_t launch_repack_tl2(const uint8_t* Wpacked, int64_t N, int K, uint8_t* Wtl2,
+                             hipStream_t stream) {
+  const int nblk = (K + kTl2BlockK - 1) / kTl2BlockK;
+  const int64_t threads = N * nblk * 4;
+  if (threads == 0) return hipSuccess;
+  repack_tl2_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
+      Wpacked, N, K, nblk, Wtl2);
+  return hipGetLastError();
+}
+
+hipError_t launch_tl2_decode(const void* x, int x_dtype, int K, const uint8_t* Wtl2, int64_t N,
+                             const float* alpha, int bits, float* y, hipStream_t stream) {
+  if (K > kTl2MaxK) return hipErrorInvalidValue;
+  if (x_dtype == 1)
+    return bits == 8 ? launch_tl2_t<uint16_t, 8>(x, Wtl2, alpha, y, K, N, stream)
+                     : launch_tl2_t<uint16_t, 4>(x, Wtl2, alpha, y, K, N, stream);
+  return bits == 8 ? launch_tl2_t<float, 8>(x, Wtl2, alpha, y, K, N, stream)
+                   : launch_tl2_t<float, 4>(x, Wtl2, alpha, y, K, N, stream);
+}
+
+}  // namespace bitnet

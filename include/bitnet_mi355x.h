@@ -208,6 +208,40 @@ bitnet_status bitnet_quantize_activations_prologue(const void* x, const void* up
                                                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* TL2 weight code (1.67 bits per weight) for single-token decode            */
+/* ------------------------------------------------------------------------ */
+
+/* Edge page (bitnet_cpp_edge.py), module docstring item 2 and class
+ * SignedUnsignedWeightPacker: a ternary triplet (w0, w1, w2) is stored as the
+ * 4-bit index (0..13) of one of the page's 14 base triplets (all zero, or
+ * first non-zero element +1) and a sign bit that negates it, 5 bits per 3
+ * weights. Layout per output column: ceil(K / 384) blocks of 80 bytes, block
+ * b covering weights 384 b .. 384 b + 383 (triplet j: weights 384 b + 3 j +
+ * 0..2; weights past K are zero). Triplet j = 32 g + 4 i + tt keeps its index
+ * in bits 4 (i % 2) .. +3 of byte 16 g + 4 (i / 2) + tt and its sign in bit i
+ * of byte 64 + 4 g + tt. The row of a column is ceil(K / 384) * 80 bytes. */
+
+/* Bytes of a TL2 weight buffer for [N, K] (0 for invalid sizes). */
+size_t bitnet_tl2_bytes(int64_t N, int64_t K);
+
+/* Re-encode 2-bit packed weights (bitnet_ternarize_weights / bitnet_pack_2bit
+ * layout, [N, K/4]) as TL2 ([N, bitnet_tl2_bytes(N, K) / N] bytes, written).
+ * Requires K % 64 == 0; both pointers 16-byte aligned. The weights' alpha is
+ * unchanged. */
+bitnet_status bitnet_pack_tl2(const uint8_t* Wpacked, int64_t N, int64_t K, uint8_t* Wtl2,
+                              hipStream_t stream);
+
+/* Single-token decode forward on TL2 weights: the same result as
+ * bitnet_hbitlinear_forward with hadamard = 0 and M = 1 (same per-token
+ * codes, exact int32 product, y = acc * alpha * s / c), one kernel, no
+ * workspace. Requires M <= 1 (BITNET_ERR_UNSUPPORTED otherwise), K % 64 == 0,
+ * K <= 4608; x 16-byte aligned, Wtl2 16-byte aligned. */
+bitnet_status bitnet_hbitlinear_forward_tl2(const void* x, bitnet_dtype x_dtype, int64_t M,
+                                            int64_t K, const uint8_t* Wtl2, int64_t N,
+                                            const float* alpha, int bits, float* y,
+                                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Low-bit KV cache                                                          */
 /* ------------------------------------------------------------------------ */
 

@@ -286,3 +286,23 @@ def test_backward_optional_outputs(lib):
     assert _bwd(lib, dx=None, Wp=None, alpha=None, codes=None) == _lib.ERR_INVALID_ARG
     # no tokens and no weight gradient: dx has no elements
     assert _bwd(lib, M=0, dw=None, dy=None, ws=None) == _lib.OK
+
+
+def test_tl2_sizes_and_validation(lib):
+    # 80 bytes per column and 384-weight block (5 bits per 3 weights)
+    assert lib.bitnet_tl2_bytes(6912, 2560) == 6912 * 7 * 80
+    assert lib.bitnet_tl2_bytes(3, 384) == 3 * 80
+    assert lib.bitnet_tl2_bytes(3, 100) == 0            # K not a multiple of 64
+    assert lib.bitnet_tl2_bytes(0, 64) == 0
+    p = lib.bitnet_pack_tl2
+    assert p(None, 4, 64, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert p(FAKE, 4, 96, FAKE, None) == _lib.ERR_ALIGN
+    assert p(FAKE, 4, 64, FAKE + 8, None) == _lib.ERR_ALIGN
+    assert p(FAKE, 0, 64, None, None) == _lib.OK
+    f = lib.bitnet_hbitlinear_forward_tl2
+    assert f(FAKE, _lib.BF16, 2, 256, FAKE, 16, FAKE, 8, FAKE, None) == _lib.ERR_UNSUPPORTED
+    assert f(FAKE, _lib.BF16, 1, 4672, FAKE, 16, FAKE, 8, FAKE, None) == _lib.ERR_UNSUPPORTED
+    assert f(FAKE, _lib.BF16, 1, 256, FAKE, 16, FAKE, 5, FAKE, None) == _lib.ERR_BAD_BITS
+    assert f(FAKE, _lib.BF16, 1, 100, FAKE, 16, FAKE, 8, FAKE, None) == _lib.ERR_ALIGN
+    assert f(None, _lib.BF16, 1, 256, FAKE, 16, FAKE, 8, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert f(None, _lib.BF16, 0, 256, None, 16, None, 8, None, None) == _lib.OK
