@@ -382,7 +382,11 @@ def main():
         else:  # a single token runs the one-wave kernel, a few tokens the multi-wave one
             roof["kernel"] = "wave_decode_kernel" if wl.M == 1 else "fused_decode_kernel"
     else:
-        roof["kernel"] = "ternary_gemm_kernel"
+        # the library's dispatch: many 256x256 tiles (and the forward's row
+        # sums) take the streamed-tile kernel
+        tiles = ((wl.M + 255) // 256) * ((wl.N + 255) // 256)
+        stream = tiles >= 1024 and wl.K % 128 == 0 and wl.K >= 512 and wl.N % 4 == 0
+        roof["kernel"] = "ternary_gemm_stream_kernel" if stream else "ternary_gemm_kernel"
     roof["algorithmic"] = ("N*K/4 packed weight bytes per launch" if decode
                            else "2*M*N*K int8 ops per launch")
     roof["launch_us_mean"] = head["matmul_kernel_us_mean"]
@@ -392,6 +396,23 @@ def main():
     if source:
         roof["traffic_source"] = source
     _log(f"[bench] {key}: forward {head['forward_us']:.2f} us, matmul {head['matmul_kernel_us_mean']:.2f} us")
+    if decode and wl.M == 1 and not wl.hadamard and wl.K <= 4608:
+        # The same forward on the TL2 weight code (edge page: 5 bits per 3
+        # weights), re-encoded on the device from each cold 2-bit copy.
+        Wt = [bl.pack_tl2(w) for w in p.Wp]
+        tl2_ms = _time_steps(torch, lambda i: bl.hbitlinear_forward_tl2(
+            p.x, Wt[i % len(Wt)], p.alpha, wl.bits, out=p.y), args.steps, args.warmup)
+        tbytes = Wt[0].numel()
+        head["tl2"] = {
+            "forward_us": tl2_ms * 1e3,
+            "weight_bytes": tbytes,
+            "bits_per_weight": tbytes * 8 / (wl.N * wl.K),
+            "weight_GBs": tbytes / (tl2_ms * 1e-3) / 1e9,
+            "vs_2bit_forward": head["forward_us"] / (tl2_ms * 1e3),
+            "kernel": "tl2_decode_kernel",
+        }
+        _log(f"[bench] {key}: TL2 forward {tl2_ms * 1e3:.2f} us ({tbytes} weight bytes)")
+        del Wt
     del p
 
     per = {key: head}

@@ -109,10 +109,10 @@ __device__ __forceinline__ unsigned slot_fields(unsigned idx4, unsigned sign4, i
 }
 
 // Single-token decode forward on TL2 weights: one wave per 16 columns and
-// all of K (NS 768-weight super-blocks, K <= 768 NS). Quantization as in the
-// 2-bit single-token kernel (Eq. 5 / Eq. 6), with each lane owning 12
-// consecutive values per super-block.
-template <typename XT, int BITS, int NS>
+// all of K (NB = ceil(K / 384) blocks in NS = ceil(NB / 2) 768-weight
+// super-blocks). Quantization as in the 2-bit single-token kernel (Eq. 5 /
+// Eq. 6), with each lane owning 12 consecutive values per super-block.
+template <typename XT, int BITS, int NB>
 __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__ xv,
                                                         const uint8_t* __restrict__ Wt,
                                                         const float* __restrict__ alpha_p,
@@ -120,12 +120,12 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
                                                         float c) {
   // codes per super-block: [bb][g][h][p] 16-byte words (768 B), then 64 zero
   // bytes read by the lanes that feed the dead MFMA rows
+  constexpr int NS = (NB + 1) / 2;
   __shared__ __attribute__((aligned(16))) int8_t qw[NS * 768 + 64];
   asm volatile("" ::"s"(K), "s"(N), "s"(c), "s"(y), "s"(xv), "s"(Wt));
   const float alpha = *alpha_p;
   const int lane = threadIdx.x;
   const int col = lane & 15, grp = lane >> 4;
-  const int nblk = (K + kTl2BlockK - 1) / kTl2BlockK;
   // x first: 12 consecutive values per super-block, then the weights
   const XT* x = reinterpret_cast<const XT*>(xv);
   Raw4<XT> xraw[NS][3];
@@ -136,16 +136,15 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
       const int k0 = kTl2SuperK * s + 12 * lane + 4 * r;
       raw_load4(x, (size_t)(k0 < K ? k0 : 0), xraw[s][r]);
     }
-  uint4 widx[2 * NS];
-  unsigned wsign[2 * NS];
+  uint4 widx[NB];
+  unsigned wsign[NB];
   {
     const int n = blockIdx.x * 16 + col;
     const int nc = n < N ? n : N - 1;
-    const uint8_t* wrow = Wt + (size_t)nc * nblk * kTl2BlockBytes;
+    const uint8_t* wrow = Wt + (size_t)nc * NB * kTl2BlockBytes;
 #pragma unroll
-    for (int b = 0; b < 2 * NS; ++b) {
-      // a block past the row's end meets all-zero codes below
-      const uint8_t* blk = wrow + (b < nblk ? b : nblk - 1) * kTl2BlockBytes;
+    for (int b = 0; b < NB; ++b) {
+      const uint8_t* blk = wrow + b * kTl2BlockBytes;
       widx[b] = *reinterpret_cast<const uint4*>(blk + 16 * grp);
       wsign[b] = *reinterpret_cast<const unsigned*>(blk + 64 + 4 * grp);
     }
@@ -226,7 +225,7 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
   // group grp of each block; lanes of token row 0 (col == 0) feed the codes.
   v4i acc1 = v4i{0, 0, 0, 0}, acc4 = v4i{0, 0, 0, 0}, acc16 = v4i{0, 0, 0, 0};
 #pragma unroll
-  for (int b = 0; b < 2 * NS; ++b) {
+  for (int b = 0; b < NB; ++b) {
     const unsigned iw[4] = {widx[b].x, widx[b].y, widx[b].z, widx[b].w};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -257,11 +256,11 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
   if (grp == 0 && n < N) y[n] = (float)dot * dequant_factor(alpha, st, c);
 }
 
-template <typename XT, int BITS, int NS>
-hipError_t launch_tl2_ns(const void* x, const uint8_t* Wt, const float* alpha, float* y, int K,
+template <typename XT, int BITS, int NB>
+hipError_t launch_tl2_nb(const void* x, const uint8_t* Wt, const float* alpha, float* y, int K,
                          int64_t N, hipStream_t stream) {
   const float c = (BITS == 8) ? kScaleInt8 : kScaleInt4;
-  tl2_decode_kernel<XT, BITS, NS><<<dim3((unsigned)((N + 15) / 16)), dim3(64), 0, stream>>>(
+  tl2_decode_kernel<XT, BITS, NB><<<dim3((unsigned)((N + 15) / 16)), dim3(64), 0, stream>>>(
       x, Wt, alpha, y, K, (int)N, c);
   return hipGetLastError();
 }
@@ -269,13 +268,13 @@ hipError_t launch_tl2_ns(const void* x, const uint8_t* Wt, const float* alpha, f
 template <typename XT, int BITS>
 hipError_t launch_tl2_t(const void* x, const uint8_t* Wt, const float* alpha, float* y, int K,
                         int64_t N, hipStream_t stream) {
-  switch ((K + kTl2SuperK - 1) / kTl2SuperK) {
-    case 1: return launch_tl2_ns<XT, BITS, 1>(x, Wt, alpha, y, K, N, stream);
-    case 2: return launch_tl2_ns<XT, BITS, 2>(x, Wt, alpha, y, K, N, stream);
-    case 3: return launch_tl2_ns<XT, BITS, 3>(x, Wt, alpha, y, K, N, stream);
-    case 4: return launch_tl2_ns<XT, BITS, 4>(x, Wt, alpha, y, K, N, stream);
-    case 5: return launch_tl2_ns<XT, BITS, 5>(x, Wt, alpha, y, K, N, stream);
-    case 6: return launch_tl2_ns<XT, BITS, 6>(x, Wt, alpha, y, K, N, stream);
+  switch ((K + kTl2BlockK - 1) / kTl2BlockK) {
+#define BITNET_TL2_CASE(nb) \
+  case nb: return launch_tl2_nb<XT, BITS, nb>(x, Wt, alpha, y, K, N, stream);
+    BITNET_TL2_CASE(1) BITNET_TL2_CASE(2) BITNET_TL2_CASE(3) BITNET_TL2_CASE(4)
+    BITNET_TL2_CASE(5) BITNET_TL2_CASE(6) BITNET_TL2_CASE(7) BITNET_TL2_CASE(8)
+    BITNET_TL2_CASE(9) BITNET_TL2_CASE(10) BITNET_TL2_CASE(11) BITNET_TL2_CASE(12)
+#undef BITNET_TL2_CASE
     default: return hipErrorInvalidValue;
   }
 }
