@@ -60,6 +60,9 @@
 namespace bitnet {
 namespace {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 constexpr int BKW = 128;     // k per wave slice per stage
 constexpr int kChunks = 8;   // MFMA groups per block in the interleaved schedule
 
@@ -107,7 +110,7 @@ __device__ __forceinline__ int add_bytes(const v4i a, int s) {
   return __builtin_amdgcn_sdot4(a.w, 0x01010101, s, false);
 }
 
-template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG>
+template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG, bool WIDE>
 __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ scales, int M, int K,
     const uint8_t* __restrict__ Wp, int N, const float* __restrict__ alpha_p, float c,
@@ -394,6 +397,58 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
   // 32x32 output layout: lane holds column l32 and, for v = 0..15, row
   // 8*(v/4) + 4*g + v%4 of its 32x32 block. q . t = q . u - sum(q).
   const float alpha = OUT_I32 ? 0.0f : *alpha_p;
+  if constexpr (WIDE && !OUT_I32) {
+    // Wide stores (N % 4 == 0, y 16-byte aligned): each 32x32 block is turned
+    // around, 16 rows at a time, through this wave's 2.5 KB of the (drained)
+    // LDS ring, so that a lane stores 16 contiguous bytes of one row: a
+    // quarter of the store instructions. Rows past M fall outside the store
+    // resource; groups of four columns past N get an out-of-range offset.
+    constexpr int TP = 40;  // row pitch in floats: rows r and r + 4 on opposite bank halves
+    float* tb = reinterpret_cast<float*>(smem) + wmn * 16 * TP;
+    const int rows = (M - m0 < S::BM) ? M - m0 : S::BM;
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc(y + (size_t)m0 * N, (short)0, rows * N * 4, 0x00020000);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int rb = wm * 32 * RT + rt * 32;
+      float f[16];
+      int rsv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = rb + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int m = m0 + r < M ? m0 + r : M - 1;
+        int rs = 0;
+        if constexpr (RSG) {
+          rs = rowsum_g[m];
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) rs += rowsum[s * S::BM + r];
+        }
+        rsv[v] = rs;
+        f[v] = dequant_factor(alpha, scales[m], c);
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int nc = n0 + wn * 32 * CT + ct * 32 + 4 * (lane & 7);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int vv = 0; vv < 8; ++vv) {
+            const int v = 8 * h + vv;
+            tb[(8 * (vv >> 2) + 4 * g + (vv & 3)) * TP + l32] = (float)(acc[rt][ct][v] - rsv[v]) * f[v];
+          }
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int r = 8 * jj + (lane >> 3);
+            const v4f o = *reinterpret_cast<const v4f*>(tb + r * TP + 4 * (lane & 7));
+            const int off = nc < N ? ((rb + 16 * h + r) * N + nc) * 4 : (int)0x80000000;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, o), yr, off, 0, 0);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
@@ -467,9 +522,6 @@ struct StreamShape {
   static_assert(LDS <= kLdsMax, "LDS");
   static_assert((S::SL - 1) * NLG + STORES <= 63, "vmcnt range");
 };
-
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 template <int RT, int CT, int WMW, int WNW>
 __global__ __launch_bounds__(64 * WMW * WNW) void ternary_gemm_stream_kernel(
@@ -741,7 +793,7 @@ __global__ __launch_bounds__(64 * WMW * WNW) void ternary_gemm_stream_kernel(
 #undef BITNET_SSTEP
 }
 
-template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG>
+template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG, bool WIDE = false>
 hipError_t launch_tile(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, float c, float* y,
                        int32_t* acc, const int32_t* rowsum, hipStream_t stream) {
@@ -750,7 +802,7 @@ hipError_t launch_tile(const int8_t* codes, const float* scales, int64_t M, int 
   const int tiles_n = (int)((N + S::BN - 1) / S::BN);
   const int tiles = tiles_m * tiles_n;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  auto kern = ternary_gemm_kernel<RT, CT, WMW, WNW, KS, OUT_I32, RSG>;
+  auto kern = ternary_gemm_kernel<RT, CT, WMW, WNW, KS, OUT_I32, RSG, WIDE>;
   if (S::LDS > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
@@ -768,9 +820,20 @@ hipError_t launch_variant(const int8_t* codes, const float* scales, int64_t M, i
   if (acc)
     return launch_tile<RT, CT, WMW, WNW, KS, true, false>(codes, scales, M, K, Wpacked, N, alpha,
                                                           c, y, acc, nullptr, stream);
-  if (rowsum)
+  // wide stores need whole groups of four columns and 16-byte rows
+  const bool wide = N % 4 == 0 && N <= (1 << 20) && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+  if (rowsum) {
+    if (wide)
+      return launch_tile<RT, CT, WMW, WNW, KS, false, true, true>(codes, scales, M, K, Wpacked, N,
+                                                                  alpha, c, y, nullptr, rowsum,
+                                                                  stream);
     return launch_tile<RT, CT, WMW, WNW, KS, false, true>(codes, scales, M, K, Wpacked, N, alpha,
                                                           c, y, nullptr, rowsum, stream);
+  }
+  if (wide)
+    return launch_tile<RT, CT, WMW, WNW, KS, false, false, true>(codes, scales, M, K, Wpacked, N,
+                                                                 alpha, c, y, nullptr, nullptr,
+                                                                 stream);
   return launch_tile<RT, CT, WMW, WNW, KS, false, false>(codes, scales, M, K, Wpacked, N, alpha, c,
                                                          y, nullptr, nullptr, stream);
 }
