@@ -108,25 +108,36 @@ __device__ __forceinline__ unsigned slot_fields(unsigned idx4, unsigned sign4, i
   return (neg & (0x2A2A2A2Au - f)) | (~neg & f);
 }
 
-// Single-token decode forward on TL2 weights: one wave per 16 columns and
-// all of K (NB = ceil(K / 384) blocks in NS = ceil(NB / 2) 768-weight
-// super-blocks). Quantization as in the 2-bit single-token kernel (Eq. 5 /
-// Eq. 6), with each lane owning 12 consecutive values per super-block.
-template <typename XT, int BITS, int NB>
-__global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__ xv,
-                                                        const uint8_t* __restrict__ Wt,
-                                                        const float* __restrict__ alpha_p,
-                                                        float* __restrict__ y, int K, int N,
-                                                        float c) {
-  // codes per super-block: [bb][g][h][p] 16-byte words (768 B), then 64 zero
-  // bytes read by the lanes that feed the dead MFMA rows
+// Single-token decode forward on TL2 weights: WV waves per 16 columns (NB =
+// ceil(K / 384) blocks in NS = ceil(NB / 2) 768-weight super-blocks; wave w
+// takes super-blocks w NSW .. w NSW + NSW - 1). Every wave reduces the
+// per-token statistic over all of x itself (the same fixed order, so the
+// same value) and quantizes only its own super-blocks; with two waves, one
+// barrier adds their dot products. Quantization as in the 2-bit single-token
+// kernel (Eq. 5 / Eq. 6), with each lane owning 12 consecutive values per
+// super-block.
+template <typename XT, int BITS, int NB, int WV>
+__global__ __launch_bounds__(64 * WV) void tl2_decode_kernel(const void* __restrict__ xv,
+                                                             const uint8_t* __restrict__ Wt,
+                                                             const float* __restrict__ alpha_p,
+                                                             float* __restrict__ y, int K, int N,
+                                                             float c) {
   constexpr int NS = (NB + 1) / 2;
-  __shared__ __attribute__((aligned(16))) int8_t qw[NS * 768 + 64];
+  constexpr int NSW = (NS + WV - 1) / WV;  // super-blocks per wave
+  // codes per wave and super-block: [bb][g][h][p] 16-byte words (768 B), then
+  // 64 zero bytes read by the lanes that feed the dead MFMA rows
+  __shared__ __attribute__((aligned(16))) int8_t qw_all[WV * NSW * 768 + 64];
+  __shared__ int part[16];
   asm volatile("" ::"s"(K), "s"(N), "s"(c), "s"(y), "s"(xv), "s"(Wt));
   const float alpha = *alpha_p;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  // x first: 12 consecutive values per super-block, then the weights
+  const int s0 = wave * NSW;  // this wave's first super-block
+  int8_t* qw = qw_all + wave * NSW * 768;
+  int8_t* const qzero = qw_all + WV * NSW * 768;
+  // x first: 12 consecutive values per super-block (all of them for the
+  // statistic, and again this wave's own for its codes), then the weights
   const XT* x = reinterpret_cast<const XT*>(xv);
   Raw4<XT> xraw[NS][3];
 #pragma unroll
@@ -136,22 +147,34 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
       const int k0 = kTl2SuperK * s + 12 * lane + 4 * r;
       raw_load4(x, (size_t)(k0 < K ? k0 : 0), xraw[s][r]);
     }
-  uint4 widx[NB];
-  unsigned wsign[NB];
+  Raw4<XT> xown[WV > 1 ? NSW : 1][3];
+  if constexpr (WV > 1) {
+#pragma unroll
+    for (int s = 0; s < NSW; ++s)
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        const int k0 = kTl2SuperK * (s0 + s) + 12 * lane + 4 * r;
+        raw_load4(x, (size_t)(k0 < K ? k0 : 0), xown[s][r]);
+      }
+  }
+  uint4 widx[2 * NSW];
+  unsigned wsign[2 * NSW];
   {
     const int n = blockIdx.x * 16 + col;
     const int nc = n < N ? n : N - 1;
     const uint8_t* wrow = Wt + (size_t)nc * NB * kTl2BlockBytes;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const uint8_t* blk = wrow + b * kTl2BlockBytes;
+    for (int b = 0; b < 2 * NSW; ++b) {
+      // a block past the row's end meets all-zero codes below
+      const int bg = 2 * s0 + b;
+      const uint8_t* blk = wrow + (bg < NB ? bg : NB - 1) * kTl2BlockBytes;
       widx[b] = *reinterpret_cast<const uint4*>(blk + 16 * grp);
       wsign[b] = *reinterpret_cast<const unsigned*>(blk + 64 + 4 * grp);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  float v[NS][12];
+  float v[NSW][12];
   float st = 0.0f;
 #pragma unroll
   for (int s = 0; s < NS; ++s)
@@ -160,8 +183,10 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
       const bool own = kTl2SuperK * s + 12 * lane + 4 * r < K;
       float w4[4];
       widen4(xraw[s][r], w4);
+      if constexpr (WV == 1) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[s][4 * r + e] = w4[e];
+        for (int e = 0; e < 4; ++e) v[s][4 * r + e] = w4[e];
+      }
       if (BITS == 8) {
         const float m = fmaxf(fmaxf(fabsf(w4[0]), fabsf(w4[1])), fmaxf(fabsf(w4[2]), fabsf(w4[3])));
         st = fmaxf(st, own ? m : 0.0f);
@@ -170,6 +195,17 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
         st += own ? m : 0.0f;
       }
     }
+  if constexpr (WV > 1) {
+#pragma unroll
+    for (int s = 0; s < NSW; ++s)
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        float w4[4];
+        widen4(xown[s][r], w4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[s][4 * r + e] = w4[e];
+      }
+  }
   st = (BITS == 8) ? wave_reduce<true>(st) : wave_reduce<false>(st);
   if (BITS == 4) st = st / (float)K;
   st += kEps;
@@ -184,11 +220,11 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
   const int bb = lane >> 5, g = (lane >> 3) & 3, i = lane & 7;
   const int wbase = ((bb * 4 + g) * 2 + (i >> 2)) * 48 + 4 * (i & 3);
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
+  for (int s = 0; s < NSW; ++s) {
     unsigned b[12];
 #pragma unroll
     for (int e = 0; e < 12; ++e) {
-      const bool own = kTl2SuperK * s + 12 * lane + e < K;
+      const bool own = kTl2SuperK * (s0 + s) + 12 * lane + e < K;
       float pr = v[s][e] * mult;
       asm volatile("" : "+v"(pr));
       b[e] = own ? __float_as_uint(__builtin_amdgcn_fmed3f(pr + kMagic, lo, hi)) : 0u;
@@ -202,7 +238,7 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
       *reinterpret_cast<unsigned*>(qw + s * 768 + wbase + 16 * p) = word;
     }
   }
-  if (lane < 16) *reinterpret_cast<unsigned*>(qw + NS * 768 + 4 * lane) = 0u;
+  if (lane < 16) *reinterpret_cast<unsigned*>(qzero + 4 * lane) = 0u;  // each wave, before its own reads
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   {
     float fs = __int_as_float(qsum);
@@ -225,13 +261,14 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
   // group grp of each block; lanes of token row 0 (col == 0) feed the codes.
   v4i acc1 = v4i{0, 0, 0, 0}, acc4 = v4i{0, 0, 0, 0}, acc16 = v4i{0, 0, 0, 0};
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
+  for (int b = 0; b < 2 * NSW; ++b) {
+    if (2 * s0 + b >= NB) break;  // past the row (uniform)
     const unsigned iw[4] = {widx[b].x, widx[b].y, widx[b].z, widx[b].w};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int8_t* qa = col == 0
                              ? qw + (b >> 1) * 768 + (((b & 1) * 4 + grp) * 2 + h) * 48
-                             : qw + NS * 768;
+                             : qzero;
       const int step = col == 0 ? 16 : 0;
       v4i u1, u4, u16;
 #pragma unroll
@@ -251,17 +288,23 @@ __global__ __launch_bounds__(64) void tl2_decode_kernel(const void* __restrict__
           *reinterpret_cast<const v4i*>(qa + 2 * step), u16, acc16, 0, 0, 0);
     }
   }
-  const int dot = acc1[0] + (acc4[0] >> 2) + (acc16[0] >> 4) - qsum;
+  int dot = acc1[0] + (acc4[0] >> 2) + (acc16[0] >> 4) - qsum;
+  if constexpr (WV == 2) {
+    if (wave == 1 && grp == 0) part[col] = dot;
+    lds_barrier();
+    if (wave == 1) return;
+    dot += part[col];
+  }
   const int n = blockIdx.x * 16 + col;
   if (grp == 0 && n < N) y[n] = (float)dot * dequant_factor(alpha, st, c);
 }
 
-template <typename XT, int BITS, int NB>
+template <typename XT, int BITS, int NB, int WV = (NB >= 4 ? 2 : 1)>
 hipError_t launch_tl2_nb(const void* x, const uint8_t* Wt, const float* alpha, float* y, int K,
                          int64_t N, hipStream_t stream) {
   const float c = (BITS == 8) ? kScaleInt8 : kScaleInt4;
-  tl2_decode_kernel<XT, BITS, NB><<<dim3((unsigned)((N + 15) / 16)), dim3(64), 0, stream>>>(
-      x, Wt, alpha, y, K, (int)N, c);
+  tl2_decode_kernel<XT, BITS, NB, WV><<<dim3((unsigned)((N + 15) / 16)), dim3(64 * WV), 0,
+                                        stream>>>(x, Wt, alpha, y, K, (int)N, c);
   return hipGetLastError();
 }
 
