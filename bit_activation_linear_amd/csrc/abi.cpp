@@ -229,7 +229,7 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
   if (need == 0) {
     return hip_status(bitnet::launch_fused_decode(x, (int)x_dtype, M, (int)K, Wpacked, N, alpha,
-                                                  bits, y, stream),
+                                                  bits, y, stream, nullptr, hadamard),
                       fn);
   }
   const ForwardWorkspace w = carve_forward(ws, M, K);
@@ -448,7 +448,7 @@ bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, 
   const bitnet::Prologue pro{up, rmsnorm ? norm_weight : nullptr, norm_eps, rmsnorm};
   if (forward_is_fused(M, K, N, hadamard)) {
     return hip_status(bitnet::launch_fused_decode(x, (int)x_dtype, M, (int)K, Wpacked, N, alpha,
-                                                  bits, y, stream, &pro),
+                                                  bits, y, stream, &pro, hadamard),
                       fn);
   }
   const ForwardWorkspace w = carve_forward(ws, M, K);

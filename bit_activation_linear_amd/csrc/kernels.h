@@ -19,6 +19,8 @@ constexpr int64_t kDecodeMaxM = 16;
 // Largest M*K whose quantization the decode kernel fuses in (the codes of the
 // whole batch sit in the workgroup's LDS).
 constexpr int64_t kFusedMaxElems = 16384;
+// Largest K the fused decode kernel transforms (one wave holds a token row).
+constexpr int64_t kFusedHadMaxK = 256;
 
 // Work decomposition of the decode (M <= 16) product. A workgroup owns `ct`
 // 16-column tiles and all of K; `sb_waves` waves take interleaved 256-k
@@ -38,7 +40,8 @@ inline GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, bool x_given, bool ha
   p.sb_waves = (int)(nSB < 16 ? nSB : 16);
   // Fusing keeps every token's codes in LDS and needs one 4-element chunk per
   // thread and row: K <= 4 * 64 * sb_waves, i.e. a single round of waves.
-  p.fused = x_given && !hadamard && M * K <= kFusedMaxElems && nSB <= 16;
+  // With the transform, a whole token row must sit in one wave: K <= 256.
+  p.fused = x_given && (!hadamard || K <= kFusedHadMaxK) && M * K <= kFusedMaxElems && nSB <= 16;
   p.ct = 1;
   p.col_groups = (int)((N + 16 * p.ct - 1) / (16 * p.ct));
   int waves = p.sb_waves;
@@ -107,7 +110,8 @@ hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int 
 // Decode forward with the quantization fused in (plan.fused must hold).
 hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
                                const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
-                               float* y, hipStream_t stream, const Prologue* pro = nullptr);
+                               float* y, hipStream_t stream, const Prologue* pro = nullptr,
+                               int hadamard = 0);
 
 // ---- Backward -------------------------------------------------------------
 

@@ -215,7 +215,7 @@ __device__ __forceinline__ void load4(const uint16_t* x, size_t i, float (&v)[4]
 // the lanes that feed them to the MFMA through a wave-private LDS region (no
 // further barrier), so little work separates the arrival of the data from
 // the product.
-template <typename XT, int BITS, int MG, int CT, int SBW, bool PRO>
+template <typename XT, int BITS, int MG, int CT, int SBW, bool PRO, bool HAD>
 __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue pro) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // The scalars the kernel needs (kernel arguments and alpha) are fetched
@@ -334,6 +334,57 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
     }
   }
 
+  // Walsh-Hadamard transform (engine page Eq. 3-4; HAD needs K <= 256, so
+  // one wave holds every token row whole: lane l has elements 4 l .. 4 l + 3).
+  // Index bits 0-1 are butterflied in registers, bits 2-7 across lanes, in
+  // bit order and with the same (a + b, a - b) steps as the transform kernel,
+  // so the unnormalized values are the same bit for bit; the 1/sqrt(K) goes
+  // into the scale and the code multiplier below.
+  if constexpr (HAD) {
+#pragma unroll
+    for (int m = 0; m < MG; ++m) {
+#pragma unroll
+      for (int h = 1; h < 4; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((e & h) == 0) {
+            const float x0 = v[m][0][e], x1 = v[m][0][e + h];
+            v[m][0][e] = x0 + x1;
+            v[m][0][e + h] = x0 - x1;
+          }
+    }
+    // Lane stages (lane bit i = index bit i + 2), every token row's exchanges
+    // of a stage issued together: partners within a row of 16 lanes through
+    // DPP (quad permutes for 1 and 2, row shifts for 4 and 8), across rows
+    // through ds_bpermute.
+#define BITNET_HAD_DPP(mk, lo_ctrl, hi_ctrl)                                                      \
+    if (4 * (mk) < a.K) {                                                                        \
+      _Pragma("unroll") for (int m = 0; m < MG; ++m)                                             \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                            \
+        const int vi = __float_as_int(v[m][0][e]);                                               \
+        const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, vi, lo_ctrl, 0xF, 0xF, true)); \
+        const float dn = __int_as_float(__builtin_amdgcn_update_dpp(0, vi, hi_ctrl, 0xF, 0xF, true)); \
+        v[m][0][e] = (lane & (mk)) ? dn - v[m][0][e] : v[m][0][e] + up;                          \
+      }                                                                                          \
+    }
+    BITNET_HAD_DPP(1, 0xB1, 0xB1)    // quad_perm [1,0,3,2]
+    BITNET_HAD_DPP(2, 0x4E, 0x4E)    // quad_perm [2,3,0,1]
+    BITNET_HAD_DPP(4, 0x104, 0x114)  // row_shl:4 (partner l + 4), row_shr:4 (l - 4)
+    BITNET_HAD_DPP(8, 0x108, 0x118)  // row_shl:8, row_shr:8
+#undef BITNET_HAD_DPP
+    for (int mk = 16; 4 * mk < a.K; mk <<= 1) {
+      float o[MG][4];
+#pragma unroll
+      for (int m = 0; m < MG; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[m][e] = __shfl_xor(v[m][0][e], mk);
+#pragma unroll
+      for (int m = 0; m < MG; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[m][0][e] = (lane & mk) ? o[m][e] - v[m][0][e] : v[m][0][e] + o[m][e];
+    }
+  }
+
   // Partial statistic of this wave's super-blocks, one per token row.
 #pragma unroll
   for (int m = 0; m < MG; ++m) {
@@ -372,7 +423,23 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
       for (int w = 0; w < nw; ++w) s = (BITS == 8) ? fmaxf(s, part[w * 16 + m]) : s + part[w * 16 + m];
       if (BITS == 4) s = s / (float)a.K;
       float mult;
-      if (PRO && pro.rms) {
+      if constexpr (HAD) {
+        // the transform kernel's arithmetic: norm = prod of log2 K factors 1/sqrt2
+        const int L = 31 - __builtin_clz(a.K);
+        float norm = __builtin_ldexpf(1.0f, -(L >> 1));
+        if (L & 1) norm *= 0.70710678118654752f;
+        if (PRO && pro.rms) {
+          float q = 0.0f;
+          for (int w = 0; w < nw; ++w) q += psq[w * 16 + m];
+          const float sraw = s * norm;
+          const float rms = sqrtf(q / (float)a.K + pro.norm_eps);
+          mult = (a.c * norm) / (sraw + kEps * rms);
+          s = sraw / rms + kEps;
+        } else {
+          s = s * norm + kEps;
+          mult = (a.c * norm) / s;
+        }
+      } else if (PRO && pro.rms) {
         float q = 0.0f;
         for (int w = 0; w < nw; ++w) q += psq[w * 16 + m];
         const float rms = sqrtf(q / (float)a.K + pro.norm_eps);
@@ -613,14 +680,14 @@ hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stre
   return hipGetLastError();
 }
 
-template <typename XT, int BITS, int MG, int CT, int SBW, bool PRO>
+template <typename XT, int BITS, int MG, int CT, int SBW, bool PRO, bool HAD>
 hipError_t launch_fused_ct(const GemvArgs& a, const Prologue& pro, hipStream_t stream) {
   const int nSB = ((a.K >> 6) + 3) >> 2;
   // at least CT waves: the finish stores column tile ct from wave ct
   const int nw = (nSB + SBW - 1) / SBW > CT ? (nSB + SBW - 1) / SBW : CT;
   const size_t lds = (size_t)nw * CT * 1024 + (size_t)nw * 16 * 4 + 64 +
                      (PRO ? (size_t)nw * 16 * 4 : 0) + (size_t)nw * SBW * a.M * 256;
-  auto kern = fused_decode_kernel<XT, BITS, MG, CT, SBW, PRO>;
+  auto kern = fused_decode_kernel<XT, BITS, MG, CT, SBW, PRO, HAD>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   const unsigned groups = (unsigned)((a.N + 16 * CT - 1) / (16 * CT));
@@ -659,12 +726,16 @@ bool try_launch_wave(const GemvArgs& a, const Prologue* pro, hipStream_t stream,
 }
 
 template <typename XT, int BITS, int MG>
-hipError_t launch_fused_t(const GemvArgs& a, const Prologue* pro, hipStream_t stream) {
+hipError_t launch_fused_t(const GemvArgs& a, const Prologue* pro, hipStream_t stream, bool had) {
+  const Prologue none{nullptr, nullptr, 0.0f, 0};
+  if (had) {
+    if (pro) return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, true, true>(a, *pro, stream);
+    return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, false, true>(a, none, stream);
+  }
   hipError_t err = hipSuccess;
   if (try_launch_wave<XT, BITS>(a, pro, stream, &err)) return err;
-  if (pro) return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, true>(a, *pro, stream);
-  const Prologue none{nullptr, nullptr, 0.0f, 0};
-  return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, false>(a, none, stream);
+  if (pro) return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, true, false>(a, *pro, stream);
+  return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, false, false>(a, none, stream);
 }
 
 }  // namespace
@@ -690,8 +761,9 @@ hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int 
 
 hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
                                const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
-                               float* y, hipStream_t stream, const Prologue* pro) {
-  const GemvPlan p = plan_gemv(M, K, N, true, false);
+                               float* y, hipStream_t stream, const Prologue* pro, int hadamard) {
+  const bool had = hadamard != 0;
+  const GemvPlan p = plan_gemv(M, K, N, true, had);
   if (!p.fused) return hipErrorInvalidValue;
   GemvArgs a{};
   a.x = x;
@@ -705,23 +777,23 @@ hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
   a.c = (bits == 8) ? kScaleInt8 : kScaleInt4;
   if (M == 1) {  // single token: the smallest code, which a cold launch fetches fastest
     if (x_dtype == 1)
-      return bits == 8 ? launch_fused_t<uint16_t, 8, 1>(a, pro, stream)
-                       : launch_fused_t<uint16_t, 4, 1>(a, pro, stream);
-    return bits == 8 ? launch_fused_t<float, 8, 1>(a, pro, stream)
-                     : launch_fused_t<float, 4, 1>(a, pro, stream);
+      return bits == 8 ? launch_fused_t<uint16_t, 8, 1>(a, pro, stream, had)
+                       : launch_fused_t<uint16_t, 4, 1>(a, pro, stream, had);
+    return bits == 8 ? launch_fused_t<float, 8, 1>(a, pro, stream, had)
+                     : launch_fused_t<float, 4, 1>(a, pro, stream, had);
   }
   if (M <= 4) {
     if (x_dtype == 1)
-      return bits == 8 ? launch_fused_t<uint16_t, 8, 4>(a, pro, stream)
-                       : launch_fused_t<uint16_t, 4, 4>(a, pro, stream);
-    return bits == 8 ? launch_fused_t<float, 8, 4>(a, pro, stream)
-                     : launch_fused_t<float, 4, 4>(a, pro, stream);
+      return bits == 8 ? launch_fused_t<uint16_t, 8, 4>(a, pro, stream, had)
+                       : launch_fused_t<uint16_t, 4, 4>(a, pro, stream, had);
+    return bits == 8 ? launch_fused_t<float, 8, 4>(a, pro, stream, had)
+                     : launch_fused_t<float, 4, 4>(a, pro, stream, had);
   }
   if (x_dtype == 1)
-    return bits == 8 ? launch_fused_t<uint16_t, 8, 16>(a, pro, stream)
-                     : launch_fused_t<uint16_t, 4, 16>(a, pro, stream);
-  return bits == 8 ? launch_fused_t<float, 8, 16>(a, pro, stream)
-                   : launch_fused_t<float, 4, 16>(a, pro, stream);
+    return bits == 8 ? launch_fused_t<uint16_t, 8, 16>(a, pro, stream, had)
+                     : launch_fused_t<uint16_t, 4, 16>(a, pro, stream, had);
+  return bits == 8 ? launch_fused_t<float, 8, 16>(a, pro, stream, had)
+                   : launch_fused_t<float, 4, 16>(a, pro, stream, had);
 }
 
 }  // namespace bitnet

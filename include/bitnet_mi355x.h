@@ -105,8 +105,9 @@ bitnet_status bitnet_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* W
 /* Bytes of workspace bitnet_hbitlinear_forward needs: the int8 codes, fp32
  * scales and int32 code row sums of the batch (M*K, 4*M and 4*M bytes, each
  * rounded up to 256). It is 0
- * when the forward runs as a single fused kernel (M <= 16, hadamard = 0,
- * M*K <= 16384, K <= 4096); ws may then be NULL. Returns 0 for invalid sizes. */
+ * when the forward runs as a single fused kernel (M <= 16, M*K <= 16384,
+ * K <= 4096, and hadamard = 0 or K <= 256); ws may then be NULL. Returns 0
+ * for invalid sizes. */
 size_t bitnet_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits, int hadamard);
 
 /* H-BitLinear forward (engine page, HBitLinear.forward after its RMSNorm;

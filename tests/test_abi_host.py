@@ -33,7 +33,9 @@ def test_version_and_empty_error(lib):
 
 def test_workspace_sizes(lib):
     # codes M*K bytes + scales 4*M bytes, each rounded up to 256 B
-    assert lib.bitnet_forward_workspace_bytes(4, 256, 256, 4, 1) == 1024 + 2 * 256
+    # with the transform, K <= 256 keeps a token row in one wave: fused, no workspace
+    assert lib.bitnet_forward_workspace_bytes(4, 256, 256, 4, 1) == 0
+    assert lib.bitnet_forward_workspace_bytes(4, 512, 256, 4, 1) == 2048 + 2 * 256
     assert lib.bitnet_forward_workspace_bytes(2048, 8192, 2048, 4, 1) == 2048 * 8192 + 2 * 8192
     assert lib.bitnet_forward_workspace_bytes(0, 64, 8, 8, 0) == 0
     assert lib.bitnet_forward_workspace_bytes(4, 100, 8, 8, 0) == 0  # invalid K
@@ -48,7 +50,7 @@ def test_workspace_sizes(lib):
     assert lib.bitnet_forward_workspace_bytes(1, 8192, 4096, 8, 0) == 8192 + 2 * 256
 
 
-def _fwd(lib, x=FAKE, xt=_lib.BF16, M=4, K=256, Wp=FAKE, N=256, alpha=FAKE, bits=4, had=1,
+def _fwd(lib, x=FAKE, xt=_lib.BF16, M=4, K=512, Wp=FAKE, N=256, alpha=FAKE, bits=4, had=1,
          y=FAKE, ws=FAKE, ws_bytes=1 << 30):
     return lib.bitnet_hbitlinear_forward(x, xt, M, K, Wp, N, alpha, bits, had, y, ws, ws_bytes, None)
 

@@ -99,6 +99,10 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     (1, 2560, 200, 8, 0, "bf16"),
     (3, 320, 47, 4, 0, "fp32"),
     (16, 1024, 130, 4, 1, "bf16"),
+    (1, 64, 40, 8, 1, "bf16"),         # fused with the transform (K <= 256): one wave per token row
+    (3, 128, 77, 4, 1, "fp32"),
+    (16, 256, 100, 8, 1, "bf16"),
+    (5, 256, 33, 4, 1, "bf16"),
     (7, 4096, 33, 8, 1, "fp32"),
     (16, 16384, 64, 4, 1, "bf16"),
     (2, 192, 31, 8, 0, "bf16"),

@@ -80,6 +80,8 @@ def _run(M, K, N, bits, had, x_dtype, swiglu, rms, gamma, seed):
 
 @pytest.mark.parametrize("M,K,N,bits,had,xdt,swiglu,rms,gamma", [
     (4, 256, 256, 4, 1, "fp32", True, True, True),       # single layer, whole prologue
+    (2, 128, 50, 8, 1, "bf16", True, True, True),        # fused with the transform
+    (1, 256, 64, 4, 1, "fp32", False, True, False),      # fused with the transform, one row
     (1, 2560, 300, 8, 0, "bf16", False, True, True),     # decode row, RMSNorm only: one-wave kernel
     (16, 16384, 96, 4, 1, "bf16", True, True, False),    # batched decode, long rows
     (300, 1024, 260, 8, 1, "bf16", False, True, False),  # prefill tile, unit-weight norm
