@@ -132,6 +132,9 @@ def test_parity_decode_shapes(M, K, N, bits, had, xdt):
     (130, 2560, 129, 8, 0, "bf16"),
     (40, 32768, 16, 4, 1, "bf16"),
     (513, 4096, 384, 4, 1, "bf16"),
+    (80, 2048, 96, 4, 1, "bf16"),      # transform with 16 elements per thread
+    (70, 16384, 64, 8, 1, "bf16"),     # transform with 512 threads per row
+    (66, 32768, 16, 4, 1, "fp32"),     # transform with 1024 threads per row
 ])
 def test_parity_prefill_shapes(M, K, N, bits, had, xdt):
     _run_case(M, K, N, bits, had, xdt, seed=M + K * 3 + N, n_out=max(1, K // 200), factor=50.0)
