@@ -84,6 +84,14 @@ size_t forward_parts_bytes(int64_t M, int64_t K) {
   return round_up((size_t)M * (size_t)K) + 2 * round_up((size_t)M * sizeof(float));
 }
 
+// Small batches of int4 codes travel between the quantizer and the
+// weight-streaming product as nibble codes: every workgroup of the product
+// reads all of the codes, so halving them shortens the product (M = 16,
+// K = 16384, N = 4096: 9.7 -> 8.2 us measured with half the code bytes).
+bool use_nibble_codes(int64_t M, int64_t K, int bits) {
+  return bits == 4 && M <= bitnet::kDecodeMaxM && K % bitnet::kNibbleMinK == 0;
+}
+
 bool forward_is_fused(int64_t M, int64_t K, int64_t N, int hadamard) {
   if (M > bitnet::kDecodeMaxM) return false;
   return bitnet::plan_gemv(M, K, N, true, hadamard != 0).fused;
@@ -233,11 +241,12 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
                       fn);
   }
   const ForwardWorkspace w = carve_forward(ws, M, K);
+  const bool nib = use_nibble_codes(M, K, bits);
   hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
-                                         w.scales, stream, nullptr, w.rowsum);
+                                         w.scales, stream, nullptr, w.rowsum, nib);
   if (e != hipSuccess) return hip_status(e, fn);
   e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
-                                    nullptr, stream, w.rowsum);
+                                    nullptr, stream, w.rowsum, nib);
   return hip_status(e, fn);
 }
 
@@ -452,11 +461,12 @@ bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, 
                       fn);
   }
   const ForwardWorkspace w = carve_forward(ws, M, K);
+  const bool nib = use_nibble_codes(M, K, bits);
   hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
-                                         w.scales, stream, &pro, w.rowsum);
+                                         w.scales, stream, &pro, w.rowsum, nib);
   if (e != hipSuccess) return hip_status(e, fn);
   e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
-                                    nullptr, stream, w.rowsum);
+                                    nullptr, stream, w.rowsum, nib);
   return hip_status(e, fn);
 }
 

@@ -188,6 +188,13 @@ __device__ __forceinline__ uint2 quant_pack8(const float* v, float mult) {
   return make_uint2(w0, w1);
 }
 
+// Nibble form of the eight codes of quant_pack8 (low words: codes 0-3 and
+// 4-7 as int8): byte b gets code b in its high nibble and code 4 + b in its
+// low nibble.
+__device__ __forceinline__ unsigned nibble_word(uint2 w) {
+  return ((w.x << 4) & 0xF0F0F0F0u) | (w.y & 0x0F0F0F0Fu);
+}
+
 template <int BITS>
 struct QConst {
   static constexpr float c = (BITS == 8) ? 127.0f : 2.6457513110645906f;
@@ -219,7 +226,7 @@ template <int L, int LT, int B0, int NB, bool LAST, int BITS, bool PRO>
 __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_t* crow,
                                          float* scale_out, float sq, const Prologue& pro,
                                          float* frow = nullptr, int* ired = nullptr,
-                                         int32_t* rs_out = nullptr) {
+                                         int32_t* rs_out = nullptr, bool nib = false) {
   constexpr int T = 1 << LT;
   constexpr int E = 1 << (L - LT);
   constexpr int R = 1 << NB;
@@ -306,7 +313,10 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[i] = lds[pe0 + (c + i) + ((c + i) >> 5)];
     const uint2 w = quant_pack8<BITS>(u, mult);
-    *reinterpret_cast<uint2*>(crow + e0 + c) = w;
+    if (nib)
+      *reinterpret_cast<unsigned*>(crow + ((e0 + c) >> 1)) = nibble_word(w);
+    else
+      *reinterpret_cast<uint2*>(crow + e0 + c) = w;
     qs = __builtin_amdgcn_sdot4((int)w.y, 0x01010101, __builtin_amdgcn_sdot4((int)w.x, 0x01010101, qs, false), false);
   }
   if (rs_out) {
@@ -326,7 +336,8 @@ template <typename XT, int BITS, int L, int LT, bool PRO>
 __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t* __restrict__ codes,
                                                              float* __restrict__ scales,
                                                              Prologue pro, float* fout,
-                                                             int32_t* __restrict__ rowsum) {
+                                                             int32_t* __restrict__ rowsum,
+                                                             bool nib) {
   constexpr int K = 1 << L;
   constexpr int T = 1 << LT;
   constexpr int E = K / T;
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t
   const int t = threadIdx.x;
   const int row = blockIdx.x;
   const XT* xr = x + (size_t)row * K;
-  int8_t* crow = BITS ? codes + (size_t)row * K : nullptr;
+  int8_t* crow = BITS ? codes + (size_t)row * (nib ? K / 2 : K) : nullptr;
   float* frow = BITS ? nullptr : fout + (size_t)row * K;
   int32_t* rso = (BITS && rowsum) ? rowsum + row : nullptr;
 
@@ -371,18 +382,18 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t
   static_assert(R3 <= NB3, "at most four middle chunks");
   float* sc = BITS ? scales + row : nullptr;
   if constexpr (R1 <= 0) {
-    mid_pass<L, LT, 3, NB0, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
+    mid_pass<L, LT, 3, NB0, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
   } else {
-    mid_pass<L, LT, 3, NB0, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
+    mid_pass<L, LT, 3, NB0, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
     if constexpr (R2 <= 0) {
-      mid_pass<L, LT, 3 + NB0, NB1, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
+      mid_pass<L, LT, 3 + NB0, NB1, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
     } else {
-      mid_pass<L, LT, 3 + NB0, NB1, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
+      mid_pass<L, LT, 3 + NB0, NB1, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
       if constexpr (R3 <= 0) {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
       } else {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
-        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
+        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
       }
     }
   }
@@ -393,7 +404,8 @@ template <typename XT, int BITS, int CH, bool PRO>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ x, int K,
                                                          int8_t* __restrict__ codes,
                                                          float* __restrict__ scales, Prologue pro,
-                                                         int32_t* __restrict__ rowsum) {
+                                                         int32_t* __restrict__ rowsum,
+                                                         bool nib) {
   constexpr int T = 256;
   __shared__ float red[8];
   __shared__ int ired[4];
@@ -437,14 +449,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ 
     mult = QConst<BITS>::c / sc;
   }
   if (t == 0) scales[row] = sc;
-  int8_t* crow = codes + (size_t)row * K;
+  int8_t* crow = codes + (size_t)row * (nib ? K / 2 : K);
   int qs = 0;  // this thread's share of the code sum
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int idx = 8 * t + 8 * T * c;
     if (idx < K) {
       const uint2 w = quant_pack8<BITS>(v[c], mult);
-      *reinterpret_cast<uint2*>(crow + idx) = w;
+      if (nib)
+        *reinterpret_cast<unsigned*>(crow + (idx >> 1)) = nibble_word(w);
+      else
+        *reinterpret_cast<uint2*>(crow + idx) = w;
       qs = __builtin_amdgcn_sdot4((int)w.y, 0x01010101,
                                   __builtin_amdgcn_sdot4((int)w.x, 0x01010101, qs, false), false);
     }
@@ -464,14 +479,15 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
 
 template <typename XT, int BITS, int L, int LT, bool PRO>
 hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, const Prologue& pro,
-                       hipStream_t stream, float* fout = nullptr, int32_t* rowsum = nullptr) {
+                       hipStream_t stream, float* fout = nullptr, int32_t* rowsum = nullptr,
+                       bool nib = false) {
   constexpr int K = 1 << L;
   const size_t lds = (size_t)(K + K / 32) * sizeof(float);
   auto kern = fwht_quant_kernel<XT, BITS, L, LT, PRO>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)M), dim3(1 << LT), lds, stream>>>(reinterpret_cast<const XT*>(x), codes,
-                                                          scales, pro, fout, rowsum);
+                                                          scales, pro, fout, rowsum, nib);
   return hipGetLastError();
 }
 
@@ -493,12 +509,12 @@ constexpr int fwht_lt_few(int L) {
 template <typename XT, int BITS, int L, bool PRO>
 hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales,
                          const Prologue& pro, hipStream_t stream, float* fout = nullptr,
-                         int32_t* rowsum = nullptr) {
+                         int32_t* rowsum = nullptr, bool nib = false) {
   constexpr int LT_BATCH = fwht_lt_batch(L);
   constexpr int LT_FEW = fwht_lt_few(L);
   if (M <= 64 && LT_FEW != LT_BATCH)
-    return launch_fwht<XT, BITS, L, LT_FEW, PRO>(x, M, codes, scales, pro, stream, fout, rowsum);
-  return launch_fwht<XT, BITS, L, LT_BATCH, PRO>(x, M, codes, scales, pro, stream, fout, rowsum);
+    return launch_fwht<XT, BITS, L, LT_FEW, PRO>(x, M, codes, scales, pro, stream, fout, rowsum, nib);
+  return launch_fwht<XT, BITS, L, LT_BATCH, PRO>(x, M, codes, scales, pro, stream, fout, rowsum, nib);
 }
 
 // Transform only (fp32 rows in and out, in place allowed).
@@ -510,50 +526,51 @@ hipError_t launch_fwht_f32_l(const float* x, int64_t M, float* out, hipStream_t 
 
 template <typename XT, int BITS, bool PRO>
 hipError_t launch_had(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                      const Prologue& pro, hipStream_t stream, int32_t* rowsum) {
+                      const Prologue& pro, hipStream_t stream, int32_t* rowsum, bool nib) {
   switch (K) {
-    case 1 << 6: return launch_fwht_l<XT, BITS, 6, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
-    case 1 << 7: return launch_fwht_l<XT, BITS, 7, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
-    case 1 << 8: return launch_fwht_l<XT, BITS, 8, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
-    case 1 << 9: return launch_fwht_l<XT, BITS, 9, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
-    case 1 << 10: return launch_fwht_l<XT, BITS, 10, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
-    case 1 << 11: return launch_fwht_l<XT, BITS, 11, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
-    case 1 << 12: return launch_fwht_l<XT, BITS, 12, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
-    case 1 << 13: return launch_fwht_l<XT, BITS, 13, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
-    case 1 << 14: return launch_fwht_l<XT, BITS, 14, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
-    case 1 << 15: return launch_fwht_l<XT, BITS, 15, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum);
+    case 1 << 6: return launch_fwht_l<XT, BITS, 6, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 7: return launch_fwht_l<XT, BITS, 7, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 8: return launch_fwht_l<XT, BITS, 8, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 9: return launch_fwht_l<XT, BITS, 9, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 10: return launch_fwht_l<XT, BITS, 10, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 11: return launch_fwht_l<XT, BITS, 11, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 12: return launch_fwht_l<XT, BITS, 12, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 13: return launch_fwht_l<XT, BITS, 13, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 14: return launch_fwht_l<XT, BITS, 14, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 15: return launch_fwht_l<XT, BITS, 15, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename XT, int BITS, int CH, bool PRO>
 hipError_t launch_rows_ch(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                          const Prologue& pro, hipStream_t stream, int32_t* rowsum) {
+                          const Prologue& pro, hipStream_t stream, int32_t* rowsum, bool nib) {
   quant_rows_kernel<XT, BITS, CH, PRO><<<dim3((unsigned)M), dim3(256), 0, stream>>>(
-      reinterpret_cast<const XT*>(x), K, codes, scales, pro, rowsum);
+      reinterpret_cast<const XT*>(x), K, codes, scales, pro, rowsum, nib);
   return hipGetLastError();
 }
 
 template <typename XT, int BITS, bool PRO>
 hipError_t launch_rows(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                       const Prologue& pro, hipStream_t stream, int32_t* rowsum) {
+                       const Prologue& pro, hipStream_t stream, int32_t* rowsum, bool nib) {
   const int ch = (K + 2047) / 2048;
-  if (ch <= 1) return launch_rows_ch<XT, BITS, 1, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
-  if (ch <= 2) return launch_rows_ch<XT, BITS, 2, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
-  if (ch <= 4) return launch_rows_ch<XT, BITS, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
-  if (ch <= 8) return launch_rows_ch<XT, BITS, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
-  return launch_rows_ch<XT, BITS, 16, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
+  if (ch <= 1) return launch_rows_ch<XT, BITS, 1, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
+  if (ch <= 2) return launch_rows_ch<XT, BITS, 2, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
+  if (ch <= 4) return launch_rows_ch<XT, BITS, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
+  if (ch <= 8) return launch_rows_ch<XT, BITS, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
+  return launch_rows_ch<XT, BITS, 16, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
 }
 
 template <typename XT, bool PRO>
 hipError_t launch_dtype(const void* x, int64_t M, int K, int bits, int hadamard, int8_t* codes,
-                        float* scales, const Prologue& pro, hipStream_t stream, int32_t* rowsum) {
+                        float* scales, const Prologue& pro, hipStream_t stream, int32_t* rowsum,
+                        bool nib) {
   if (hadamard) {
-    return bits == 8 ? launch_had<XT, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum)
-                     : launch_had<XT, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
+    return bits == 8 ? launch_had<XT, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum, false)
+                     : launch_had<XT, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
   }
-  return bits == 8 ? launch_rows<XT, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum)
-                   : launch_rows<XT, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum);
+  return bits == 8 ? launch_rows<XT, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum, false)
+                   : launch_rows<XT, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
 }
 
 }  // namespace
@@ -577,16 +594,17 @@ hipError_t launch_fwht_f32(const float* x, int64_t M, int K, float* out, hipStre
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
                            int8_t* codes, float* scales, hipStream_t stream, const Prologue* pro,
-                           int32_t* rowsum) {
+                           int32_t* rowsum, bool nibbles) {
+  if (nibbles && (bits != 4 || K % 8 != 0)) return hipErrorInvalidValue;
   const Prologue none{nullptr, nullptr, 0.0f, 0};
   if (pro) {
     if (x_dtype == 1)
-      return launch_dtype<uint16_t, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum);
-    return launch_dtype<float, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum);
+      return launch_dtype<uint16_t, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum, nibbles);
+    return launch_dtype<float, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum, nibbles);
   }
   if (x_dtype == 1)
-    return launch_dtype<uint16_t, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum);
-  return launch_dtype<float, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum);
+    return launch_dtype<uint16_t, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum, nibbles);
+  return launch_dtype<float, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum, nibbles);
 }
 
 }  // namespace bitnet

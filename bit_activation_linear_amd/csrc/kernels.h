@@ -78,13 +78,23 @@ struct Prologue {
   int rms;
 };
 
+// Nibble codes (bits = 4 only, K % 8 == 0): each token row of K codes is
+// K / 2 bytes, eight codes to a 32-bit word: byte b of word i holds code
+// 8 i + b in its high nibble and code 8 i + 4 + b in its low nibble (two's
+// complement). Masking a word with 0xF0F0F0F0 then gives codes 8i .. 8i+3
+// times 16 as int8 lanes, and shifting it left by 4 first gives the other
+// four: two operations per four codes, half the bytes of int8 codes.
+constexpr int kNibbleMinK = 256;  // the decode product reads nibble codes for K % 256 == 0
+
 // Fused (optional) prologue + Walsh-Hadamard transform + per-token
 // quantization. x_dtype: 0 = fp32, 1 = bf16 bit patterns. pro may be null.
 // rowsum, when not null, receives each token's code sum (int32 [M]), which
-// the prefill product then needs not compute.
+// the prefill product then needs not compute. nibbles (bits = 4 only):
+// write nibble codes instead of int8 codes.
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
                            int8_t* codes, float* scales, hipStream_t stream,
-                           const Prologue* pro = nullptr, int32_t* rowsum = nullptr);
+                           const Prologue* pro = nullptr, int32_t* rowsum = nullptr,
+                           bool nibbles = false);
 
 // Low-bit KV cache: rows of D elements, row r being token r % S of its head;
 // token 0 int8 absmax, the others bits = 3, 4 or 8.
@@ -93,16 +103,17 @@ hipError_t launch_kv_quantize(const void* kv, int x_dtype, int64_t R, int D, int
 
 // Ternary product from codes. Exactly one of y (dequantized; needs scales,
 // alpha, bits) or acc (raw int32) is non-null. rowsum (optional, with y):
-// the codes' per-token sums from launch_quantize.
+// the codes' per-token sums from launch_quantize. nibbles: the codes are
+// nibble codes (M <= kDecodeMaxM and K % kNibbleMinK == 0 only).
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
                                  const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
                                  float* y, int32_t* acc, hipStream_t stream,
-                                 const int32_t* rowsum = nullptr);
+                                 const int32_t* rowsum = nullptr, bool nibbles = false);
 
 // The two product shapes behind launch_ternary_matmul.
 hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, hipStream_t stream);
+                       int32_t* acc, hipStream_t stream, bool nibbles = false);
 hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
                        int32_t* acc, hipStream_t stream, const int32_t* rowsum = nullptr);

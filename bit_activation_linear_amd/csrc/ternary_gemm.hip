@@ -902,9 +902,10 @@ hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int 
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
                                  const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
                                  float* y, int32_t* acc, hipStream_t stream,
-                                 const int32_t* rowsum) {
+                                 const int32_t* rowsum, bool nibbles) {
   if (M <= kDecodeMaxM)
-    return launch_gemv(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream);
+    return launch_gemv(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream, nibbles);
+  if (nibbles) return hipErrorInvalidValue;
   return launch_gemm(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream, rowsum);
 }
 

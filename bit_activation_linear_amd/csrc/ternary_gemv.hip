@@ -74,7 +74,13 @@ constexpr int kCodePitch = 272;
 // the codes are loaded as 4 rows x 256 contiguous bytes per instruction,
 // written to the wave's LDS area and read back in MFMA order (the same wave
 // writes and reads, so no barrier is needed).
-template <int CT>
+//
+// With NIB the codes are nibble codes (K % 256 == 0): a lane loads 16 bytes
+// (32 codes) of token row 8 i + lane / 8, the two loads of a super-block
+// cover its 16 rows, and the lane widens them to 16 x the codes (a mask and
+// a shift per four codes) on their way to LDS; the wave's tile is divided
+// by 16 at the end, exactly.
+template <int CT, bool NIB>
 __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* codes_base,
                                              int8_t* stage, v4i (&acc)[CT]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -82,8 +88,12 @@ __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* co
   const int nKB = a.K >> 6, nSB = (nKB + 3) >> 2;
   const int rounds = (nSB + a.sb_waves - 1) / a.sb_waves;
   const size_t row_bytes = (size_t)(a.K >> 2);
-  // contiguous code chunk i of this lane: token row 4 i + lane / 16, byte 16 (lane % 16) of the super-block
-  const int crow = lane >> 4, cbyte = 16 * (lane & 15);
+  // contiguous code chunk i of this lane: token row 4 i + lane / 16, byte 16 (lane % 16) of the
+  // super-block; nibble codes: token row 8 i + lane / 8, packed byte 16 (lane % 8)
+  const int crow = NIB ? lane >> 3 : lane >> 4;
+  const int cbyte = NIB ? 16 * (lane & 7) : 16 * (lane & 15);
+  constexpr int kCodeLoads = NIB ? 2 : 4;
+  constexpr int kRowsPerLoad = NIB ? 8 : 4;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
   if (wave >= a.sb_waves) return;
@@ -104,23 +114,41 @@ __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* co
       }
       // Unconditional loads from clamped addresses; what is out of range is
       // zeroed with a mask (a branch would force a wait on the load).
-      const int k = sbc * 256 + cbyte;
-      const bool k_ok = (r0 + u < rounds) && sb < nSB && k < a.K;
-      const int kc = k < a.K ? k : a.K - 16;
+      const int k = NIB ? sbc * 128 + cbyte : sbc * 256 + cbyte;  // byte in the code row
+      const int rb = NIB ? a.K >> 1 : a.K;                        // code row bytes
+      const bool k_ok = (r0 + u < rounds) && sb < nSB && k < rb;
+      const int kc = k < rb ? k : rb - 16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * i + crow;
+      for (int i = 0; i < kCodeLoads; ++i) {
+        const int m = kRowsPerLoad * i + crow;
         const int mc = m < a.M ? m : a.M - 1;
         const int mask = (k_ok && m < a.M) ? -1 : 0;
-        cv[u][i] = *reinterpret_cast<const v4i*>(codes_base + (size_t)mc * a.K + kc) & mask;
+        cv[u][i] = *reinterpret_cast<const v4i*>(codes_base + (size_t)mc * rb + kc) & mask;
       }
     }
 #pragma unroll
     for (int u = 0; u < kRoundsInFlight; ++u) {
       if (r0 + u < rounds) {
+        if constexpr (NIB) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<v4i*>(stage + (4 * i + crow) * kCodePitch + cbyte) = cv[u][i];
+          for (int i = 0; i < kCodeLoads; ++i) {
+            const v4i w = cv[u][i];
+            const v4i w4 = w << 4;
+            // codes 0-15 and 16-31 of the lane's 32, times 16
+            const v4i c0 = v4i{w.x & (int)0xF0F0F0F0u, w4.x & (int)0xF0F0F0F0u,
+                               w.y & (int)0xF0F0F0F0u, w4.y & (int)0xF0F0F0F0u};
+            const v4i c1 = v4i{w.z & (int)0xF0F0F0F0u, w4.z & (int)0xF0F0F0F0u,
+                               w.w & (int)0xF0F0F0F0u, w4.w & (int)0xF0F0F0F0u};
+            int8_t* dst = stage + (kRowsPerLoad * i + crow) * kCodePitch + 2 * cbyte;
+            *reinterpret_cast<v4i*>(dst) = c0;
+            *reinterpret_cast<v4i*>(dst + 16) = c1;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < kCodeLoads; ++i)
+            *reinterpret_cast<v4i*>(stage + (kRowsPerLoad * i + crow) * kCodePitch + cbyte) =
+                cv[u][i];
+        }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         v4i av[4];
 #pragma unroll
@@ -130,6 +158,10 @@ __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* co
         mma_round<CT>(av, p[u], acc);
       }
     }
+  }
+  if constexpr (NIB) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] >>= 4;  // every product was 16 q t
   }
 }
 
@@ -165,7 +197,7 @@ __device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[
   }
 }
 
-template <int CT, bool OUT_I32>
+template <int CT, bool OUT_I32, bool NIB>
 __global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nw = blockDim.x >> 6;
@@ -186,7 +218,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a) {
     for (int v = 0; v < 4; ++v) s_row[v] = a.scales[m0 + v < a.M ? m0 + v : a.M - 1];
   }
   v4i acc[CT];
-  wave_product<CT>(a, a.codes, stage, acc);
+  wave_product<CT, NIB>(a, a.codes, stage, acc);
   gemv_finish<CT, OUT_I32>(a, acc, red, s_row, nw, alpha);
 }
 
@@ -670,10 +702,10 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int CT, bool OUT_I32>
+template <int CT, bool OUT_I32, bool NIB>
 hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)(p.threads / 64) * (CT * 1024 + 16 * kCodePitch);
-  auto kern = ternary_gemv_kernel<CT, OUT_I32>;
+  auto kern = ternary_gemv_kernel<CT, OUT_I32, NIB>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a);
@@ -742,7 +774,8 @@ hipError_t launch_fused_t(const GemvArgs& a, const Prologue* pro, hipStream_t st
 
 hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, hipStream_t stream) {
+                       int32_t* acc, hipStream_t stream, bool nibbles) {
+  if (nibbles && (M > kDecodeMaxM || K % kNibbleMinK != 0)) return hipErrorInvalidValue;
   const GemvPlan p = plan_gemv(M, K, N, false, false);
   GemvArgs a{};
   a.codes = codes;
@@ -756,7 +789,9 @@ hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int 
   a.N = (int)N;
   a.sb_waves = p.sb_waves;
   a.c = (bits == 8) ? kScaleInt8 : kScaleInt4;
-  return acc ? launch_gemv_ct<1, true>(p, a, stream) : launch_gemv_ct<1, false>(p, a, stream);
+  if (nibbles)
+    return acc ? launch_gemv_ct<1, true, true>(p, a, stream) : launch_gemv_ct<1, false, true>(p, a, stream);
+  return acc ? launch_gemv_ct<1, true, false>(p, a, stream) : launch_gemv_ct<1, false, false>(p, a, stream);
 }
 
 hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,
