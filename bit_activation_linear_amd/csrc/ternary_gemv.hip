@@ -19,6 +19,12 @@
 // s_barrier); the default __syncthreads() would also wait for every global
 // load in flight, draining the weight stream at each barrier.
 //
+// The product reads the whole code matrix once per workgroup, so for int4
+// codes the forward hands them over two to a byte (nibble codes, see
+// kernels.h): the lanes widen them to 16 q on their way to LDS and the tile
+// is divided by 16 at the end, exactly. At M = 16, K = 16384, N = 4096 this
+// takes the product from 9.7 to 8.2 us.
+//
 // With hadamard = 0 and a small batch the per-token quantization (Eq. 5-6)
 // runs in the same kernel: each wave quantizes the slice of the (tiny) x that
 // its own MFMAs consume, with one workgroup barrier to combine the per-token

@@ -102,9 +102,10 @@ bitnet_status bitnet_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* W
 /* Forward                                                                   */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of workspace bitnet_hbitlinear_forward needs: the int8 codes, fp32
+/* Bytes of workspace bitnet_hbitlinear_forward needs: the codes, fp32
  * scales and int32 code row sums of the batch (M*K, 4*M and 4*M bytes, each
- * rounded up to 256). It is 0
+ * rounded up to 256; with bits = 4, M <= 16 and K % 256 == 0 the codes are
+ * held two to a byte and fill half of their part). It is 0
  * when the forward runs as a single fused kernel (M <= 16, M*K <= 16384,
  * K <= 4096, and hadamard = 0 or K <= 256); ws may then be NULL. Returns 0
  * for invalid sizes. */
@@ -132,7 +133,9 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
 /* The two stages of the forward, exposed for inspection and timing. They run
  * the kernels of the forward's two-launch path; where the forward fuses both
  * stages into one kernel (see bitnet_forward_workspace_bytes) that kernel
- * takes the same quantization and product steps in the same precision. */
+ * takes the same quantization and product steps in the same precision, and
+ * where it passes int4 codes two to a byte (see above) the product's result
+ * is the same integer, so the output is the same bit for bit. */
 
 /* Transform + per-token quantization only (Eq. 3-6): writes int8 codes
  * [M, K] and fp32 scales s [M] (s = stat + eps, the value the dequantization
