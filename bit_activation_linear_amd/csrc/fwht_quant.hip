@@ -150,7 +150,7 @@ __device__ __forceinline__ void apply_prologue8(const Prologue& pro, const XT* u
     float u[8];
     load8(up_row + idx, u);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (v[e] / (1.0f + expf(-v[e]))) * u[e];
+    for (int e = 0; e < 8; ++e) v[e] = silu(v[e]) * u[e];
   }
   if (pro.rms) {
 #pragma unroll

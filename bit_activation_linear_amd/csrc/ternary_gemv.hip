@@ -358,7 +358,7 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
           if (pro.up) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              v[m][r][e] = (v[m][r][e] / (1.0f + expf(-v[m][r][e]))) * u[m][r][e];
+              v[m][r][e] = silu(v[m][r][e]) * u[m][r][e];
           }
           if (pro.rms) {
 #pragma unroll
