@@ -22,8 +22,8 @@
 // The product reads the whole code matrix once per workgroup, so for int4
 // codes the forward hands them over two to a byte (nibble codes, see
 // kernels.h): the lanes widen them to 16 q on their way to LDS and the tile
-// is divided by 16 at the end, exactly. At M = 16, K = 16384, N = 4096 this
-// takes the product from 9.7 to 8.2 us.
+// is divided by 16 at the end, exactly. At M = 16, K = 16384, N = 4096 the
+// product traces at 8.9 us on nibble codes against 10.0 us on int8 codes.
 //
 // With hadamard = 0 and a small batch the per-token quantization (Eq. 5-6)
 // runs in the same kernel: each wave quantizes the slice of the (tiny) x that
