@@ -41,6 +41,7 @@ constexpr float kEps = 1e-7f;
 constexpr int kRoundsInFlight = 4;  // super-blocks whose loads a lane issues together
 constexpr int kFusedCt = 2;         // 16-column tiles per workgroup in the fused decode kernel
 constexpr int kFusedSbw = 1;        // 256-k super-blocks per wave in the fused decode kernel
+constexpr int kFusedHadCt = 1;      // ... with the transform (K <= 256: one wave, no idle second)
 
 struct GemvArgs {
   const int8_t* codes;
@@ -767,8 +768,8 @@ template <typename XT, int BITS, int MG>
 hipError_t launch_fused_t(const GemvArgs& a, const Prologue* pro, hipStream_t stream, bool had) {
   const Prologue none{nullptr, nullptr, 0.0f, 0};
   if (had) {
-    if (pro) return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, true, true>(a, *pro, stream);
-    return launch_fused_ct<XT, BITS, MG, kFusedCt, kFusedSbw, false, true>(a, none, stream);
+    if (pro) return launch_fused_ct<XT, BITS, MG, kFusedHadCt, kFusedSbw, true, true>(a, *pro, stream);
+    return launch_fused_ct<XT, BITS, MG, kFusedHadCt, kFusedSbw, false, true>(a, none, stream);
   }
   hipError_t err = hipSuccess;
   if (try_launch_wave<XT, BITS>(a, pro, stream, &err)) return err;
