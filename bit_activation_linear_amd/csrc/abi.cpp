@@ -89,7 +89,7 @@ size_t forward_parts_bytes(int64_t M, int64_t K) {
 // reads all of the codes, so halving them shortens the product (M = 16,
 // K = 16384, N = 4096: 10.0 -> 8.9 us per product launch).
 bool use_nibble_codes(int64_t M, int64_t K, int bits) {
-  return bits == 4 && M <= bitnet::kDecodeMaxM && K % bitnet::kNibbleMinK == 0;
+  return bits == 4 && M <= bitnet::kDecodeMaxM && K % bitnet::kNibbleKMultiple == 0;
 }
 
 bool forward_is_fused(int64_t M, int64_t K, int64_t N, int hadamard) {

@@ -95,7 +95,7 @@ __device__ __forceinline__ float silu(float g) {
 // complement). Masking a word with 0xF0F0F0F0 then gives codes 8i .. 8i+3
 // times 16 as int8 lanes, and shifting it left by 4 first gives the other
 // four: two operations per four codes, half the bytes of int8 codes.
-constexpr int kNibbleMinK = 256;  // the decode product reads nibble codes for K % 256 == 0
+constexpr int kNibbleKMultiple = 256;  // the decode product reads nibble codes when K is a multiple
 
 // Fused (optional) prologue + Walsh-Hadamard transform + per-token
 // quantization. x_dtype: 0 = fp32, 1 = bf16 bit patterns. pro may be null.
@@ -115,7 +115,7 @@ hipError_t launch_kv_quantize(const void* kv, int x_dtype, int64_t R, int D, int
 // Ternary product from codes. Exactly one of y (dequantized; needs scales,
 // alpha, bits) or acc (raw int32) is non-null. rowsum (optional, with y):
 // the codes' per-token sums from launch_quantize. nibbles: the codes are
-// nibble codes (M <= kDecodeMaxM and K % kNibbleMinK == 0 only).
+// nibble codes (M <= kDecodeMaxM and K % kNibbleKMultiple == 0 only).
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
                                  const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
                                  float* y, int32_t* acc, hipStream_t stream,

@@ -782,7 +782,7 @@ hipError_t launch_fused_t(const GemvArgs& a, const Prologue* pro, hipStream_t st
 hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
                        int32_t* acc, hipStream_t stream, bool nibbles) {
-  if (nibbles && (M > kDecodeMaxM || K % kNibbleMinK != 0)) return hipErrorInvalidValue;
+  if (nibbles && (M > kDecodeMaxM || K % kNibbleKMultiple != 0)) return hipErrorInvalidValue;
   const GemvPlan p = plan_gemv(M, K, N, false, false);
   GemvArgs a{};
   a.codes = codes;
