@@ -498,12 +498,12 @@ hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, c
 // K = 1024 - 4096 and E = 32 from K = 8192 on, at most 1024 threads
 // (K = 16384: 17.1 us for 1024 rows against 24.9 with E = 64; K = 32768:
 // 20.9 against 37.9 with E = 128). For a handful of long rows (M <= 64,
-// decode) E = 8 up to K = 2048 and at K = 8192, E = 16 at K = 4096 and
-// E = 32 from K = 16384 on (M = 16, K = 16384: 5.09 us against 5.65 with
-// E = 16).
+// decode) E = 8 up to K = 2048, E = 16 at K = 4096 and 8192 (M = 16,
+// K = 8192: 4.30 us against 4.93 with E = 8) and E = 32 from K = 16384 on
+// (M = 16, K = 16384: 5.09 us against 5.65 with E = 16).
 constexpr int fwht_lt_batch(int L) { return L <= 9 ? L - 3 : (L <= 12 ? L - 4 : (L - 5 < 10 ? L - 5 : 10)); }
 constexpr int fwht_lt_few(int L) {
-  return L == 12 ? 8 : (L >= 14 ? (L - 5 < 10 ? L - 5 : 10) : (L - 3 < 10 ? L - 3 : 10));
+  return L <= 11 ? (L - 3 < 10 ? L - 3 : 10) : (L <= 13 ? L - 4 : (L - 5 < 10 ? L - 5 : 10));
 }
 
 template <typename XT, int BITS, int L, bool PRO>

@@ -104,6 +104,7 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     (16, 256, 100, 8, 1, "bf16"),
     (5, 256, 33, 4, 1, "bf16"),
     (7, 4096, 33, 8, 1, "fp32"),
+    (12, 8192, 40, 4, 1, "bf16"),      # transform, 16 elements per thread for a few long rows
     (16, 16384, 64, 4, 1, "bf16"),
     (2, 192, 31, 8, 0, "bf16"),
     (5, 32768, 40, 8, 0, "fp32"),
