@@ -105,6 +105,9 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     (5, 256, 33, 4, 1, "bf16"),
     (7, 4096, 33, 8, 1, "fp32"),
     (12, 8192, 40, 4, 1, "bf16"),      # transform, 16 elements per thread for a few long rows
+    (16, 512, 70, 4, 1, "bf16"),       # nibble codes, shortest row they take with the transform
+    (16, 4352, 50, 4, 0, "bf16"),      # nibble codes without the transform, 17 super-blocks
+    (13, 1280, 33, 4, 0, "fp32"),      # nibble codes, fp32 input, ragged M
     (16, 16384, 64, 4, 1, "bf16"),
     (2, 192, 31, 8, 0, "bf16"),
     (5, 32768, 40, 8, 0, "fp32"),
