@@ -1,5 +1,5 @@
-// Device helpers shared by the single-token decode kernels: raw activation
-// loads that are widened to fp32 later, and a wave-wide DPP reduction.
+// Device helpers shared by the decode and quantizer kernels: raw activation
+// loads that are widened to fp32 later, and wave-wide DPP reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,6 +55,20 @@ __device__ __forceinline__ float wave_reduce(float v) {
   BITNET_DPP_STEP(0x143, 0xC, false)  // row_bcast:31 -> lane 63: whole wave
 #undef BITNET_DPP_STEP
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Wave-wide sum of integers of any sign (zero is the identity), exact, in
+// the same DPP steps; every lane gets the result.
+__device__ __forceinline__ int wave_sum_int(int v) {
+#define BITNET_DPP_ISTEP(ctrl, rmask, bc) v += __builtin_amdgcn_update_dpp(0, v, ctrl, rmask, 0xF, bc);
+  BITNET_DPP_ISTEP(0x111, 0xF, true)
+  BITNET_DPP_ISTEP(0x112, 0xF, true)
+  BITNET_DPP_ISTEP(0x114, 0xF, true)
+  BITNET_DPP_ISTEP(0x118, 0xF, true)
+  BITNET_DPP_ISTEP(0x142, 0xA, false)
+  BITNET_DPP_ISTEP(0x143, 0xC, false)
+#undef BITNET_DPP_ISTEP
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 }  // namespace bitnet

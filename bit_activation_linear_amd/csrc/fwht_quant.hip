@@ -31,6 +31,7 @@
 // reduced together with the statistic (one barrier), and it enters only the
 // scale and the code multiplier.
 #include "kernels.h"
+#include "decode_common.cuh"
 
 namespace bitnet {
 namespace {
@@ -91,48 +92,12 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Whole-wave max or sum of non-negative values with DPP row shifts and row
-// broadcasts (zero is the identity of both; a fixed order, so sums are
-// reproducible), every lane getting the result: a few cycles per step where
-// a lane shuffle goes through LDS.
-template <bool IS_MAX>
-__device__ __forceinline__ float wave_total(float v) {
-#define BITNET_DPP_STEP(ctrl, rmask, bc)                                                      \
-  {                                                                                           \
-    const float o = __int_as_float(                                                           \
-        __builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rmask, 0xF, bc));             \
-    v = IS_MAX ? fmaxf(v, o) : v + o;                                                         \
-  }
-  BITNET_DPP_STEP(0x111, 0xF, true)   // row_shr:1
-  BITNET_DPP_STEP(0x112, 0xF, true)   // row_shr:2
-  BITNET_DPP_STEP(0x114, 0xF, true)   // row_shr:4
-  BITNET_DPP_STEP(0x118, 0xF, true)   // row_shr:8: lane 15 of each row holds the row's total
-  BITNET_DPP_STEP(0x142, 0xA, false)  // row_bcast:15: lanes 31 and 63 hold two rows'
-  BITNET_DPP_STEP(0x143, 0xC, false)  // row_bcast:31: lane 63 holds the wave's
-#undef BITNET_DPP_STEP
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// The same for a sum of integers (of any sign: zero is the identity).
-__device__ __forceinline__ int wave_total_int(int v) {
-#define BITNET_DPP_ISTEP(ctrl, rmask, bc) \
-  v += __builtin_amdgcn_update_dpp(0, v, ctrl, rmask, 0xF, bc);
-  BITNET_DPP_ISTEP(0x111, 0xF, true)
-  BITNET_DPP_ISTEP(0x112, 0xF, true)
-  BITNET_DPP_ISTEP(0x114, 0xF, true)
-  BITNET_DPP_ISTEP(0x118, 0xF, true)
-  BITNET_DPP_ISTEP(0x142, 0xA, false)
-  BITNET_DPP_ISTEP(0x143, 0xC, false)
-#undef BITNET_DPP_ISTEP
-  return __builtin_amdgcn_readlane(v, 63);
-}
-
 // Workgroup reduction of the per-thread statistic (fixed order), T threads.
 template <int BITS, int T>
 __device__ __forceinline__ float block_stat(float s, float* red) {
   constexpr int W = T < 64 ? T : 64;
   if constexpr (T >= 64)
-    s = wave_total<BITS == 8>(s);
+    s = wave_reduce<BITS == 8>(s);
   else
     s = (BITS == 8) ? group_max<W>(s) : group_sum<W>(s);
   constexpr int NW = (T + 63) / 64;
@@ -155,8 +120,8 @@ template <int BITS, int T>
 __device__ __forceinline__ float2 block_stat2(float s, float q, float* red) {
   constexpr int W = T < 64 ? T : 64;
   if constexpr (T >= 64) {
-    s = wave_total<BITS == 8>(s);
-    q = wave_total<false>(q);
+    s = wave_reduce<BITS == 8>(s);
+    q = wave_reduce<false>(q);
   } else {
     s = (BITS == 8) ? group_max<W>(s) : group_sum<W>(s);
     q = group_sum<W>(q);
@@ -256,7 +221,7 @@ template <int T>
 __device__ __forceinline__ int block_isum(int v, int* ired) {
   constexpr int W = T < 64 ? T : 64;
   if constexpr (T >= 64) {
-    v = wave_total_int(v);
+    v = wave_sum_int(v);
   } else {
 #pragma unroll
     for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, W);

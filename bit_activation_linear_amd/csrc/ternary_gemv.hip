@@ -651,22 +651,7 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a, const float
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
   // Wave-wide code row sum (exact int32 in float-free DPP steps).
-  {
-    float fs = __int_as_float(qsum);
-#define BITNET_ISUM(ctrl, rmask, bc)                                                            \
-  {                                                                                             \
-    const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(fs), ctrl, rmask, 0xF, bc);     \
-    fs = __int_as_float(__float_as_int(fs) + o);                                                \
-  }
-    BITNET_ISUM(0x111, 0xF, true)
-    BITNET_ISUM(0x112, 0xF, true)
-    BITNET_ISUM(0x114, 0xF, true)
-    BITNET_ISUM(0x118, 0xF, true)
-    BITNET_ISUM(0x142, 0xA, false)
-    BITNET_ISUM(0x143, 0xC, false)
-#undef BITNET_ISUM
-    qsum = __builtin_amdgcn_readlane(__float_as_int(fs), 63);
-  }
+  qsum = wave_sum_int(qsum);
 
   // MFMA operand: lane (col, grp) feeds token row col (only row 0 is live),
   // block 4 sb + grp, times the stored field u = t + 1 in {0, 1, 2};

@@ -240,22 +240,7 @@ __global__ __launch_bounds__(64 * WV) void tl2_decode_kernel(const void* __restr
   }
   if (lane < 16) *reinterpret_cast<unsigned*>(qzero + 4 * lane) = 0u;  // each wave, before its own reads
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  {
-    float fs = __int_as_float(qsum);
-#define BITNET_ISUM(ctrl, rmask, bc)                                                            \
-  {                                                                                             \
-    const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(fs), ctrl, rmask, 0xF, bc);     \
-    fs = __int_as_float(__float_as_int(fs) + o);                                                \
-  }
-    BITNET_ISUM(0x111, 0xF, true)
-    BITNET_ISUM(0x112, 0xF, true)
-    BITNET_ISUM(0x114, 0xF, true)
-    BITNET_ISUM(0x118, 0xF, true)
-    BITNET_ISUM(0x142, 0xA, false)
-    BITNET_ISUM(0x143, 0xC, false)
-#undef BITNET_ISUM
-    qsum = __builtin_amdgcn_readlane(__float_as_int(fs), 63);
-  }
+  qsum = wave_sum_int(qsum);
 
   // MFMA operands: lane (col, grp) feeds column col's slots 4 h .. 4 h + 3 of
   // group grp of each block; lanes of token row 0 (col == 0) feed the codes.
