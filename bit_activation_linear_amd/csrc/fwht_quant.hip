@@ -31,7 +31,7 @@
 // reduced together with the statistic (one barrier), and it enters only the
 // scale and the code multiplier.
 #include "kernels.h"
-#include "decode_common.cuh"
+#include "decode_common.h"
 
 namespace bitnet {
 namespace {

@@ -31,7 +31,7 @@
 // bank-conflict-free; one barrier per stage; the next 32-k block's operands
 // are read while the current block's MFMAs run.
 #include "kernels.h"
-#include "ternary_common.cuh"
+#include "ternary_common.h"
 
 namespace bitnet {
 namespace {

@@ -64,7 +64,7 @@
 // workgroups resident on one XCD at a time share code rows and weight columns
 // through its L2.
 #include "kernels.h"
-#include "ternary_common.cuh"
+#include "ternary_common.h"
 
 namespace bitnet {
 namespace {

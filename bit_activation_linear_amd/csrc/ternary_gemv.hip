@@ -31,8 +31,8 @@
 // statistic, all while its weight loads are in flight, so the decode forward
 // is one launch.
 #include "kernels.h"
-#include "ternary_common.cuh"
-#include "decode_common.cuh"
+#include "ternary_common.h"
+#include "decode_common.h"
 
 namespace bitnet {
 namespace {
@@ -272,8 +272,11 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
   const int lane = t & 63, wave = t >> 6;
   v4i* red = reinterpret_cast<v4i*>(smem);                                // [nw][CT][64]
   float* part = reinterpret_cast<float*>(smem + (size_t)nw * CT * 1024);  // [nw][16]
-  float* srow = part + nw * 16;                                           // [16]
-  float* psq = srow + 16;  // [nw][16] partial sums of squares (prologue with RMSNorm)
+  // [nw][16] row scales: each wave writes its own copy and reads only that,
+  // so no wave depends on another's write (every wave computes the same
+  // values, bit for bit, from the same partials in the same order)
+  float* srow = part + nw * 16;
+  float* psq = srow + nw * 16;  // [nw][16] partial sums of squares (prologue with RMSNorm)
   // this wave's codes: [SBW][M][256]
   int8_t* qw = reinterpret_cast<int8_t*>(psq + (PRO ? nw * 16 : 0)) +
                (size_t)wave * SBW * a.M * 256;
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
         s += kEps;
         mult = a.c / s;
       }
-      if (wave == 0 && lane == m) srow[m] = s;
+      if (lane == m) srow[wave * 16 + m] = s;
 #pragma unroll
       for (int r = 0; r < SBW; ++r) {
         unsigned word = 0;
@@ -524,7 +527,7 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
   {
     const int m0 = 4 * (lane >> 4);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s_row[v] = srow[m0 + v < a.M ? m0 + v : 0];
+    for (int v = 0; v < 4; ++v) s_row[v] = srow[wave * 16 + (m0 + v < a.M ? m0 + v : 0)];
   }
   gemv_finish<CT, false>(a, acc, red, s_row, nw, alpha);
 }
@@ -709,7 +712,7 @@ hipError_t launch_fused_ct(const GemvArgs& a, const Prologue& pro, hipStream_t s
   const int nSB = ((a.K >> 6) + 3) >> 2;
   // at least CT waves: the finish stores column tile ct from wave ct
   const int nw = (nSB + SBW - 1) / SBW > CT ? (nSB + SBW - 1) / SBW : CT;
-  const size_t lds = (size_t)nw * CT * 1024 + (size_t)nw * 16 * 4 + 64 +
+  const size_t lds = (size_t)nw * CT * 1024 + 2 * (size_t)nw * 16 * 4 +
                      (PRO ? (size_t)nw * 16 * 4 : 0) + (size_t)nw * SBW * a.M * 256;
   auto kern = fused_decode_kernel<XT, BITS, MG, CT, SBW, PRO, HAD>;
   hipError_t e = ensure_lds(kern, lds);

@@ -32,15 +32,13 @@
 // and writes the codes of their first, second and third weights as three
 // words.
 #include "kernels.h"
-#include "ternary_common.cuh"
-#include "decode_common.cuh"
+#include "ternary_common.h"
+#include "decode_common.h"
 
 namespace bitnet {
 namespace {
 
 constexpr float kEps = 1e-7f;
-constexpr int kTl2BlockK = 384;       // weights per block
-constexpr int kTl2BlockBytes = 80;    // 64 index bytes + 16 sign bytes
 constexpr int kTl2SuperK = 768;       // weights per super-block (two blocks)
 
 // One thread per (column, block, group): 32 triplets = 96 weights read from
@@ -312,10 +310,6 @@ hipError_t launch_tl2_t(const void* x, const uint8_t* Wt, const float* alpha, fl
 }
 
 }  // namespace
-
-size_t tl2_bytes(int64_t N, int64_t K) {
-  return (size_t)N * (size_t)((K + kTl2BlockK - 1) / kTl2BlockK) * kTl2BlockBytes;
-}
 
 hipError_t launch_repack_tl2(const uint8_t* Wpacked, int64_t N, int K, uint8_t* Wtl2,
                              hipStream_t stream) {
