@@ -103,3 +103,29 @@ def assert_y_with_flips(y_gpu, q_gpu, t_gpu, q_ref, t_ref, s_ref, alpha, bits, y
     err = float(np.linalg.norm(excess) / max(np.linalg.norm(y_ref), 1e-300))
     assert err <= Y_TOL, f"y: error beyond the flip allowance {err:.3e} > {Y_TOL}"
     return err
+
+
+def assert_y_in_band(y_gpu, t_gpu, q_ref, p_ref, t_ref, s_ref, alpha, bits, y_ref):
+    """End-to-end check of a forward whose codes are not visible (the fused
+    single-kernel decode, the TL2 decode): its codes may differ from the
+    oracle's only by the +-1 flips the rounding band allows, i.e. at the
+    positions whose oracle pre-round value lies within 1e-4 of a .5 boundary.
+    Each such position may move y[m, n] by alpha * s_m / c * |t[n, k]|, and
+    each weight flip by alpha * s_m / c * |q[m, k]|; that allowance is taken
+    off each element's error and the rest must meet the 1e-3 rule. With no
+    position in the band this is the plain relative Frobenius check."""
+    t_gpu = np.asarray(t_gpu, dtype=np.float64)
+    t_ref = np.asarray(t_ref, dtype=np.float64)
+    q_ref = np.asarray(q_ref, dtype=np.float64)
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    in_band = (oracle.quant_boundary_distance(p_ref) < BAND).astype(np.float64)
+    dt = np.abs(t_gpu - t_ref)
+    if not in_band.any() and not dt.any():
+        return assert_y_close(y_gpu, y_ref)
+    c = oracle.INT8_SCALE if bits == 8 else oracle.INT4_SCALE
+    allowance = (in_band @ np.abs(t_gpu).T + np.abs(q_ref) @ dt.T) * \
+        (alpha * np.asarray(s_ref)[:, None] / c)
+    excess = np.maximum(np.abs(y_gpu - y_ref) - allowance * (1 + 1e-6), 0.0)
+    err = float(np.linalg.norm(excess) / max(np.linalg.norm(y_ref), 1e-300))
+    assert err <= Y_TOL, f"y: error beyond the rounding-band allowance {err:.3e} > {Y_TOL}"
+    return err

@@ -16,7 +16,8 @@ import torch
 import oracle
 import bit_activation_linear_amd as bl
 from bit_activation_linear_amd import workloads
-from parity_util import assert_codes_match, assert_packed_match, assert_y_close, assert_y_with_flips, decode_packed
+from parity_util import (assert_codes_match, assert_packed_match, assert_y_close, assert_y_in_band,
+                         assert_y_with_flips, decode_packed)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -69,11 +70,12 @@ def _run(M, K, N, bits, had, x_dtype, swiglu, rms, gamma, seed):
                         ref["s"], a_ref, bits, ref["y64"])
     # The forward is those two stages, bit for bit, except for the decode
     # shapes it runs as one fused kernel: there the statistic and the sum of
-    # squares are reduced in another order, an ulp of a scale can move a code
-    # on a rounding boundary, and one moved code shifts an output row.
+    # squares are reduced in another order, so an ulp of a scale can move a
+    # code on a rounding boundary. That forward is compared with the oracle
+    # directly, each code in the rounding band allowed its bounded effect.
     if bl.forward_workspace_bytes(M, K, N, bits, had) == 0:
-        assert_y_close(y.cpu().numpy(), y2.cpu().numpy().astype(np.float64), what="fused vs staged",
-                       tol=2e-3)
+        assert_y_in_band(y.cpu().numpy(), decode_packed(Wp.cpu().numpy()), ref["q"], ref["p"],
+                         t_ref, ref["s"], a_ref, bits, ref["y64"])
     else:
         np.testing.assert_array_equal(y.cpu().numpy(), y2.cpu().numpy())
 

@@ -7,8 +7,9 @@ SignedUnsignedWeightPacker) on the GPU, through the C ABI.
   bytes. It takes the same quantization steps as the 2-bit single-token
   kernel: with int8 (absmax, order-free) its output must equal the 2-bit
   forward's bit for bit; with int4 the absmean sums in another order, and a
-  code on a rounding boundary may move. Both are also compared with the fp64
-  oracle at the forward's tolerance.
+  code on a rounding boundary may move. Both are compared with the fp64
+  oracle at the forward's tolerance, each code in the rounding band allowed
+  its bounded effect on the output.
 """
 
 import sys
@@ -20,7 +21,7 @@ import torch
 import oracle
 import bit_activation_linear_amd as bl
 from bit_activation_linear_amd import workloads
-from parity_util import assert_y_close
+from parity_util import assert_y_close, assert_y_in_band
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -73,12 +74,12 @@ def test_forward_tl2(K, N, bits, xdt):
     torch.cuda.synchronize()
     t_ref, a_ref, _ = oracle.ternarize(case["W"])
     ref = oracle.forward(case["x"], xdt, t_ref, a_ref, bits, 0)
-    assert_y_close(y_tl2.cpu().numpy(), ref["y64"], what="TL2 forward vs oracle")
+    # the TL2 kernel's codes are not visible: compared with the oracle, each
+    # code in the rounding band allowed its bounded effect on y
+    assert_y_in_band(y_tl2.cpu().numpy(), t_ref, ref["q"], ref["p"], t_ref, ref["s"], a_ref, bits,
+                     ref["y64"])
     if bits == 8:
         np.testing.assert_array_equal(y_tl2.cpu().numpy(), y_2b.cpu().numpy())
-    else:
-        assert_y_close(y_tl2.cpu().numpy(), y_2b.cpu().numpy().astype(np.float64),
-                       what="TL2 vs 2-bit forward", tol=2e-3)
 
 
 def test_forward_tl2_headline_full_size():

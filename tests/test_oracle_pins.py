@@ -233,6 +233,67 @@ def test_zero_row_quantizes_to_zero():
         np.testing.assert_array_equal(s, [oracle.EPS, oracle.EPS])
 
 
+def test_quant_boundary_distance_hand_values():
+    """Distance of a pre-round value from the nearest rounding boundary
+    (k + 1/2) of RoundClip ([engine] Eq. 1, 5, 6): values worked by hand."""
+    p = np.array([2.5, 2.0, -1.49, -2.5, 126.99995, 0.0, 0.25, -0.75, 7.5001])
+    want = np.array([0.0, 0.5, 0.01, 0.0, 0.49995, 0.5, 0.25, 0.25, 0.0001])
+    np.testing.assert_allclose(oracle.quant_boundary_distance(p), want, rtol=0, atol=1e-9)
+
+
+def test_quant_boundary_distance_is_the_rounding_margin():
+    """d(p) is exactly how far p can move before rint(p) changes: every shift
+    below d keeps the rounded value, a shift just beyond d (towards the
+    boundary) changes it. A slip such as |p - rint(p)| (the distance to the
+    integer, 1/2 - d) fails this."""
+    rng = np.random.default_rng(41)
+    p = rng.uniform(-130, 130, 20000)
+    d = oracle.quant_boundary_distance(p)
+    assert np.all((d >= 0) & (d <= 0.5))
+    toward = np.sign(p - np.rint(p))  # direction of the nearer boundary
+    toward[toward == 0] = 1.0
+    keep = d > 1e-9
+    inside = p + 0.999 * d * toward
+    beyond = p + (d + 1e-7) * toward
+    np.testing.assert_array_equal(np.rint(inside[keep]), np.rint(p[keep]))
+    assert np.all(np.rint(beyond[keep & (d < 0.4999)]) != np.rint(p[keep & (d < 0.4999)]))
+
+
+def test_in_band_rule_accepts_band_flips_and_rejects_others():
+    """The GPU parity rule for forwards whose codes are not visible: a +-1
+    code flip at a position inside the 1e-4 band is absorbed by its bounded
+    effect on y; the same flip at a position outside the band is not (the
+    mistake is planted in an oracle result, on the CPU)."""
+    from parity_util import assert_y_in_band
+
+    rng = np.random.default_rng(43)
+    M, K, N = 3, 128, 24
+    x = rng.standard_normal((M, K))
+    W = rng.standard_normal((N, K)) * 0.02
+    t, a, _ = oracle.ternarize(W)
+    q, s, p = oracle.quantize_activations(x, 4)
+    # place one value of row 1 exactly on a rounding boundary's band
+    k_band = 5
+    p = p.copy()
+    p[1, k_band] = np.floor(p[1, k_band]) + 0.5 + 3e-5
+    y_ref = oracle.dequantize(oracle.ternary_matmul_i64(q, t), a, s, 4)
+    assert_y_in_band(y_ref, t, q, p, t, s, a, 4, y_ref)
+    # one flipped code moves its output row well past 1e-3 of ||y|| here;
+    # flipped inside the band it is allowed, outside it is not
+    def flipped(k):
+        q2 = q.astype(np.int64).copy()
+        q2[1, k] += 1
+        return oracle.dequantize(oracle.ternary_matmul_i64(q2, t), a, s, 4)
+    y_in = flipped(k_band)
+    assert_y_in_band(y_in, t, q, p, t, s, a, 4, y_ref)
+    k_out = 9
+    assert oracle.quant_boundary_distance(p[1, k_out]) > 1e-4
+    y_out = flipped(k_out)
+    assert np.linalg.norm(y_out - y_ref) > 1e-3 * np.linalg.norm(y_ref)
+    with pytest.raises(AssertionError):
+        assert_y_in_band(y_out, t, q, p, t, s, a, 4, y_ref)
+
+
 def test_quant_rejects_bad_bits():
     with pytest.raises(ValueError):
         oracle.quantize_activations(np.zeros((1, 4)), 6)
