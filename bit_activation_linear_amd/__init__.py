@@ -14,12 +14,14 @@ from .api import (  # noqa: F401
     hbitlinear_backward,
     hbitlinear_forward,
     hbitlinear_forward_prologue,
+    hbitlinear_forward_stages,
     hbitlinear_forward_tl2,
     kv_quantize,
     pack_2bit,
     pack_tl2,
     quantize_activations,
     quantize_activations_prologue,
+    stream_read,
     ternarize_weights,
     ternary_gemm_i32,
     ternary_linear_dequant,

@@ -49,6 +49,8 @@ SIGNATURES = {
                                          _ptr, _ptr, _size, _ptr]),
     "bitnet_quantize_activations": (_int, [_ptr, _int, _i64, _i64, _int, _int, _ptr, _ptr, _ptr,
                                            _ptr]),
+    "bitnet_hbitlinear_forward_stages": (_int, [_ptr, _int, _i64, _i64, _ptr, _i64, _ptr, _int,
+                                                _int, _ptr, _ptr, _size, _int, _ptr]),
     "bitnet_ternary_gemm_i32": (_int, [_ptr, _i64, _i64, _ptr, _i64, _ptr, _ptr]),
     "bitnet_ternary_linear_dequant": (_int, [_ptr, _ptr, _ptr, _i64, _i64, _ptr, _i64, _ptr,
                                              _int, _ptr, _ptr]),
@@ -67,7 +69,13 @@ SIGNATURES = {
     "bitnet_backward_workspace_bytes": (_size, [_i64, _i64, _i64, _int, _int, _int]),
     "bitnet_hbitlinear_backward": (_int, [_ptr, _int, _i64, _i64, _ptr, _ptr, _i64, _ptr, _ptr,
                                           _int, _int, _ptr, _ptr, _ptr, _size, _ptr]),
+    "bitnet_stream_read": (_int, [_ptr, _size, _ptr, _ptr]),
+    "bitnet_test_fail_next_launch": (None, [_int]),
 }
+
+# stages of bitnet_hbitlinear_forward_stages
+STAGE_QUANTIZE = 1
+STAGE_PRODUCT = 2
 
 _lock = threading.Lock()
 _lib = None

@@ -36,6 +36,31 @@ def _require(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_out(t: torch.Tensor, name: str, dtype, shape, device) -> None:
+    """A caller-supplied output: the C ABI only sees its address, so its
+    dtype, shape, device and contiguity are checked here (a tensor that is too
+    small or of the wrong type would be written past its end)."""
+    _require(t, name, (dtype,), len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _check_workspace(ws: torch.Tensor, need: int, device) -> None:
+    _require(ws, "workspace", (torch.uint8,), 1)
+    if ws.device != device:
+        raise ValueError(f"workspace must be on {device}, got {ws.device}")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} are required")
+
+
+def _same_device(device, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def _x_dtype(x: torch.Tensor) -> int:
     return _lib.BF16 if x.dtype == torch.bfloat16 else _lib.F32
 
@@ -50,11 +75,14 @@ def ternarize_weights(W: torch.Tensor, out: Optional[torch.Tensor] = None,
     N, K = W.shape
     if out is None:
         out = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    _check_out(out, "out", torch.uint8, (N, K // 4), W.device)
     if alpha is None:
         alpha = torch.empty((1,), dtype=torch.float32, device=W.device)
+    _check_out(alpha, "alpha", torch.float32, (1,), W.device)
+    ws_bytes = _lib.load().bitnet_ternarize_workspace_bytes(N, K)
     if workspace is None:
-        ws_bytes = _lib.load().bitnet_ternarize_workspace_bytes(N, K)
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
+    _check_workspace(workspace, ws_bytes, W.device)
     _lib.call("bitnet_ternarize_weights", W.data_ptr(), N, K, out.data_ptr(), alpha.data_ptr(),
               workspace.data_ptr(), workspace.numel(), _stream_ptr(W))
     return out, alpha
@@ -66,6 +94,7 @@ def pack_2bit(T: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tens
     N, K = T.shape
     if out is None:
         out = torch.empty((N, K // 4), dtype=torch.uint8, device=T.device)
+    _check_out(out, "out", torch.uint8, (N, K // 4), T.device)
     _lib.call("bitnet_pack_2bit", T.data_ptr(), N, K, out.data_ptr(), _stream_ptr(T))
     return out
 
@@ -82,8 +111,7 @@ def pack_tl2(Wpacked: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch
     nbytes = tl2_bytes(N, K)
     if out is None:
         out = torch.empty((N, nbytes // max(N, 1)), dtype=torch.uint8, device=Wpacked.device)
-    elif out.numel() < nbytes:
-        raise ValueError("out is smaller than the TL2 encoding")
+    _check_out(out, "out", torch.uint8, (N, nbytes // max(N, 1)), Wpacked.device)
     _lib.call("bitnet_pack_tl2", Wpacked.data_ptr(), N, K, out.data_ptr(), _stream_ptr(Wpacked))
     return out
 
@@ -98,8 +126,10 @@ def hbitlinear_forward_tl2(x: torch.Tensor, Wtl2: torch.Tensor, alpha: torch.Ten
     N = Wtl2.shape[0]
     if Wtl2.numel() != tl2_bytes(N, K):
         raise ValueError("Wtl2 does not hold the TL2 encoding of [N, K] weights")
+    _same_device(x.device, Wtl2=Wtl2, alpha=alpha)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check_out(out, "out", torch.float32, (M, N), x.device)
     _lib.call("bitnet_hbitlinear_forward_tl2", x.data_ptr(), _x_dtype(x), M, K, Wtl2.data_ptr(), N,
               alpha.data_ptr(), int(bits), out.data_ptr(), _stream_ptr(x))
     return out
@@ -120,16 +150,54 @@ def hbitlinear_forward(x: torch.Tensor, Wpacked: torch.Tensor, alpha: torch.Tens
     N = Wpacked.shape[0]
     if Wpacked.shape[1] * 4 != K:
         raise ValueError(f"Wpacked has {Wpacked.shape[1]} bytes per row, expected K/4 = {K // 4}")
+    _same_device(x.device, Wpacked=Wpacked, alpha=alpha)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check_out(out, "out", torch.float32, (M, N), x.device)
     need = forward_workspace_bytes(M, K, N, bits, hadamard)
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _check_workspace(workspace, need, x.device)
     ws_ptr, ws_len = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
     _lib.call("bitnet_hbitlinear_forward", x.data_ptr(), _x_dtype(x), M, K, Wpacked.data_ptr(), N,
               alpha.data_ptr(), int(bits), int(hadamard), out.data_ptr(), ws_ptr, ws_len,
               _stream_ptr(x))
     return out
+
+
+def hbitlinear_forward_stages(x: torch.Tensor, Wpacked: torch.Tensor, alpha: torch.Tensor,
+                              bits: int, hadamard: int, stages: int, out: torch.Tensor,
+                              workspace: torch.Tensor) -> torch.Tensor:
+    """One stage of the forward on its own kernels and workspace format:
+    stages = 1 writes the transform + quantization stage's results into
+    `workspace`, 2 reads them and writes `out`, 3 is the whole forward."""
+    _require(x, "x", (torch.float32, torch.bfloat16), 2)
+    _require(Wpacked, "Wpacked", (torch.uint8,), 2)
+    _require(alpha, "alpha", (torch.float32,), 1)
+    M, K = x.shape
+    N = Wpacked.shape[0]
+    if Wpacked.shape[1] * 4 != K:
+        raise ValueError(f"Wpacked has {Wpacked.shape[1]} bytes per row, expected K/4 = {K // 4}")
+    _same_device(x.device, Wpacked=Wpacked, alpha=alpha)
+    _check_out(out, "out", torch.float32, (M, N), x.device)
+    need = forward_workspace_bytes(M, K, N, bits, hadamard)
+    _check_workspace(workspace, need, x.device)
+    _lib.call("bitnet_hbitlinear_forward_stages", x.data_ptr(), _x_dtype(x), M, K,
+              Wpacked.data_ptr(), N, alpha.data_ptr(), int(bits), int(hadamard), out.data_ptr(),
+              workspace.data_ptr(), workspace.numel(), int(stages), _stream_ptr(x))
+    return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Plain read of every byte of `buf` (contiguous, numel * itemsize a
+    multiple of 16) with no arithmetic: the streaming-read ceiling that the
+    forward's weight stream is measured against. `sink`: int32 [1]."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous tensor on a HIP device")
+    _check_out(sink, "sink", torch.int32, (1,), buf.device)
+    _lib.call("bitnet_stream_read", buf.data_ptr(), buf.numel() * buf.element_size(),
+              sink.data_ptr(), _stream_ptr(buf))
 
 
 def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
@@ -144,10 +212,10 @@ def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
         codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if scales is None:
         scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check_out(codes, "codes", torch.int8, (M, K), x.device)
+    _check_out(scales, "scales", torch.float32, (M,), x.device)
     if rowsum is not None:
-        _require(rowsum, "rowsum", (torch.int32,), 1)
-        if rowsum.shape[0] != M:
-            raise ValueError("rowsum must have one entry per token")
+        _check_out(rowsum, "rowsum", torch.int32, (M,), x.device)
     _lib.call("bitnet_quantize_activations", x.data_ptr(), _x_dtype(x), M, K, int(bits),
               int(hadamard), codes.data_ptr(), scales.data_ptr(),
               rowsum.data_ptr() if rowsum is not None else None, _stream_ptr(x))
@@ -157,13 +225,9 @@ def quantize_activations(x: torch.Tensor, bits: int, hadamard: int,
 def _prologue_args(x: torch.Tensor, up: Optional[torch.Tensor], rmsnorm: bool,
                    norm_weight: Optional[torch.Tensor]):
     if up is not None:
-        _require(up, "up", (x.dtype,), 2)
-        if up.shape != x.shape:
-            raise ValueError(f"up must have x's shape {tuple(x.shape)}, got {tuple(up.shape)}")
+        _check_out(up, "up", x.dtype, tuple(x.shape), x.device)
     if norm_weight is not None:
-        _require(norm_weight, "norm_weight", (torch.float32,), 1)
-        if norm_weight.shape[0] != x.shape[1]:
-            raise ValueError("norm_weight must have K elements")
+        _check_out(norm_weight, "norm_weight", torch.float32, (x.shape[1],), x.device)
     return (up.data_ptr() if up is not None else None, int(bool(rmsnorm)),
             norm_weight.data_ptr() if (rmsnorm and norm_weight is not None) else None)
 
@@ -188,11 +252,14 @@ def hbitlinear_forward_prologue(x: torch.Tensor, Wpacked: torch.Tensor, alpha: t
     if Wpacked.shape[1] * 4 != K:
         raise ValueError(f"Wpacked has {Wpacked.shape[1]} bytes per row, expected K/4 = {K // 4}")
     up_ptr, rms, g_ptr = _prologue_args(x, up, rmsnorm, norm_weight)
+    _same_device(x.device, Wpacked=Wpacked, alpha=alpha)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check_out(out, "out", torch.float32, (M, N), x.device)
     need = forward_prologue_workspace_bytes(M, K, N, bits, hadamard)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _check_workspace(workspace, need, x.device)
     _lib.call("bitnet_hbitlinear_forward_prologue", x.data_ptr(), up_ptr, _x_dtype(x), M, K, rms,
               g_ptr, float(norm_eps), Wpacked.data_ptr(), N, alpha.data_ptr(), int(bits),
               int(hadamard), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
@@ -265,13 +332,20 @@ def hbitlinear_backward(dy: torch.Tensor, codes: torch.Tensor, scales: torch.Ten
         raise ValueError("codes and scales must have one row per row of dy")
     if Wpacked.shape[0] != N or Wpacked.shape[1] * 4 != K:
         raise ValueError(f"Wpacked must be [N, K/4] = [{N}, {K // 4}], got {tuple(Wpacked.shape)}")
+    _same_device(dy.device, codes=codes, scales=scales, Wpacked=Wpacked, alpha=alpha)
     if want_dx and dx is None:
         dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
     if want_dw and dw is None:
         dw = torch.empty((N, K), dtype=torch.float32, device=dy.device)
+    if want_dx:
+        _check_out(dx, "dx", torch.float32, (M, K), dy.device)
+    if want_dw:
+        _check_out(dw, "dw", torch.float32, (N, K), dy.device)
     need = backward_workspace_bytes(M, K, N, dy.dtype, want_dx, want_dw)
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=dy.device)
+    if workspace is not None:
+        _check_workspace(workspace, need, dy.device)
     ws_ptr, ws_len = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
     _lib.call("bitnet_hbitlinear_backward", dy.data_ptr(), _x_dtype(dy), M, N, codes.data_ptr(),
               scales.data_ptr(), K, Wpacked.data_ptr(), alpha.data_ptr(), int(bits), int(hadamard),
@@ -289,8 +363,10 @@ def ternary_gemm_i32(codes: torch.Tensor, Wpacked: torch.Tensor,
     N = Wpacked.shape[0]
     if Wpacked.shape[1] * 4 != K:
         raise ValueError("Wpacked row length does not match K/4")
+    _same_device(codes.device, Wpacked=Wpacked)
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=codes.device)
+    _check_out(out, "out", torch.int32, (M, N), codes.device)
     _lib.call("bitnet_ternary_gemm_i32", codes.data_ptr(), M, K, Wpacked.data_ptr(), N,
               out.data_ptr(), _stream_ptr(codes))
     return out
@@ -309,12 +385,14 @@ def ternary_linear_dequant(codes: torch.Tensor, scales: torch.Tensor, Wpacked: t
     N = Wpacked.shape[0]
     if Wpacked.shape[1] * 4 != K:
         raise ValueError("Wpacked row length does not match K/4")
+    if scales.shape[0] != M:
+        raise ValueError("scales must have one entry per token")
+    _same_device(codes.device, scales=scales, Wpacked=Wpacked, alpha=alpha)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    _check_out(out, "out", torch.float32, (M, N), codes.device)
     if rowsum is not None:
-        _require(rowsum, "rowsum", (torch.int32,), 1)
-        if rowsum.shape[0] != M:
-            raise ValueError("rowsum must have one entry per token")
+        _check_out(rowsum, "rowsum", torch.int32, (M,), codes.device)
     _lib.call("bitnet_ternary_linear_dequant", codes.data_ptr(), scales.data_ptr(),
               rowsum.data_ptr() if rowsum is not None else None, M, K, Wpacked.data_ptr(), N,
               alpha.data_ptr(), int(bits), out.data_ptr(), _stream_ptr(codes))

@@ -14,6 +14,9 @@
 namespace {
 
 thread_local std::string g_last_error;
+// HIP error the next launch on this thread reports instead of launching (test
+// hook; 0 = none).
+thread_local int g_injected_error = 0;
 
 bitnet_status fail(bitnet_status st, const char* fmt, ...) {
   char buf[512];
@@ -35,14 +38,26 @@ bitnet_status hip_status(hipError_t e, const char* what) {
   return fail(BITNET_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
+// Called by every entry point after its arguments have been validated and
+// before its first launch: a pending injected error is reported as that
+// launch's failure (BITNET_ERR_HIP) and nothing is launched.
+bitnet_status launch_guard(const char* fn) {
+  if (g_injected_error == 0) return BITNET_OK;
+  const hipError_t e = static_cast<hipError_t>(g_injected_error);
+  g_injected_error = 0;
+  return hip_status(e, fn);
+}
+
 size_t round_up(size_t v) { return bitnet::ws_round(v); }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
-// Largest M the prefill grid addresses (grid.y <= 65535 tiles of 128 rows).
-constexpr int64_t kMaxM = (int64_t)65535 * 128;
+// Largest M: the kernels carry token counts, row indices and the prefill
+// tile count as 32-bit ints (the tile count (M / 128 + 1) (N / 128 + 1) must
+// stay below 2^31 as well; checked with N below).
+constexpr int64_t kMaxM = (int64_t)1 << 23;
 
 bitnet_status check_dims(const char* fn, int64_t M, int64_t K, int64_t N) {
   if (M < 0 || K < 0 || N < 0)
@@ -50,7 +65,7 @@ bitnet_status check_dims(const char* fn, int64_t M, int64_t K, int64_t N) {
                 (long long)M, (long long)K, (long long)N);
   if (K == 0 || K % 64 != 0)
     return fail(BITNET_ERR_ALIGN, "%s: K=%lld must be a positive multiple of 64", fn, (long long)K);
-  if (M > kMaxM || N > INT_MAX)
+  if (M > kMaxM || N > INT_MAX || (M / 128 + 1) * (N / 128 + 1) >= ((int64_t)1 << 31))
     return fail(BITNET_ERR_UNSUPPORTED, "%s: M=%lld or N=%lld too large", fn, (long long)M,
                 (long long)N);
   return BITNET_OK;
@@ -121,6 +136,8 @@ int bitnet_abi_version(void) { return BITNET_ABI_VERSION; }
 
 const char* bitnet_last_error(void) { return g_last_error.c_str(); }
 
+void bitnet_test_fail_next_launch(int hip_error) { g_injected_error = hip_error; }
+
 size_t bitnet_ternarize_workspace_bytes(int64_t N, int64_t K) {
   (void)N;
   (void)K;
@@ -140,6 +157,7 @@ bitnet_status bitnet_ternarize_weights(const float* W, int64_t N, int64_t K, uin
                 bitnet_ternarize_workspace_bytes(N, K));
   if (!aligned(W, 16) || !aligned(Wpacked, 16) || !aligned(ws, 16) || !aligned(alpha, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   double* partials = static_cast<double*>(ws);
   int n_partials = 0;
   hipError_t e = bitnet::launch_absmean_partial(W, N * K, partials, &n_partials, stream);
@@ -156,6 +174,7 @@ bitnet_status bitnet_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* W
   if (!T || !Wpacked) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(T, 16) || !aligned(Wpacked, 16))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   return hip_status(bitnet::launch_pack_2bit(T, N, K, Wpacked, stream), fn);
 }
 
@@ -175,6 +194,7 @@ bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, i
   if (!x || !codes || !scales) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(rowsum, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   return hip_status(bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, codes,
                                             scales, stream, nullptr, rowsum),
                     fn);
@@ -192,6 +212,7 @@ bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
   if (!codes || !Wpacked || !acc) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(codes, 16) || !aligned(Wpacked, 16) || !aligned(acc, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   return hip_status(bitnet::launch_ternary_matmul(codes, nullptr, M, (int)K, Wpacked, N, nullptr,
                                                   8, nullptr, acc, stream),
                     fn);
@@ -213,16 +234,24 @@ bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* sc
   if (!aligned(codes, 16) || !aligned(Wpacked, 16) || !aligned(y, 4) || !aligned(scales, 4) ||
       !aligned(alpha, 4) || !aligned(rowsum, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   return hip_status(bitnet::launch_ternary_matmul(codes, scales, M, (int)K, Wpacked, N, alpha,
                                                   bits, y, nullptr, stream, rowsum),
                     fn);
 }
 
-bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int64_t M, int64_t K,
-                                        const uint8_t* Wpacked, int64_t N, const float* alpha,
-                                        int bits, int hadamard, float* y, void* ws,
-                                        size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "bitnet_hbitlinear_forward";
+}  // extern "C"
+
+namespace {
+
+// The forward, or the stages of it that `stages` selects (both for the
+// forward itself).
+bitnet_status forward_impl(const char* fn, const void* x, bitnet_dtype x_dtype, int64_t M,
+                           int64_t K, const uint8_t* Wpacked, int64_t N, const float* alpha,
+                           int bits, int hadamard, float* y, void* ws, size_t ws_bytes, int stages,
+                           hipStream_t stream) {
+  if (stages < 1 || stages > 3)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: stages=%d must be 1, 2 or 3", fn, stages);
   if (bitnet_status st = check_dims(fn, M, K, N)) return st;
   if (bitnet_status st = check_quant_args(fn, K, bits, hadamard, x_dtype)) return st;
   if (M == 0 || N == 0) return ok();
@@ -235,6 +264,10 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
   if (!aligned(x, 16) || !aligned(Wpacked, 16) || (need > 0 && !aligned(ws, 16)) ||
       !aligned(y, 4) || !aligned(alpha, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (need == 0 && stages != BITNET_STAGE_QUANTIZE + BITNET_STAGE_PRODUCT)
+    return fail(BITNET_ERR_UNSUPPORTED,
+                "%s: this shape runs as one fused kernel; its stages cannot run apart", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   if (need == 0) {
     return hip_status(bitnet::launch_fused_decode(x, (int)x_dtype, M, (int)K, Wpacked, N, alpha,
                                                   bits, y, stream, nullptr, hadamard),
@@ -242,12 +275,49 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
   }
   const ForwardWorkspace w = carve_forward(ws, M, K);
   const bool nib = use_nibble_codes(M, K, bits);
-  hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
-                                         w.scales, stream, nullptr, w.rowsum, nib);
-  if (e != hipSuccess) return hip_status(e, fn);
-  e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
-                                    nullptr, stream, w.rowsum, nib);
+  hipError_t e = hipSuccess;
+  if (stages & BITNET_STAGE_QUANTIZE) {
+    e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes, w.scales,
+                                stream, nullptr, w.rowsum, nib);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  if (stages & BITNET_STAGE_PRODUCT)
+    e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
+                                      nullptr, stream, w.rowsum, nib);
   return hip_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int64_t M, int64_t K,
+                                        const uint8_t* Wpacked, int64_t N, const float* alpha,
+                                        int bits, int hadamard, float* y, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  return forward_impl("bitnet_hbitlinear_forward", x, x_dtype, M, K, Wpacked, N, alpha, bits,
+                      hadamard, y, ws, ws_bytes, BITNET_STAGE_QUANTIZE + BITNET_STAGE_PRODUCT,
+                      stream);
+}
+
+bitnet_status bitnet_hbitlinear_forward_stages(const void* x, bitnet_dtype x_dtype, int64_t M,
+                                               int64_t K, const uint8_t* Wpacked, int64_t N,
+                                               const float* alpha, int bits, int hadamard,
+                                               float* y, void* ws, size_t ws_bytes, int stages,
+                                               hipStream_t stream) {
+  return forward_impl("bitnet_hbitlinear_forward_stages", x, x_dtype, M, K, Wpacked, N, alpha,
+                      bits, hadamard, y, ws, ws_bytes, stages, stream);
+}
+
+bitnet_status bitnet_stream_read(const void* p, size_t bytes, uint32_t* sink,
+                                 hipStream_t stream) {
+  const char* fn = "bitnet_stream_read";
+  if (bytes == 0) return ok();
+  if (!p || !sink) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(p, 16) || !aligned(sink, 4) || bytes % 16 != 0)
+    return fail(BITNET_ERR_ALIGN, "%s: p must be 16-byte aligned and bytes a multiple of 16", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
+  return hip_status(bitnet::launch_stream_read(p, bytes, sink, stream), fn);
 }
 
 size_t bitnet_forward_prologue_workspace_bytes(int64_t M, int64_t K, int64_t N, int bits,
@@ -356,6 +426,7 @@ bitnet_status bitnet_hbitlinear_backward(const void* dy, bitnet_dtype dy_dtype, 
       !aligned(dx, 4) || !aligned(dw, 4) || !aligned(scales, 4) || !aligned(alpha, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
 
+  if (bitnet_status st = launch_guard(fn)) return st;
   const BackwardWorkspace w = carve_backward(ws, M, K, N);
   hipError_t e = hipSuccess;
   if (dx && M > 0) {
@@ -427,6 +498,7 @@ bitnet_status bitnet_quantize_activations_prologue(const void* x, const void* up
   if (!x || !codes || !scales) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   const bitnet::Prologue pro{up, rmsnorm ? norm_weight : nullptr, norm_eps, rmsnorm};
   return hip_status(bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, codes,
                                             scales, stream, &pro),
@@ -454,6 +526,7 @@ bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, 
   if (!aligned(x, 16) || !aligned(Wpacked, 16) || !aligned(ws, 16) || !aligned(y, 4) ||
       !aligned(alpha, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   const bitnet::Prologue pro{up, rmsnorm ? norm_weight : nullptr, norm_eps, rmsnorm};
   if (forward_is_fused(M, K, N, hadamard)) {
     return hip_status(bitnet::launch_fused_decode(x, (int)x_dtype, M, (int)K, Wpacked, N, alpha,
@@ -494,6 +567,7 @@ bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R
   if (!kv || !codes || !scales) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(kv, 16) || !aligned(codes, 16) || !aligned(scales, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   return hip_status(bitnet::launch_kv_quantize(kv, (int)x_dtype, R, (int)D, (int)S, bits, codes,
                                                scales, stream),
                     fn);
@@ -512,6 +586,7 @@ bitnet_status bitnet_pack_tl2(const uint8_t* Wpacked, int64_t N, int64_t K, uint
   if (!Wpacked || !Wtl2) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(Wpacked, 16) || !aligned(Wtl2, 16))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   return hip_status(bitnet::launch_repack_tl2(Wpacked, N, (int)K, Wtl2, stream), fn);
 }
 
@@ -532,6 +607,7 @@ bitnet_status bitnet_hbitlinear_forward_tl2(const void* x, bitnet_dtype x_dtype,
   if (!x || !Wtl2 || !alpha || !y) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(x, 16) || !aligned(Wtl2, 16) || !aligned(y, 4) || !aligned(alpha, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
   return hip_status(bitnet::launch_tl2_decode(x, (int)x_dtype, (int)K, Wtl2, N, alpha, bits, y,
                                               stream),
                     fn);

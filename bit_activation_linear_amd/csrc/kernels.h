@@ -171,12 +171,21 @@ hipError_t launch_fwht_f32(const float* x, int64_t M, int K, float* out, hipStre
 // TL2 weight code (edge page mirror consolidation, 5 bits per 3 weights):
 // blocks of 128 triplets per column (64 index bytes, 16 sign bytes).
 constexpr int kTl2MaxK = 6 * 768;  // single-token TL2 decode: six 768-weight super-blocks
-size_t tl2_bytes(int64_t N, int64_t K);
+constexpr int kTl2BlockK = 384;     // weights per block
+constexpr int kTl2BlockBytes = 80;  // 64 index bytes + 16 sign bytes
+inline size_t tl2_bytes(int64_t N, int64_t K) {
+  return (size_t)N * (size_t)((K + kTl2BlockK - 1) / kTl2BlockK) * kTl2BlockBytes;
+}
 // 2-bit packed weights [N, K/4] -> TL2 [N, tl2_bytes / N].
 hipError_t launch_repack_tl2(const uint8_t* Wpacked, int64_t N, int K, uint8_t* Wtl2,
                              hipStream_t stream);
 // Single-token decode forward (M = 1, no transform, K <= kTl2MaxK) on TL2 weights.
 hipError_t launch_tl2_decode(const void* x, int x_dtype, int K, const uint8_t* Wtl2, int64_t N,
                              const float* alpha, int bits, float* y, hipStream_t stream);
+
+// Measurement: read `bytes` (a multiple of 16 is read; the tail is ignored)
+// with 16-byte loads and no arithmetic; sink receives a word only in the
+// (practically never met) case that the data's XOR equals a fixed constant.
+hipError_t launch_stream_read(const void* p, size_t bytes, unsigned* sink, hipStream_t stream);
 
 }  // namespace bitnet

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define BITNET_ABI_VERSION 2
+#define BITNET_ABI_VERSION 3
 #define BITNET_EPS 1e-7f
 /* Largest K the fused transform + quantizer stages in one CU's LDS (fp32). */
 #define BITNET_MAX_K 32768
@@ -92,9 +92,13 @@ bitnet_status bitnet_ternarize_weights(const float* W, int64_t N, int64_t K, uin
                                        float* alpha, void* ws, size_t ws_bytes,
                                        hipStream_t stream);
 
-/* Packs ternary values held one per int8 [N, K] into the block-64 layout.
- * Values are mapped by sign (negative -> -1, zero -> 0, positive -> +1).
- * Requires K % 64 == 0. */
+/* Packs ternary values held one per int8 [N, K] into the block-64 layout:
+ * the edge page's I2_S format (bitnet_cpp_edge.py, Table 1: 2 bits per
+ * weight, a ternary value per 2-bit field) with the blog page's LUT code
+ * w -> w + 1 (youngju.dev BitNet page, LUT simulation). Values are mapped by
+ * sign (negative -> -1, zero -> 0, positive -> +1).
+ *   T        int8 [N, K], read.   Wpacked  uint8 [N, K/4], written.
+ * Requires K % 64 == 0; both pointers 16-byte aligned. N = 0 is a no-op. */
 bitnet_status bitnet_pack_2bit(const int8_t* T, int64_t N, int64_t K, uint8_t* Wpacked,
                                hipStream_t stream);
 
@@ -130,6 +134,24 @@ bitnet_status bitnet_hbitlinear_forward(const void* x, bitnet_dtype x_dtype, int
                                         int bits, int hadamard, float* y, void* ws,
                                         size_t ws_bytes, hipStream_t stream);
 
+/* The forward, or one of its two stages, on the forward's own kernels and
+ * workspace format: stages = BITNET_STAGE_QUANTIZE writes the transform and
+ * quantization stage's results (codes, scales, code row sums) into ws;
+ * BITNET_STAGE_PRODUCT reads them from ws and writes y; both (3) is exactly
+ * bitnet_hbitlinear_forward. Running stage 1 then stage 2 on the same ws
+ * gives the forward's y bit for bit. Where the forward runs as one fused
+ * kernel (bitnet_forward_workspace_bytes = 0) only stages = 3 is accepted
+ * (BITNET_ERR_UNSUPPORTED otherwise). Arguments and errors as for
+ * bitnet_hbitlinear_forward; stages outside 1..3 is BITNET_ERR_INVALID_ARG.
+ * Used to time each stage's kernel alone. */
+#define BITNET_STAGE_QUANTIZE 1
+#define BITNET_STAGE_PRODUCT 2
+bitnet_status bitnet_hbitlinear_forward_stages(const void* x, bitnet_dtype x_dtype, int64_t M,
+                                               int64_t K, const uint8_t* Wpacked, int64_t N,
+                                               const float* alpha, int bits, int hadamard,
+                                               float* y, void* ws, size_t ws_bytes, int stages,
+                                               hipStream_t stream);
+
 /* The two stages of the forward, exposed for inspection and timing. They run
  * the kernels of the forward's two-launch path; where the forward fuses both
  * stages into one kernel (see bitnet_forward_workspace_bytes) that kernel
@@ -148,8 +170,14 @@ bitnet_status bitnet_quantize_activations(const void* x, bitnet_dtype x_dtype, i
                                           float* scales, int32_t* rowsum, hipStream_t stream);
 
 /* Exact integer product only: acc[m, n] = sum_k codes[m, k] * t[n, k], int32.
- * codes: int8 [M, K] with values in [-128, 127]. Requires K % 64 == 0 and
- * K <= BITNET_MAX_K. */
+ * This is the engine page's F.linear(x_q, w_q) of HBitLinear.forward before
+ * its two scales (the blog page's BitLinear_b158 integer form; the edge
+ * page's I2_S multiply-add, Table 1, "lossless"): every sum is exact, since
+ * |codes| <= 128 and K <= 32768.
+ *   codes    int8 [M, K], values in [-128, 127].
+ *   Wpacked  uint8 [N, K/4], block-64 layout.   acc  int32 [M, N], written.
+ * Requires K % 64 == 0 and K <= BITNET_MAX_K; codes and Wpacked 16-byte
+ * aligned, acc 4-byte aligned. */
 bitnet_status bitnet_ternary_gemm_i32(const int8_t* codes, int64_t M, int64_t K,
                                       const uint8_t* Wpacked, int64_t N, int32_t* acc,
                                       hipStream_t stream);
@@ -302,6 +330,25 @@ bitnet_status bitnet_hbitlinear_backward(const void* dy, bitnet_dtype dy_dtype, 
                                          int64_t K, const uint8_t* Wpacked, const float* alpha,
                                          int bits, int hadamard, float* dx, float* dw, void* ws,
                                          size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Measurement and test hooks                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Reads `bytes` at p with 16-byte loads and no arithmetic (a plain streaming
+ * read, no step of the layer): the bandwidth ceiling the forward's weight
+ * stream is measured against, and a way to push a buffer out of the caches.
+ * sink (one uint32 on the device) is written only if the XOR of all words
+ * read equals a fixed constant. Requires p 16-byte aligned and bytes % 16 == 0;
+ * bytes = 0 is a no-op. */
+bitnet_status bitnet_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/* Test hook: the next entry point on the calling thread that passes its
+ * argument checks fails as if its first kernel launch had returned the HIP
+ * error code hip_error (BITNET_ERR_HIP, with that code in
+ * bitnet_last_error()), and launches nothing; 0 clears a pending error.
+ * Makes no HIP call, so error handling can be exercised without a device. */
+void bitnet_test_fail_next_launch(int hip_error);
 
 #ifdef __cplusplus
 }

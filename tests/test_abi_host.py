@@ -2,20 +2,37 @@
 
 The library must load without a device, export every function the header
 declares, and reject every invalid argument before touching HIP.
+
+With BITNET_TEST_HOST_LIB set (tests/test_abi_sanitized.py does this in a
+child process), the same checks run against a host-only build of the ABI
+(abi.cpp with recording launcher stubs, under AddressSanitizer and
+UndefinedBehaviorSanitizer), and the dispatch tests at the end check which
+launchers valid calls reach.
 """
 
 import ctypes
+import os
 
 import pytest
 
 from bit_activation_linear_amd import _lib
 
 FAKE = 0x10000  # a 16-B aligned non-null address; never dereferenced on these paths
+HOST_LIB = os.environ.get("BITNET_TEST_HOST_LIB")
 
 
 @pytest.fixture(scope="module")
 def lib():
-    return _lib.load()
+    if not HOST_LIB:
+        return _lib.load()
+    host = ctypes.CDLL(HOST_LIB)
+    for name, (res, args) in _lib.SIGNATURES.items():
+        fn = getattr(host, name)
+        fn.restype = res
+        fn.argtypes = args
+    host.bitnet_stub_calls.restype = ctypes.c_char_p
+    _lib._lib = host  # _lib.call goes to the host build in this (child) process
+    return host
 
 
 def test_exports_every_declared_symbol(lib):
@@ -28,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_empty_error(lib):
-    assert lib.bitnet_abi_version() == 2
+    assert lib.bitnet_abi_version() == 3
 
 
 def test_workspace_sizes(lib):
@@ -308,3 +325,144 @@ def test_tl2_sizes_and_validation(lib):
     assert f(FAKE, _lib.BF16, 1, 100, FAKE, 16, FAKE, 8, FAKE, None) == _lib.ERR_ALIGN
     assert f(None, _lib.BF16, 1, 256, FAKE, 16, FAKE, 8, FAKE, None) == _lib.ERR_INVALID_ARG
     assert f(None, _lib.BF16, 0, 256, None, 16, None, 8, None, None) == _lib.OK
+
+
+def _stages(lib, stages, M=4, K=512, N=256, bits=4, had=1, x=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.bitnet_hbitlinear_forward_stages(x, _lib.BF16, M, K, FAKE, N, FAKE, bits, had, FAKE,
+                                                ws, ws_bytes, stages, None)
+
+
+def test_forward_stages_validation(lib):
+    assert _stages(lib, 0) == _lib.ERR_INVALID_ARG
+    assert _stages(lib, 4) == _lib.ERR_INVALID_ARG
+    assert _stages(lib, 1, bits=5) == _lib.ERR_BAD_BITS
+    assert _stages(lib, 2, x=None) == _lib.ERR_INVALID_ARG
+    assert _stages(lib, 1, ws=None, ws_bytes=0) == _lib.ERR_INVALID_ARG
+    # a shape the forward runs as one fused kernel has no separate stages
+    assert _stages(lib, 1, M=1, K=2560, N=6912, bits=8, had=0) == _lib.ERR_UNSUPPORTED
+    assert b"fused" in lib.bitnet_last_error()
+    assert _stages(lib, 2, M=0) == _lib.OK
+
+
+def test_stream_read_validation(lib):
+    f = lib.bitnet_stream_read
+    assert f(None, 1024, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert f(FAKE, 1024, None, None) == _lib.ERR_INVALID_ARG
+    assert f(FAKE + 8, 1024, FAKE, None) == _lib.ERR_ALIGN
+    assert f(FAKE, 1000, FAKE, None) == _lib.ERR_ALIGN
+    assert f(None, 0, None, None) == _lib.OK
+
+
+# Every entry point that launches work, with arguments that pass validation:
+# with an injected launch error each must report BITNET_ERR_HIP, name itself
+# and the HIP code in bitnet_last_error(), and launch nothing (the hook is
+# taken before any HIP call, so no device is needed).
+LAUNCHING_CALLS = {
+    "bitnet_ternarize_weights": (FAKE, 4, 64, FAKE, FAKE, FAKE, 1 << 20, None),
+    "bitnet_pack_2bit": (FAKE, 4, 64, FAKE, None),
+    "bitnet_hbitlinear_forward": (FAKE, _lib.BF16, 4, 512, FAKE, 256, FAKE, 4, 1, FAKE, FAKE,
+                                  1 << 30, None),
+    "bitnet_hbitlinear_forward_stages": (FAKE, _lib.BF16, 4, 512, FAKE, 256, FAKE, 4, 1, FAKE,
+                                         FAKE, 1 << 30, 1, None),
+    "bitnet_quantize_activations": (FAKE, _lib.F32, 2, 64, 8, 0, FAKE, FAKE, None, None),
+    "bitnet_ternary_gemm_i32": (FAKE, 2, 64, FAKE, 3, FAKE, None),
+    "bitnet_ternary_linear_dequant": (FAKE, FAKE, None, 2, 64, FAKE, 3, FAKE, 8, FAKE, None),
+    "bitnet_hbitlinear_forward_prologue": (FAKE, FAKE, _lib.BF16, 4, 256, 1, FAKE, 1e-7, FAKE, 256,
+                                           FAKE, 4, 1, FAKE, FAKE, 1 << 30, None),
+    "bitnet_quantize_activations_prologue": (FAKE, None, _lib.F32, 2, 64, 1, None, 1e-7, 8, 0,
+                                             FAKE, FAKE, None),
+    "bitnet_kv_quantize": (FAKE, _lib.BF16, 16, 128, 8, 3, FAKE, FAKE, None),
+    "bitnet_pack_tl2": (FAKE, 4, 64, FAKE, None),
+    "bitnet_hbitlinear_forward_tl2": (FAKE, _lib.BF16, 1, 256, FAKE, 16, FAKE, 8, FAKE, None),
+    "bitnet_hbitlinear_backward": (FAKE, _lib.BF16, 128, 192, FAKE, FAKE, 256, FAKE, FAKE, 8, 1,
+                                   FAKE, FAKE, FAKE, 1 << 30, None),
+    "bitnet_stream_read": (FAKE, 1024, FAKE, None),
+}
+
+HIP_ERROR_OUT_OF_MEMORY = 2  # hipErrorOutOfMemory
+
+
+@pytest.mark.parametrize("name", sorted(LAUNCHING_CALLS))
+def test_injected_launch_error_is_reported(lib, name):
+    lib.bitnet_test_fail_next_launch(HIP_ERROR_OUT_OF_MEMORY)
+    assert getattr(lib, name)(*LAUNCHING_CALLS[name]) == _lib.ERR_HIP
+    msg = lib.bitnet_last_error().decode()
+    assert name in msg and "HIP error 2" in msg, msg
+    with pytest.raises(_lib.BitNetError) as ei:
+        lib.bitnet_test_fail_next_launch(HIP_ERROR_OUT_OF_MEMORY)
+        _lib.call(name, *LAUNCHING_CALLS[name])
+    assert ei.value.status == _lib.ERR_HIP
+
+
+def test_injected_error_is_taken_once_and_not_by_failed_validation(lib):
+    lib.bitnet_test_fail_next_launch(HIP_ERROR_OUT_OF_MEMORY)
+    # an argument error comes first and leaves the injected error pending
+    assert lib.bitnet_pack_2bit(None, 4, 64, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert lib.bitnet_pack_2bit(FAKE, 4, 64, FAKE, None) == _lib.ERR_HIP
+    # cleared: a no-op call succeeds and clears the message
+    lib.bitnet_test_fail_next_launch(HIP_ERROR_OUT_OF_MEMORY)
+    lib.bitnet_test_fail_next_launch(0)
+    assert lib.bitnet_pack_2bit(FAKE, 0, 64, None, None) == _lib.OK
+    assert lib.bitnet_last_error() == b""
+
+
+def test_every_launching_entry_point_is_covered():
+    """Every declared entry point that returns a status and takes a stream is
+    in the injected-error table."""
+    with open(_lib.HEADER_PATH) as f:
+        text = f.read()
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    launching = set(re.findall(r"bitnet_status\s+(bitnet_[a-z0-9_]+)\s*\([^;]*hipStream_t", text))
+    assert launching == set(LAUNCHING_CALLS)
+
+
+# ---- dispatch, on the host build only (its launchers record their names) ----
+stub_only = pytest.mark.skipif(not HOST_LIB, reason="needs the host-only sanitizer build")
+
+
+def _calls(lib, fn, *args):
+    lib.bitnet_stub_reset()
+    assert fn(*args) == _lib.OK, lib.bitnet_last_error()
+    return lib.bitnet_stub_calls().decode().split()
+
+
+@stub_only
+@pytest.mark.parametrize("M,K,N,bits,had,want", [
+    (1, 2560, 6912, 8, 0, ["fused_decode"]),                    # single-token decode
+    (4, 256, 256, 4, 1, ["fused_decode"]),                      # transform fused for K <= 256
+    (16, 16384, 4096, 4, 1, ["quantize_nibbles", "matmul_nibbles"]),
+    (16, 16384, 4096, 8, 1, ["quantize", "matmul"]),
+    (2048, 8192, 2048, 4, 1, ["quantize", "matmul"]),           # prefill: never nibble codes
+    (3, 192, 40, 4, 0, ["fused_decode"]),
+])
+def test_forward_dispatch(lib, M, K, N, bits, had, want):
+    need = lib.bitnet_forward_workspace_bytes(M, K, N, bits, had)
+    ws = ctypes.create_string_buffer(max(need, 16) + 256)
+    ws_addr = (ctypes.addressof(ws) + 255) // 256 * 256
+    got = _calls(lib, lib.bitnet_hbitlinear_forward, FAKE, _lib.BF16, M, K, FAKE, N, FAKE, bits,
+                 had, FAKE, ws_addr if need else None, need, None)
+    assert got == want
+    if need:
+        q = _calls(lib, lib.bitnet_hbitlinear_forward_stages, FAKE, _lib.BF16, M, K, FAKE, N, FAKE,
+                   bits, had, FAKE, ws_addr, need, _lib.STAGE_QUANTIZE, None)
+        p = _calls(lib, lib.bitnet_hbitlinear_forward_stages, FAKE, _lib.BF16, M, K, FAKE, N, FAKE,
+                   bits, had, FAKE, ws_addr, need, _lib.STAGE_PRODUCT, None)
+        assert q + p == want
+
+
+@stub_only
+def test_other_dispatch(lib):
+    ws = ctypes.create_string_buffer(1 << 16)
+    a = (ctypes.addressof(ws) + 255) // 256 * 256
+    assert _calls(lib, lib.bitnet_ternarize_weights, FAKE, 4, 64, FAKE, FAKE, a, 1 << 14,
+                  None) == ["absmean_partial", "ternarize_pack"]
+    assert _calls(lib, lib.bitnet_ternary_gemm_i32, FAKE, 2, 64, FAKE, 3, FAKE, None) == ["matmul_i32"]
+    # backward with an fp32 dy: dx from split halves and the transform, then dw
+    bws = lib.bitnet_backward_workspace_bytes(128, 256, 192, _lib.F32, 1, 1)
+    big = ctypes.create_string_buffer(bws + 256)
+    b = (ctypes.addressof(big) + 255) // 256 * 256
+    assert _calls(lib, lib.bitnet_hbitlinear_backward, FAKE, _lib.F32, 128, 192, FAKE, FAKE, 256,
+                  FAKE, FAKE, 8, 1, FAKE, FAKE, b, bws, None) == [
+        "expand_transpose", "split_rows", "bf16_gemm_nt", "fwht_f32", "scale_transpose_split",
+        "codes_transpose", "bf16_gemm_nt"]
