@@ -85,6 +85,9 @@ def _time_replays(torch, fn, steps, reps):
     torch.cuda.synchronize()
     out = []
     for _ in range(reps):
+        if _FLUSH is not None:
+            _FLUSH()
+            torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record()
@@ -96,19 +99,43 @@ def _time_replays(torch, fn, steps, reps):
     return out
 
 
+class CacheFlush:
+    """Reads a 1 GiB buffer with the library's plain streaming-read kernel:
+    afterwards neither the XCD L2 caches (4 MB each) nor the 256 MB Infinity
+    Cache hold any of the timed calls' inputs, whatever they touched before."""
+
+    def __init__(self, torch, bl, dev, nbytes=1 << 30):
+        self.bl = bl
+        self.buf = torch.zeros((nbytes,), dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.bl.stream_read(self.buf, self.sink)
+
+
+_FLUSH = None
+
+
 def _time_steps(torch, fn, steps, warmup):
     """ms per call over exactly `steps` calls replayed from one HIP graph.
 
-    `warmup` eager calls and one untimed replay come first; the timed replay
-    is bracketed by synchronizations and a pair of HIP events on the stream
-    the kernels run on. Launching from a graph keeps the host's per-call
-    Python overhead out of the GPU's timeline."""
+    `warmup` eager calls and one untimed replay come first; then the caches
+    are flushed (1 GiB streamed through them), so that the timed replay
+    starts cold at any step count; the timed replay is bracketed by
+    synchronizations and a pair of HIP events on the stream the kernels run
+    on. Within the replay, consecutive calls read different weight copies
+    (more than 512 MB of them), so none is served from the caches either.
+    Launching from a graph keeps the host's per-call Python overhead out of
+    the GPU's timeline."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     g = _capture(torch, fn, steps)
     g.replay()
     torch.cuda.synchronize()
+    if _FLUSH is not None:
+        _FLUSH()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
@@ -151,9 +178,12 @@ class Prepared:
         bl.hbitlinear_forward(self.x, self.Wp[i % self.copies], self.alpha, wl.bits, wl.hadamard,
                               out=self.y, workspace=self.ws if self.ws.numel() else None)
 
-    def matmul_only(self, bl, i):
-        bl.ternary_linear_dequant(self.codes, self.scales, self.Wp[i % self.copies], self.alpha,
-                                  self.wl.bits, out=self.y, rowsum=self.rowsum)
+    def stage(self, bl, i, stages):
+        """One stage of the forward on its own kernel and workspace (the
+        product reads what the quantization stage left in the workspace)."""
+        wl = self.wl
+        bl.hbitlinear_forward_stages(self.x, self.Wp[i % self.copies], self.alpha, wl.bits,
+                                     wl.hadamard, stages, out=self.y, workspace=self.ws)
 
     def free_latent(self):
         self.W = None
@@ -168,16 +198,24 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
     wl = p.wl
     u = _work_units(wl)
     fwd_ms = _time_steps(torch, lambda i: p.forward(bl, i), steps, warmup)
+    quant_ms = None
     if p.fused:
         # the forward is one kernel: it is the product kernel
         mm_mean = fwd_ms
     else:
-        mm_mean = _time_steps(torch, lambda i: p.matmul_only(bl, i), steps, warmup)
+        # each stage of the forward alone, on the forward's own kernels: the
+        # product reads the workspace the quantization stage wrote (for small
+        # int4 batches, nibble codes)
+        p.stage(bl, 0, 1)
+        torch.cuda.synchronize()
+        mm_mean = _time_steps(torch, lambda i: p.stage(bl, i, 2), steps, warmup)
+        quant_ms = _time_steps(torch, lambda i: p.stage(bl, i, 1), steps, warmup)
     res = {
         "M": wl.M, "K": wl.K, "N": wl.N, "bits": wl.bits, "hadamard": wl.hadamard,
         "x_dtype": wl.x_dtype, "cold_weight_copies": p.copies, "fused_single_kernel": p.fused,
         "forward_us": fwd_ms * 1e3,
         "matmul_kernel_us_mean": mm_mean * 1e3,
+        "quantize_stage_us": None if quant_ms is None else quant_ms * 1e3,
         "forward_weight_GBs": u["weight_bytes"] / (fwd_ms * 1e-3) / 1e9,
         "forward_TOPS": u["ops"] / (fwd_ms * 1e-3) / 1e12,
         "matmul_weight_GBs": u["weight_bytes"] / (mm_mean * 1e-3) / 1e9,
@@ -186,6 +224,14 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
     if wl.M <= 16:
         res["matmul_hbm_frac"] = res["matmul_weight_GBs"] / HBM_PEAK_GBS
         if p.copies > 1:
+            # the plain streaming-read ceiling: the library's read-only kernel
+            # over the same cold weight copies, timed the same way
+            sink = torch.zeros((1,), dtype=torch.int32, device=dev)
+            sr_ms = _time_steps(torch, lambda i: bl.stream_read(p.Wp[i % p.copies], sink), steps,
+                                warmup)
+            res["stream_read_same_bytes_us"] = sr_ms * 1e3
+            res["stream_read_same_bytes_GBs"] = u["weight_bytes"] / (sr_ms * 1e-3) / 1e9
+            res["matmul_over_stream_read"] = mm_mean / sr_ms
             # the same forward on one weight copy, served from the caches
             res["forward_us_warm"] = _time_steps(torch, lambda i: p.forward(bl, 0), steps, warmup) * 1e3
     else:
@@ -225,8 +271,8 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
         res["backward_TFLOPs"] = bflops / (b_ms * 1e-3) / 1e12
         res["backward_bf16_mfma_frac"] = res["backward_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
         res["backward"] = ("dx = H(alpha dy . t) and dw = dy^T . x_q from a bf16 dy; 4*M*N*K "
-                           "algorithmic flops on bf16 MFMA (dw runs two passes: hi and lo parts "
-                           "of dy*s/c)")
+                           "algorithmic flops on bf16 MFMA (dw multiplies the hi and lo bf16 "
+                           "parts of dy*s/c in one pass, twice the MFMA work of one part)")
         del dy, dx, dw, bws
     if key == "prefill_int8_m8192_k4096_n14336" or key == "int4_hadamard_m4_k256_n256":
         # on-device ternarize + pack: two fp32 reads of W plus the packed write
@@ -327,6 +373,83 @@ def _cpu_baseline(key, budget_s):
     }
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _time_oracle_forward(key, budget_s, threads):
+    """Seconds per whole oracle forward call of `key` (weight preparation
+    excluded), with the BLAS pool limited to `threads`."""
+    import oracle
+    from bit_activation_linear_amd import workloads
+    from threadpoolctl import threadpool_limits
+    wl = workloads.WORKLOADS[key]
+    case = workloads.make_workload(key, seed=0)
+    t, alpha, _ = oracle.ternarize(case["W"])
+    with threadpool_limits(limits=threads):
+        oracle.forward(case["x"], wl.x_dtype, t, alpha, wl.bits, wl.hadamard)  # warm-up
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.forward(case["x"], wl.x_dtype, t, alpha, wl.bits, wl.hadamard)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 10000:
+                break
+    return el / reps, reps
+
+
+def _cpu_other_workloads(budget_s):
+    """The oracle on the single-layer, headline and batched-decode workloads,
+    on every host core and on one core (a reported baseline, not a target)."""
+    from bit_activation_linear_amd import workloads
+    cores = len(os.sched_getaffinity(0))
+    out = {}
+    for key in ("int4_hadamard_m4_k256_n256", "decode_int8_m1_k2560_n6912",
+                "decode_int4_hadamard_m16_k16384_n4096"):
+        wl = workloads.WORKLOADS[key]
+        r = {"weight_bytes": wl.N * wl.K // 4}
+        for label, th in (("all_cores", cores), ("one_core", 1)):
+            per, reps = _time_oracle_forward(key, budget_s, th)
+            r[label] = {"threads": th, "seconds_per_call": per, "calls": reps,
+                        "weight_GBs": (wl.N * wl.K / 4) / per / 1e9}
+        out[key] = r
+    return out
+
+
+def _clocks():
+    """Current GPU core and memory clocks (sysfs DPM tables, else amd-smi as a
+    child process); None where neither is readable."""
+    import glob
+    import subprocess
+    res = {}
+    for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/{name}")):
+            try:
+                with open(path) as f:
+                    cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+                if cur:
+                    res[name] = cur[0]
+                    break
+            except OSError:
+                continue
+    if len(res) < 2:
+        try:
+            out = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                                 text=True, timeout=20)
+            if out.returncode == 0:
+                res["amd_smi_clock"] = json.loads(out.stdout)
+        except (OSError, subprocess.SubprocessError, ValueError):
+            pass
+    return res or None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,6 +473,9 @@ def main():
     _lib.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    global _FLUSH
+    _FLUSH = CacheFlush(torch, bl, dev)
+    clocks_before = _clocks()
 
     key = args.workload
     wl = workloads.WORKLOADS[key]
@@ -362,12 +488,14 @@ def main():
     reps = _time_replays(torch, lambda i: p.forward(bl, i), args.steps, 7)
     reps_us = sorted(r * 1e3 for r in reps)
     head["forward_us_replays_p10_p50_p90"] = [reps_us[0], reps_us[3], reps_us[-1]]
+    stream_us = None
     if decode and p.copies > 1:
         dst = torch.empty_like(p.Wp[0])
         cp_ms = _time_steps(torch, lambda i: dst.copy_(p.Wp[i % p.copies]), args.steps, 5)
         head["copy_same_bytes_us"] = cp_ms * 1e3
         head["copy_same_bytes_read_GBs"] = p.Wp[0].numel() / (cp_ms * 1e-3) / 1e9
         del dst
+        stream_us = head.get("stream_read_same_bytes_us")
     if decode:
         value, unit = head["forward_weight_GBs"], "GB/s"
         roof = {"bound": "hbm", "achieved": head["matmul_weight_GBs"], "peak": HBM_PEAK_GBS,
@@ -390,7 +518,13 @@ def main():
     roof["algorithmic"] = ("N*K/4 packed weight bytes per launch" if decode
                            else "2*M*N*K int8 ops per launch")
     roof["launch_us_mean"] = head["matmul_kernel_us_mean"]
-    roof["timing"] = "HIP events around one HIP-graph replay of back-to-back launches"
+    roof["timing"] = ("HIP events around one HIP-graph replay of back-to-back launches, caches "
+                      "flushed before it")
+    if stream_us is not None:
+        # context, not the denominator: the plain read-only kernel over the
+        # same cold bytes, and the product's time relative to it
+        roof["stream_read_ceiling_GBs"] = head["stream_read_same_bytes_GBs"]
+        roof["launch_us_over_stream_read_us"] = head["matmul_kernel_us_mean"] / stream_us
     traffic, source = _recorded_traffic(roof["kernel"], key)
     roof["traffic"] = traffic
     if source:
@@ -434,10 +568,14 @@ def main():
         kv = _measure_kv(torch, bl, dev, max(20, args.steps // 4), max(5, args.warmup // 2))
         _log(f"[bench] kv cache: " + ", ".join(f"{b}-bit {r['us']:.2f} us" for b, r in kv["bits"].items()))
 
+    clocks_after = _clocks()
     cpu = None
     if not args.no_cpu:
         _log("[bench] CPU oracle baseline")
         cpu = _cpu_baseline(key, args.cpu_seconds)
+        cpu["model"] = _cpu_model()
+        if not args.no_extra:
+            cpu["other_workloads"] = _cpu_other_workloads(args.cpu_seconds / 4)
 
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
@@ -448,6 +586,7 @@ def main():
                    "hadamard": wl.hadamard, "x_dtype": wl.x_dtype,
                    "cold_weight_copies": head["cold_weight_copies"]},
         "roofline": roof, "cpu_baseline": cpu, "per_workload": per, "kv_cache": kv,
+        "clocks": {"before": clocks_before, "after": clocks_after},
     }
     print(json.dumps(line), flush=True)
 
