@@ -83,11 +83,16 @@ def fwht_dense(x: np.ndarray) -> np.ndarray:
 def fwht(x: np.ndarray) -> np.ndarray:
     """Fast Walsh-Hadamard transform along the last axis, fp64.
 
-    [engine] fast_hadamard_transform: reject a non-power-of-2 length; then for
-    half-widths h = 1, 2, 4, ..., n/2 pair element i with element i + h inside
-    every aligned block of 2h elements and replace (u, v) by
-    ((u + v)/sqrt 2, (u - v)/sqrt 2). The page casts the result back to the
-    input dtype; here it stays fp64 (no intermediate rounding)."""
+    [engine] Eq. 3-4 define H_m recursively as (1/sqrt 2) [[H, H], [H, -H]]
+    over H_{m-1}, i.e. H_n is the Kronecker product of log2(n) copies of the
+    2x2 factor (1/sqrt 2) [[1, 1], [1, -1]], one per bit of the index. The
+    factor of bit b mixes each pair of elements whose indices differ only in
+    bit b: with i the index whose bit b is clear and j = i XOR 2^b,
+    (x_i, x_j) -> ((x_i + x_j)/sqrt 2, (x_i - x_j)/sqrt 2). Applying the
+    factors for b = 0, 1, ..., log2(n) - 1 is the O(n log n) fast transform
+    of fast_hadamard_transform (which rejects a non-power-of-2 length and
+    casts the result back to the input dtype; here it stays fp64, with no
+    intermediate rounding)."""
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[-1]
     if not _is_pow2(n):
@@ -95,13 +100,16 @@ def fwht(x: np.ndarray) -> np.ndarray:
     lead = x.shape[:-1]
     y = x.reshape(-1, n).copy()
     r = 1.0 / math.sqrt(2.0)
-    h = 1
-    while h < n:
-        blocks = y.reshape(y.shape[0], n // (2 * h), 2, h)
-        first = blocks[:, :, 0, :]
-        second = blocks[:, :, 1, :]
-        y = np.stack(((first + second) * r, (first - second) * r), axis=2).reshape(-1, n)
-        h *= 2
+    index = np.arange(n)
+    bit = 1
+    while bit < n:
+        i = index[(index & bit) == 0]   # bit b clear
+        j = i ^ bit                     # the partner: bit b set
+        u = y[:, i]
+        v = y[:, j]
+        y[:, i] = (u + v) * r
+        y[:, j] = (u - v) * r
+        bit <<= 1
     return y.reshape(*lead, n)
 
 

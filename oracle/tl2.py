@@ -7,8 +7,8 @@ Source: the [edge] page (Quillan-Ronin "bitnet_cpp_edge.py", the bitnet.cpp
 simulation): its module docstring item 2 (element-wise mirror consolidation:
 the 27 states of a ternary triplet fold onto 14 unsigned states, stored as a
 4-bit index plus a sign bit, 5 bits per 3 weights) and class
-SignedUnsignedWeightPacker (the table of 14 base triplets and the
-pack/unpack of triplets).
+SignedUnsignedWeightPacker (its table of 14 base triplets and the pack /
+unpack of triplets).
 
 Readings where the page is silent or does something this library does not:
   * The page packs only the first floor(K/3) triplets of a row and drops the
@@ -19,41 +19,46 @@ Readings where the page is silent or does something this library does not:
     bytes of sign bits) is a contract of this library, not of the page; it
     stores exactly 5 bits per triplet.
 
-Parity status: pinned (tests/test_oracle_tl2.py: the table against the
-mirror rule and all 27 states, a closed form of the index, round trips, hand
-built bytes, 5/3 bits per weight).
+Parity status: pinned (tests/test_oracle_tl2.py: the decoded states against
+the page's own table of base triplets (tests/golden/tl2_base_triplets.json)
+and the mirror rule over all 27 states, round trips, hand built bytes, 5/3
+bits per weight).
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-# [edge] SignedUnsignedWeightPacker: the 14 base triplets, in the page's order.
-# Each is either all zero or has its first non-zero element equal to +1; a
-# triplet is stored as the index of the base triplet equal to it (sign 0) or
-# to its negation (sign 1).
-BASE_TRIPLETS = [
-    (0, 0, 0), (0, 0, 1), (0, 1, -1), (0, 1, 0), (0, 1, 1),
-    (1, -1, -1), (1, -1, 0), (1, -1, 1), (1, 0, -1), (1, 0, 0),
-    (1, 0, 1), (1, 1, -1), (1, 1, 0), (1, 1, 1),
-]
+# [edge] module docstring item 2 (mirror consolidation): a ternary triplet
+# and its negation share one stored state, so the 27 triplets fold onto 14
+# unsigned states plus a sign. Reading a triplet as the balanced-ternary
+# number v = 9 w0 + 3 w1 + w2 (v in [-13, 13], negation is v -> -v), the
+# unsigned state is |v| (the zero triplet, or one whose leading non-zero digit
+# is +1) and the sign is v < 0. The page's SignedUnsignedWeightPacker lists
+# the 14 unsigned states in increasing |v|, so the page's index of a state is
+# |v| itself (pinned against the page's table in tests/golden).
+N_STATES = 14
 
 TRIPLETS_PER_BLOCK = 128
 BLOCK_K = 3 * TRIPLETS_PER_BLOCK      # 384 weights per device block
 BLOCK_BYTES = 64 + 16                 # 4-bit indices, then sign bits
 
 
-def _tables():
-    enc = {}
-    dec = {}
-    for i, b in enumerate(BASE_TRIPLETS):
-        enc[b] = (i, 0)
-        dec[(i, 0)] = b
-        if b != (0, 0, 0):
-            neg = (-b[0], -b[1], -b[2])
-            enc[neg] = (i, 1)
-            dec[(i, 1)] = neg
-    return enc, dec
+def triplet_value(t: np.ndarray) -> np.ndarray:
+    """Balanced-ternary value 9 w0 + 3 w1 + w2 of each triplet (last axis 3)."""
+    t = np.asarray(t, dtype=np.int64)
+    return 9 * t[..., 0] + 3 * t[..., 1] + t[..., 2]
+
+
+def triplets_of_value(v: np.ndarray) -> np.ndarray:
+    """Inverse of triplet_value: the balanced-ternary digits (w0, w1, w2) in
+    {-1, 0, 1} of v in [-13, 13] (last digit first: w2 = ((v + 1) mod 3) - 1)."""
+    v = np.asarray(v, dtype=np.int64)
+    w2 = (v + 1) % 3 - 1
+    v1 = (v - w2) // 3
+    w1 = (v1 + 1) % 3 - 1
+    w0 = (v1 - w1) // 3
+    return np.stack([w0, w1, w2], axis=-1).astype(np.int8)
 
 
 def encode_triplets(t: np.ndarray):
@@ -66,26 +71,19 @@ def encode_triplets(t: np.ndarray):
     T = (K + 2) // 3
     padded = np.zeros((N, 3 * T), dtype=np.int64)
     padded[:, :K] = t
-    enc, _ = _tables()
-    idx = np.zeros((N, T), dtype=np.uint8)
-    sign = np.zeros((N, T), dtype=np.uint8)
-    for n in range(N):
-        for j in range(T):
-            i, s = enc[tuple(int(v) for v in padded[n, 3 * j:3 * j + 3])]
-            idx[n, j] = i
-            sign[n, j] = s
-    return idx, sign
+    v = triplet_value(padded.reshape(N, T, 3))
+    return np.abs(v).astype(np.uint8), (v < 0).astype(np.uint8)
 
 
 def decode_triplets(idx: np.ndarray, sign: np.ndarray, K: int) -> np.ndarray:
     """Ternary int8 [N, K] from indices and sign bits (the padding dropped)."""
-    _, dec = _tables()
+    idx = np.asarray(idx, dtype=np.int64)
+    sign = np.asarray(sign, dtype=np.int64)
+    if idx.size and (idx.max() >= N_STATES or sign.max() > 1):
+        raise ValueError("TL2 index must lie in 0..13 and the sign in {0, 1}")
     N, T = idx.shape
-    out = np.zeros((N, 3 * T), dtype=np.int8)
-    for n in range(N):
-        for j in range(T):
-            out[n, 3 * j:3 * j + 3] = dec[(int(idx[n, j]), int(sign[n, j]))]
-    return out[:, :K]
+    v = np.where(sign == 1, -idx, idx)
+    return triplets_of_value(v).reshape(N, 3 * T)[:, :K]
 
 
 def _slot(j: int):

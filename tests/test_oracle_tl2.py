@@ -1,13 +1,17 @@
 """Pins of the oracle's TL2 weight code (edge page: module docstring item 2,
 element-wise mirror consolidation; class SignedUnsignedWeightPacker).
 
-The table is checked against the mirror rule itself (every one of the 27
-ternary triplets is exactly one base triplet or its negation, and a base
-triplet is zero or starts with +1), the index against a closed form, the
-encodings against round trips and hand-built bytes, and the size against the
-page's 5 bits per 3 weights."""
+The oracle derives index and sign from the balanced-ternary value of a
+triplet; its states are checked against the page's own table of base
+triplets (tests/golden/tl2_base_triplets.json) and the mirror rule itself
+(every one of the 27 ternary triplets is exactly one base triplet or its
+negation, and a base triplet is zero or starts with +1), the encodings against
+round trips and hand-built bytes, and the size against the page's 5 bits per
+3 weights."""
 
 import itertools
+import json
+import os
 
 import numpy as np
 import pytest
@@ -15,8 +19,24 @@ import pytest
 from oracle import tl2
 
 
-def test_base_triplets_follow_the_mirror_rule():
-    base = tl2.BASE_TRIPLETS
+def _page_table(golden_dir):
+    with open(os.path.join(golden_dir, "tl2_base_triplets.json")) as f:
+        return [tuple(b) for b in json.load(f)["base_triplets"]]
+
+
+def test_decoded_states_are_the_pages_table(golden_dir):
+    """Index i with sign 0 decodes to the page's i-th base triplet, with sign
+    1 to its negation (edge page, SignedUnsignedWeightPacker's table)."""
+    page = _page_table(golden_dir)
+    idx = np.arange(14, dtype=np.uint8).reshape(1, 14)
+    pos = tl2.decode_triplets(idx, np.zeros_like(idx), 42).reshape(14, 3)
+    neg = tl2.decode_triplets(idx, np.ones_like(idx), 42).reshape(14, 3)
+    assert [tuple(int(v) for v in r) for r in pos] == page
+    assert [tuple(int(v) for v in r) for r in neg] == [tuple(-v for v in b) for b in page]
+
+
+def test_pages_table_follows_the_mirror_rule(golden_dir):
+    base = _page_table(golden_dir)
     assert len(base) == 14 == (27 + 1) // 2           # ceil(27 / 2) states
     assert len(set(base)) == 14
     for b in base:
@@ -26,10 +46,22 @@ def test_base_triplets_follow_the_mirror_rule():
     assert covered == set(itertools.product((-1, 0, 1), repeat=3))
 
 
-def test_index_is_the_balanced_ternary_value():
-    # the page's order: base triplet i has 9 w0 + 3 w1 + w2 == i
-    for i, (w0, w1, w2) in enumerate(tl2.BASE_TRIPLETS):
-        assert 9 * w0 + 3 * w1 + w2 == i
+def test_encoding_uses_the_pages_positions(golden_dir):
+    """Each of the 27 triplets encodes to the position of the page's entry
+    equal to it (sign 0) or to its negation (sign 1)."""
+    page = _page_table(golden_dir)
+    states = list(itertools.product((-1, 0, 1), repeat=3))
+    idx, sign = tl2.encode_triplets(np.array(states, dtype=np.int8).reshape(1, -1))
+    for j, st in enumerate(states):
+        if st in page:
+            assert (idx[0, j], sign[0, j]) == (page.index(st), 0)
+        else:
+            assert (idx[0, j], sign[0, j]) == (page.index(tuple(-v for v in st)), 1)
+
+
+def test_decode_rejects_out_of_range_codes():
+    with pytest.raises(ValueError):
+        tl2.decode_triplets(np.array([[14]], dtype=np.uint8), np.array([[0]], dtype=np.uint8), 3)
 
 
 def test_every_state_encodes_and_decodes():
