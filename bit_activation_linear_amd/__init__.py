@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     forward_workspace_bytes,
     hbitlinear_backward,
     hbitlinear_forward,
+    hbitlinear_forward_noalloc,
     hbitlinear_forward_prologue,
     hbitlinear_forward_stages,
     hbitlinear_forward_tl2,

@@ -69,9 +69,14 @@ SIGNATURES = {
     "bitnet_backward_workspace_bytes": (_size, [_i64, _i64, _i64, _int, _int, _int]),
     "bitnet_hbitlinear_backward": (_int, [_ptr, _int, _i64, _i64, _ptr, _ptr, _i64, _ptr, _ptr,
                                           _int, _int, _ptr, _ptr, _ptr, _size, _ptr]),
+    "bitnet_hbitlinear_forward_noalloc": (_int, [_ptr, _int, _i64, _i64, _ptr, _i64, _ptr, _int,
+                                                 _int, _ptr, _ptr]),
     "bitnet_stream_read": (_int, [_ptr, _size, _ptr, _ptr]),
     "bitnet_test_fail_next_launch": (None, [_int]),
 }
+
+# bytes of the fixed scratch of bitnet_hbitlinear_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # stages of bitnet_hbitlinear_forward_stages
 STAGE_QUANTIZE = 1

@@ -189,6 +189,26 @@ def hbitlinear_forward_stages(x: torch.Tensor, Wpacked: torch.Tensor, alpha: tor
     return out
 
 
+def hbitlinear_forward_noalloc(x: torch.Tensor, Wpacked: torch.Tensor, alpha: torch.Tensor,
+                               bits: int, hadamard: int, out: torch.Tensor) -> torch.Tensor:
+    """The forward into the caller's `out` (fp32 [M, N]) with the library's
+    fixed device scratch as its workspace: the library allocates nothing.
+    Calls that overlap in time on one GPU race on that scratch."""
+    _require(x, "x", (torch.float32, torch.bfloat16), 2)
+    _require(Wpacked, "Wpacked", (torch.uint8,), 2)
+    _require(alpha, "alpha", (torch.float32,), 1)
+    M, K = x.shape
+    N = Wpacked.shape[0]
+    if Wpacked.shape[1] * 4 != K:
+        raise ValueError(f"Wpacked has {Wpacked.shape[1]} bytes per row, expected K/4 = {K // 4}")
+    _same_device(x.device, Wpacked=Wpacked, alpha=alpha)
+    _check_out(out, "out", torch.float32, (M, N), x.device)
+    _lib.call("bitnet_hbitlinear_forward_noalloc", x.data_ptr(), _x_dtype(x), M, K,
+              Wpacked.data_ptr(), N, alpha.data_ptr(), int(bits), int(hadamard), out.data_ptr(),
+              _stream_ptr(x))
+    return out
+
+
 def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
     """Plain read of every byte of `buf` (contiguous, numel * itemsize a
     multiple of 16) with no arithmetic: the streaming-read ceiling that the

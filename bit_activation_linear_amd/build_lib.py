@@ -23,7 +23,8 @@ LIB_NAME = "libbitnet_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["abi.cpp", "ternarize.hip", "fwht_quant.hip", "ternary_gemv.hip", "ternary_gemm.hip",
-           "kv_quant.hip", "grad.hip", "tl2.hip", "measure.hip"]
+           "kv_quant.hip", "grad.hip", "tl2.hip", "measure.hip",
+           "noalloc.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

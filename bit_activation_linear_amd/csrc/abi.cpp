@@ -244,12 +244,18 @@ bitnet_status bitnet_ternary_linear_dequant(const int8_t* codes, const float* sc
 
 namespace {
 
+static_assert(BITNET_NOALLOC_SCRATCH_BYTES == bitnet::kNoAllocScratchBytes,
+              "the header's scratch size is the library's");
+
 // The forward, or the stages of it that `stages` selects (both for the
-// forward itself).
+// forward itself). With fixed_scratch the workspace is the library's fixed
+// device array instead of the caller's ws (which is then ignored): its size
+// is checked with the other arguments, and its address, looked up once per
+// device, is taken only after every check has passed.
 bitnet_status forward_impl(const char* fn, const void* x, bitnet_dtype x_dtype, int64_t M,
                            int64_t K, const uint8_t* Wpacked, int64_t N, const float* alpha,
                            int bits, int hadamard, float* y, void* ws, size_t ws_bytes, int stages,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool fixed_scratch = false) {
   if (stages < 1 || stages > 3)
     return fail(BITNET_ERR_INVALID_ARG, "%s: stages=%d must be 1, 2 or 3", fn, stages);
   if (bitnet_status st = check_dims(fn, M, K, N)) return st;
@@ -258,16 +264,25 @@ bitnet_status forward_impl(const char* fn, const void* x, bitnet_dtype x_dtype, 
   if (!x || !Wpacked || !alpha || !y)
     return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   const size_t need = forward_ws_bytes(M, K, N, hadamard);
-  if (need > 0 && (!ws || ws_bytes < need))
+  if (fixed_scratch) {
+    if (need > bitnet::kNoAllocScratchBytes)
+      return fail(BITNET_ERR_UNSUPPORTED,
+                  "%s: M=%lld K=%lld needs %zu B of scratch, above the fixed %zu B", fn,
+                  (long long)M, (long long)K, need, bitnet::kNoAllocScratchBytes);
+  } else if (need > 0 && (!ws || ws_bytes < need)) {
     return fail(BITNET_ERR_INVALID_ARG, "%s: workspace %zu B < required %zu B", fn,
                 ws ? ws_bytes : (size_t)0, need);
-  if (!aligned(x, 16) || !aligned(Wpacked, 16) || (need > 0 && !aligned(ws, 16)) ||
-      !aligned(y, 4) || !aligned(alpha, 4))
+  }
+  if (!aligned(x, 16) || !aligned(Wpacked, 16) ||
+      (need > 0 && !fixed_scratch && !aligned(ws, 16)) || !aligned(y, 4) || !aligned(alpha, 4))
     return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
   if (need == 0 && stages != BITNET_STAGE_QUANTIZE + BITNET_STAGE_PRODUCT)
     return fail(BITNET_ERR_UNSUPPORTED,
                 "%s: this shape runs as one fused kernel; its stages cannot run apart", fn);
   if (bitnet_status st = launch_guard(fn)) return st;
+  if (fixed_scratch && need > 0) {
+    if (hipError_t e = bitnet::noalloc_scratch(&ws)) return hip_status(e, fn);
+  }
   if (need == 0) {
     return hip_status(bitnet::launch_fused_decode(x, (int)x_dtype, M, (int)K, Wpacked, N, alpha,
                                                   bits, y, stream, nullptr, hadamard),
@@ -307,6 +322,15 @@ bitnet_status bitnet_hbitlinear_forward_stages(const void* x, bitnet_dtype x_dty
                                                hipStream_t stream) {
   return forward_impl("bitnet_hbitlinear_forward_stages", x, x_dtype, M, K, Wpacked, N, alpha,
                       bits, hadamard, y, ws, ws_bytes, stages, stream);
+}
+
+bitnet_status bitnet_hbitlinear_forward_noalloc(const void* x, bitnet_dtype x_dtype, int64_t M,
+                                                int64_t K, const uint8_t* Wpacked, int64_t N,
+                                                const float* alpha, int bits, int hadamard,
+                                                float* y, hipStream_t stream) {
+  return forward_impl("bitnet_hbitlinear_forward_noalloc", x, x_dtype, M, K, Wpacked, N, alpha,
+                      bits, hadamard, y, nullptr, 0, BITNET_STAGE_QUANTIZE + BITNET_STAGE_PRODUCT,
+                      stream, /*fixed_scratch=*/true);
 }
 
 bitnet_status bitnet_stream_read(const void* p, size_t bytes, uint32_t* sink,

@@ -183,6 +183,12 @@ hipError_t launch_repack_tl2(const uint8_t* Wpacked, int64_t N, int K, uint8_t* 
 hipError_t launch_tl2_decode(const void* x, int x_dtype, int K, const uint8_t* Wtl2, int64_t N,
                              const float* alpha, int bits, float* y, hipStream_t stream);
 
+// Forward scratch of the entry point that allocates nothing: a fixed device
+// array (one per GPU). noalloc_scratch gives its address on the current
+// device, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Measurement: read `bytes` (a multiple of 16 is read; the tail is ignored)
 // with 16-byte loads and no arithmetic; sink receives a word only in the
 // (practically never met) case that the data's XOR equals a fixed constant.

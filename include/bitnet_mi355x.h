@@ -332,6 +332,35 @@ bitnet_status bitnet_hbitlinear_backward(const void* dy, bitnet_dtype dy_dtype, 
                                          size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Forward for callers that cannot allocate                                  */
+/* ------------------------------------------------------------------------ */
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as bitnet_hbitlinear_forward, with the same kernels, arguments
+ * (minus the workspace), results (bit for bit) and errors, whose workspace is
+ * a fixed device array inside the library instead of the caller's: the call
+ * allocates nothing. Each GPU the library runs on holds its own
+ * BITNET_NOALLOC_SCRATCH_BYTES array from the first load of the library's
+ * code on it until the process ends; its address on a device is looked up
+ * (hipGetSymbolAddress, no allocation) on the first call made with that
+ * device current.
+ *   Limit: a shape whose bitnet_forward_workspace_bytes exceeds
+ *   BITNET_NOALLOC_SCRATCH_BYTES (about M * K > 64 Mi codes) is rejected with
+ *   BITNET_ERR_UNSUPPORTED before anything is launched.
+ *   Concurrency: every call on one GPU shares that GPU's array, and each
+ *   call's quantization stage overwrites all of the workspace it uses before
+ *   its product stage reads it (nothing needs clearing). Calls that overlap
+ *   in time on one GPU (different streams, or host threads without ordering)
+ *   race on the array and give wrong results; calls ordered on one stream do
+ *   not. */
+#define BITNET_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+bitnet_status bitnet_hbitlinear_forward_noalloc(const void* x, bitnet_dtype x_dtype, int64_t M,
+                                                int64_t K, const uint8_t* Wpacked, int64_t N,
+                                                const float* alpha, int bits, int hadamard,
+                                                float* y, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Measurement and test hooks                                                */
 /* ------------------------------------------------------------------------ */
 

@@ -97,5 +97,9 @@ hipError_t launch_tl2_decode(const void*, int, int, const uint8_t*, int64_t, con
 hipError_t launch_stream_read(const void*, size_t, unsigned*, hipStream_t) {
   return record("stream_read");
 }
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = reinterpret_cast<void*>(static_cast<uintptr_t>(0x100000));  // never dereferenced
+  return record("noalloc_scratch");
+}
 
 }  // namespace bitnet

@@ -377,6 +377,8 @@ LAUNCHING_CALLS = {
     "bitnet_hbitlinear_backward": (FAKE, _lib.BF16, 128, 192, FAKE, FAKE, 256, FAKE, FAKE, 8, 1,
                                    FAKE, FAKE, FAKE, 1 << 30, None),
     "bitnet_stream_read": (FAKE, 1024, FAKE, None),
+    "bitnet_hbitlinear_forward_noalloc": (FAKE, _lib.BF16, 4, 512, FAKE, 256, FAKE, 4, 1, FAKE,
+                                          None),
 }
 
 HIP_ERROR_OUT_OF_MEMORY = 2  # hipErrorOutOfMemory
@@ -466,3 +468,34 @@ def test_other_dispatch(lib):
                   FAKE, FAKE, 8, 1, FAKE, FAKE, b, bws, None) == [
         "expand_transpose", "split_rows", "bf16_gemm_nt", "fwht_f32", "scale_transpose_split",
         "codes_transpose", "bf16_gemm_nt"]
+
+
+def test_noalloc_validation(lib):
+    f = lib.bitnet_hbitlinear_forward_noalloc
+    # a batch whose workspace exceeds the fixed scratch is refused up front
+    assert f(FAKE, _lib.BF16, 8192, 16384, FAKE, 64, FAKE, 8, 0, FAKE, None) == _lib.ERR_UNSUPPORTED
+    assert b"scratch" in lib.bitnet_last_error()
+    # the limit is the workspace the forward needs: codes M * K plus 8 B of
+    # scales and row sums per token (each part rounded up to 256 B)
+    M, K = 65536 - 512, 1024
+    assert lib.bitnet_forward_workspace_bytes(M, K, 64, 8, 0) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.bitnet_forward_workspace_bytes(M + 256, K, 64, 8, 0) > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, _lib.BF16, M + 256, K, FAKE, 64, FAKE, 8, 0, FAKE, None) == _lib.ERR_UNSUPPORTED
+    lib.bitnet_test_fail_next_launch(HIP_ERROR_OUT_OF_MEMORY)  # stop before any launch
+    assert f(FAKE, _lib.BF16, M, K, FAKE, 64, FAKE, 8, 0, FAKE, None) == _lib.ERR_HIP
+    # the other checks are the forward's
+    assert f(None, _lib.BF16, 4, 512, FAKE, 256, FAKE, 4, 1, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert f(FAKE, _lib.BF16, 4, 512, FAKE, 256, FAKE, 5, 1, FAKE, None) == _lib.ERR_BAD_BITS
+    assert f(FAKE, _lib.BF16, 4, 192, FAKE, 256, FAKE, 4, 1, FAKE, None) == _lib.ERR_NOT_POW2
+    assert f(FAKE + 2, _lib.BF16, 4, 512, FAKE, 256, FAKE, 4, 1, FAKE, None) == _lib.ERR_ALIGN
+    assert f(None, _lib.BF16, 0, 512, None, 256, None, 4, 1, None, None) == _lib.OK
+
+
+@stub_only
+def test_noalloc_dispatch(lib):
+    f = lib.bitnet_hbitlinear_forward_noalloc
+    assert _calls(lib, f, FAKE, _lib.BF16, 64, 1024, FAKE, 256, FAKE, 8, 1, FAKE,
+                  None) == ["noalloc_scratch", "quantize", "matmul"]
+    # a fused shape needs no scratch and does not look it up
+    assert _calls(lib, f, FAKE, _lib.BF16, 1, 2560, FAKE, 6912, FAKE, 8, 0, FAKE,
+                  None) == ["fused_decode"]
