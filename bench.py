@@ -85,9 +85,9 @@ def _time_replays(torch, fn, steps, reps):
     torch.cuda.synchronize()
     out = []
     for _ in range(reps):
+        torch.cuda.synchronize()
         if _FLUSH is not None:
             _FLUSH()
-            torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record()
@@ -119,14 +119,18 @@ _FLUSH = None
 def _time_steps(torch, fn, steps, warmup):
     """ms per call over exactly `steps` calls replayed from one HIP graph.
 
-    `warmup` eager calls and one untimed replay come first; then the caches
-    are flushed (1 GiB streamed through them), so that the timed replay
-    starts cold at any step count; the timed replay is bracketed by
-    synchronizations and a pair of HIP events on the stream the kernels run
-    on. Within the replay, consecutive calls read different weight copies
-    (more than 512 MB of them), so none is served from the caches either.
-    Launching from a graph keeps the host's per-call Python overhead out of
-    the GPU's timeline."""
+    `warmup` eager calls and one untimed replay come first; then, after a
+    synchronization, the caches are flushed (1 GiB streamed through them), so
+    that the timed replay starts cold at any step count. The timed replay is
+    bracketed by a pair of HIP events on the stream the kernels run on and by
+    synchronizations. The host enqueues the flush, the start event and the
+    graph back to back: while the GPU streams the flush, the host submits the
+    graph, so that the time between the two events is the `steps` calls and
+    not the host's submission of them (about 10 us, which at 20 steps would
+    add half a microsecond to every step). Within the replay, consecutive
+    calls read different weight copies (more than 512 MB of them), so none is
+    served from the caches either. Launching from a graph keeps the host's
+    per-call Python overhead out of the GPU's timeline."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -135,7 +139,6 @@ def _time_steps(torch, fn, steps, warmup):
     torch.cuda.synchronize()
     if _FLUSH is not None:
         _FLUSH()
-        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
