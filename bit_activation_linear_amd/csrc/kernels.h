@@ -124,7 +124,8 @@ hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64
 // The two product shapes behind launch_ternary_matmul.
 hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, hipStream_t stream, bool nibbles = false);
+                       int32_t* acc, hipStream_t stream, bool nibbles = false,
+                       const int32_t* rowsum = nullptr);
 hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
                        int32_t* acc, hipStream_t stream, const int32_t* rowsum = nullptr);

@@ -73,7 +73,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int BKW = 128;     // k per wave slice per stage
-constexpr int kChunks = 8;   // MFMA groups per block in the interleaved schedule
 
 template <int RT, int CT, int WMW, int WNW, int KS>
 struct Shape {
@@ -95,10 +94,12 @@ struct Shape {
   static constexpr int ROWSUM = RING - KS * BM * 4;  // int32 row sums [KS][BM], after the ring drains
   static constexpr int LDS = RING;
   static constexpr int PART = RT * CT * 4096;  // one wave's accumulators in bytes
+  // MFMA groups per 64-weight block in the interleaved schedule
+  static constexpr int CH = (2 * RT * CT) < 8 ? 2 * RT * CT : 8;
   static_assert(NA_W * NW == NA && NB_W * NW == NB && NB_W >= 1, "uneven staging");
   static_assert(SLOT * 2 <= kLdsMax, "two stage slots do not fit in LDS");
   static_assert(KS == 1 || (KS / 2) * WMW * WNW * PART <= ROWSUM, "reduction does not fit");
-  static_assert((2 * RT * CT) % kChunks == 0, "MFMA groups");
+  static_assert((2 * RT * CT) % CH == 0, "MFMA groups");
 };
 
 // The 2-bit fields at bit offset sh of each byte: u = t + 1 for 16 weights.
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
     _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) asm volatile("" : "+v"(B_[hh][ct]));      \
     _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) asm volatile("" : "+v"(A_[hh][rt]));      \
   }
-  // One block's MFMAs (operands A_, B_) cut into kChunks groups separated by
+  // One block's MFMAs (operands A_, B_) cut into S::CH groups separated by
   // scheduling barriers. Group 0 gives the next block's LDS reads (issued
   // just before) time to land; the unpacking of its weights into NB_, the
   // row sums of A_ and, when LD_ is set, this wave's share of the loads of
@@ -260,22 +261,22 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
   constexpr int kUnpackPerBlock = 2 * CT;
   constexpr int kSumPerBlock = 2 * RT;
 #define BITNET_STEP(A_, B_, NB_, LD_, lks_, lslot_)                                             \
-  _Pragma("unroll") for (int ch = 0; ch < kChunks; ++ch) {                                      \
+  _Pragma("unroll") for (int ch = 0; ch < S::CH; ++ch) {                                      \
     _Pragma("unroll") for (int e = 0; e < kUnpackPerBlock; ++e) {                               \
-      if (1 + e * (kChunks - 1) / kUnpackPerBlock == ch)                                        \
+      if (1 + e * (S::CH - 1) / kUnpackPerBlock == ch)                                        \
         NB_[e / CT][e % CT] = unpack_u(pw[e % CT], 2 * g + 4 * (e / CT));                       \
     }                                                                                           \
     _Pragma("unroll") for (int e = 0; e < kSumPerBlock; ++e) {                                  \
-      if (!RSG && 1 + e * (kChunks - 1) / kSumPerBlock == ch)                                   \
+      if (!RSG && 1 + e * (S::CH - 1) / kSumPerBlock == ch)                                   \
         rsum[e % RT] = add_bytes(A_[e / RT][e % RT], rsum[e % RT]);                             \
     }                                                                                           \
     if (LD_) {                                                                                  \
       _Pragma("unroll") for (int i = 0; i < S::NL_W; ++i) {                                     \
-        if (i * kChunks / S::NL_W == ch) BITNET_LOAD(lks_, lslot_, i)                           \
+        if (i * S::CH / S::NL_W == ch) BITNET_LOAD(lks_, lslot_, i)                           \
       }                                                                                         \
     }                                                                                           \
-    _Pragma("unroll") for (int f = ch * (kMfmaPerBlock / kChunks);                              \
-                           f < (ch + 1) * (kMfmaPerBlock / kChunks); ++f) {                     \
+    _Pragma("unroll") for (int f = ch * (kMfmaPerBlock / S::CH);                              \
+                           f < (ch + 1) * (kMfmaPerBlock / S::CH); ++f) {                     \
       const int hh = f / (RT * CT), rt = (f / CT) % RT, ct = f % CT;                            \
       acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct], acc[rt][ct],  \
                                                           0, 0, 0);                             \
@@ -669,18 +670,18 @@ __global__ __launch_bounds__(64 * WMW * WNW) void ternary_gemm_stream_kernel(
   constexpr int kMfmaPerBlock = 2 * RT * CT;
   constexpr int kUnpackPerBlock = 2 * CT;
 #define BITNET_SSTEP(A_, B_, NB_, LD_, lslot_)                                                  \
-  _Pragma("unroll") for (int ch = 0; ch < kChunks; ++ch) {                                      \
+  _Pragma("unroll") for (int ch = 0; ch < S::CH; ++ch) {                                      \
     _Pragma("unroll") for (int e = 0; e < kUnpackPerBlock; ++e) {                               \
-      if (1 + e * (kChunks - 1) / kUnpackPerBlock == ch)                                        \
+      if (1 + e * (S::CH - 1) / kUnpackPerBlock == ch)                                        \
         NB_[e / CT][e % CT] = unpack_u(pw[e % CT], 2 * g + 4 * (e / CT));                       \
     }                                                                                           \
     if (LD_) {                                                                                  \
       _Pragma("unroll") for (int q = 0; q < T::NLG; ++q) {                                      \
-        if (q * kChunks / T::NLG == ch) BITNET_SLOAD(lslot_, q)                                 \
+        if (q * S::CH / T::NLG == ch) BITNET_SLOAD(lslot_, q)                                 \
       }                                                                                         \
     }                                                                                           \
-    _Pragma("unroll") for (int f = ch * (kMfmaPerBlock / kChunks);                              \
-                           f < (ch + 1) * (kMfmaPerBlock / kChunks); ++f) {                     \
+    _Pragma("unroll") for (int f = ch * (kMfmaPerBlock / S::CH);                              \
+                           f < (ch + 1) * (kMfmaPerBlock / S::CH); ++f) {                     \
       const int hh = f / (RT * CT), rt = (f / CT) % RT, ct = f % CT;                            \
       acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct], acc[rt][ct],  \
                                                           0, 0, 0);                             \
@@ -904,7 +905,7 @@ hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64
                                  float* y, int32_t* acc, hipStream_t stream,
                                  const int32_t* rowsum, bool nibbles) {
   if (M <= kDecodeMaxM)
-    return launch_gemv(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream, nibbles);
+    return launch_gemv(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream, nibbles, rowsum);
   if (nibbles) return hipErrorInvalidValue;
   return launch_gemm(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream, rowsum);
 }

@@ -55,6 +55,33 @@ struct GemvArgs {
   float c;
 };
 
+// With the codes' row sums known, the B operand is the stored field u = t + 1
+// masked in place (fields 0, 1, 2 worth u, 4u, 16u: one AND per dword) and
+// field 3 shifted down to 16u; three accumulators keep the scales apart, and
+// q . t = q . u - sum(q) is taken in the epilogue. Without row sums each
+// field is expanded to t in {-1, 0, 1} (a shift, a mask and a byte lookup).
+template <int CT>
+__device__ __forceinline__ void mma_round_u(const v4i (&av)[4], const uint4 (&p)[CT], v4i (&a1)[CT],
+                                            v4i (&a4)[CT], v4i (&a16)[CT]) {
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const uint4 w = p[ct];
+    v4i u;
+    u.x = (int)(w.x & 0x03030303u); u.y = (int)(w.y & 0x03030303u);
+    u.z = (int)(w.z & 0x03030303u); u.w = (int)(w.w & 0x03030303u);
+    a1[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], u, a1[ct], 0, 0, 0);
+    u.x = (int)(w.x & 0x0C0C0C0Cu); u.y = (int)(w.y & 0x0C0C0C0Cu);
+    u.z = (int)(w.z & 0x0C0C0C0Cu); u.w = (int)(w.w & 0x0C0C0C0Cu);
+    a4[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[1], u, a4[ct], 0, 0, 0);
+    u.x = (int)(w.x & 0x30303030u); u.y = (int)(w.y & 0x30303030u);
+    u.z = (int)(w.z & 0x30303030u); u.w = (int)(w.w & 0x30303030u);
+    a16[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[2], u, a16[ct], 0, 0, 0);
+    u.x = (int)((w.x >> 2) & 0x30303030u); u.y = (int)((w.y >> 2) & 0x30303030u);
+    u.z = (int)((w.z >> 2) & 0x30303030u); u.w = (int)((w.w >> 2) & 0x30303030u);
+    a16[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[3], u, a16[ct], 0, 0, 0);
+  }
+}
+
 template <int CT>
 __device__ __forceinline__ void mma_round(const v4i (&av)[4], const uint4 (&p)[CT], v4i (&acc)[CT]) {
 #pragma unroll
@@ -87,13 +114,23 @@ constexpr int kCodePitch = 272;
 // cover its 16 rows, and the lane widens them to 16 x the codes (a mask and
 // a shift per four codes) on their way to LDS; the wave's tile is divided
 // by 16 at the end, exactly.
-template <int CT, bool NIB>
+//
+// Every workgroup reads the whole code matrix; workgroup b starts its walk
+// over the super-blocks at super-block b mod nSB, so that the workgroups of an
+// XCD do not all request the same code lines of its L2 at the same moment.
+//
+// RSG: the codes' row sums are given (u-field operands, see mma_round_u).
+template <int CT, bool NIB, bool RSG>
 __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* codes_base,
                                              int8_t* stage, v4i (&acc)[CT]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int nKB = a.K >> 6, nSB = (nKB + 3) >> 2;
   const int rounds = (nSB + a.sb_waves - 1) / a.sb_waves;
+  const int rot = (int)(blockIdx.x % (unsigned)nSB);
+  v4i a4[CT], a16[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) a4[ct] = a16[ct] = v4i{0, 0, 0, 0};
   const size_t row_bytes = (size_t)(a.K >> 2);
   // contiguous code chunk i of this lane: token row 4 i + lane / 16, byte 16 (lane % 16) of the
   // super-block; nibble codes: token row 8 i + lane / 8, packed byte 16 (lane % 8)
@@ -109,8 +146,9 @@ __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* co
     v4i cv[kRoundsInFlight][4];
 #pragma unroll
     for (int u = 0; u < kRoundsInFlight; ++u) {
-      const int sb = wave + a.sb_waves * (r0 + u);
-      const int sbc = sb < nSB ? sb : nSB - 1;
+      const int sbl = wave + a.sb_waves * (r0 + u);  // place in the walk
+      const bool live = (r0 + u < rounds) && sbl < nSB;
+      const int sbc = live ? (sbl + rot < nSB ? sbl + rot : sbl + rot - nSB) : nSB - 1;
       const int kb = sbc * 4 + grp;
       const int kbc = kb < nKB ? kb : nKB - 1;
 #pragma unroll
@@ -123,7 +161,7 @@ __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* co
       // zeroed with a mask (a branch would force a wait on the load).
       const int k = NIB ? sbc * 128 + cbyte : sbc * 256 + cbyte;  // byte in the code row
       const int rb = NIB ? a.K >> 1 : a.K;                        // code row bytes
-      const bool k_ok = (r0 + u < rounds) && sb < nSB && k < rb;
+      const bool k_ok = live && k < rb;
       const int kc = k < rb ? k : rb - 16;
 #pragma unroll
       for (int i = 0; i < kCodeLoads; ++i) {
@@ -162,23 +200,31 @@ __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* co
         for (int j = 0; j < 4; ++j)
           av[j] = *reinterpret_cast<const v4i*>(stage + col * kCodePitch + 64 * grp + 16 * j);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        mma_round<CT>(av, p[u], acc);
+        if constexpr (RSG) mma_round_u<CT>(av, p[u], acc, a4, a16);
+        else mma_round<CT>(av, p[u], acc);
       }
     }
   }
+  if constexpr (RSG) {
+    // q . u over the three scales (exact: a4 holds multiples of 4, a16 of 16)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = acc[ct] + (a4[ct] >> 2) + (a16[ct] >> 4);
+  }
   if constexpr (NIB) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ct] >>= 4;  // every product was 16 q t
+    for (int ct = 0; ct < CT; ++ct) acc[ct] >>= 4;  // every product was 16 q u (or 16 q t)
   }
 }
 
 // Add the waves' 16x16 tiles and store. 16x16 MFMA layout: lane l holds rows
 // 4*(l/16) + v, column l%16.
 // s_row[v] is the scale of output row 4 (l / 16) + v of the finishing lane
-// (loaded ahead by the caller, like alpha).
+// and rs[v] its code row sum when the tiles hold q . u (loaded ahead by the
+// caller, like alpha; zero otherwise).
 template <int CT, bool OUT_I32>
 __device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[CT], v4i* red,
-                                            const float (&s_row)[4], int nw, float alpha) {
+                                            const float (&s_row)[4], const int (&rs)[4], int nw,
+                                            float alpha) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
 #pragma unroll
@@ -199,13 +245,13 @@ __device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[
     if (OUT_I32) {
       a.acc_out[o] = total[v];
     } else {
-      a.y[o] = (float)total[v] * dequant_factor(alpha, s_row[v], a.c);
+      a.y[o] = (float)(total[v] - rs[v]) * dequant_factor(alpha, s_row[v], a.c);
     }
   }
 }
 
-template <int CT, bool OUT_I32, bool NIB>
-__global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a) {
+template <int CT, bool OUT_I32, bool NIB, bool RSG>
+__global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a, const int32_t* rowsum) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nw = blockDim.x >> 6;
   v4i* red = reinterpret_cast<v4i*>(smem);  // [nw][CT][64]
@@ -218,15 +264,20 @@ __global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a) {
                "s"(a.codes), "s"(nw));
   float alpha = 0.0f;
   float s_row[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int rs[4] = {0, 0, 0, 0};
   if (!OUT_I32) {
     alpha = *a.alpha;
     const int m0 = 4 * ((threadIdx.x & 63) >> 4);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s_row[v] = a.scales[m0 + v < a.M ? m0 + v : a.M - 1];
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + v < a.M ? m0 + v : a.M - 1;
+      s_row[v] = a.scales[m];
+      if (RSG) rs[v] = rowsum[m];
+    }
   }
   v4i acc[CT];
-  wave_product<CT, NIB>(a, a.codes, stage, acc);
-  gemv_finish<CT, OUT_I32>(a, acc, red, s_row, nw, alpha);
+  wave_product<CT, NIB, RSG>(a, a.codes, stage, acc);
+  gemv_finish<CT, OUT_I32>(a, acc, red, s_row, rs, nw, alpha);
 }
 
 __device__ __forceinline__ void load4(const float* x, size_t i, float (&v)[4]) {
@@ -529,7 +580,8 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
 #pragma unroll
     for (int v = 0; v < 4; ++v) s_row[v] = srow[wave * 16 + (m0 + v < a.M ? m0 + v : 0)];
   }
-  gemv_finish<CT, false>(a, acc, red, s_row, nw, alpha);
+  const int no_rs[4] = {0, 0, 0, 0};
+  gemv_finish<CT, false>(a, acc, red, s_row, no_rs, nw, alpha);
 }
 
 // Single-token decode forward, one wave per 16 output columns and all of K
@@ -697,13 +749,14 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int CT, bool OUT_I32, bool NIB>
-hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, hipStream_t stream) {
+template <int CT, bool OUT_I32, bool NIB, bool RSG>
+hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, const int32_t* rowsum,
+                          hipStream_t stream) {
   const size_t lds = (size_t)(p.threads / 64) * (CT * 1024 + 16 * kCodePitch);
-  auto kern = ternary_gemv_kernel<CT, OUT_I32, NIB>;
+  auto kern = ternary_gemv_kernel<CT, OUT_I32, NIB, RSG>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a);
+  kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a, rowsum);
   return hipGetLastError();
 }
 
@@ -769,7 +822,7 @@ hipError_t launch_fused_t(const GemvArgs& a, const Prologue* pro, hipStream_t st
 
 hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, hipStream_t stream, bool nibbles) {
+                       int32_t* acc, hipStream_t stream, bool nibbles, const int32_t* rowsum) {
   if (nibbles && (M > kDecodeMaxM || K % kNibbleKMultiple != 0)) return hipErrorInvalidValue;
   const GemvPlan p = plan_gemv(M, K, N, false, false);
   GemvArgs a{};
@@ -784,9 +837,14 @@ hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int 
   a.N = (int)N;
   a.sb_waves = p.sb_waves;
   a.c = (bits == 8) ? kScaleInt8 : kScaleInt4;
-  if (nibbles)
-    return acc ? launch_gemv_ct<1, true, true>(p, a, stream) : launch_gemv_ct<1, false, true>(p, a, stream);
-  return acc ? launch_gemv_ct<1, true, false>(p, a, stream) : launch_gemv_ct<1, false, false>(p, a, stream);
+  if (acc)
+    return nibbles ? launch_gemv_ct<1, true, true, false>(p, a, nullptr, stream)
+                   : launch_gemv_ct<1, true, false, false>(p, a, nullptr, stream);
+  if (rowsum)
+    return nibbles ? launch_gemv_ct<1, false, true, true>(p, a, rowsum, stream)
+                   : launch_gemv_ct<1, false, false, true>(p, a, rowsum, stream);
+  return nibbles ? launch_gemv_ct<1, false, true, false>(p, a, nullptr, stream)
+                 : launch_gemv_ct<1, false, false, false>(p, a, nullptr, stream);
 }
 
 hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,

@@ -55,7 +55,7 @@ hipError_t launch_ternary_matmul(const int8_t*, const float*, int64_t, int, cons
   return record(acc ? "matmul_i32" : (nibbles ? "matmul_nibbles" : "matmul"));
 }
 hipError_t launch_gemv(const int8_t*, const float*, int64_t, int, const uint8_t*, int64_t,
-                       const float*, int, float*, int32_t*, hipStream_t, bool) {
+                       const float*, int, float*, int32_t*, hipStream_t, bool, const int32_t*) {
   return record("gemv");
 }
 hipError_t launch_gemm(const int8_t*, const float*, int64_t, int, const uint8_t*, int64_t,
