@@ -25,6 +25,9 @@ Parity status per function (mirrors the design notes):
   forward_prologue     pinned (reduces to forward; torch module chain on small shapes)
   kv_quantize          pinned (hand values per branch, reduction to the pinned
                        activation quantizers, 3-bit range and error bounds)
+  kv_pack / kv_unpack  pinned (hand-built bytes at 3 and 4 bits, round trips,
+                       numpy's own bit packing of the same stream); the bit
+                       layout is a contract of this library, not of the pages
   backward             pinned (torch autograd through the STE forward, adjoint
                        identities, Eq. 8 via H*H = I, hand values, brute force)
   tl2 (module)         pinned (tests/test_oracle_tl2.py: the mirror table against
@@ -47,7 +50,9 @@ from .hbitlinear import (  # noqa: F401
     hadamard_matrix,
     kv_code_params,
     kv_dequantize,
+    kv_pack,
     kv_quantize,
+    kv_unpack,
     pack_2bit,
     quant_boundary_distance,
     quantize_activations,

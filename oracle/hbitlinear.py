@@ -360,6 +360,49 @@ def kv_dequantize(q: np.ndarray, s: np.ndarray, bits: int) -> np.ndarray:
     return out
 
 
+# Packed storage of the low-bit KV codes. The engine page keeps the
+# fake-quantized tensor; storing the b-bit codes b bits apiece is this
+# library's layout, not the page's. Codes are b-bit two's complement
+# ([-8, 7] at 4 bits, [-4, 3] at 3 bits), laid out as one little-endian bit
+# stream per token row: code k of the row occupies bits b k .. b k + b - 1
+# (bit i of the stream is bit i % 8 of byte i // 8). At 4 bits that is two
+# codes per byte, code 2 i in the low nibble of byte i; at 3 bits, eight codes
+# per three bytes.
+
+def kv_pack(q: np.ndarray, bits: int) -> np.ndarray:
+    """uint8 [R, D * bits / 8] packing of the codes q [R, D] (bits 3 or 4)."""
+    if bits not in (3, 4):
+        raise ValueError("packed KV codes are 3 or 4 bits wide")
+    q = np.asarray(q, dtype=np.int64)
+    R, D = q.shape
+    if (D * bits) % 8:
+        raise ValueError("a packed row must be a whole number of bytes")
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    if q.size and (q.min() < lo or q.max() > hi):
+        raise ValueError(f"codes outside the {bits}-bit range")
+    out = np.zeros((R, D * bits // 8), dtype=np.uint8)
+    field = q & ((1 << bits) - 1)  # two's complement in b bits
+    for k in range(D):
+        for b in range(bits):
+            pos = bits * k + b
+            out[:, pos // 8] |= (((field[:, k] >> b) & 1) << (pos % 8)).astype(np.uint8)
+    return out
+
+
+def kv_unpack(packed: np.ndarray, bits: int, D: int) -> np.ndarray:
+    """int8 codes [R, D] of a kv_pack'ed array (sign-extended from b bits)."""
+    if bits not in (3, 4):
+        raise ValueError("packed KV codes are 3 or 4 bits wide")
+    packed = np.asarray(packed, dtype=np.int64)
+    R = packed.shape[0]
+    field = np.zeros((R, D), dtype=np.int64)
+    for k in range(D):
+        for b in range(bits):
+            pos = bits * k + b
+            field[:, k] |= ((packed[:, pos // 8] >> (pos % 8)) & 1) << b
+    return np.where(field >= (1 << (bits - 1)), field - (1 << bits), field).astype(np.int8)
+
+
 # ---------------------------------------------------------------------------
 # Backward — [engine] Eq. 8 (HadamardTransformFunction: the gradient of the
 # transform is the transform of the gradient, H being symmetric and

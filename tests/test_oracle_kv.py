@@ -72,3 +72,46 @@ def test_single_token_and_bad_bits():
     assert q.tolist() == [[[127, -42, 0, 11]]]  # only BOS: int8
     with pytest.raises(ValueError):
         oracle.kv_quantize(kv, 2)
+
+
+# ---- packed storage of the 3- and 4-bit codes ------------------------------
+
+def test_kv_pack_hand_built_bytes():
+    # 4 bits, two's complement nibbles, code 2i in the low nibble of byte i:
+    #   1 -> 0001, -1 -> 1111: byte 0 = 1111 0001 = 0xF1
+    #   7 -> 0111, -8 -> 1000: byte 1 = 1000 0111 = 0x87
+    np.testing.assert_array_equal(oracle.kv_pack(np.array([[1, -1, 7, -8]]), 4), [[0xF1, 0x87]])
+    # 3 bits, code k at stream bits 3k .. 3k+2, least significant bit first:
+    #   1 = 001, -1 = 111, 3 = 011, -4 = 100, 0 = 000, 2 = 010, -2 = 110, -3 = 101
+    #   stream bits 0..7   = 1,0,0, 1,1,1, 1,1   -> byte 0 = 0b11111001 = 0xF9
+    #   stream bits 8..15  = 0, 0,0,1, 0,0,0, 0  -> byte 1 = 0b00001000 = 0x08
+    #   stream bits 16..23 = 1,0, 0,1,1, 1,0,1   -> byte 2 = 0b10111001 = 0xB9
+    q = np.array([[1, -1, 3, -4, 0, 2, -2, -3]])
+    np.testing.assert_array_equal(oracle.kv_pack(q, 3), [[0xF9, 0x08, 0xB9]])
+    np.testing.assert_array_equal(oracle.kv_unpack(np.array([[0xF9, 0x08, 0xB9]]), 3, 8), q)
+    np.testing.assert_array_equal(oracle.kv_unpack(np.array([[0xF1, 0x87]]), 4, 4), [[1, -1, 7, -8]])
+
+
+@pytest.mark.parametrize("bits,D", [(4, 8), (4, 128), (4, 24), (3, 8), (3, 128), (3, 96)])
+def test_kv_pack_round_trip_and_numpy_bit_order(bits, D):
+    rng = np.random.default_rng(D + bits)
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    q = rng.integers(lo, hi + 1, size=(5, D))
+    packed = oracle.kv_pack(q, bits)
+    assert packed.shape == (5, D * bits // 8)
+    np.testing.assert_array_equal(oracle.kv_unpack(packed, bits, D), q)
+    # the same stream through numpy's own little-endian bit packer
+    field = (q & ((1 << bits) - 1))[:, :, None]
+    stream = ((field >> np.arange(bits)) & 1).astype(np.uint8).reshape(5, D * bits)
+    np.testing.assert_array_equal(packed, np.packbits(stream, axis=1, bitorder="little"))
+
+
+def test_kv_pack_rejects_what_it_cannot_hold():
+    with pytest.raises(ValueError):
+        oracle.kv_pack(np.array([[8, 0]]), 4)
+    with pytest.raises(ValueError):
+        oracle.kv_pack(np.array([[-5, 0, 0, 0, 0, 0, 0, 0]]), 3)
+    with pytest.raises(ValueError):
+        oracle.kv_pack(np.zeros((1, 4), dtype=np.int64), 3)  # 12 bits: not whole bytes
+    with pytest.raises(ValueError):
+        oracle.kv_pack(np.zeros((1, 8), dtype=np.int64), 8)
