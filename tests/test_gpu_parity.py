@@ -106,6 +106,11 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     (5, 256, 33, 4, 1, "bf16"),
     (7, 4096, 33, 8, 1, "fp32"),
     (12, 8192, 40, 4, 1, "bf16"),      # transform, 16 elements per thread for a few long rows
+    (16, 16384, 130, 8, 1, "fp32"),    # transform, 32 elements per thread, int8 codes
+    (3, 8192, 77, 8, 1, "bf16"),
+    (1, 16384, 40, 4, 1, "bf16"),      # one long row with the transform, nibble codes
+    (16, 8192, 16, 4, 1, "bf16"),      # a single column tile
+    (5, 16384, 300, 4, 1, "fp32"),
     (16, 512, 70, 4, 1, "bf16"),       # nibble codes, shortest row they take with the transform
     (16, 4352, 50, 4, 0, "bf16"),      # nibble codes without the transform, 17 super-blocks
     (13, 1280, 33, 4, 0, "fp32"),      # nibble codes, fp32 input, ragged M
@@ -363,3 +368,61 @@ def test_module_wrapper():
     t, a, _ = oracle.ternarize(case["W"])
     ref = oracle.forward(case["x"], "fp32", t, a, 4, 1)
     assert_y_close(y.cpu().numpy(), ref["y64"])
+
+
+@pytest.mark.parametrize("M,K,N,bits,had", [
+    (16, 16384, 130, 4, 1),    # nibble codes between the stages
+    (200, 1024, 300, 8, 0),    # prefill tile
+    (5, 2048, 77, 8, 1),       # transform kernel + weight-streaming product
+])
+def test_forward_stages_compose_to_the_forward(M, K, N, bits, had):
+    """The quantization stage then the product stage, on one workspace, give
+    the forward's output bit for bit; a fused shape refuses a lone stage."""
+    _say(f"stages M={M} K={K} N={N} bits={bits} hadamard={had}")
+    case = workloads.make_case(M, K, N, x_dtype="bf16", n_out=8, factor=30.0, seed=M + K)
+    x = _to_dev_x(case["x"], "bf16")
+    Wp, alpha = bl.ternarize_weights(torch.from_numpy(case["W"]).to(DEV))
+    ws = torch.empty((bl.forward_workspace_bytes(M, K, N, bits, had),), dtype=torch.uint8,
+                     device=DEV)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    bl.hbitlinear_forward_stages(x, Wp, alpha, bits, had, 1, out=y, workspace=ws)
+    bl.hbitlinear_forward_stages(x, Wp, alpha, bits, had, 2, out=y, workspace=ws)
+    y_ref = bl.hbitlinear_forward(x, Wp, alpha, bits, had)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), y_ref.cpu().numpy())
+    xs = _to_dev_x(workloads.make_case(1, 2560, 16, x_dtype="bf16", seed=1)["x"], "bf16")
+    Wps = torch.full((16, 640), 0x55, dtype=torch.uint8, device=DEV)
+    with pytest.raises(bl.BitNetError):
+        bl.hbitlinear_forward_stages(xs, Wps, alpha, 8, 0, 1, out=torch.empty((1, 16), device=DEV),
+                                     workspace=torch.empty((16,), dtype=torch.uint8, device=DEV))
+
+
+def test_stream_read_reads_without_writing():
+    _say("stream read")
+    buf = torch.zeros((3 * 2 ** 20 + 4096,), dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    bl.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert sink.item() == 7  # zero data never matches the sink's constant
+    with pytest.raises(ValueError):
+        bl.stream_read(buf, torch.zeros((2,), dtype=torch.int32, device=DEV))
+
+
+def test_binding_rejects_wrong_outputs():
+    _say("binding output checks")
+    x = torch.zeros((4, 256), dtype=torch.float32, device=DEV)
+    Wp = torch.full((32, 64), 0x55, dtype=torch.uint8, device=DEV)
+    alpha = torch.ones((1,), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        bl.hbitlinear_forward(x, Wp, alpha, 8, 1, out=torch.empty((4, 31), device=DEV))
+    with pytest.raises(TypeError):
+        bl.hbitlinear_forward(x, Wp, alpha, 8, 1,
+                              out=torch.empty((4, 32), dtype=torch.float16, device=DEV))
+    with pytest.raises(ValueError):
+        bl.hbitlinear_forward(x, Wp, alpha, 8, 1, out=torch.empty((4, 32)))
+    with pytest.raises(ValueError):
+        bl.quantize_activations(x, 8, 1, codes=torch.empty((4, 128), dtype=torch.int8, device=DEV))
+    with pytest.raises(ValueError):
+        bl.ternarize_weights(torch.zeros((32, 256), device=DEV),
+                             out=torch.empty((32, 32), dtype=torch.uint8, device=DEV))
+
