@@ -303,7 +303,8 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
 def _measure_kv(torch, bl, dev, steps, warmup):
     """Low-bit KV-cache quantizer on a 32-head, 4096-token, head_dim 128 bf16
     cache (seeded N(0,1) values with a few x8 outlier channels): HBM bytes are
-    2 read + 1 written per element and 4 written per token."""
+    2 read + 1 written per element and 4 written per token; with the codes
+    packed, bits/8 written per element."""
     from bit_activation_linear_amd import workloads
     B, H, S, D = 1, 32, 4096, 128
     case = workloads.make_case(B * H * S, D, 1, x_dtype="bf16", n_out=4, factor=8.0, seed=0)
@@ -317,6 +318,17 @@ def _measure_kv(torch, bl, dev, steps, warmup):
                          steps, warmup)
         res["bits"][bits] = {"us": ms * 1e3, "GBs": nbytes / (ms * 1e-3) / 1e9,
                              "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        # the same codes stored bits/8 bytes per element (BOS rows apart):
+        # 2 B read + bits/8 B written per element, 4 B per token, D B per head
+        packed = torch.empty((B, H, S, D * bits // 8), dtype=torch.uint8, device=dev)
+        bos = torch.empty((B, H, D), dtype=torch.int8, device=dev)
+        pbytes = B * H * S * (2 * D + D * bits // 8 + 4) + B * H * D
+        ms = _time_steps(torch, lambda i, b=bits: bl.kv_quantize_packed(
+            kv, b, packed=packed, bos_codes=bos, scales=scales), steps, warmup)
+        res["bits"][bits]["packed"] = {"us": ms * 1e3, "bytes_per_call": pbytes,
+                                       "GBs": pbytes / (ms * 1e-3) / 1e9,
+                                       "hbm_frac": pbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       "cache_bytes_per_element": bits / 8}
     return res
 
 
@@ -569,7 +581,8 @@ def main():
     kv = None
     if not args.no_extra:
         kv = _measure_kv(torch, bl, dev, max(20, args.steps // 4), max(5, args.warmup // 2))
-        _log(f"[bench] kv cache: " + ", ".join(f"{b}-bit {r['us']:.2f} us" for b, r in kv["bits"].items()))
+        _log(f"[bench] kv cache: " + ", ".join(f"{b}-bit {r['us']:.2f} us (packed {r['packed']['us']:.2f} us)"
+                                                for b, r in kv["bits"].items()))
 
     clocks_after = _clocks()
     cpu = None

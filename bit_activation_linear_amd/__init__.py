@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     hbitlinear_forward_stages,
     hbitlinear_forward_tl2,
     kv_quantize,
+    kv_quantize_packed,
     pack_2bit,
     pack_tl2,
     quantize_activations,

@@ -62,6 +62,8 @@ SIGNATURES = {
                                                     ctypes.c_float, _int, _int, _ptr, _ptr,
                                                     _ptr]),
     "bitnet_kv_quantize": (_int, [_ptr, _int, _i64, _i64, _i64, _int, _ptr, _ptr, _ptr]),
+    "bitnet_kv_quantize_packed": (_int, [_ptr, _int, _i64, _i64, _i64, _int, _ptr, _ptr, _ptr,
+                                         _ptr]),
     "bitnet_tl2_bytes": (_size, [_i64, _i64]),
     "bitnet_pack_tl2": (_int, [_ptr, _i64, _i64, _ptr, _ptr]),
     "bitnet_hbitlinear_forward_tl2": (_int, [_ptr, _int, _i64, _i64, _ptr, _i64, _ptr, _int, _ptr,

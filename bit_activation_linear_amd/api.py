@@ -324,6 +324,37 @@ def kv_quantize(kv: torch.Tensor, bits: int, codes: Optional[torch.Tensor] = Non
     return codes, scales
 
 
+def kv_quantize_packed(kv: torch.Tensor, bits: int, packed: Optional[torch.Tensor] = None,
+                       bos_codes: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """kv_quantize with the 3- or 4-bit codes stored `bits` bits apiece:
+    kv [B, H, S, D] -> (packed uint8 [B, H, S, D * bits / 8], one little-endian
+    bit stream per token with the BOS rows zero; bos_codes int8 [B, H, D],
+    the BOS tokens' int8 codes; scales fp32 [B, H, S])."""
+    _require(kv, "kv", (torch.float32, torch.bfloat16), 4)
+    B, H, S, D = kv.shape
+    if bits not in (3, 4) or (D * bits) % 8:
+        raise ValueError("packed KV codes are 3 or 4 bits wide and fill whole bytes")
+    row = D * bits // 8
+    if packed is None:
+        packed = torch.empty((B, H, S, row), dtype=torch.uint8, device=kv.device)
+    if bos_codes is None:
+        bos_codes = torch.empty((B, H, D), dtype=torch.int8, device=kv.device)
+    if scales is None:
+        scales = torch.empty((B, H, S), dtype=torch.float32, device=kv.device)
+    _require(packed, "packed", (torch.uint8,), 4)
+    _require(bos_codes, "bos_codes", (torch.int8,), 3)
+    _require(scales, "scales", (torch.float32,), 3)
+    if (tuple(packed.shape) != (B, H, S, row) or tuple(bos_codes.shape) != (B, H, D)
+            or tuple(scales.shape) != (B, H, S)):
+        raise ValueError("packed must be [B, H, S, D*bits/8], bos_codes [B, H, D], scales [B, H, S]")
+    _lib.call("bitnet_kv_quantize_packed", kv.data_ptr(), _x_dtype(kv), B * H * S, D, S,
+              int(bits), packed.data_ptr(), bos_codes.data_ptr(), scales.data_ptr(),
+              _stream_ptr(kv))
+    return packed, bos_codes, scales
+
+
 def backward_workspace_bytes(M: int, K: int, N: int, dy_dtype: torch.dtype, want_dx: bool = True,
                              want_dw: bool = True) -> int:
     code = _lib.BF16 if dy_dtype == torch.bfloat16 else _lib.F32

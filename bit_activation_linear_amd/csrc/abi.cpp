@@ -567,17 +567,20 @@ bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, 
   return hip_status(e, fn);
 }
 
-bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R, int64_t D,
-                                 int64_t S, int bits, int8_t* codes, float* scales,
-                                 hipStream_t stream) {
-  const char* fn = "bitnet_kv_quantize";
+namespace {
+
+bitnet_status kv_check(const char* fn, int64_t R, int64_t D, int64_t S, int bits,
+                       bitnet_dtype x_dtype, bool packed) {
   if (R < 0 || D < 0 || S < 0)
     return fail(BITNET_ERR_INVALID_ARG, "%s: negative size (R=%lld D=%lld S=%lld)", fn,
                 (long long)R, (long long)D, (long long)S);
-  if (bits != 3 && bits != 4 && bits != 8)
-    return fail(BITNET_ERR_BAD_BITS, "%s: bits=%d must be 3, 4 or 8", fn, bits);
+  if (packed ? (bits != 3 && bits != 4) : (bits != 3 && bits != 4 && bits != 8))
+    return fail(BITNET_ERR_BAD_BITS, "%s: bits=%d must be %s", fn, bits, packed ? "3 or 4" : "3, 4 or 8");
   if (D % 8 != 0 || D < 8)
     return fail(BITNET_ERR_ALIGN, "%s: D=%lld must be a positive multiple of 8", fn, (long long)D);
+  if (packed && bits == 3 && D % 32 != 0)
+    return fail(BITNET_ERR_ALIGN, "%s: D=%lld must be a multiple of 32 for 3-bit packing", fn,
+                (long long)D);
   if (D > 512)
     return fail(BITNET_ERR_UNSUPPORTED, "%s: D=%lld exceeds 512", fn, (long long)D);
   if (S < 1 || R % S != 0)
@@ -587,6 +590,16 @@ bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R
     return fail(BITNET_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, x_dtype);
   if (S > INT_MAX || R > (int64_t)INT_MAX * 64)
     return fail(BITNET_ERR_UNSUPPORTED, "%s: R or S too large", fn);
+  return BITNET_OK;
+}
+
+}  // namespace
+
+bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R, int64_t D,
+                                 int64_t S, int bits, int8_t* codes, float* scales,
+                                 hipStream_t stream) {
+  const char* fn = "bitnet_kv_quantize";
+  if (bitnet_status st = kv_check(fn, R, D, S, bits, x_dtype, false)) return st;
   if (R == 0) return ok();
   if (!kv || !codes || !scales) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned(kv, 16) || !aligned(codes, 16) || !aligned(scales, 4))
@@ -594,6 +607,22 @@ bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R
   if (bitnet_status st = launch_guard(fn)) return st;
   return hip_status(bitnet::launch_kv_quantize(kv, (int)x_dtype, R, (int)D, (int)S, bits, codes,
                                                scales, stream),
+                    fn);
+}
+
+bitnet_status bitnet_kv_quantize_packed(const void* kv, bitnet_dtype x_dtype, int64_t R,
+                                        int64_t D, int64_t S, int bits, uint8_t* packed,
+                                        int8_t* bos_codes, float* scales, hipStream_t stream) {
+  const char* fn = "bitnet_kv_quantize_packed";
+  if (bitnet_status st = kv_check(fn, R, D, S, bits, x_dtype, true)) return st;
+  if (R == 0) return ok();
+  if (!kv || !packed || !bos_codes || !scales)
+    return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(kv, 16) || !aligned(packed, 4) || !aligned(bos_codes, 8) || !aligned(scales, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
+  return hip_status(bitnet::launch_kv_quantize(kv, (int)x_dtype, R, (int)D, (int)S, bits,
+                                               bos_codes, scales, stream, packed),
                     fn);
 }
 

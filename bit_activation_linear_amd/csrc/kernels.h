@@ -108,9 +108,12 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bit
                            bool nibbles = false);
 
 // Low-bit KV cache: rows of D elements, row r being token r % S of its head;
-// token 0 int8 absmax, the others bits = 3, 4 or 8.
+// token 0 int8 absmax, the others bits = 3, 4 or 8. With packed (bits 3 or 4
+// only), the non-BOS codes go to packed [R, D * bits / 8] as one bit stream
+// per row and codes is the [R / S, D] array of the BOS rows' int8 codes.
 hipError_t launch_kv_quantize(const void* kv, int x_dtype, int64_t R, int D, int S, int bits,
-                              int8_t* codes, float* scales, hipStream_t stream);
+                              int8_t* codes, float* scales, hipStream_t stream,
+                              uint8_t* packed = nullptr);
 
 // Ternary product from codes. Exactly one of y (dequantized; needs scales,
 // alpha, bits) or acc (raw int32) is non-null. rowsum (optional, with y):

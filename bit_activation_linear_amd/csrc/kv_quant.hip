@@ -15,6 +15,14 @@
 // (rounded up to a power of two), each holding one 16-byte (bf16) or two
 // 16-byte (fp32) loads, so a wave covers 64 / G tokens and every per-token
 // statistic is a butterfly over G lanes of one wave: no LDS, no barrier.
+//
+// Packed output (PACK, bits 3 and 4): the codes of the non-BOS tokens are
+// stored b bits apiece, one little-endian bit stream per token row (code k at
+// stream bits b k .. b k + b - 1, two's complement), so the cache holds
+// b / 8 bytes per element: a lane's eight codes are one 32-bit word at 4 bits
+// and 24 bits at 3 bits, of which four neighbouring lanes make three words.
+// BOS rows keep their int8 codes in a separate [R / S, D] array (their slot
+// of the packed array is zeroed).
 #include "kernels.h"
 
 namespace bitnet {
@@ -55,10 +63,11 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // One token row per group of G lanes; lane j of a group owns elements
 // 8j .. 8j+7 (j < D / 8).
-template <typename XT, int BITS, int G>
+template <typename XT, int BITS, int G, bool PACK>
 __global__ __launch_bounds__(256) void kv_quant_kernel(const XT* __restrict__ kv, int64_t R, int D,
                                                        int S, int8_t* __restrict__ codes,
-                                                       float* __restrict__ scales) {
+                                                       float* __restrict__ scales,
+                                                       uint8_t* __restrict__ packed) {
   constexpr int kRowsPerBlock = 256 / G;
   const int t = threadIdx.x;
   const int j = t % G;
@@ -90,53 +99,80 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const XT* __restrict__ kv
   }
   const float s = st + kEps;
   const float mult = c / s;
+  int q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = (int)fminf(fmaxf(__builtin_rintf(v[e] * mult), lo), hi);
+  if (row_ok && j == 0) scales[row] = s;
   unsigned w[2] = {0u, 0u};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float q = fminf(fmaxf(__builtin_rintf(v[e] * mult), lo), hi);
-    w[e >> 2] |= ((unsigned)(int)q & 0xFFu) << (8 * (e & 3));
+  for (int e = 0; e < 8; ++e) w[e >> 2] |= ((unsigned)q[e] & 0xFFu) << (8 * (e & 3));
+  if constexpr (!PACK) {
+    if (row_ok && own) *reinterpret_cast<uint2*>(codes + row * D + 8 * j) = make_uint2(w[0], w[1]);
+  } else {
+    // BOS rows: int8 codes into the BOS array, zeros in the packed slot
+    if (row_ok && own && bos)
+      *reinterpret_cast<uint2*>(codes + (row / S) * D + 8 * j) = make_uint2(w[0], w[1]);
+    unsigned f = 0u;  // the lane's eight b-bit fields, code e at bits b e
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f |= ((unsigned)q[e] & ((1u << BITS) - 1u)) << (BITS * e);
+    if (bos) f = 0u;
+    if constexpr (BITS == 4) {
+      if (row_ok && own) *reinterpret_cast<unsigned*>(packed + row * (D / 2) + 4 * j) = f;
+    } else {
+      // lanes 4a .. 4a+3 hold 96 stream bits: lane 4a + b (b < 3) stores
+      // word b, the low bits of its own field shifted down and its right
+      // neighbour's shifted up
+      const unsigned nxt = (unsigned)__shfl_down((int)f, 1, 64);
+      const int b = j & 3;
+      const unsigned word = (f >> (8 * b)) | (nxt << (24 - 8 * b));
+      if (row_ok && own && b < 3)
+        *reinterpret_cast<unsigned*>(packed + row * (3 * D / 8) + 12 * (j >> 2) + 4 * b) = word;
+    }
   }
-  if (row_ok && own) *reinterpret_cast<uint2*>(codes + row * D + 8 * j) = make_uint2(w[0], w[1]);
-  if (row_ok && j == 0) scales[row] = s;
 }
 
-template <typename XT, int BITS, int G>
+template <typename XT, int BITS, int G, bool PACK>
 hipError_t launch_kv_g(const void* kv, int64_t R, int D, int S, int8_t* codes, float* scales,
-                       hipStream_t stream) {
+                       uint8_t* packed, hipStream_t stream) {
   constexpr int kRowsPerBlock = 256 / G;
   const int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
-  kv_quant_kernel<XT, BITS, G><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-      reinterpret_cast<const XT*>(kv), R, D, S, codes, scales);
+  kv_quant_kernel<XT, BITS, G, PACK><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      reinterpret_cast<const XT*>(kv), R, D, S, codes, scales, packed);
   return hipGetLastError();
 }
 
-template <typename XT, int BITS>
+template <typename XT, int BITS, bool PACK>
 hipError_t launch_kv_bits(const void* kv, int64_t R, int D, int S, int8_t* codes, float* scales,
-                          hipStream_t stream) {
+                          uint8_t* packed, hipStream_t stream) {
   const int lanes = D / 8;
-  if (lanes <= 1) return launch_kv_g<XT, BITS, 1>(kv, R, D, S, codes, scales, stream);
-  if (lanes <= 2) return launch_kv_g<XT, BITS, 2>(kv, R, D, S, codes, scales, stream);
-  if (lanes <= 4) return launch_kv_g<XT, BITS, 4>(kv, R, D, S, codes, scales, stream);
-  if (lanes <= 8) return launch_kv_g<XT, BITS, 8>(kv, R, D, S, codes, scales, stream);
-  if (lanes <= 16) return launch_kv_g<XT, BITS, 16>(kv, R, D, S, codes, scales, stream);
-  if (lanes <= 32) return launch_kv_g<XT, BITS, 32>(kv, R, D, S, codes, scales, stream);
-  return launch_kv_g<XT, BITS, 64>(kv, R, D, S, codes, scales, stream);
+  if (lanes <= 1) return launch_kv_g<XT, BITS, 1, PACK>(kv, R, D, S, codes, scales, packed, stream);
+  if (lanes <= 2) return launch_kv_g<XT, BITS, 2, PACK>(kv, R, D, S, codes, scales, packed, stream);
+  if (lanes <= 4) return launch_kv_g<XT, BITS, 4, PACK>(kv, R, D, S, codes, scales, packed, stream);
+  if (lanes <= 8) return launch_kv_g<XT, BITS, 8, PACK>(kv, R, D, S, codes, scales, packed, stream);
+  if (lanes <= 16) return launch_kv_g<XT, BITS, 16, PACK>(kv, R, D, S, codes, scales, packed, stream);
+  if (lanes <= 32) return launch_kv_g<XT, BITS, 32, PACK>(kv, R, D, S, codes, scales, packed, stream);
+  return launch_kv_g<XT, BITS, 64, PACK>(kv, R, D, S, codes, scales, packed, stream);
 }
 
 template <typename XT>
 hipError_t launch_kv_dtype(const void* kv, int64_t R, int D, int S, int bits, int8_t* codes,
-                           float* scales, hipStream_t stream) {
-  if (bits == 3) return launch_kv_bits<XT, 3>(kv, R, D, S, codes, scales, stream);
-  if (bits == 4) return launch_kv_bits<XT, 4>(kv, R, D, S, codes, scales, stream);
-  return launch_kv_bits<XT, 8>(kv, R, D, S, codes, scales, stream);
+                           float* scales, uint8_t* packed, hipStream_t stream) {
+  if (packed) {
+    if (bits == 3) return launch_kv_bits<XT, 3, true>(kv, R, D, S, codes, scales, packed, stream);
+    if (bits == 4) return launch_kv_bits<XT, 4, true>(kv, R, D, S, codes, scales, packed, stream);
+    return hipErrorInvalidValue;
+  }
+  if (bits == 3) return launch_kv_bits<XT, 3, false>(kv, R, D, S, codes, scales, nullptr, stream);
+  if (bits == 4) return launch_kv_bits<XT, 4, false>(kv, R, D, S, codes, scales, nullptr, stream);
+  return launch_kv_bits<XT, 8, false>(kv, R, D, S, codes, scales, nullptr, stream);
 }
 
 }  // namespace
 
 hipError_t launch_kv_quantize(const void* kv, int x_dtype, int64_t R, int D, int S, int bits,
-                              int8_t* codes, float* scales, hipStream_t stream) {
-  if (x_dtype == 1) return launch_kv_dtype<uint16_t>(kv, R, D, S, bits, codes, scales, stream);
-  return launch_kv_dtype<float>(kv, R, D, S, bits, codes, scales, stream);
+                              int8_t* codes, float* scales, hipStream_t stream, uint8_t* packed) {
+  if (x_dtype == 1) return launch_kv_dtype<uint16_t>(kv, R, D, S, bits, codes, scales, packed, stream);
+  return launch_kv_dtype<float>(kv, R, D, S, bits, codes, scales, packed, stream);
 }
 
 }  // namespace bitnet

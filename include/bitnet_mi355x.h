@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define BITNET_ABI_VERSION 3
+#define BITNET_ABI_VERSION 4
 #define BITNET_EPS 1e-7f
 /* Largest K the fused transform + quantizer stages in one CU's LDS (fp32). */
 #define BITNET_MAX_K 32768
@@ -294,6 +294,25 @@ bitnet_status bitnet_hbitlinear_forward_tl2(const void* x, bitnet_dtype x_dtype,
 bitnet_status bitnet_kv_quantize(const void* kv, bitnet_dtype x_dtype, int64_t R, int64_t D,
                                  int64_t S, int bits, int8_t* codes, float* scales,
                                  hipStream_t stream);
+
+/* The same quantization (same codes and scales) with the 3- or 4-bit codes
+ * stored b bits apiece, so that the cache holds b / 8 bytes per element. The
+ * page keeps the fake-quantized tensor; this packing is this library's layout:
+ *   packed     uint8 [R, D * bits / 8], written: one little-endian bit stream
+ *              per token row, code k at stream bits bits*k .. bits*k+bits-1
+ *              (stream bit i is bit i % 8 of byte i / 8), two's complement
+ *              (at 4 bits: code 2i in the low nibble of byte i, 2i+1 in the
+ *              high one). The rows of BOS tokens are zero here.
+ *   bos_codes  int8 [R / S, D], written: the BOS token's 8-bit codes of each
+ *              head, in head order.
+ *   scales     fp32 [R], written, as above (BOS rows included).
+ * Requires bits = 3 or 4 (else BITNET_ERR_BAD_BITS), D % 8 == 0 (D % 32 == 0
+ * at 3 bits, so that rows are whole 32-bit words; else BITNET_ERR_ALIGN),
+ * 8 <= D <= 512, S >= 1, R % S == 0; kv 16-byte, packed 4-byte, bos_codes
+ * 8-byte aligned. R = 0 is a no-op. */
+bitnet_status bitnet_kv_quantize_packed(const void* kv, bitnet_dtype x_dtype, int64_t R,
+                                        int64_t D, int64_t S, int bits, uint8_t* packed,
+                                        int8_t* bos_codes, float* scales, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Backward                                                                  */

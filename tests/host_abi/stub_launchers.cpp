@@ -46,8 +46,8 @@ hipError_t launch_quantize(const void*, int, int64_t, int, int, int, int8_t*, fl
   return record(nibbles ? "quantize_nibbles" : "quantize");
 }
 hipError_t launch_kv_quantize(const void*, int, int64_t, int, int, int, int8_t*, float*,
-                              hipStream_t) {
-  return record("kv_quantize");
+                              hipStream_t, uint8_t* packed) {
+  return record(packed ? "kv_quantize_packed" : "kv_quantize");
 }
 hipError_t launch_ternary_matmul(const int8_t*, const float*, int64_t, int, const uint8_t*, int64_t,
                                  const float*, int, float*, int32_t* acc, hipStream_t,

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_empty_error(lib):
-    assert lib.bitnet_abi_version() == 3
+    assert lib.bitnet_abi_version() == 4
 
 
 def test_workspace_sizes(lib):
@@ -247,6 +247,32 @@ def test_kv_quantize_empty_is_noop(lib):
     assert lib.bitnet_kv_quantize(None, _lib.BF16, 0, 64, 4, 4, None, None, None) == _lib.OK
 
 
+@pytest.mark.parametrize("args,status", [
+    (dict(bits=8), _lib.ERR_BAD_BITS),        # packing is for 3 and 4 bits
+    (dict(bits=2), _lib.ERR_BAD_BITS),
+    (dict(bits=3, D=40), _lib.ERR_ALIGN),     # 3-bit rows must be whole 32-bit words
+    (dict(bits=4, D=12), _lib.ERR_ALIGN),
+    (dict(bits=4, D=520), _lib.ERR_UNSUPPORTED),
+    (dict(R=10, S=4), _lib.ERR_INVALID_ARG),
+    (dict(bos=None), _lib.ERR_INVALID_ARG),
+    (dict(packed=None), _lib.ERR_INVALID_ARG),
+    (dict(packed=FAKE + 2), _lib.ERR_ALIGN),
+    (dict(bos=FAKE + 4), _lib.ERR_ALIGN),
+    (dict(kv=FAKE + 8), _lib.ERR_ALIGN),
+])
+def test_kv_quantize_packed_validation(lib, args, status):
+    a = dict(kv=FAKE, dt=_lib.BF16, R=16, D=128, S=8, bits=3, packed=FAKE, bos=FAKE, scales=FAKE)
+    a.update(args)
+    assert lib.bitnet_kv_quantize_packed(a["kv"], a["dt"], a["R"], a["D"], a["S"], a["bits"],
+                                         a["packed"], a["bos"], a["scales"], None) == status
+    assert lib.bitnet_last_error() != b""
+
+
+def test_kv_quantize_packed_empty_is_noop(lib):
+    assert lib.bitnet_kv_quantize_packed(None, _lib.BF16, 0, 64, 4, 4, None, None, None,
+                                         None) == _lib.OK
+
+
 def test_backward_workspace_sizes(lib):
     # dx: t^T in bf16 (K*N*2); an fp32 dy adds its two bf16 halves (2*M*N*2)
     assert lib.bitnet_backward_workspace_bytes(128, 256, 192, _lib.BF16, 1, 0) == 256 * 192 * 2
@@ -372,6 +398,7 @@ LAUNCHING_CALLS = {
     "bitnet_quantize_activations_prologue": (FAKE, None, _lib.F32, 2, 64, 1, None, 1e-7, 8, 0,
                                              FAKE, FAKE, None),
     "bitnet_kv_quantize": (FAKE, _lib.BF16, 16, 128, 8, 3, FAKE, FAKE, None),
+    "bitnet_kv_quantize_packed": (FAKE, _lib.BF16, 16, 128, 8, 3, FAKE, FAKE, FAKE, None),
     "bitnet_pack_tl2": (FAKE, 4, 64, FAKE, None),
     "bitnet_hbitlinear_forward_tl2": (FAKE, _lib.BF16, 1, 256, FAKE, 16, FAKE, 8, FAKE, None),
     "bitnet_hbitlinear_backward": (FAKE, _lib.BF16, 128, 192, FAKE, FAKE, 256, FAKE, FAKE, 8, 1,
@@ -460,6 +487,10 @@ def test_other_dispatch(lib):
     assert _calls(lib, lib.bitnet_ternarize_weights, FAKE, 4, 64, FAKE, FAKE, a, 1 << 14,
                   None) == ["absmean_partial", "ternarize_pack"]
     assert _calls(lib, lib.bitnet_ternary_gemm_i32, FAKE, 2, 64, FAKE, 3, FAKE, None) == ["matmul_i32"]
+    assert _calls(lib, lib.bitnet_kv_quantize, FAKE, _lib.BF16, 16, 128, 8, 4, FAKE, FAKE,
+                  None) == ["kv_quantize"]
+    assert _calls(lib, lib.bitnet_kv_quantize_packed, FAKE, _lib.BF16, 16, 128, 8, 4, FAKE, FAKE,
+                  FAKE, None) == ["kv_quantize_packed"]
     # backward with an fp32 dy: dx from split halves and the transform, then dw
     bws = lib.bitnet_backward_workspace_bytes(128, 256, 192, _lib.F32, 1, 1)
     big = ctypes.create_string_buffer(bws + 256)

@@ -72,3 +72,36 @@ def test_kv_quantize_parity_large(B, H, S, D, xdt, bits):
     q, s, p = oracle.kv_quantize(ref_in, bits)
     assert_codes_match(codes.cpu().numpy(), q, p)
     np.testing.assert_allclose(scales.cpu().numpy(), s, rtol=2e-6)
+
+
+@pytest.mark.parametrize("B,H,S,D,xdt,bits", [
+    (1, 2, 5, 64, "bf16", 4),
+    (1, 2, 5, 64, "bf16", 3),
+    (2, 8, 33, 128, "bf16", 3),
+    (1, 4, 7, 96, "fp32", 3),     # G = 16 lanes, three groups of four store
+    (1, 4, 7, 40, "fp32", 4),     # five lanes of a row
+    (1, 1, 1, 32, "bf16", 3),     # only a BOS token: its packed row is zero
+    (3, 2, 4, 512, "bf16", 4),
+    (1, 32, 4096, 128, "bf16", 3),  # the timed cache
+    (1, 33, 4001, 128, "bf16", 4),  # a ragged last workgroup
+])
+def test_kv_quantize_packed_parity(B, H, S, D, xdt, bits):
+    """Packed storage: the bytes are the oracle's packing of the unpacked
+    entry point's codes (same kernel arithmetic), those codes match the
+    oracle's, and the BOS codes and scales are the unpacked call's."""
+    print(f"kv packed case B={B} H={H} S={S} D={D} x={xdt} bits={bits}", flush=True)
+    x_np, kv = _kv(B, H, S, D, xdt, seed=11 + B + H + S + D + bits)
+    packed, bos, scales = bl.kv_quantize_packed(kv, bits)
+    codes, scales_u = bl.kv_quantize(kv, bits)
+    torch.cuda.synchronize()
+    c = codes.cpu().numpy()
+    ref_in = oracle.widen_input(x_np, xdt).reshape(B, H, S, D)
+    q, s, p = oracle.kv_quantize(ref_in, bits)
+    assert_codes_match(c, q, p)
+    np.testing.assert_array_equal(scales.cpu().numpy(), scales_u.cpu().numpy())
+    np.testing.assert_array_equal(bos.cpu().numpy(), c[:, :, 0, :])
+    rest = c.copy()
+    rest[:, :, 0, :] = 0  # BOS rows are zero in the packed array
+    want = oracle.kv_pack(rest.reshape(-1, D), bits).reshape(B, H, S, D * bits // 8)
+    np.testing.assert_array_equal(packed.cpu().numpy(), want)
+    assert packed.numel() * 8 == B * H * S * D * bits
