@@ -235,6 +235,11 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
             res["stream_read_same_bytes_us"] = sr_ms * 1e3
             res["stream_read_same_bytes_GBs"] = u["weight_bytes"] / (sr_ms * 1e-3) / 1e9
             res["matmul_over_stream_read"] = mm_mean / sr_ms
+            # the launch floor: the same read-only kernel over 4 KiB (one
+            # workgroup), timed the same way
+            tiny = torch.zeros((4096,), dtype=torch.uint8, device=dev)
+            res["launch_floor_us"] = _time_steps(torch, lambda i: bl.stream_read(tiny, sink), steps,
+                                                 warmup) * 1e3
             # the same forward on one weight copy, served from the caches
             res["forward_us_warm"] = _time_steps(torch, lambda i: p.forward(bl, 0), steps, warmup) * 1e3
     else:
