@@ -102,8 +102,8 @@ def test_prologue_parity(M, K, N, bits, had, xdt, swiglu, rms, gamma):
 
 def test_prologue_without_parts_matches_plain_forward():
     """No SwiGLU and no RMSNorm: the prologue path computes exactly the plain
-    forward's codes and scales (same kernels with the prologue switched off at
-    run time) and the same output."""
+    forward's codes and scales (a prologue with both parts off runs the plain
+    quantizer) and the same output."""
     case = workloads.make_case(40, 2048, 70, x_dtype="bf16", n_out=20, factor=30.0, seed=9)
     x = _to_dev(case["x"], "bf16")
     Wp, alpha = bl.ternarize_weights(torch.from_numpy(case["W"]).to(DEV))
