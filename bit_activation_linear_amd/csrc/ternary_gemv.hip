@@ -97,17 +97,20 @@ __device__ __forceinline__ void mma_round(const v4i (&av)[4], const uint4 (&p)[C
 // MFMA operand read touches start on distinct banks).
 constexpr int kCodePitch = 272;
 
+__device__ __forceinline__ uint4 as_u4(const v4i v) {
+  return uint4{(unsigned)v.x, (unsigned)v.y, (unsigned)v.z, (unsigned)v.w};
+}
+
 // The wave's share of the product; codes_base is the [M, K] code matrix.
 //
-// Weights: lane (col, grp) loads the packed block 4 sb + grp of its column
-// (the four lanes of a column cover 64 contiguous bytes). Codes: the MFMA
-// wants row col, block 4 sb + grp, k-quarter j from that lane, a pattern that
-// touches 64 separate 16-byte pieces per load instruction; every workgroup
-// streams the whole code matrix, and at that rate the L2 -> CU path serves
-// such scattered loads at well under half the rate of contiguous ones. So
-// the codes are loaded as 4 rows x 256 contiguous bytes per instruction,
-// written to the wave's LDS area and read back in MFMA order (the same wave
-// writes and reads, so no barrier is needed).
+// Codes: the MFMA wants row col, block 4 sb + grp, k-quarter j from lane
+// (col, grp), a pattern that touches 64 separate 16-byte pieces per load
+// instruction; every workgroup streams the whole code matrix, and at that
+// rate the L2 -> CU path serves such scattered loads at well under half the
+// rate of contiguous ones. So the codes are loaded as 4 rows x 256
+// contiguous bytes per instruction, written to the wave's LDS area and read
+// back in MFMA order (the same wave writes and reads, so no barrier is
+// needed).
 //
 // With NIB the codes are nibble codes (K % 256 == 0): a lane loads 16 bytes
 // (32 codes) of token row 8 i + lane / 8, the two loads of a super-block
@@ -115,19 +118,39 @@ constexpr int kCodePitch = 272;
 // a shift per four codes) on their way to LDS; the wave's tile is divided
 // by 16 at the end, exactly.
 //
+// Weights, by single super-blocks: lane (col, grp) loads the packed block
+// 4 sb + grp of its column straight into its MFMA operand, so one load
+// instruction touches 16 rows x 64 bytes, half of 16 cache lines.
+// By pairs of super-blocks (PAIR; nibble codes, K % 512 == 0): a wave owns
+// 128 bytes of each of its 16 rows and loads them as 8 rows x 128 bytes per
+// instruction, whole cache lines (at M = 16, K = 16384, N = 4096 the
+// product takes about 0.7 us less than with half lines). Lane L of
+// instruction h fetches row 8 h + L / 8, 16-byte block (L % 8) ^ (L / 8) ^ h
+// of the 128, and the wave passes them through its own 2 KiB of LDS (in lane
+// order, so an operand read of block b of row r finds it at slot
+// b ^ (r % 8) ^ (r / 8) of that row: 16 lanes, 64 distinct banks) into MFMA
+// order.
+//
 // Every workgroup reads the whole code matrix; workgroup b starts its walk
-// over the super-blocks at super-block b mod nSB, so that the workgroups of an
-// XCD do not all request the same code lines of its L2 at the same moment.
+// over the super-blocks (or pairs) at b mod their count, so that the
+// workgroups of an XCD do not all request the same code lines of its L2 at
+// the same moment.
 //
 // RSG: the codes' row sums are given (u-field operands, see mma_round_u).
-template <int CT, bool NIB, bool RSG>
+template <int CT, bool NIB, bool RSG, bool PAIR>
 __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* codes_base,
-                                             int8_t* stage, v4i (&acc)[CT]) {
+                                             int8_t* stage, v4i* wstage, v4i (&acc)[CT]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int nKB = a.K >> 6, nSB = (nKB + 3) >> 2;
-  const int rounds = (nSB + a.sb_waves - 1) / a.sb_waves;
-  const int rot = (int)(blockIdx.x % (unsigned)nSB);
+  // work units: super-blocks, or pairs of them
+  const int nU = PAIR ? nSB >> 1 : nSB;
+  const int rounds = (nU + a.sb_waves - 1) / a.sb_waves;
+  __builtin_assume(rounds >= 1);  // at least sb_waves units
+  const int rot = (int)(blockIdx.x % (unsigned)nU);
+  // units whose loads a lane issues together (four super-blocks either way)
+  constexpr int kUnitsInFlight = PAIR ? kRoundsInFlight / 2 : kRoundsInFlight;
+  constexpr int kSbPerUnit = PAIR ? 2 : 1;
   v4i a4[CT], a16[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) a4[ct] = a16[ct] = v4i{0, 0, 0, 0};
@@ -141,70 +164,126 @@ __device__ __forceinline__ void wave_product(const GemvArgs& a, const int8_t* co
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
   if (wave >= a.sb_waves) return;
-  for (int r0 = 0; r0 < rounds; r0 += kRoundsInFlight) {
-    uint4 p[kRoundsInFlight][CT];
-    v4i cv[kRoundsInFlight][4];
+
+  // Unconditional loads from clamped addresses; what is out of range is
+  // zeroed with a mask (a branch would force a wait on the load).
+  auto load_codes = [&](const int sbc, const bool live, v4i (&cv)[4]) {
+    const int k = NIB ? sbc * 128 + cbyte : sbc * 256 + cbyte;  // byte in the code row
+    const int rb = NIB ? a.K >> 1 : a.K;                        // code row bytes
+    const bool k_ok = live && k < rb;
+    const int kc = k < rb ? k : rb - 16;
 #pragma unroll
-    for (int u = 0; u < kRoundsInFlight; ++u) {
-      const int sbl = wave + a.sb_waves * (r0 + u);  // place in the walk
-      const bool live = (r0 + u < rounds) && sbl < nSB;
-      const int sbc = live ? (sbl + rot < nSB ? sbl + rot : sbl + rot - nSB) : nSB - 1;
-      const int kb = sbc * 4 + grp;
-      const int kbc = kb < nKB ? kb : nKB - 1;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int n = (blockIdx.x * CT + ct) * 16 + col;
-        const int nc = n < a.N ? n : a.N - 1;
-        p[u][ct] = *reinterpret_cast<const uint4*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
-      }
-      // Unconditional loads from clamped addresses; what is out of range is
-      // zeroed with a mask (a branch would force a wait on the load).
-      const int k = NIB ? sbc * 128 + cbyte : sbc * 256 + cbyte;  // byte in the code row
-      const int rb = NIB ? a.K >> 1 : a.K;                        // code row bytes
-      const bool k_ok = live && k < rb;
-      const int kc = k < rb ? k : rb - 16;
+    for (int i = 0; i < kCodeLoads; ++i) {
+      const int m = kRowsPerLoad * i + crow;
+      const int mc = m < a.M ? m : a.M - 1;
+      const int mask = (k_ok && m < a.M) ? -1 : 0;
+      cv[i] = *reinterpret_cast<const v4i*>(codes_base + (size_t)mc * rb + kc) & mask;
+    }
+  };
+  // One super-block: its codes through LDS into MFMA order, then the MFMAs.
+  auto multiply = [&](const v4i (&cv)[4], const uint4 (&pw)[CT]) {
+    if constexpr (NIB) {
 #pragma unroll
       for (int i = 0; i < kCodeLoads; ++i) {
-        const int m = kRowsPerLoad * i + crow;
-        const int mc = m < a.M ? m : a.M - 1;
-        const int mask = (k_ok && m < a.M) ? -1 : 0;
-        cv[u][i] = *reinterpret_cast<const v4i*>(codes_base + (size_t)mc * rb + kc) & mask;
+        const v4i w = cv[i];
+        const v4i w4 = w << 4;
+        // codes 0-15 and 16-31 of the lane's 32, times 16
+        const v4i c0 = v4i{w.x & (int)0xF0F0F0F0u, w4.x & (int)0xF0F0F0F0u,
+                           w.y & (int)0xF0F0F0F0u, w4.y & (int)0xF0F0F0F0u};
+        const v4i c1 = v4i{w.z & (int)0xF0F0F0F0u, w4.z & (int)0xF0F0F0F0u,
+                           w.w & (int)0xF0F0F0F0u, w4.w & (int)0xF0F0F0F0u};
+        // codes 32 c .. 32 c + 15 of the row at byte 16 c, the next 16 at
+        // 128 + 16 c: eight lanes of a row then write 128 contiguous bytes
+        int8_t* dst = stage + (kRowsPerLoad * i + crow) * kCodePitch + cbyte;
+        *reinterpret_cast<v4i*>(dst) = c0;
+        *reinterpret_cast<v4i*>(dst + 128) = c1;
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kCodeLoads; ++i)
+        *reinterpret_cast<v4i*>(stage + (kRowsPerLoad * i + crow) * kCodePitch + cbyte) = cv[i];
     }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    v4i av[4];
 #pragma unroll
-    for (int u = 0; u < kRoundsInFlight; ++u) {
-      if (r0 + u < rounds) {
-        if constexpr (NIB) {
+    for (int j = 0; j < 4; ++j) {
+      // codes 64 grp + 16 j .. + 15 of row col
+      const int at = NIB ? 128 * (j & 1) + 32 * grp + 16 * (j >> 1) : 64 * grp + 16 * j;
+      av[j] = *reinterpret_cast<const v4i*>(stage + col * kCodePitch + at);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if constexpr (RSG) mma_round_u<CT>(av, pw, acc, a4, a16);
+    else mma_round<CT>(av, pw, acc);
+  };
+
+  // One round: the loads of up to four super-blocks, then their MFMAs.
+  auto round = [&](const int r0) {
+    // (vector-typed, so that the compiler keeps them in registers)
+    v4i p[kUnitsInFlight][CT][kSbPerUnit];
+    v4i cv[kUnitsInFlight][kSbPerUnit][4];
 #pragma unroll
-          for (int i = 0; i < kCodeLoads; ++i) {
-            const v4i w = cv[u][i];
-            const v4i w4 = w << 4;
-            // codes 0-15 and 16-31 of the lane's 32, times 16
-            const v4i c0 = v4i{w.x & (int)0xF0F0F0F0u, w4.x & (int)0xF0F0F0F0u,
-                               w.y & (int)0xF0F0F0F0u, w4.y & (int)0xF0F0F0F0u};
-            const v4i c1 = v4i{w.z & (int)0xF0F0F0F0u, w4.z & (int)0xF0F0F0F0u,
-                               w.w & (int)0xF0F0F0F0u, w4.w & (int)0xF0F0F0F0u};
-            int8_t* dst = stage + (kRowsPerLoad * i + crow) * kCodePitch + 2 * cbyte;
-            *reinterpret_cast<v4i*>(dst) = c0;
-            *reinterpret_cast<v4i*>(dst + 16) = c1;
+    for (int u = 0; u < kUnitsInFlight; ++u) {
+      const int ul = wave + a.sb_waves * (r0 + u);  // place in the walk
+      const bool live = (r0 + u < rounds) && ul < nU;
+      const int uc = live ? (ul + rot < nU ? ul + rot : ul + rot - nU) : nU - 1;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        if constexpr (PAIR) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int n = (blockIdx.x * CT + ct) * 16 + 8 * h + (lane >> 3);
+            const int nc = n < a.N ? n : a.N - 1;
+            const int blk = (lane & 7) ^ (lane >> 3) ^ h;
+            p[u][ct][h] = *reinterpret_cast<const v4i*>(a.Wp + (size_t)nc * row_bytes +
+                                                        (size_t)uc * 128 + 16 * blk);
           }
         } else {
-#pragma unroll
-          for (int i = 0; i < kCodeLoads; ++i)
-            *reinterpret_cast<v4i*>(stage + (kRowsPerLoad * i + crow) * kCodePitch + cbyte) =
-                cv[u][i];
+          const int kb = uc * 4 + grp;
+          const int kbc = kb < nKB ? kb : nKB - 1;
+          const int n = (blockIdx.x * CT + ct) * 16 + col;
+          const int nc = n < a.N ? n : a.N - 1;
+          p[u][ct][0] =
+              *reinterpret_cast<const v4i*>(a.Wp + (size_t)nc * row_bytes + (size_t)kbc * 16);
         }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        v4i av[4];
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          av[j] = *reinterpret_cast<const v4i*>(stage + col * kCodePitch + 64 * grp + 16 * j);
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        if constexpr (RSG) mma_round_u<CT>(av, p[u], acc, a4, a16);
-        else mma_round<CT>(av, p[u], acc);
+      for (int s = 0; s < kSbPerUnit; ++s) load_codes(kSbPerUnit * uc + s, live, cv[u][s]);
+    }
+    // every load of the round is issued before the first use of one (the
+    // scheduler would otherwise pull the weights' LDS writes up between them)
+    if constexpr (PAIR) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kUnitsInFlight; ++u) {
+      if (r0 + u < rounds) {
+        if constexpr (PAIR) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) wstage[(ct * 2 + h) * 64 + lane] = p[u][ct][h];
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          const int r8 = col & 7, hi = col >> 3;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            uint4 pw[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+              pw[ct] = as_u4(wstage[(ct * 2 + hi) * 64 + r8 * 8 + ((4 * s + grp) ^ r8 ^ hi)]);
+            multiply(cv[u][s], pw);
+          }
+        } else {
+          uint4 pw[CT];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) pw[ct] = as_u4(p[u][ct][0]);
+          multiply(cv[u][0], pw);
+        }
       }
     }
-  }
+  };
+  // The first round is not inside the loop: at a loop header the compiler waits for every
+  // load in flight (a later round's unused loads may target the registers it reuses), which
+  // on entry would hold the weight stream back until alpha, the scales and the row sums land.
+  round(0);
+  for (int r0 = kUnitsInFlight; r0 < rounds; r0 += kUnitsInFlight) round(r0);
   if constexpr (RSG) {
     // q . u over the three scales (exact: a4 holds multiples of 4, a16 of 16)
 #pragma unroll
@@ -250,13 +329,23 @@ __device__ __forceinline__ void gemv_finish(const GemvArgs& a, const v4i (&acc)[
   }
 }
 
-template <int CT, bool OUT_I32, bool NIB, bool RSG>
+// LDS of the product per wave: its tile for the final sum, its code staging
+// area and, with PAIR, its weight staging area.
+template <int CT, bool PAIR>
+constexpr size_t gemv_lds_per_wave() {
+  return (size_t)CT * 1024 + 16 * kCodePitch + (PAIR ? (size_t)CT * 2048 : 0);
+}
+
+template <int CT, bool OUT_I32, bool NIB, bool RSG, bool PAIR>
 __global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a, const int32_t* rowsum) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6;
   v4i* red = reinterpret_cast<v4i*>(smem);  // [nw][CT][64]
   int8_t* stage = reinterpret_cast<int8_t*>(smem + (size_t)nw * CT * 1024) +
-                  (size_t)(threadIdx.x >> 6) * 16 * kCodePitch;
+                  (size_t)wave * 16 * kCodePitch;
+  v4i* wstage = reinterpret_cast<v4i*>(smem + (size_t)nw * (CT * 1024 + 16 * kCodePitch) +
+                                       (size_t)wave * CT * 2048);
   // Scalars, alpha and the finishing lanes' row scales are fetched before
   // the weight stream: a small load issued behind it waits about a
   // microsecond.
@@ -276,7 +365,7 @@ __global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a, const in
     }
   }
   v4i acc[CT];
-  wave_product<CT, NIB, RSG>(a, a.codes, stage, acc);
+  wave_product<CT, NIB, RSG, PAIR>(a, a.codes, stage, wstage, acc);
   gemv_finish<CT, OUT_I32>(a, acc, red, s_row, rs, nw, alpha);
 }
 
@@ -752,8 +841,23 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
 template <int CT, bool OUT_I32, bool NIB, bool RSG>
 hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, const int32_t* rowsum,
                           hipStream_t stream) {
-  const size_t lds = (size_t)(p.threads / 64) * (CT * 1024 + 16 * kCodePitch);
-  auto kern = ternary_gemv_kernel<CT, OUT_I32, NIB, RSG>;
+  // Whole-line weight loads by pairs of super-blocks when every pair is
+  // whole (K % 512 == 0) and there are enough pairs to give every wave one;
+  // on nibble codes only (int8 codes take twice the registers, and the pair
+  // layout would spill them).
+  if constexpr (NIB) {
+    const int nSB = ((a.K >> 6) + 3) >> 2;
+    if (a.K % 512 == 0 && nSB / 2 >= p.sb_waves) {
+      const size_t lds = (size_t)(p.threads / 64) * gemv_lds_per_wave<CT, true>();
+      auto kern = ternary_gemv_kernel<CT, OUT_I32, NIB, RSG, true>;
+      hipError_t e = ensure_lds(kern, lds);
+      if (e != hipSuccess) return e;
+      kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a, rowsum);
+      return hipGetLastError();
+    }
+  }
+  const size_t lds = (size_t)(p.threads / 64) * gemv_lds_per_wave<CT, false>();
+  auto kern = ternary_gemv_kernel<CT, OUT_I32, NIB, RSG, false>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a, rowsum);
