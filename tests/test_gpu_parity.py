@@ -128,6 +128,9 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     (1, 4096, 50, 4, 0, "fp32"),       # one-wave kernel (single token), sixteen super-blocks
     (1, 1344, 77, 8, 0, "bf16"),       # one-wave kernel, 21 blocks: a partial last super-block
     (3, 1344, 40, 8, 0, "bf16"),       # multi-wave fused kernel, partial last super-block
+    (4, 32768, 70, 4, 1, "bf16"),      # nibble codes by pairs of super-blocks, two rounds per wave
+    (16, 24576, 33, 4, 0, "bf16"),     # pairs, three per wave: a second round half live
+    (7, 9728, 45, 4, 0, "fp32"),       # pairs, 19 of them over 16 waves
 ])
 def test_parity_decode_shapes(M, K, N, bits, had, xdt):
     _run_case(M, K, N, bits, had, xdt, seed=M * 7 + K + N, n_out=max(1, K // 100), factor=30.0)
