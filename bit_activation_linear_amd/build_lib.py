@@ -37,6 +37,11 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}",
 ]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source extras. The decode kernels take their leading arguments in SGPRs
+# that the command processor fills before the wave starts (kernel-argument
+# preloading; the code keeps a prologue that loads them for firmware
+# without it).
+SOURCE_FLAGS = {"ternary_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _hipcc() -> str:
@@ -50,7 +55,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *COMMON_FLAGS]
     if src.endswith(".hip"):
-        cmd += ["-x", "hip", *DEVICE_FLAGS]
+        cmd += ["-x", "hip", *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, [])]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:

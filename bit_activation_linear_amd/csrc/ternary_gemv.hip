@@ -689,8 +689,8 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue
 // DPP reduction and 1/rms enters only the scale and the code multiplier, as
 // in the other quantizer kernels.
 template <typename XT, int BITS, int NSB, bool RMS, bool FULL>
-__global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a, const float* gamma,
-                                                         float norm_eps) {
+__device__ __forceinline__ void wave_decode(const GemvArgs& a, const float* gamma,
+                                            float norm_eps) {
   // [sb][256] codes, then 64 zero bytes that the lanes feeding dead MFMA rows
   // (and blocks past K) read instead of masking their operands
   __shared__ __attribute__((aligned(16))) int8_t qw[NSB * 256 + 64];
@@ -846,6 +846,33 @@ __global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a, const float
   if (grp == 0 && n < a.N) a.y[n] = (float)dot * dequant_factor(alpha, st, a.c);
 }
 
+// The kernel without RMSNorm takes the argument block (loaded by the wave);
+// the one with RMSNorm takes scalar arguments, which this file is built to
+// have the command processor preload into SGPRs before the wave starts.
+// Measured at M = 1, K = 2560, N = 6912: preloading takes the RMSNorm forward
+// from 4.00 to 3.66 us but the whole-super-block forward without it from
+// 3.45 to 3.68 us (its waves live shorter, the launch period grows).
+template <typename XT, int BITS, int NSB, bool FULL>
+__global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
+  wave_decode<XT, BITS, NSB, false, FULL>(a, nullptr, 0.0f);
+}
+
+template <typename XT, int BITS, int NSB, bool FULL>
+__global__ __launch_bounds__(64) void wave_decode_rms_kernel(const void* x_in, const uint8_t* Wp,
+                                                             const float* alpha_p, float* y,
+                                                             int K, int N, float c,
+                                                             const float* gamma, float norm_eps) {
+  GemvArgs a{};
+  a.x = x_in;
+  a.Wp = Wp;
+  a.alpha = alpha_p;
+  a.y = y;
+  a.K = K;
+  a.N = N;
+  a.c = c;
+  wave_decode<XT, BITS, NSB, true, FULL>(a, gamma, norm_eps);
+}
+
 template <typename Kern>
 hipError_t ensure_lds(Kern kern, size_t bytes) {
   if (bytes <= 48 * 1024) return hipSuccess;
@@ -898,16 +925,16 @@ template <typename XT, int BITS, int NSB, bool FULL>
 void launch_wave_full(const GemvArgs& a, const Prologue* pro, hipStream_t stream) {
   const dim3 grid((unsigned)((a.N + 15) / 16));
   if (pro && pro->rms)
-    wave_decode_kernel<XT, BITS, NSB, true, FULL><<<grid, dim3(64), 0, stream>>>(a, pro->gamma,
-                                                                                 pro->norm_eps);
+    wave_decode_rms_kernel<XT, BITS, NSB, FULL><<<grid, dim3(64), 0, stream>>>(
+        a.x, a.Wp, a.alpha, a.y, a.K, a.N, a.c, pro->gamma, pro->norm_eps);
   else
-    wave_decode_kernel<XT, BITS, NSB, false, FULL><<<grid, dim3(64), 0, stream>>>(a, nullptr, 0.0f);
+    wave_decode_kernel<XT, BITS, NSB, FULL><<<grid, dim3(64), 0, stream>>>(a);
 }
 
 // FULL: every super-block is whole (K = 256 NSB), so the kernel drops its
 // range checks (703 -> 596 VALU per wave at K = 2560: 3.49 -> 3.45 us).
-// With the RMSNorm prologue the same variant measured slower (4.00 ->
-// 4.27 us), so that one keeps its checks.
+// With the RMSNorm prologue the same variant measured slower (3.67 ->
+// 3.92 us), so that one keeps its checks.
 template <typename XT, int BITS, int NSB>
 hipError_t launch_wave_nsb(const GemvArgs& a, const Prologue* pro, hipStream_t stream) {
   if (a.K == 256 * NSB && !(pro && pro->rms))
