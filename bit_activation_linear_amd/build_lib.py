@@ -37,11 +37,13 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}",
 ]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source extras. The decode kernels take their leading arguments in SGPRs
-# that the command processor fills before the wave starts (kernel-argument
-# preloading; the code keeps a prologue that loads them for firmware
-# without it).
-SOURCE_FLAGS = {"ternary_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+# Per-source extras. The single-token decode kernels take their first two
+# arguments (the activation and weight addresses) in SGPRs that the command
+# processor fills before the wave starts (kernel-argument preloading, counted
+# in arguments; the code keeps a prologue that loads them for firmware
+# without the feature). Kernels whose first argument is a struct are not
+# affected.
+SOURCE_FLAGS = {"ternary_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
 
 
 def _hipcc() -> str:

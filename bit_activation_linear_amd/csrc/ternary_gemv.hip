@@ -846,14 +846,26 @@ __device__ __forceinline__ void wave_decode(const GemvArgs& a, const float* gamm
   if (grp == 0 && n < a.N) a.y[n] = (float)dot * dequant_factor(alpha, st, a.c);
 }
 
-// The kernel without RMSNorm takes the argument block (loaded by the wave);
-// the one with RMSNorm takes scalar arguments, which this file is built to
-// have the command processor preload into SGPRs before the wave starts.
-// Measured at M = 1, K = 2560, N = 6912: preloading takes the RMSNorm forward
-// from 4.00 to 3.66 us but the whole-super-block forward without it from
-// 3.45 to 3.68 us (its waves live shorter, the launch period grows).
+// Scalar kernel arguments, the first two of which (the x and weight
+// addresses) this file is built to have the command processor preload into
+// SGPRs before the wave starts, so that the x and weight loads need not wait
+// for a load of the argument block. Measured at M = 1, K = 2560, N = 6912
+// (cold weights, 200 launches per replay): the forward without RMSNorm takes
+// 3.45 us reading the argument block and about 3.1-3.2 us with the first two
+// to six arguments preloaded (3.67 us with all seven); with RMSNorm 4.00 ->
+// 3.67 us.
 template <typename XT, int BITS, int NSB, bool FULL>
-__global__ __launch_bounds__(64) void wave_decode_kernel(GemvArgs a) {
+__global__ __launch_bounds__(64) void wave_decode_kernel(const void* x_in, const uint8_t* Wp,
+                                                         const float* alpha_p, float* y, int K,
+                                                         int N, float c) {
+  GemvArgs a{};
+  a.x = x_in;
+  a.Wp = Wp;
+  a.alpha = alpha_p;
+  a.y = y;
+  a.K = K;
+  a.N = N;
+  a.c = c;
   wave_decode<XT, BITS, NSB, false, FULL>(a, nullptr, 0.0f);
 }
 
@@ -928,7 +940,8 @@ void launch_wave_full(const GemvArgs& a, const Prologue* pro, hipStream_t stream
     wave_decode_rms_kernel<XT, BITS, NSB, FULL><<<grid, dim3(64), 0, stream>>>(
         a.x, a.Wp, a.alpha, a.y, a.K, a.N, a.c, pro->gamma, pro->norm_eps);
   else
-    wave_decode_kernel<XT, BITS, NSB, FULL><<<grid, dim3(64), 0, stream>>>(a);
+    wave_decode_kernel<XT, BITS, NSB, FULL><<<grid, dim3(64), 0, stream>>>(a.x, a.Wp, a.alpha, a.y,
+                                                                        a.K, a.N, a.c);
 }
 
 // FULL: every super-block is whole (K = 256 NSB), so the kernel drops its
