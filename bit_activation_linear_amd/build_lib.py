@@ -37,13 +37,18 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}",
 ]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source extras. The single-token decode kernels take their first two
-# arguments (the activation and weight addresses) in SGPRs that the command
-# processor fills before the wave starts (kernel-argument preloading, counted
-# in arguments; the code keeps a prologue that loads them for firmware
-# without the feature). Kernels whose first argument is a struct are not
-# affected.
-SOURCE_FLAGS = {"ternary_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
+# Per-source extras. Latency-bound kernels take their leading arguments (the
+# addresses their first loads need) in SGPRs that the command processor fills
+# before the wave starts (kernel-argument preloading, counted in arguments;
+# the code keeps a prologue that loads them for firmware without the
+# feature), instead of waiting for a load of the argument block: the
+# single-token decode kernels their activation and weight addresses, the
+# transform-and-quantize kernels their input address. Kernels whose first
+# argument is a struct are not affected.
+SOURCE_FLAGS = {
+    "ternary_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"],
+    "fwht_quant.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=1"],
+}
 
 
 def _hipcc() -> str:

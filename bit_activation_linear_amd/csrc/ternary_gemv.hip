@@ -336,8 +336,24 @@ constexpr size_t gemv_lds_per_wave() {
   return (size_t)CT * 1024 + 16 * kCodePitch + (PAIR ? (size_t)CT * 2048 : 0);
 }
 
+// Scalar arguments: the first two (the weight and code addresses) are
+// preloaded into SGPRs (see the single-token kernels below).
 template <int CT, bool OUT_I32, bool NIB, bool RSG, bool PAIR>
-__global__ __launch_bounds__(1024) void ternary_gemv_kernel(GemvArgs a, const int32_t* rowsum) {
+__global__ __launch_bounds__(1024) void ternary_gemv_kernel(
+    const uint8_t* Wp, const int8_t* codes, const float* scales, const float* alpha_p, float* y,
+    int32_t* acc_out, const int32_t* rowsum, int M, int K, int N, int sb_waves, float c) {
+  GemvArgs a{};
+  a.Wp = Wp;
+  a.codes = codes;
+  a.scales = scales;
+  a.alpha = alpha_p;
+  a.y = y;
+  a.acc_out = acc_out;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.sb_waves = sb_waves;
+  a.c = c;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6;
@@ -906,7 +922,8 @@ hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, const int32_t* r
       auto kern = ternary_gemv_kernel<CT, OUT_I32, NIB, RSG, true>;
       hipError_t e = ensure_lds(kern, lds);
       if (e != hipSuccess) return e;
-      kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a, rowsum);
+      kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(
+        a.Wp, a.codes, a.scales, a.alpha, a.y, a.acc_out, rowsum, a.M, a.K, a.N, a.sb_waves, a.c);
       return hipGetLastError();
     }
   }
@@ -914,7 +931,8 @@ hipError_t launch_gemv_ct(const GemvPlan& p, const GemvArgs& a, const int32_t* r
   auto kern = ternary_gemv_kernel<CT, OUT_I32, NIB, RSG, false>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(a, rowsum);
+  kern<<<dim3((unsigned)p.col_groups), dim3(p.threads), lds, stream>>>(
+        a.Wp, a.codes, a.scales, a.alpha, a.y, a.acc_out, rowsum, a.M, a.K, a.N, a.sb_waves, a.c);
   return hipGetLastError();
 }
 
