@@ -42,12 +42,17 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # before the wave starts (kernel-argument preloading, counted in arguments;
 # the code keeps a prologue that loads them for firmware without the
 # feature), instead of waiting for a load of the argument block: the
-# single-token decode kernels their activation and weight addresses, the
-# transform-and-quantize kernels their input address. Kernels whose first
-# argument is a struct are not affected.
+# single-token decode kernels (2-bit and TL2) and the small-batch decode
+# kernels their activation (or code) and weight addresses, the
+# transform-and-quantize kernels and the KV-cache quantizer their input
+# address. Kernels whose first argument is a struct are not affected.
 SOURCE_FLAGS = {
     "ternary_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"],
     "fwht_quant.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=1"],
+    "tl2.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"],
+    "kv_quant.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=1"],
+    # the read-only ceiling kernel gets the same start as the kernels it is a ceiling for
+    "measure.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=1"],
 }
 
 

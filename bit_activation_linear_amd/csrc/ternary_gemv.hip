@@ -411,7 +411,20 @@ __device__ __forceinline__ void load4(const uint16_t* x, size_t i, float (&v)[4]
 // further barrier), so little work separates the arrival of the data from
 // the product.
 template <typename XT, int BITS, int MG, int CT, int SBW, bool PRO, bool HAD>
-__global__ __launch_bounds__(1024) void fused_decode_kernel(GemvArgs a, Prologue pro) {
+__global__ __launch_bounds__(1024) void fused_decode_kernel(
+    const void* x_in, const uint8_t* Wp, const float* alpha_p, float* y, int M, int K, int N,
+    float c, const void* up, const float* gamma, float norm_eps, int rms) {
+  // scalar arguments, the x and weight addresses preloaded into SGPRs
+  GemvArgs a{};
+  a.x = x_in;
+  a.Wp = Wp;
+  a.alpha = alpha_p;
+  a.y = y;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.c = c;
+  const Prologue pro{up, gamma, norm_eps, rms};
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // The scalars the kernel needs (kernel arguments and alpha) are fetched
   // before the weight stream goes out, and pinned there: a small load issued
@@ -947,7 +960,8 @@ hipError_t launch_fused_ct(const GemvArgs& a, const Prologue& pro, hipStream_t s
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   const unsigned groups = (unsigned)((a.N + 16 * CT - 1) / (16 * CT));
-  kern<<<dim3(groups), dim3(64 * nw), lds, stream>>>(a, pro);
+  kern<<<dim3(groups), dim3(64 * nw), lds, stream>>>(a.x, a.Wp, a.alpha, a.y, a.M, a.K, a.N, a.c,
+                                                    pro.up, pro.gamma, pro.norm_eps, pro.rms);
   return hipGetLastError();
 }
 
