@@ -201,7 +201,7 @@ constexpr H64Operands make_h64_operands() {
 }
 __constant__ H64Operands kH64 = make_h64_operands();
 
-template <int BITS, int L>
+template <int BITS, int L, bool F8>
 __global__ __launch_bounds__(64 << (L - 11)) void fwht_mfma_quant_kernel(
     const uint16_t* __restrict__ x, int8_t* __restrict__ codes, float* __restrict__ scales,
     int32_t* __restrict__ rowsum, bool nib, int M) {
@@ -213,6 +213,7 @@ __global__ __launch_bounds__(64 << (L - 11)) void fwht_mfma_quant_kernel(
   constexpr int G = 1 << (L - 10);  // a group: the elements that differ in bits 8, 11 .. L-1
   constexpr int Q = E / G;          // groups per thread
   static_assert(L >= 11 && L <= 15, "2048 <= K <= 32768");
+  static_assert(!F8 || BITS == 4, "fp8 pairs hold 4-bit codes");
   extern __shared__ float lds[];
   float* red = lds + RowLds<L, LT>::kRowFloats;
   int* ired = reinterpret_cast<int*>(red + RowLds<L, LT>::kRedFloats);
@@ -306,22 +307,53 @@ __global__ __launch_bounds__(64 << (L - 11)) void fwht_mfma_quant_kernel(
     const float sc = stat * norm + kEps;
     const float mult = (QConst<BITS>::c * norm) / sc;
     if (t == 0) scales[row] = sc;
-    int8_t* crow = codes + (size_t)row * (nib ? K / 2 : K);
-    const int e0 = t * E;
-    const int pe0 = pad_idx(e0);  // e0 is a multiple of 32: the padding of e0 + i is e0's
+    int8_t* crow = codes + (size_t)row * (nib && !F8 ? K / 2 : K);
     int qs = 0;
+    if constexpr (F8) {
+      // fp8 pairs: thread t writes the row's bytes 32 t .. 32 t + 31, those of
+      // lane group g = t % 2 of 64-weight block t / 2, whose byte 2 i + h is
+      // the code of the block's weight 16 g + i + 32 h (i < 16, h < 2). The
+      // codes clip(rint(v * mult)) are exact in fp8 E4M3 and in the float sum
+      // that gives the row sum. Runs of 16 elements never cross a padding step.
+      const int k0 = 64 * (t >> 1) + 16 * (t & 1);
+      const int q0 = pad_idx(k0), q1 = pad_idx(k0 + 32);
+      float fs = 0.0f;
+      unsigned wd[8];
 #pragma unroll
-    for (int c = 0; c < E; c += 8) {
-      float z[8];
+      for (int j = 0; j < 8; ++j) {
+        // word j: weights i = 2 j and 2 j + 1 of the two runs
+        const float z[4] = {lds[q0 + 2 * j], lds[q1 + 2 * j], lds[q0 + 2 * j + 1],
+                            lds[q1 + 2 * j + 1]};
+        float r[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) z[i] = lds[pe0 + c + i];
-      const uint2 wq = quant_pack8<BITS>(z, mult);
-      if (nib)
-        *reinterpret_cast<unsigned*>(crow + ((e0 + c) >> 1)) = nibble_word(wq);
-      else
-        *reinterpret_cast<uint2*>(crow + e0 + c) = wq;
-      qs = __builtin_amdgcn_sdot4((int)wq.y, 0x01010101,
-                                  __builtin_amdgcn_sdot4((int)wq.x, 0x01010101, qs, false), false);
+        for (int e = 0; e < 4; ++e) {
+          r[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(z[e] * mult), QConst<BITS>::lo,
+                                         QConst<BITS>::hi);
+          fs += r[e];
+        }
+        const int lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+        wd[j] = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], lo2, true);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(crow + 32 * t);
+      dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+      qs = (int)fs;
+    } else {
+      const int e0 = t * E;
+      const int pe0 = pad_idx(e0);  // e0 is a multiple of 32: the padding of e0 + i is e0's
+#pragma unroll
+      for (int c = 0; c < E; c += 8) {
+        float z[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[i] = lds[pe0 + c + i];
+        const uint2 wq = quant_pack8<BITS>(z, mult);
+        if (nib)
+          *reinterpret_cast<unsigned*>(crow + ((e0 + c) >> 1)) = nibble_word(wq);
+        else
+          *reinterpret_cast<uint2*>(crow + e0 + c) = wq;
+        qs = __builtin_amdgcn_sdot4((int)wq.y, 0x01010101,
+                                    __builtin_amdgcn_sdot4((int)wq.x, 0x01010101, qs, false), false);
+      }
     }
     if (rowsum) {
       const int total = block_isum<T>(qs, ired);
@@ -338,10 +370,11 @@ constexpr int64_t kCus = 256;
 
 template <int BITS, int L>
 hipError_t launch_fwht_mfma(const void* x, int64_t M, int8_t* codes, float* scales,
-                            hipStream_t stream, int32_t* rowsum, bool nib) {
+                            hipStream_t stream, int32_t* rowsum, bool nib, bool f8) {
   constexpr int LT = L - 5;
   const size_t lds = RowLds<L, LT>::kBytes;
-  auto kern = fwht_mfma_quant_kernel<BITS, L>;
+  if (f8 && BITS != 4) return hipErrorInvalidValue;
+  auto kern = f8 ? fwht_mfma_quant_kernel<BITS, L, BITS == 4> : fwht_mfma_quant_kernel<BITS, L, false>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   // as many workgroups as fit on the chip at once (LDS bounds them), each
@@ -372,10 +405,11 @@ constexpr int fwht_lt_few(int L) {
 template <typename XT, int BITS, int L, bool PRO>
 hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales,
                          const Prologue& pro, hipStream_t stream, float* fout = nullptr,
-                         int32_t* rowsum = nullptr, bool nib = false) {
+                         int32_t* rowsum = nullptr, bool nib = false, bool f8 = false) {
   // bf16 rows of 2048 or more elements take the matrix cores for index bits 0-5
   if constexpr (std::is_same<XT, uint16_t>::value && BITS != 0 && !PRO && L >= 11)
-    return launch_fwht_mfma<BITS, L>(x, M, codes, scales, stream, rowsum, nib);
+    return launch_fwht_mfma<BITS, L>(x, M, codes, scales, stream, rowsum, nib, f8);
+  if (f8) return hipErrorInvalidValue;  // fp8 pairs come from the matrix-core kernel only
   constexpr int LT_BATCH = fwht_lt_batch(L);
   constexpr int LT_FEW = fwht_lt_few(L);
   if (M <= 64 && LT_FEW != LT_BATCH)
@@ -392,18 +426,19 @@ hipError_t launch_fwht_f32_l(const float* x, int64_t M, float* out, hipStream_t 
 
 template <typename XT, int BITS, bool PRO>
 hipError_t launch_had(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                      const Prologue& pro, hipStream_t stream, int32_t* rowsum, bool nib) {
+                      const Prologue& pro, hipStream_t stream, int32_t* rowsum, bool nib,
+                      bool f8) {
   switch (K) {
-    case 1 << 6: return launch_fwht_l<XT, BITS, 6, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
-    case 1 << 7: return launch_fwht_l<XT, BITS, 7, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
-    case 1 << 8: return launch_fwht_l<XT, BITS, 8, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
-    case 1 << 9: return launch_fwht_l<XT, BITS, 9, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
-    case 1 << 10: return launch_fwht_l<XT, BITS, 10, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
-    case 1 << 11: return launch_fwht_l<XT, BITS, 11, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
-    case 1 << 12: return launch_fwht_l<XT, BITS, 12, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
-    case 1 << 13: return launch_fwht_l<XT, BITS, 13, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
-    case 1 << 14: return launch_fwht_l<XT, BITS, 14, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
-    case 1 << 15: return launch_fwht_l<XT, BITS, 15, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib);
+    case 1 << 6: return launch_fwht_l<XT, BITS, 6, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
+    case 1 << 7: return launch_fwht_l<XT, BITS, 7, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
+    case 1 << 8: return launch_fwht_l<XT, BITS, 8, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
+    case 1 << 9: return launch_fwht_l<XT, BITS, 9, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
+    case 1 << 10: return launch_fwht_l<XT, BITS, 10, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
+    case 1 << 11: return launch_fwht_l<XT, BITS, 11, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
+    case 1 << 12: return launch_fwht_l<XT, BITS, 12, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
+    case 1 << 13: return launch_fwht_l<XT, BITS, 13, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
+    case 1 << 14: return launch_fwht_l<XT, BITS, 14, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
+    case 1 << 15: return launch_fwht_l<XT, BITS, 15, PRO>(x, M, codes, scales, pro, stream, nullptr, rowsum, nib, f8);
     default: return hipErrorInvalidValue;
   }
 }
@@ -430,11 +465,13 @@ hipError_t launch_rows(const void* x, int64_t M, int K, int8_t* codes, float* sc
 template <typename XT, bool PRO>
 hipError_t launch_dtype(const void* x, int64_t M, int K, int bits, int hadamard, int8_t* codes,
                         float* scales, const Prologue& pro, hipStream_t stream, int32_t* rowsum,
-                        bool nib) {
+                        bool nib, bool f8) {
   if (hadamard) {
-    return bits == 8 ? launch_had<XT, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum, false)
-                     : launch_had<XT, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
+    return bits == 8
+               ? launch_had<XT, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum, false, f8)
+               : launch_had<XT, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib, f8);
   }
+  if (f8) return hipErrorInvalidValue;
   return bits == 8 ? launch_rows<XT, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum, false)
                    : launch_rows<XT, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
 }
@@ -460,18 +497,19 @@ hipError_t launch_fwht_f32(const float* x, int64_t M, int K, float* out, hipStre
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
                            int8_t* codes, float* scales, hipStream_t stream, const Prologue* pro,
-                           int32_t* rowsum, bool nibbles) {
+                           int32_t* rowsum, bool nibbles, bool fp8_pairs) {
   if (nibbles && (bits != 4 || K % 8 != 0)) return hipErrorInvalidValue;
+  if (fp8_pairs && (nibbles || bits != 4 || x_dtype != 1 || !hadamard)) return hipErrorInvalidValue;
   const Prologue none{nullptr, nullptr, 0.0f, 0};
   if (pro && !pro->up && !pro->rms) pro = nullptr;  // nothing to apply: the plain quantizer
   if (pro) {
     if (x_dtype == 1)
-      return launch_dtype<uint16_t, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum, nibbles);
-    return launch_dtype<float, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum, nibbles);
+      return launch_dtype<uint16_t, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum, nibbles, fp8_pairs);
+    return launch_dtype<float, true>(x, M, K, bits, hadamard, codes, scales, *pro, stream, rowsum, nibbles, fp8_pairs);
   }
   if (x_dtype == 1)
-    return launch_dtype<uint16_t, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum, nibbles);
-  return launch_dtype<float, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum, nibbles);
+    return launch_dtype<uint16_t, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum, nibbles, fp8_pairs);
+  return launch_dtype<float, false>(x, M, K, bits, hadamard, codes, scales, none, stream, rowsum, nibbles, fp8_pairs);
 }
 
 }  // namespace bitnet

@@ -97,15 +97,32 @@ __device__ __forceinline__ float silu(float g) {
 // four: two operations per four codes, half the bytes of int8 codes.
 constexpr int kNibbleKMultiple = 256;  // the decode product reads nibble codes when K is a multiple
 
+// FP8 pairs: a code form of the forward's workspace that only the prefill
+// product reads. The 4-bit codes of a row are stored one byte each as fp8
+// E4M3 (exact for integers up to 16), in the order of the fp4 weight fields
+// the product unpacks: byte 32 g + 2 i + h of each 64-weight block holds
+// the code of the block's weight 16 g + i + 32 h (g, h < 2, i < 16). The
+// matrix-core transform kernel writes them (bf16 rows, K >= 2048, with the
+// transform, no prologue), and the 128 x 128-tile product reads them, the
+// one that runs when there are fewer than 1024 tiles of 256 x 256.
+inline bool fp8_pair_gemm_ok(int64_t M, int64_t K, int64_t N, int bits) {
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  return bits == 4 && M > kDecodeMaxM && K % 64 == 0 && big_tiles < 1024;
+}
+inline bool fp8_pair_quant_ok(int64_t K, int bits, int hadamard, int x_dtype, bool prologue) {
+  return bits == 4 && hadamard && x_dtype == 1 && !prologue && K >= 2048 && K <= 32768;
+}
+
 // Fused (optional) prologue + Walsh-Hadamard transform + per-token
 // quantization. x_dtype: 0 = fp32, 1 = bf16 bit patterns. pro may be null.
 // rowsum, when not null, receives each token's code sum (int32 [M]), which
 // the prefill product then needs not compute. nibbles (bits = 4 only):
-// write nibble codes instead of int8 codes.
+// write nibble codes instead of int8 codes; fp8_pairs: write fp8 pairs
+// (fp8_pair_quant_ok only).
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
                            int8_t* codes, float* scales, hipStream_t stream,
                            const Prologue* pro = nullptr, int32_t* rowsum = nullptr,
-                           bool nibbles = false);
+                           bool nibbles = false, bool fp8_pairs = false);
 
 // Low-bit KV cache: rows of D elements, row r being token r % S of its head;
 // token 0 int8 absmax, the others bits = 3, 4 or 8. With packed (bits 3 or 4
@@ -118,11 +135,13 @@ hipError_t launch_kv_quantize(const void* kv, int x_dtype, int64_t R, int D, int
 // Ternary product from codes. Exactly one of y (dequantized; needs scales,
 // alpha, bits) or acc (raw int32) is non-null. rowsum (optional, with y):
 // the codes' per-token sums from launch_quantize. nibbles: the codes are
-// nibble codes (M <= kDecodeMaxM and K % kNibbleKMultiple == 0 only).
+// nibble codes (M <= kDecodeMaxM and K % kNibbleKMultiple == 0 only);
+// fp8_pairs: the codes are fp8 pairs (fp8_pair_gemm_ok, with y and rowsum).
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
                                  const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
                                  float* y, int32_t* acc, hipStream_t stream,
-                                 const int32_t* rowsum = nullptr, bool nibbles = false);
+                                 const int32_t* rowsum = nullptr, bool nibbles = false,
+                                 bool fp8_pairs = false);
 
 // The two product shapes behind launch_ternary_matmul.
 hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int K,
@@ -131,7 +150,8 @@ hipError_t launch_gemv(const int8_t* codes, const float* scales, int64_t M, int 
                        const int32_t* rowsum = nullptr);
 hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, hipStream_t stream, const int32_t* rowsum = nullptr);
+                       int32_t* acc, hipStream_t stream, const int32_t* rowsum = nullptr,
+                       bool fp8_pairs = false);
 
 // Decode forward with the quantization fused in (plan.fused must hold).
 hipError_t launch_fused_decode(const void* x, int x_dtype, int64_t M, int K,

@@ -58,6 +58,24 @@
 // l % 32 and the 16 consecutive k of group g = l / 32. Sub-step h (k32) of a
 // slice uses k = 32h + 16g + [0, 16) for both operands.
 //
+// FP8 pairs (F8; 4-bit codes the quantizer wrote as fp8 pairs, row sums
+// given). The int4 codes are exact in fp8 E4M3 and u = t + 1 is exact in
+// fp4 E2M1 as u / 2 (the field itself in a nibble's low bits), so one
+// v_mfma_f32_32x32x64_f8f6f4 (fp8 A, fp4 B) multiplies a whole 64-weight
+// block, exactly: every partial sum is a multiple of 1/2 below 2^19, and
+// 2 acc = q . u. The B operand of lane group g is (p >> 2g) & 0x33333333 per
+// packed word: nibble 2i + h of it (i = 4 d + c for byte c of word d) holds
+// the weight 16 g + i + 32 h, and the quantizer stores that weight's code at
+// byte 32 g + 2i + h of the block. The instruction pairs fp4 nibble e of
+// lane group g with fp8 byte e % 16 of lane group (e / 16) when g = 0 and
+// with byte 16 + e % 16 of that lane group when g = 1 (measured with a
+// layout probe), so lane group g's fp8 operand is the block's bytes 16 g ..
+// 16 g + 15 and then 32 + 16 g .. 32 + 16 g + 15: the same two 16-byte
+// chunks as its two int8 sub-steps. Measured at M = 2048, K = 8192, N = 2048: half as many
+// MFMA instructions, and a quarter of the unpacking, take the product from
+// 39 to 34 us (a timing variant with fp6 codes, whose MFMA runs twice as
+// fast, measured the same: the matrix pipe is not what holds this product).
+//
 // Tile order. Workgroups are dispatched round-robin over the eight XCDs
 // (each with its own L2), so workgroup L runs on XCD L % 8. Each XCD gets a
 // contiguous range of tiles walked band by band (four M-tiles wide), so the
@@ -112,6 +130,30 @@ __device__ __forceinline__ v4i unpack_u(const uint4 p, int sh) {
   return r;
 }
 
+// The fp4 (E2M1) B operand of lane group g: fields g and g + 2 of every byte
+// of a packed block, each in a nibble's low bits (the value u / 2).
+__device__ __forceinline__ v4i unpack_f4(const uint4 p, int g) {
+  v4i r;
+  r.x = (int)((p.x >> (2 * g)) & 0x33333333u);
+  r.y = (int)((p.y >> (2 * g)) & 0x33333333u);
+  r.z = (int)((p.z >> (2 * g)) & 0x33333333u);
+  r.w = (int)((p.w >> (2 * g)) & 0x33333333u);
+  return r;
+}
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// acc += A (32 fp8 codes per lane, a0 then a1) x B (32 fp4 fields per lane),
+// the accumulator kept as the bits of its fp32 values.
+__device__ __forceinline__ v16i mma_f8f4(const v4i a0, const v4i a1, const v4i b, const v16i acc) {
+  const v8i a = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  const v8i bb = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};  // fp4 reads the first four words
+  return __builtin_bit_cast(
+      v16i, __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, __builtin_bit_cast(v16f, acc),
+                                                              0, 4, 0, 0, 0, 0));
+}
+
 // Sum of the 16 signed bytes of a code fragment, added to s.
 __device__ __forceinline__ int add_bytes(const v4i a, int s) {
   s = __builtin_amdgcn_sdot4(a.x, 0x01010101, s, false);
@@ -120,13 +162,14 @@ __device__ __forceinline__ int add_bytes(const v4i a, int s) {
   return __builtin_amdgcn_sdot4(a.w, 0x01010101, s, false);
 }
 
-template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG, bool WIDE>
+template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG, bool WIDE, bool F8>
 __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ scales, int M, int K,
     const uint8_t* __restrict__ Wp, int N, const float* __restrict__ alpha_p, float c,
     float* __restrict__ y, int32_t* __restrict__ acc_out, const int32_t* __restrict__ rowsum_g,
     int tiles_m, int tiles_n) {
   using S = Shape<RT, CT, WMW, WNW, KS>;
+  static_assert(!F8 || (RSG && !OUT_I32), "fp8 pairs come with their row sums");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   // XCD-aware tile order.
@@ -195,7 +238,8 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
   }
 
   // Operand reads. Codes: row wm*32RT + rt*32 + l32 of this wave's slice,
-  // logical chunk 2h + g (sub-step h) at its swizzled position. Weights:
+  // logical chunk 2h + g (sub-step h) at its swizzled position (with F8 the
+  // two chunks of a block are the two halves of one fp8 operand). Weights:
   // block blk of column wn*32CT + ct*32 + l32.
   int a_rd[4];
   {
@@ -233,22 +277,29 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
             *reinterpret_cast<const v4i*>(sb_ + a_rd[2 * (blk_) + hh] + rt * 32 * BKW);         \
   }
 #define BITNET_UNPACK(B_)                                                                       \
-  _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                              \
+  _Pragma("unroll") for (int hh = 0; hh < (F8 ? 1 : 2); ++hh)                                   \
       _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) B_[hh][ct] =                            \
-          unpack_u(pw[ct], 2 * g + 4 * hh);
+          F8 ? unpack_f4(pw[ct], g) : unpack_u(pw[ct], 2 * g + 4 * hh);
 #define BITNET_MMA(A_, B_)                                                                      \
-  _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                              \
-      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                       \
-    if (!RSG) rsum[rt] = add_bytes(A_[hh][rt], rsum[rt]);                                       \
-    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) acc[rt][ct] =                             \
-        __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct], acc[rt][ct], 0, 0, 0);    \
+  if constexpr (F8) {                                                                           \
+    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                           \
+        _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) acc[rt][ct] =                         \
+            mma_f8f4(A_[0][rt], A_[1][rt], B_[0][ct], acc[rt][ct]);                             \
+  } else {                                                                                      \
+    _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                            \
+        _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                     \
+      if (!RSG) rsum[rt] = add_bytes(A_[hh][rt], rsum[rt]);                                     \
+      _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) acc[rt][ct] =                           \
+          __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct], acc[rt][ct], 0, 0, 0);  \
+    }                                                                                           \
   }
   // The empty asm statements pin the next block's operands (codes read and
   // weights unpacked) to the step that prepares them: otherwise the compiler
   // sinks that work to its first use, past the MFMAs it is meant to overlap.
 #define BITNET_PIN(A_, B_)                                                                      \
   _Pragma("unroll") for (int hh = 0; hh < 2; ++hh) {                                            \
-    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) asm volatile("" : "+v"(B_[hh][ct]));      \
+    _Pragma("unroll") for (int ct = 0; ct < CT; ++ct) if (!F8 || hh == 0)                       \
+        asm volatile("" : "+v"(B_[hh][ct]));                                                    \
     _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) asm volatile("" : "+v"(A_[hh][rt]));      \
   }
   // One block's MFMAs (operands A_, B_) cut into S::CH groups separated by
@@ -257,29 +308,38 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
   // row sums of A_ and, when LD_ is set, this wave's share of the loads of
   // stage lks_ into slot lslot_ are spread over the later groups, so the
   // matrix pipe always has work queued.
-  constexpr int kMfmaPerBlock = 2 * RT * CT;
-  constexpr int kUnpackPerBlock = 2 * CT;
+  constexpr int kMfmaPerBlock = F8 ? RT * CT : 2 * RT * CT;
+  constexpr int kUnpackPerBlock = F8 ? CT : 2 * CT;
   constexpr int kSumPerBlock = 2 * RT;
+  constexpr int CHB = kMfmaPerBlock < 8 ? kMfmaPerBlock : 8;  // MFMA groups per block
+  static_assert(kMfmaPerBlock % CHB == 0, "MFMA groups");
 #define BITNET_STEP(A_, B_, NB_, LD_, lks_, lslot_)                                             \
-  _Pragma("unroll") for (int ch = 0; ch < S::CH; ++ch) {                                      \
+  _Pragma("unroll") for (int ch = 0; ch < CHB; ++ch) {                                        \
     _Pragma("unroll") for (int e = 0; e < kUnpackPerBlock; ++e) {                               \
-      if (1 + e * (S::CH - 1) / kUnpackPerBlock == ch)                                        \
-        NB_[e / CT][e % CT] = unpack_u(pw[e % CT], 2 * g + 4 * (e / CT));                       \
+      if (1 + e * (CHB - 1) / kUnpackPerBlock == ch) {                                        \
+        if constexpr (F8) NB_[0][e] = unpack_f4(pw[e], g);                                      \
+        else NB_[e / CT][e % CT] = unpack_u(pw[e % CT], 2 * g + 4 * (e / CT));                  \
+      }                                                                                         \
     }                                                                                           \
     _Pragma("unroll") for (int e = 0; e < kSumPerBlock; ++e) {                                  \
-      if (!RSG && 1 + e * (S::CH - 1) / kSumPerBlock == ch)                                   \
+      if (!RSG && 1 + e * (CHB - 1) / kSumPerBlock == ch)                                     \
         rsum[e % RT] = add_bytes(A_[e / RT][e % RT], rsum[e % RT]);                             \
     }                                                                                           \
     if (LD_) {                                                                                  \
       _Pragma("unroll") for (int i = 0; i < S::NL_W; ++i) {                                     \
-        if (i * S::CH / S::NL_W == ch) BITNET_LOAD(lks_, lslot_, i)                           \
+        if (i * CHB / S::NL_W == ch) BITNET_LOAD(lks_, lslot_, i)                             \
       }                                                                                         \
     }                                                                                           \
-    _Pragma("unroll") for (int f = ch * (kMfmaPerBlock / S::CH);                              \
-                           f < (ch + 1) * (kMfmaPerBlock / S::CH); ++f) {                     \
-      const int hh = f / (RT * CT), rt = (f / CT) % RT, ct = f % CT;                            \
-      acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct], acc[rt][ct],  \
-                                                          0, 0, 0);                             \
+    _Pragma("unroll") for (int f = ch * (kMfmaPerBlock / CHB);                                \
+                           f < (ch + 1) * (kMfmaPerBlock / CHB); ++f) {                       \
+      if constexpr (F8) {                                                                       \
+        const int rt = f / CT, ct = f % CT;                                                     \
+        acc[rt][ct] = mma_f8f4(A_[0][rt], A_[1][rt], B_[0][ct], acc[rt][ct]);                   \
+      } else {                                                                                  \
+        const int hh = f / (RT * CT), rt = (f / CT) % RT, ct = f % CT;                          \
+        acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A_[hh][rt], B_[hh][ct],             \
+                                                            acc[rt][ct], 0, 0, 0);              \
+      }                                                                                         \
     }                                                                                           \
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
@@ -343,6 +403,17 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS) void ternary_gemm_kernel(
 #undef BITNET_STEP
 #undef BITNET_PIN
 #undef BITNET_LOAD
+  if constexpr (F8) {
+    // fp32 sums of q u / 2, exact: q . u = 2 acc, an integer (converted as
+    // whole vectors: a bit cast of one vector element read element 0)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const v16f f = __builtin_bit_cast(v16f, acc[rt][ct]);
+        acc[rt][ct] = __builtin_convertvector(f * 2.0f, v16i);
+      }
+  }
 
   // No load may still be writing LDS past this point, and no wave may still
   // be reading the ring, whose tail now takes the row sums.
@@ -803,7 +874,8 @@ __global__ __launch_bounds__(64 * WMW * WNW) void ternary_gemm_stream_kernel(
 #undef BITNET_SSTEP
 }
 
-template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG, bool WIDE = false>
+template <int RT, int CT, int WMW, int WNW, int KS, bool OUT_I32, bool RSG, bool WIDE = false,
+          bool F8 = false>
 hipError_t launch_tile(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, float c, float* y,
                        int32_t* acc, const int32_t* rowsum, hipStream_t stream) {
@@ -812,7 +884,7 @@ hipError_t launch_tile(const int8_t* codes, const float* scales, int64_t M, int 
   const int tiles_n = (int)((N + S::BN - 1) / S::BN);
   const int tiles = tiles_m * tiles_n;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  auto kern = ternary_gemm_kernel<RT, CT, WMW, WNW, KS, OUT_I32, RSG, WIDE>;
+  auto kern = ternary_gemm_kernel<RT, CT, WMW, WNW, KS, OUT_I32, RSG, WIDE, F8>;
   if (S::LDS > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
@@ -879,8 +951,18 @@ hipError_t launch_stream(const int8_t* codes, const float* scales, const int32_t
 
 hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int K,
                        const uint8_t* Wpacked, int64_t N, const float* alpha, int bits, float* y,
-                       int32_t* acc, hipStream_t stream, const int32_t* rowsum) {
+                       int32_t* acc, hipStream_t stream, const int32_t* rowsum,
+                       bool f8) {
   const float c = (bits == 8) ? kScaleInt8 : kScaleInt4;
+  if (f8) {
+    if (!fp8_pair_gemm_ok(M, K, N, bits) || !rowsum || acc) return hipErrorInvalidValue;
+    if (N % 4 == 0 && N <= (1 << 20) && (reinterpret_cast<uintptr_t>(y) & 15) == 0)
+      return launch_tile<2, 2, 2, 2, 2, false, true, true, true>(codes, scales, M, K, Wpacked, N,
+                                                                 alpha, c, y, nullptr, rowsum,
+                                                                 stream);
+    return launch_tile<2, 2, 2, 2, 2, false, true, false, true>(codes, scales, M, K, Wpacked, N,
+                                                                alpha, c, y, nullptr, rowsum, stream);
+  }
   // Two waves per SIMD (eight per workgroup, 64 x 128 or 128 x 64 per wave,
   // accumulators in VGPRs): while one wave waits on LDS or the stage barrier
   // the other issues MFMAs, which measured 13-18% faster than one wave of
@@ -903,11 +985,14 @@ hipError_t launch_gemm(const int8_t* codes, const float* scales, int64_t M, int 
 hipError_t launch_ternary_matmul(const int8_t* codes, const float* scales, int64_t M, int K,
                                  const uint8_t* Wpacked, int64_t N, const float* alpha, int bits,
                                  float* y, int32_t* acc, hipStream_t stream,
-                                 const int32_t* rowsum, bool nibbles) {
-  if (M <= kDecodeMaxM)
+                                 const int32_t* rowsum, bool nibbles, bool fp8_pairs) {
+  if (M <= kDecodeMaxM) {
+    if (fp8_pairs) return hipErrorInvalidValue;
     return launch_gemv(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream, nibbles, rowsum);
+  }
   if (nibbles) return hipErrorInvalidValue;
-  return launch_gemm(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream, rowsum);
+  return launch_gemm(codes, scales, M, K, Wpacked, N, alpha, bits, y, acc, stream, rowsum,
+                     fp8_pairs);
 }
 
 }  // namespace bitnet

@@ -42,8 +42,8 @@ hipError_t launch_pack_2bit(const int8_t*, int64_t, int64_t, uint8_t*, hipStream
   return record("pack_2bit");
 }
 hipError_t launch_quantize(const void*, int, int64_t, int, int, int, int8_t*, float*, hipStream_t,
-                           const Prologue*, int32_t*, bool nibbles) {
-  return record(nibbles ? "quantize_nibbles" : "quantize");
+                           const Prologue*, int32_t*, bool nibbles, bool fp8_pairs) {
+  return record(fp8_pairs ? "quantize_fp8_pairs" : (nibbles ? "quantize_nibbles" : "quantize"));
 }
 hipError_t launch_kv_quantize(const void*, int, int64_t, int, int, int, int8_t*, float*,
                               hipStream_t, uint8_t* packed) {
@@ -51,15 +51,16 @@ hipError_t launch_kv_quantize(const void*, int, int64_t, int, int, int, int8_t*,
 }
 hipError_t launch_ternary_matmul(const int8_t*, const float*, int64_t, int, const uint8_t*, int64_t,
                                  const float*, int, float*, int32_t* acc, hipStream_t,
-                                 const int32_t*, bool nibbles) {
-  return record(acc ? "matmul_i32" : (nibbles ? "matmul_nibbles" : "matmul"));
+                                 const int32_t*, bool nibbles, bool fp8_pairs) {
+  return record(acc ? "matmul_i32"
+                    : (fp8_pairs ? "matmul_fp8_pairs" : (nibbles ? "matmul_nibbles" : "matmul")));
 }
 hipError_t launch_gemv(const int8_t*, const float*, int64_t, int, const uint8_t*, int64_t,
                        const float*, int, float*, int32_t*, hipStream_t, bool, const int32_t*) {
   return record("gemv");
 }
 hipError_t launch_gemm(const int8_t*, const float*, int64_t, int, const uint8_t*, int64_t,
-                       const float*, int, float*, int32_t*, hipStream_t, const int32_t*) {
+                       const float*, int, float*, int32_t*, hipStream_t, const int32_t*, bool) {
   return record("gemm");
 }
 hipError_t launch_fused_decode(const void*, int, int64_t, int, const uint8_t*, int64_t,

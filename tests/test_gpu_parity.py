@@ -247,6 +247,45 @@ def test_parity_many_tiles(M, K, N, bits, had):
     assert_y_close(y_np[rows], y_ref)
 
 
+# FP8 pairs -----------------------------------------------------------------
+# 4-bit codes of bf16 rows with the transform (K >= 2048) reach the 128x128
+# tile product as fp8 E4M3 bytes in the order of the fp4 weight fields, one
+# fp8 x fp4 MFMA per 64-weight block with fp32 sums (exact: half-integers
+# below 2^19). The forward must equal, bit for bit, the int8-code product of
+# the public quantizer's codes with their row sums, and the oracle.
+@pytest.mark.parametrize("M,K,N", [
+    (17, 2048, 40),       # one row past the decode batch, one ragged tile
+    (300, 4096, 260),     # ragged rows and columns
+    (129, 32768, 130),    # the longest row
+    (1000, 2048, 2048),   # many tiles, eight stages each
+    (2100, 16384, 64),    # a partial tile row at the bottom
+])
+def test_fp8_pair_forward_exact(M, K, N):
+    _say(f"fp8 pairs M={M} K={K} N={N}")
+    case = workloads.make_case(M, K, N, x_dtype="bf16", n_out=max(1, K // 100), factor=30.0,
+                               seed=M + K + N)
+    x = _to_dev_x(case["x"], "bf16")
+    W = torch.from_numpy(case["W"]).to(DEV)
+    Wp, alpha = bl.ternarize_weights(W)
+    y = bl.hbitlinear_forward(x, Wp, alpha, 4, 1)
+    rowsum = torch.empty((M,), dtype=torch.int32, device=DEV)
+    codes, scales = bl.quantize_activations(x, 4, 1, rowsum=rowsum)
+    y2 = bl.ternary_linear_dequant(codes, scales, Wp, alpha, 4, rowsum=rowsum)
+    torch.cuda.synchronize()
+    del W
+    y_np = y.cpu().numpy()
+    np.testing.assert_array_equal(y_np, y2.cpu().numpy())
+    del y2
+    t_ref, a_ref, _ = oracle.ternarize(case["W"])
+    x64 = oracle.widen_input(case["x"], "bf16")
+    q_ref, s_ref, p_ref = oracle.quantize_activations(oracle.fwht(x64), 4)
+    assert_codes_match(codes.cpu().numpy(), q_ref, p_ref)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 40), replace=False)]))
+    _, y_ref = oracle.forward_from_codes(q_ref[rows], s_ref[rows], t_ref, a_ref, 4)
+    assert_y_close(y_np[rows], y_ref)
+
+
 # Edge and degenerate cases ------------------------------------------------
 def test_zero_weights_give_zero_output():
     _say("zero weights")
@@ -332,6 +371,7 @@ def test_bitwise_deterministic():
     (1, 2560, 700, 8, 0),      # one fused kernel
     (16, 16384, 300, 4, 1),    # transform + streaming product
     (200, 1024, 300, 4, 1),    # prefill tile
+    (200, 2048, 300, 4, 1),    # prefill tile on fp8 pairs
 ])
 def test_graph_replay_matches_eager(M, K, N, bits, had):
     _say(f"graph replay M={M} K={K} N={N}")
