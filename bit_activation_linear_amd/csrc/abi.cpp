@@ -107,13 +107,11 @@ bool use_nibble_codes(int64_t M, int64_t K, int bits) {
   return bits == 4 && M <= bitnet::kDecodeMaxM && K % bitnet::kNibbleKMultiple == 0;
 }
 
-// The forward's 4-bit codes go from the matrix-core transform kernel to the
-// 128 x 128-tile product as fp8 pairs when both can take them (one fp8 x fp4
-// MFMA per 64-weight block instead of two int8 ones).
-bool use_fp8_pairs(int64_t M, int64_t K, int64_t N, int bits, int hadamard, int x_dtype,
-                   bool prologue) {
-  return bitnet::fp8_pair_quant_ok(K, bits, hadamard, x_dtype, prologue) &&
-         bitnet::fp8_pair_gemm_ok(M, K, N, bits);
+// The forward's 4-bit codes go from the transform kernels to the 128 x
+// 128-tile product as fp8 pairs when both can take them (one fp8 x fp4 MFMA
+// per 64-weight block instead of two int8 ones).
+bool use_fp8_pairs(int64_t M, int64_t K, int64_t N, int bits, int hadamard) {
+  return bitnet::fp8_pair_quant_ok(bits, hadamard) && bitnet::fp8_pair_gemm_ok(M, K, N, bits);
 }
 
 bool forward_is_fused(int64_t M, int64_t K, int64_t N, int hadamard) {
@@ -299,7 +297,7 @@ bitnet_status forward_impl(const char* fn, const void* x, bitnet_dtype x_dtype, 
   }
   const ForwardWorkspace w = carve_forward(ws, M, K);
   const bool nib = use_nibble_codes(M, K, bits);
-  const bool f8 = use_fp8_pairs(M, K, N, bits, hadamard, x_dtype, false);
+  const bool f8 = use_fp8_pairs(M, K, N, bits, hadamard);
   hipError_t e = hipSuccess;
   if (stages & BITNET_STAGE_QUANTIZE) {
     e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes, w.scales,
@@ -569,11 +567,12 @@ bitnet_status bitnet_hbitlinear_forward_prologue(const void* x, const void* up, 
   }
   const ForwardWorkspace w = carve_forward(ws, M, K);
   const bool nib = use_nibble_codes(M, K, bits);
+  const bool f8 = use_fp8_pairs(M, K, N, bits, hadamard);
   hipError_t e = bitnet::launch_quantize(x, (int)x_dtype, M, (int)K, bits, hadamard, w.codes,
-                                         w.scales, stream, &pro, w.rowsum, nib);
+                                         w.scales, stream, &pro, w.rowsum, nib, f8);
   if (e != hipSuccess) return hip_status(e, fn);
   e = bitnet::launch_ternary_matmul(w.codes, w.scales, M, (int)K, Wpacked, N, alpha, bits, y,
-                                    nullptr, stream, w.rowsum, nib);
+                                    nullptr, stream, w.rowsum, nib, f8);
   return hip_status(e, fn);
 }
 

@@ -48,12 +48,12 @@ __global__ __launch_bounds__(1 << LT) void fwht_quant_kernel(const XT* x, int8_t
                                                              float* __restrict__ scales,
                                                              Prologue pro, float* fout,
                                                              int32_t* __restrict__ rowsum,
-                                                             bool nib) {
+                                                             bool nib, bool f8) {
   extern __shared__ float lds[];
   const int row = blockIdx.x;
   float v[1 << (L - LT)];
   load_row<XT, L, LT>(x + (size_t)row * (1 << L), v);
-  transform_row<XT, BITS, L, LT, PRO>(v, row, codes, scales, pro, fout, rowsum, nib, lds);
+  transform_row<XT, BITS, L, LT, PRO>(v, row, codes, scales, pro, fout, rowsum, nib, lds, f8);
 }
 
 // No transform: thread t owns the 8-element vectors at 8t + 2048c, c < CH.
@@ -137,13 +137,13 @@ hipError_t ensure_lds(Kern kern, size_t bytes) {
 template <typename XT, int BITS, int L, int LT, bool PRO>
 hipError_t launch_fwht(const void* x, int64_t M, int8_t* codes, float* scales, const Prologue& pro,
                        hipStream_t stream, float* fout = nullptr, int32_t* rowsum = nullptr,
-                       bool nib = false) {
+                       bool nib = false, bool f8 = false) {
   const size_t lds = RowLds<L, LT>::kBytes;
   auto kern = fwht_quant_kernel<XT, BITS, L, LT, PRO>;
   hipError_t e = ensure_lds(kern, lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)M), dim3(1 << LT), lds, stream>>>(reinterpret_cast<const XT*>(x), codes,
-                                                          scales, pro, fout, rowsum, nib);
+                                                          scales, pro, fout, rowsum, nib, f8);
   return hipGetLastError();
 }
 
@@ -310,34 +310,7 @@ __global__ __launch_bounds__(64 << (L - 11)) void fwht_mfma_quant_kernel(
     int8_t* crow = codes + (size_t)row * (nib && !F8 ? K / 2 : K);
     int qs = 0;
     if constexpr (F8) {
-      // fp8 pairs: thread t writes the row's bytes 32 t .. 32 t + 31, those of
-      // lane group g = t % 2 of 64-weight block t / 2, whose byte 2 i + h is
-      // the code of the block's weight 16 g + i + 32 h (i < 16, h < 2). The
-      // codes clip(rint(v * mult)) are exact in fp8 E4M3 and in the float sum
-      // that gives the row sum. Runs of 16 elements never cross a padding step.
-      const int k0 = 64 * (t >> 1) + 16 * (t & 1);
-      const int q0 = pad_idx(k0), q1 = pad_idx(k0 + 32);
-      float fs = 0.0f;
-      unsigned wd[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        // word j: weights i = 2 j and 2 j + 1 of the two runs
-        const float z[4] = {lds[q0 + 2 * j], lds[q1 + 2 * j], lds[q0 + 2 * j + 1],
-                            lds[q1 + 2 * j + 1]};
-        float r[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          r[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(z[e] * mult), QConst<BITS>::lo,
-                                         QConst<BITS>::hi);
-          fs += r[e];
-        }
-        const int lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-        wd[j] = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], lo2, true);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(crow + 32 * t);
-      dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
-      qs = (int)fs;
+      qs = store_fp8_pairs<E>(lds, t * E, mult, crow);  // the row's bytes 32 t .. 32 t + 31
     } else {
       const int e0 = t * E;
       const int pe0 = pad_idx(e0);  // e0 is a multiple of 32: the padding of e0 + i is e0's
@@ -409,12 +382,13 @@ hipError_t launch_fwht_l(const void* x, int64_t M, int8_t* codes, float* scales,
   // bf16 rows of 2048 or more elements take the matrix cores for index bits 0-5
   if constexpr (std::is_same<XT, uint16_t>::value && BITS != 0 && !PRO && L >= 11)
     return launch_fwht_mfma<BITS, L>(x, M, codes, scales, stream, rowsum, nib, f8);
-  if (f8) return hipErrorInvalidValue;  // fp8 pairs come from the matrix-core kernel only
   constexpr int LT_BATCH = fwht_lt_batch(L);
   constexpr int LT_FEW = fwht_lt_few(L);
+  if (f8 && (BITS != 4 || (1 << (L - LT_BATCH)) > 32 || (1 << (L - LT_FEW)) > 32))
+    return hipErrorInvalidValue;  // fp8 pairs: 4-bit codes, at most 32 elements per thread
   if (M <= 64 && LT_FEW != LT_BATCH)
-    return launch_fwht<XT, BITS, L, LT_FEW, PRO>(x, M, codes, scales, pro, stream, fout, rowsum, nib);
-  return launch_fwht<XT, BITS, L, LT_BATCH, PRO>(x, M, codes, scales, pro, stream, fout, rowsum, nib);
+    return launch_fwht<XT, BITS, L, LT_FEW, PRO>(x, M, codes, scales, pro, stream, fout, rowsum, nib, f8);
+  return launch_fwht<XT, BITS, L, LT_BATCH, PRO>(x, M, codes, scales, pro, stream, fout, rowsum, nib, f8);
 }
 
 // Transform only (fp32 rows in and out, in place allowed).
@@ -499,7 +473,7 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bit
                            int8_t* codes, float* scales, hipStream_t stream, const Prologue* pro,
                            int32_t* rowsum, bool nibbles, bool fp8_pairs) {
   if (nibbles && (bits != 4 || K % 8 != 0)) return hipErrorInvalidValue;
-  if (fp8_pairs && (nibbles || bits != 4 || x_dtype != 1 || !hadamard)) return hipErrorInvalidValue;
+  if (fp8_pairs && (nibbles || !fp8_pair_quant_ok(bits, hadamard))) return hipErrorInvalidValue;
   const Prologue none{nullptr, nullptr, 0.0f, 0};
   if (pro && !pro->up && !pro->rms) pro = nullptr;  // nothing to apply: the plain quantizer
   if (pro) {

@@ -198,6 +198,44 @@ struct QConst {
   static constexpr float hi = (BITS == 8) ? 127.0f : 7.0f;
 };
 
+// 4-bit codes as fp8 pairs (the prefill product's code form): bytes P ..
+// P + E - 1 of a row (P a multiple of E, E = 8, 16 or 32), where byte
+// 32 g + 2 i + h of every 64-weight block holds the code of the block's
+// weight 16 g + i + 32 h. lds holds the row (padded index) and mult is the
+// code multiplier: the codes clip(rint(v * mult)), the same as quant_pack8's,
+// are exact in fp8 E4M3 and in the float sum returned (their sum). The two
+// runs of E / 2 elements never cross a padding step.
+template <int E>
+__device__ __forceinline__ int store_fp8_pairs(const float* lds, int P, float mult, int8_t* crow) {
+  static_assert(E == 8 || E == 16 || E == 32, "fp8-pair chunk");
+  const int k0 = (P & ~63) + 16 * ((P >> 5) & 1) + ((P & 31) >> 1);
+  const int q0 = pad_idx(k0), q1 = pad_idx(k0 + 32);
+  float fs = 0.0f;
+  unsigned wd[E / 4];
+#pragma unroll
+  for (int j = 0; j < E / 4; ++j) {
+    // word j: elements 2 j and 2 j + 1 of the two runs
+    const float z[4] = {lds[q0 + 2 * j], lds[q1 + 2 * j], lds[q0 + 2 * j + 1], lds[q1 + 2 * j + 1]};
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(z[e] * mult), QConst<4>::lo, QConst<4>::hi);
+      fs += r[e];
+    }
+    const int lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+    wd[j] = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], lo2, true);
+  }
+  if constexpr (E == 8) {
+    *reinterpret_cast<uint2*>(crow + P) = make_uint2(wd[0], wd[1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < E / 16; ++q)
+      *reinterpret_cast<uint4*>(crow + P + 16 * q) =
+          make_uint4(wd[4 * q], wd[4 * q + 1], wd[4 * q + 2], wd[4 * q + 3]);
+  }
+  return (int)fs;
+}
+
 // One middle chunk: butterflies over index bits [B0, B0 + NB). Thread t owns
 // the groups g = t + T*gi (gi < E >> NB); a group is the 2^NB elements
 // base(g) + (j << B0). LAST: quantize from registers and store the codes,
@@ -226,7 +264,8 @@ template <int L, int LT, int B0, int NB, bool LAST, int BITS, bool PRO>
 __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_t* crow,
                                          float* scale_out, float sq, const Prologue& pro,
                                          float* frow = nullptr, int* ired = nullptr,
-                                         int32_t* rs_out = nullptr, bool nib = false) {
+                                         int32_t* rs_out = nullptr, bool nib = false,
+                                         bool f8 = false) {
   constexpr int T = 1 << LT;
   constexpr int E = 1 << (L - LT);
   constexpr int R = 1 << NB;
@@ -307,17 +346,21 @@ __device__ __forceinline__ void mid_pass(float* v, float* lds, float* red, int8_
   const int e0 = t * E;
   const int pe0 = pad_idx(e0);  // e0 is a multiple of E, c + i < E
   int qs = 0;  // this thread's share of the code sum
+  if (BITS == 4 && E <= 32 && f8) {
+    qs = store_fp8_pairs<(E <= 32 ? E : 32)>(lds, e0, mult, crow);
+  } else {
 #pragma unroll
-  for (int c = 0; c < E; c += 8) {
-    float u[8];
+    for (int c = 0; c < E; c += 8) {
+      float u[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = lds[pe0 + (c + i) + ((c + i) >> 5)];
-    const uint2 w = quant_pack8<BITS>(u, mult);
-    if (nib)
-      *reinterpret_cast<unsigned*>(crow + ((e0 + c) >> 1)) = nibble_word(w);
-    else
-      *reinterpret_cast<uint2*>(crow + e0 + c) = w;
-    qs = __builtin_amdgcn_sdot4((int)w.y, 0x01010101, __builtin_amdgcn_sdot4((int)w.x, 0x01010101, qs, false), false);
+      for (int i = 0; i < 8; ++i) u[i] = lds[pe0 + (c + i) + ((c + i) >> 5)];
+      const uint2 w = quant_pack8<BITS>(u, mult);
+      if (nib)
+        *reinterpret_cast<unsigned*>(crow + ((e0 + c) >> 1)) = nibble_word(w);
+      else
+        *reinterpret_cast<uint2*>(crow + e0 + c) = w;
+      qs = __builtin_amdgcn_sdot4((int)w.y, 0x01010101, __builtin_amdgcn_sdot4((int)w.x, 0x01010101, qs, false), false);
+    }
   }
   if (rs_out) {
     const int total = block_isum<T>(qs, ired);
@@ -402,7 +445,7 @@ struct RowLds {
 template <typename XT, int BITS, int L, int LT, bool PRO>
 __device__ __forceinline__ void transform_row(float* v, int row, int8_t* codes, float* scales,
                                               const Prologue& pro, float* fout, int32_t* rowsum,
-                                              bool nib, float* smem) {
+                                              bool nib, float* smem, bool f8 = false) {
   constexpr int K = 1 << L;
   constexpr int T = 1 << LT;
   constexpr int E = K / T;
@@ -440,18 +483,18 @@ __device__ __forceinline__ void transform_row(float* v, int row, int8_t* codes, 
   static_assert(R3 <= NB3, "at most four middle chunks");
   float* sc = BITS ? scales + row : nullptr;
   if constexpr (R1 <= 0) {
-    mid_pass<L, LT, 3, NB0, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
+    mid_pass<L, LT, 3, NB0, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib, f8);
   } else {
-    mid_pass<L, LT, 3, NB0, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
+    mid_pass<L, LT, 3, NB0, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib, f8);
     if constexpr (R2 <= 0) {
-      mid_pass<L, LT, 3 + NB0, NB1, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
+      mid_pass<L, LT, 3 + NB0, NB1, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib, f8);
     } else {
-      mid_pass<L, LT, 3 + NB0, NB1, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
+      mid_pass<L, LT, 3 + NB0, NB1, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib, f8);
       if constexpr (R3 <= 0) {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib, f8);
       } else {
-        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
-        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib);
+        mid_pass<L, LT, 3 + NB0 + NB1, NB2, false, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib, f8);
+        mid_pass<L, LT, 3 + NB0 + NB1 + NB2, R3, true, BITS, PRO>(v, lds, red, crow, sc, sq, pro, frow, ired, rso, nib, f8);
       }
     }
   }

@@ -102,23 +102,21 @@ constexpr int kNibbleKMultiple = 256;  // the decode product reads nibble codes 
 // E4M3 (exact for integers up to 16), in the order of the fp4 weight fields
 // the product unpacks: byte 32 g + 2 i + h of each 64-weight block holds
 // the code of the block's weight 16 g + i + 32 h (g, h < 2, i < 16). The
-// matrix-core transform kernel writes them (bf16 rows, K >= 2048, with the
-// transform, no prologue), and the 128 x 128-tile product reads them, the
-// one that runs when there are fewer than 1024 tiles of 256 x 256.
+// transform kernels write them (4-bit codes with the transform), and the
+// 128 x 128-tile product reads them, the one that runs when there are fewer
+// than 1024 tiles of 256 x 256.
 inline bool fp8_pair_gemm_ok(int64_t M, int64_t K, int64_t N, int bits) {
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   return bits == 4 && M > kDecodeMaxM && K % 64 == 0 && big_tiles < 1024;
 }
-inline bool fp8_pair_quant_ok(int64_t K, int bits, int hadamard, int x_dtype, bool prologue) {
-  return bits == 4 && hadamard && x_dtype == 1 && !prologue && K >= 2048 && K <= 32768;
-}
+inline bool fp8_pair_quant_ok(int bits, int hadamard) { return bits == 4 && hadamard; }
 
 // Fused (optional) prologue + Walsh-Hadamard transform + per-token
 // quantization. x_dtype: 0 = fp32, 1 = bf16 bit patterns. pro may be null.
 // rowsum, when not null, receives each token's code sum (int32 [M]), which
 // the prefill product then needs not compute. nibbles (bits = 4 only):
 // write nibble codes instead of int8 codes; fp8_pairs: write fp8 pairs
-// (fp8_pair_quant_ok only).
+// (fp8_pair_quant_ok only; K is then a power of two of at least 64).
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,
                            int8_t* codes, float* scales, hipStream_t stream,
                            const Prologue* pro = nullptr, int32_t* rowsum = nullptr,

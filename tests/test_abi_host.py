@@ -465,7 +465,8 @@ def _calls(lib, fn, *args):
     (2048, 8192, 2048, 4, 1, ["quantize_fp8_pairs", "matmul_fp8_pairs"]),  # bf16, transform, 4-bit
     (2048, 8192, 2048, 8, 1, ["quantize", "matmul"]),           # prefill: never nibble codes
     (8192, 8192, 8192, 4, 1, ["quantize", "matmul"]),           # 1024 tiles of 256: int8 codes
-    (2048, 1024, 2048, 4, 1, ["quantize", "matmul"]),           # K < 2048: int8 codes
+    (2048, 1024, 2048, 4, 1, ["quantize_fp8_pairs", "matmul_fp8_pairs"]),  # the butterfly kernel
+    (2048, 1024, 2048, 4, 0, ["quantize", "matmul"]),           # no transform: int8 codes
     (3, 192, 40, 4, 0, ["fused_decode"]),
 ])
 def test_forward_dispatch(lib, M, K, N, bits, had, want):

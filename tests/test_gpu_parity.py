@@ -248,23 +248,30 @@ def test_parity_many_tiles(M, K, N, bits, had):
 
 
 # FP8 pairs -----------------------------------------------------------------
-# 4-bit codes of bf16 rows with the transform (K >= 2048) reach the 128x128
-# tile product as fp8 E4M3 bytes in the order of the fp4 weight fields, one
-# fp8 x fp4 MFMA per 64-weight block with fp32 sums (exact: half-integers
-# below 2^19). The forward must equal, bit for bit, the int8-code product of
-# the public quantizer's codes with their row sums, and the oracle.
-@pytest.mark.parametrize("M,K,N", [
-    (17, 2048, 40),       # one row past the decode batch, one ragged tile
-    (300, 4096, 260),     # ragged rows and columns
-    (129, 32768, 130),    # the longest row
-    (1000, 2048, 2048),   # many tiles, eight stages each
-    (2100, 16384, 64),    # a partial tile row at the bottom
+# 4-bit codes with the transform reach the 128x128 tile product as fp8 E4M3
+# bytes in the order of the fp4 weight fields, one fp8 x fp4 MFMA per
+# 64-weight block with fp32 sums (exact: half-integers below 2^19). Both
+# transform kernels write them: the matrix-core one (bf16, K >= 2048) and the
+# butterfly one (8, 16 or 32 elements per thread). The forward must equal, bit
+# for bit, the int8-code product of the public quantizer's codes with their
+# row sums, and the oracle.
+@pytest.mark.parametrize("M,K,N,xdt", [
+    (17, 2048, 40, "bf16"),       # one row past the decode batch, one ragged tile
+    (300, 4096, 260, "bf16"),     # ragged rows and columns
+    (129, 32768, 130, "bf16"),    # the longest row
+    (1000, 2048, 2048, "bf16"),   # many tiles, eight stages each
+    (2100, 16384, 64, "bf16"),    # a partial tile row at the bottom
+    (17, 64, 40, "fp32"),         # the shortest row: butterflies, 8 elements per thread
+    (100, 1024, 130, "fp32"),     # 16 elements per thread
+    (40, 4096, 96, "fp32"),       # few rows: 16 elements per thread
+    (300, 512, 200, "bf16"),      # bf16 below 2048: butterflies
+    (70, 16384, 64, "fp32"),      # 32 elements per thread
 ])
-def test_fp8_pair_forward_exact(M, K, N):
-    _say(f"fp8 pairs M={M} K={K} N={N}")
-    case = workloads.make_case(M, K, N, x_dtype="bf16", n_out=max(1, K // 100), factor=30.0,
+def test_fp8_pair_forward_exact(M, K, N, xdt):
+    _say(f"fp8 pairs M={M} K={K} N={N} x={xdt}")
+    case = workloads.make_case(M, K, N, x_dtype=xdt, n_out=max(1, K // 100), factor=30.0,
                                seed=M + K + N)
-    x = _to_dev_x(case["x"], "bf16")
+    x = _to_dev_x(case["x"], xdt)
     W = torch.from_numpy(case["W"]).to(DEV)
     Wp, alpha = bl.ternarize_weights(W)
     y = bl.hbitlinear_forward(x, Wp, alpha, 4, 1)
@@ -277,7 +284,7 @@ def test_fp8_pair_forward_exact(M, K, N):
     np.testing.assert_array_equal(y_np, y2.cpu().numpy())
     del y2
     t_ref, a_ref, _ = oracle.ternarize(case["W"])
-    x64 = oracle.widen_input(case["x"], "bf16")
+    x64 = oracle.widen_input(case["x"], xdt)
     q_ref, s_ref, p_ref = oracle.quantize_activations(oracle.fwht(x64), 4)
     assert_codes_match(codes.cpu().numpy(), q_ref, p_ref)
     rng = np.random.default_rng(3)

@@ -87,7 +87,9 @@ def _run(M, K, N, bits, had, x_dtype, swiglu, rms, gamma, seed):
     (1, 2560, 300, 8, 0, "bf16", False, True, True),     # decode row, RMSNorm only: one-wave kernel
     (16, 16384, 96, 4, 1, "bf16", True, True, False),    # batched decode, long rows
     (300, 1024, 260, 8, 1, "bf16", False, True, False),  # prefill tile, unit-weight norm
-    (129, 8192, 130, 4, 1, "bf16", True, True, True),    # Wdown-style prefill
+    (129, 8192, 130, 4, 1, "bf16", True, True, True),    # Wdown-style prefill (fp8-pair product)
+    (100, 512, 64, 4, 1, "fp32", True, True, True),      # fp8 pairs, 8 elements per thread
+    (40, 2048, 96, 4, 1, "bf16", False, True, True),     # fp8 pairs, few rows, 16 elements per thread
     (64, 4096, 200, 8, 0, "fp32", True, False, False),   # SwiGLU product only
     (3, 64, 17, 4, 0, "bf16", True, True, True),         # smallest K, ragged N (fused decode)
     (4, 4096, 90, 4, 0, "bf16", True, True, True),       # fused decode kernel, whole prologue
