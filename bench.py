@@ -242,6 +242,34 @@ def _measure_workload(torch, bl, key, dev, steps, warmup):
                                                  warmup) * 1e3
             # the same forward on one weight copy, served from the caches
             res["forward_us_warm"] = _time_steps(torch, lambda i: p.forward(bl, 0), steps, warmup) * 1e3
+        if wl.M > 1 and p.copies > 1:
+            # The batched TL2 forward (edge page: TL2 GEMV on a batch; no
+            # transform) on the TL2 re-encoding of each cold copy, against the
+            # 2-bit forward without the transform on the same input, and the
+            # 2-bit product of int8 codes (the TL2 product's code form).
+            Wt = [bl.pack_tl2(w) for w in p.Wp]
+            tws = torch.empty((bl.tl2_forward_workspace_bytes(wl.M, wl.K),), dtype=torch.uint8,
+                              device=dev)
+            t_ms = _time_steps(torch, lambda i: bl.hbitlinear_forward_tl2(
+                p.x, Wt[i % len(Wt)], p.alpha, wl.bits, out=p.y, workspace=tws), steps, warmup)
+            fws = torch.empty((max(1, bl.forward_workspace_bytes(wl.M, wl.K, wl.N, wl.bits, 0)),),
+                              dtype=torch.uint8, device=dev)
+            f_ms = _time_steps(torch, lambda i: bl.hbitlinear_forward(
+                p.x, p.Wp[i % p.copies], p.alpha, wl.bits, 0, out=p.y, workspace=fws), steps, warmup)
+            rs = torch.empty((wl.M,), dtype=torch.int32, device=dev)
+            c8, s8 = bl.quantize_activations(p.x, wl.bits, 0, rowsum=rs)
+            m8_ms = _time_steps(torch, lambda i: bl.ternary_linear_dequant(
+                c8, s8, p.Wp[i % p.copies], p.alpha, wl.bits, rowsum=rs, out=p.y), steps, warmup)
+            tbytes = Wt[0].numel()
+            res["tl2_no_transform"] = {
+                "forward_us": t_ms * 1e3,
+                "weight_bytes": tbytes,
+                "bits_per_weight": tbytes * 8 / (wl.N * wl.K),
+                "forward_2bit_us": f_ms * 1e3,
+                "product_2bit_int8_codes_us": m8_ms * 1e3,
+                "kernels": "quant_rows_kernel (TL2 code order) + tl2_gemv_kernel",
+            }
+            del Wt, tws, fws
     else:
         res["matmul_mfma_frac"] = res["matmul_TOPS"] / INT8_MFMA_PEAK_TOPS
     # The engine page's whole HBitLinear.forward: RMSNorm (unit weight plus a

@@ -28,5 +28,6 @@ from .api import (  # noqa: F401
     ternary_gemm_i32,
     ternary_linear_dequant,
     tl2_bytes,
+    tl2_forward_workspace_bytes,
 )
 from ._lib import BitNetError  # noqa: F401

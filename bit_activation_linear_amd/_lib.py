@@ -65,6 +65,9 @@ SIGNATURES = {
     "bitnet_kv_quantize_packed": (_int, [_ptr, _int, _i64, _i64, _i64, _int, _ptr, _ptr, _ptr,
                                          _ptr]),
     "bitnet_tl2_bytes": (_size, [_i64, _i64]),
+    "bitnet_tl2_forward_workspace_bytes": (_size, [_i64, _i64]),
+    "bitnet_hbitlinear_forward_tl2_batched": (_int, [_ptr, _int, _i64, _i64, _ptr, _i64, _ptr,
+                                                     _int, _ptr, _ptr, _size, _ptr]),
     "bitnet_pack_tl2": (_int, [_ptr, _i64, _i64, _ptr, _ptr]),
     "bitnet_hbitlinear_forward_tl2": (_int, [_ptr, _int, _i64, _i64, _ptr, _i64, _ptr, _int, _ptr,
                                              _ptr]),

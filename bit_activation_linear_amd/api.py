@@ -116,9 +116,14 @@ def pack_tl2(Wpacked: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch
     return out
 
 
+def tl2_forward_workspace_bytes(M: int, K: int) -> int:
+    return int(_lib.load().bitnet_tl2_forward_workspace_bytes(M, K))
+
+
 def hbitlinear_forward_tl2(x: torch.Tensor, Wtl2: torch.Tensor, alpha: torch.Tensor, bits: int,
-                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y fp32 [1, N]: the single-token forward (no transform) on TL2 weights."""
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y fp32 [M, N] (M <= 16): the forward (no transform) on TL2 weights."""
     _require(x, "x", (torch.float32, torch.bfloat16), 2)
     _require(Wtl2, "Wtl2", (torch.uint8,), 2)
     _require(alpha, "alpha", (torch.float32,), 1)
@@ -130,8 +135,15 @@ def hbitlinear_forward_tl2(x: torch.Tensor, Wtl2: torch.Tensor, alpha: torch.Ten
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _check_out(out, "out", torch.float32, (M, N), x.device)
-    _lib.call("bitnet_hbitlinear_forward_tl2", x.data_ptr(), _x_dtype(x), M, K, Wtl2.data_ptr(), N,
-              alpha.data_ptr(), int(bits), out.data_ptr(), _stream_ptr(x))
+    need = tl2_forward_workspace_bytes(M, K)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _check_workspace(workspace, need, x.device)
+    ws_ptr, ws_len = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
+    _lib.call("bitnet_hbitlinear_forward_tl2_batched", x.data_ptr(), _x_dtype(x), M, K,
+              Wtl2.data_ptr(), N, alpha.data_ptr(), int(bits), out.data_ptr(), ws_ptr, ws_len,
+              _stream_ptr(x))
     return out
 
 

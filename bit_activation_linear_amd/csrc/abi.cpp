@@ -675,4 +675,48 @@ bitnet_status bitnet_hbitlinear_forward_tl2(const void* x, bitnet_dtype x_dtype,
                     fn);
 }
 
+size_t bitnet_tl2_forward_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % 64 != 0 || M > bitnet::kDecodeMaxM) return 0;
+  if (M == 1 && K <= bitnet::kTl2MaxK) return 0;  // the single-token kernel
+  return round_up((size_t)M * (size_t)bitnet::tl2_code_row(K)) + 2 * round_up((size_t)M * 4);
+}
+
+bitnet_status bitnet_hbitlinear_forward_tl2_batched(const void* x, bitnet_dtype x_dtype,
+                                                    int64_t M, int64_t K, const uint8_t* Wtl2,
+                                                    int64_t N, const float* alpha, int bits,
+                                                    float* y, void* ws, size_t ws_bytes,
+                                                    hipStream_t stream) {
+  const char* fn = "bitnet_hbitlinear_forward_tl2_batched";
+  if (bitnet_status st = check_dims(fn, M, K, N)) return st;
+  if (bitnet_status st = check_quant_args(fn, K, bits, 0, x_dtype)) return st;
+  if (M > bitnet::kDecodeMaxM)
+    return fail(BITNET_ERR_UNSUPPORTED, "%s: M=%lld, the TL2 product takes at most %lld tokens",
+                fn, (long long)M, (long long)bitnet::kDecodeMaxM);
+  if (M == 0 || N == 0) return ok();
+  if (!x || !Wtl2 || !alpha || !y) return fail(BITNET_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  const size_t need = bitnet_tl2_forward_workspace_bytes(M, K);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(BITNET_ERR_INVALID_ARG, "%s: workspace %zu B < required %zu B", fn,
+                ws ? ws_bytes : (size_t)0, need);
+  if (!aligned(x, 16) || !aligned(Wtl2, 16) || (need > 0 && !aligned(ws, 16)) || !aligned(y, 4) ||
+      !aligned(alpha, 4))
+    return fail(BITNET_ERR_ALIGN, "%s: misaligned pointer", fn);
+  if (bitnet_status st = launch_guard(fn)) return st;
+  if (need == 0)
+    return hip_status(bitnet::launch_tl2_decode(x, (int)x_dtype, (int)K, Wtl2, N, alpha, bits, y,
+                                                stream),
+                      fn);
+  char* base = static_cast<char*>(ws);
+  int8_t* codes = reinterpret_cast<int8_t*>(base);
+  const size_t cbytes = round_up((size_t)M * (size_t)bitnet::tl2_code_row(K));
+  float* scales = reinterpret_cast<float*>(base + cbytes);
+  int32_t* rowsum = reinterpret_cast<int32_t*>(base + cbytes + round_up((size_t)M * 4));
+  hipError_t e = bitnet::launch_quantize_tl2_order(x, (int)x_dtype, M, (int)K, bits, codes, scales,
+                                                   rowsum, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(bitnet::launch_tl2_gemv(codes, scales, rowsum, M, (int)K, Wtl2, N, alpha, bits,
+                                            y, stream),
+                    fn);
+}
+
 }  // extern "C"

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ 
                                                          int8_t* __restrict__ codes,
                                                          float* __restrict__ scales, Prologue pro,
                                                          int32_t* __restrict__ rowsum,
-                                                         bool nib) {
+                                                         bool nib, bool tl2) {
   constexpr int T = 256;
   __shared__ float red[8];
   __shared__ int ired[4];
@@ -106,19 +106,36 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const XT* __restrict__ 
     mult = QConst<BITS>::c / sc;
   }
   if (t == 0) scales[row] = sc;
-  int8_t* crow = codes + (size_t)row * (nib ? K / 2 : K);
+  // TL2 order (the batched TL2 product's code form): rows of whole 384-code
+  // blocks, the code of weight 3 j + p of a block at its byte 128 p + j, the
+  // codes past K zero.
+  const int ktl2 = (K + kTl2BlockK - 1) / kTl2BlockK * kTl2BlockK;
+  int8_t* crow = codes + (size_t)row * (tl2 ? ktl2 : (nib ? K / 2 : K));
   int qs = 0;  // this thread's share of the code sum
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int idx = 8 * t + 8 * T * c;
     if (idx < K) {
       const uint2 w = quant_pack8<BITS>(v[c], mult);
-      if (nib)
+      if (tl2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = idx + e, kb = k / kTl2BlockK, r = k - kb * kTl2BlockK;
+          crow[kb * kTl2BlockK + 128 * (r % 3) + r / 3] =
+              (int8_t)(((e < 4 ? w.x : w.y) >> (8 * (e & 3))) & 0xFFu);
+        }
+      } else if (nib)
         *reinterpret_cast<unsigned*>(crow + (idx >> 1)) = nibble_word(w);
       else
         *reinterpret_cast<uint2*>(crow + idx) = w;
       qs = __builtin_amdgcn_sdot4((int)w.y, 0x01010101,
                                   __builtin_amdgcn_sdot4((int)w.x, 0x01010101, qs, false), false);
+    }
+  }
+  if (tl2) {
+    for (int k = K + t; k < ktl2; k += T) {
+      const int kb = k / kTl2BlockK, r = k - kb * kTl2BlockK;
+      crow[kb * kTl2BlockK + 128 * (r % 3) + r / 3] = 0;
     }
   }
   if (rowsum) {
@@ -419,21 +436,23 @@ hipError_t launch_had(const void* x, int64_t M, int K, int8_t* codes, float* sca
 
 template <typename XT, int BITS, int CH, bool PRO>
 hipError_t launch_rows_ch(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                          const Prologue& pro, hipStream_t stream, int32_t* rowsum, bool nib) {
+                          const Prologue& pro, hipStream_t stream, int32_t* rowsum, bool nib,
+                          bool tl2 = false) {
   quant_rows_kernel<XT, BITS, CH, PRO><<<dim3((unsigned)M), dim3(256), 0, stream>>>(
-      reinterpret_cast<const XT*>(x), K, codes, scales, pro, rowsum, nib);
+      reinterpret_cast<const XT*>(x), K, codes, scales, pro, rowsum, nib, tl2);
   return hipGetLastError();
 }
 
 template <typename XT, int BITS, bool PRO>
 hipError_t launch_rows(const void* x, int64_t M, int K, int8_t* codes, float* scales,
-                       const Prologue& pro, hipStream_t stream, int32_t* rowsum, bool nib) {
+                       const Prologue& pro, hipStream_t stream, int32_t* rowsum, bool nib,
+                       bool tl2 = false) {
   const int ch = (K + 2047) / 2048;
-  if (ch <= 1) return launch_rows_ch<XT, BITS, 1, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
-  if (ch <= 2) return launch_rows_ch<XT, BITS, 2, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
-  if (ch <= 4) return launch_rows_ch<XT, BITS, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
-  if (ch <= 8) return launch_rows_ch<XT, BITS, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
-  return launch_rows_ch<XT, BITS, 16, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib);
+  if (ch <= 1) return launch_rows_ch<XT, BITS, 1, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib, tl2);
+  if (ch <= 2) return launch_rows_ch<XT, BITS, 2, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib, tl2);
+  if (ch <= 4) return launch_rows_ch<XT, BITS, 4, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib, tl2);
+  if (ch <= 8) return launch_rows_ch<XT, BITS, 8, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib, tl2);
+  return launch_rows_ch<XT, BITS, 16, PRO>(x, M, K, codes, scales, pro, stream, rowsum, nib, tl2);
 }
 
 template <typename XT, bool PRO>
@@ -467,6 +486,17 @@ hipError_t launch_fwht_f32(const float* x, int64_t M, int K, float* out, hipStre
     case 1 << 15: return launch_fwht_f32_l<15>(x, M, out, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_quantize_tl2_order(const void* x, int x_dtype, int64_t M, int K, int bits,
+                                     int8_t* codes, float* scales, int32_t* rowsum,
+                                     hipStream_t stream) {
+  const Prologue none{nullptr, nullptr, 0.0f, 0};
+  if (x_dtype == 1)
+    return bits == 8 ? launch_rows<uint16_t, 8, false>(x, M, K, codes, scales, none, stream, rowsum, false, true)
+                     : launch_rows<uint16_t, 4, false>(x, M, K, codes, scales, none, stream, rowsum, false, true);
+  return bits == 8 ? launch_rows<float, 8, false>(x, M, K, codes, scales, none, stream, rowsum, false, true)
+                   : launch_rows<float, 4, false>(x, M, K, codes, scales, none, stream, rowsum, false, true);
 }
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t M, int K, int bits, int hadamard,

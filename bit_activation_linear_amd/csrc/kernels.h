@@ -201,6 +201,19 @@ inline size_t tl2_bytes(int64_t N, int64_t K) {
 // 2-bit packed weights [N, K/4] -> TL2 [N, tl2_bytes / N].
 hipError_t launch_repack_tl2(const uint8_t* Wpacked, int64_t N, int K, uint8_t* Wtl2,
                              hipStream_t stream);
+// Per-token quantization (no transform) with the codes in TL2 order: rows of
+// tl2_code_row(K) bytes, whole 384-code blocks, the code of weight 3 j + p of
+// a block at its byte 128 p + j, the codes past K zero; scales and row sums
+// as launch_quantize's.
+inline int64_t tl2_code_row(int64_t K) { return (K + kTl2BlockK - 1) / kTl2BlockK * kTl2BlockK; }
+hipError_t launch_quantize_tl2_order(const void* x, int x_dtype, int64_t M, int K, int bits,
+                                     int8_t* codes, float* scales, int32_t* rowsum,
+                                     hipStream_t stream);
+// Batched TL2 product (1 <= M <= 16) from TL2-order codes, their scales and
+// row sums: y [M, N].
+hipError_t launch_tl2_gemv(const int8_t* codes, const float* scales, const int32_t* rowsum,
+                           int64_t M, int K, const uint8_t* Wtl2, int64_t N, const float* alpha,
+                           int bits, float* y, hipStream_t stream);
 // Single-token decode forward (M = 1, no transform, K <= kTl2MaxK) on TL2 weights.
 hipError_t launch_tl2_decode(const void* x, int x_dtype, int K, const uint8_t* Wtl2, int64_t N,
                              const float* alpha, int bits, float* y, hipStream_t stream);

@@ -283,6 +283,105 @@ __global__ __launch_bounds__(64 * WV) void tl2_decode_kernel(const void* __restr
   if (grp == 0 && n < N) y[n] = (float)dot * dequant_factor(alpha, st, c);
 }
 
+// Batched TL2 product (the edge page's TL2 GEMV takes a batch of tokens):
+// y[m, n] for M <= 16 token rows from int8 codes in TL2 order (per row,
+// blocks of 384 codes, the code of weight 3 j + p of a block at its byte
+// 128 p + j, the codes past K zero) with the codes' row sums. A workgroup
+// owns 16 output columns and wave w the blocks w, w + NW, ...; per block a
+// lane (col, grp) loads its column's index and sign words of group grp and,
+// for token row col, the six 16-byte code operands (field p, half h: bytes
+// 128 p + 32 grp + 16 h of the block), so that MFMA k = 16 grp + e meets the
+// group's triplet 16 h + e in both operands, as in the single-token kernel.
+// Up to kTl2Rounds blocks' loads go out together; one barrier adds the
+// waves' tiles.
+constexpr int kTl2Rounds = 3;
+
+__global__ __launch_bounds__(1024) void tl2_gemv_kernel(const int8_t* __restrict__ codes,
+                                                       const float* __restrict__ scales,
+                                                       const int32_t* __restrict__ rowsum,
+                                                       const uint8_t* __restrict__ Wt,
+                                                       const float* __restrict__ alpha_p,
+                                                       float* __restrict__ y, int M, int K, int N,
+                                                       float c) {
+  __shared__ v4i red[16 * 64];
+  const int nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int nblk = (K + kTl2BlockK - 1) / kTl2BlockK;
+  const int ktl2 = nblk * kTl2BlockK;
+  const int n = blockIdx.x * 16 + col;
+  const uint8_t* wrow = Wt + (size_t)(n < N ? n : N - 1) * nblk * kTl2BlockBytes;
+  const int8_t* crow = codes + (size_t)(col < M ? col : M - 1) * ktl2;
+  // the epilogue's operands, fetched before the weight stream
+  const float alpha = *alpha_p;
+  float s_row[4];
+  int rs[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * grp + v < M ? 4 * grp + v : M - 1;
+    s_row[v] = scales[m];
+    rs[v] = rowsum[m];
+  }
+  v4i acc1 = v4i{0, 0, 0, 0}, acc4 = v4i{0, 0, 0, 0}, acc16 = v4i{0, 0, 0, 0};
+  auto round = [&](const int b0) {
+    uint4 widx[kTl2Rounds];
+    unsigned wsign[kTl2Rounds];
+    v4i a[kTl2Rounds][2][3];
+#pragma unroll
+    for (int r = 0; r < kTl2Rounds; ++r) {
+      const int b = b0 + r * nw;
+      const int bc = b < nblk ? b : nblk - 1;  // a dead block reloads the last one, unused
+      widx[r] = *reinterpret_cast<const uint4*>(wrow + (size_t)bc * kTl2BlockBytes + 16 * grp);
+      wsign[r] = *reinterpret_cast<const unsigned*>(wrow + (size_t)bc * kTl2BlockBytes + 64 + 4 * grp);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          a[r][h][p] = *reinterpret_cast<const v4i*>(crow + (size_t)bc * kTl2BlockK + 128 * p +
+                                                     32 * grp + 16 * h);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < kTl2Rounds; ++r) {
+      if (b0 + r * nw >= nblk) break;  // uniform
+      const unsigned iw[4] = {widx[r].x, widx[r].y, widx[r].z, widx[r].w};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4i u1, u4, u16;
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          const int slot = 4 * h + sl;
+          const unsigned idx4 = (iw[slot >> 1] >> (4 * (slot & 1))) & 0x0F0F0F0Fu;
+          const unsigned f = slot_fields(idx4, wsign[r], slot);
+          u1[sl] = (int)(f & 0x03030303u);
+          u4[sl] = (int)(f & 0x0C0C0C0Cu);
+          u16[sl] = (int)(f & 0x30303030u);
+        }
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[r][h][0], u1, acc1, 0, 0, 0);
+        acc4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[r][h][1], u4, acc4, 0, 0, 0);
+        acc16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[r][h][2], u16, acc16, 0, 0, 0);
+      }
+    }
+  };
+  // The first round is not inside the loop (a loop header would wait for
+  // every load in flight before the first one's use).
+  round(wave);
+  for (int b0 = wave + kTl2Rounds * nw; b0 < nblk; b0 += kTl2Rounds * nw) round(b0);
+  // q . u over the three scales (exact: acc4 holds multiples of 4, acc16 of 16)
+  red[wave * 64 + lane] = acc1 + (acc4 >> 2) + (acc16 >> 4);
+  lds_barrier();
+  if (wave != 0 || n >= N) return;
+  v4i total = red[lane];
+  for (int w = 1; w < nw; ++w) total += red[w * 64 + lane];
+  // 16x16 MFMA layout: lane l holds rows 4 (l / 16) + v, column l % 16
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * grp + v;
+    if (m < M) y[(size_t)m * N + n] = (float)(total[v] - rs[v]) * dequant_factor(alpha, s_row[v], c);
+  }
+}
+
 // Waves per 16 columns: one per super-block, at most four (measured at
 // K = 2560, four super-blocks: 4.8 us against 5.45 us with two waves of
 // two).
@@ -318,6 +417,18 @@ hipError_t launch_repack_tl2(const uint8_t* Wpacked, int64_t N, int K, uint8_t* 
   if (threads == 0) return hipSuccess;
   repack_tl2_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
       Wpacked, N, K, nblk, Wtl2);
+  return hipGetLastError();
+}
+
+hipError_t launch_tl2_gemv(const int8_t* codes, const float* scales, const int32_t* rowsum,
+                           int64_t M, int K, const uint8_t* Wtl2, int64_t N, const float* alpha,
+                           int bits, float* y, hipStream_t stream) {
+  if (M < 1 || M > 16 || K < 1) return hipErrorInvalidValue;
+  const int nblk = (K + kTl2BlockK - 1) / kTl2BlockK;
+  const int nw = nblk < 16 ? nblk : 16;
+  const float c = (bits == 8) ? kScaleInt8 : kScaleInt4;
+  tl2_gemv_kernel<<<dim3((unsigned)((N + 15) / 16)), dim3(64 * nw), 0, stream>>>(
+      codes, scales, rowsum, Wtl2, alpha, y, (int)M, K, (int)N, c);
   return hipGetLastError();
 }
 

@@ -273,6 +273,24 @@ bitnet_status bitnet_hbitlinear_forward_tl2(const void* x, bitnet_dtype x_dtype,
                                             const float* alpha, int bits, float* y,
                                             hipStream_t stream);
 
+/* Batched forward on TL2 weights. Edge page (bitnet_cpp_edge.py), class
+ * TL2KernelEdge, method compute_gemv, which takes a batch of tokens x [B, K]:
+ * the same result as bitnet_hbitlinear_forward with hadamard = 0 for
+ * 1 <= M <= 16 tokens and any K % 64 == 0 up to BITNET_MAX_K (per-token codes,
+ * exact int32 product, y = acc * alpha * s / c). One token with
+ * K <= 4608 runs the single-token kernel and needs no workspace; otherwise the
+ * tokens are quantized into ws (codes in the product's own order, scales and
+ * code row sums: bitnet_tl2_forward_workspace_bytes(M, K) bytes, 16-byte
+ * aligned, caller-owned, contents undefined afterwards) and the product runs
+ * 16 output columns per workgroup. M > 16: BITNET_ERR_UNSUPPORTED. x and Wtl2
+ * 16-byte aligned. */
+size_t bitnet_tl2_forward_workspace_bytes(int64_t M, int64_t K);
+bitnet_status bitnet_hbitlinear_forward_tl2_batched(const void* x, bitnet_dtype x_dtype,
+                                                    int64_t M, int64_t K, const uint8_t* Wtl2,
+                                                    int64_t N, const float* alpha, int bits,
+                                                    float* y, void* ws, size_t ws_bytes,
+                                                    hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Low-bit KV cache                                                          */
 /* ------------------------------------------------------------------------ */

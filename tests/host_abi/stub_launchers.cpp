@@ -55,6 +55,14 @@ hipError_t launch_ternary_matmul(const int8_t*, const float*, int64_t, int, cons
   return record(acc ? "matmul_i32"
                     : (fp8_pairs ? "matmul_fp8_pairs" : (nibbles ? "matmul_nibbles" : "matmul")));
 }
+hipError_t launch_quantize_tl2_order(const void*, int, int64_t, int, int, int8_t*, float*, int32_t*,
+                                     hipStream_t) {
+  return record("quantize_tl2_order");
+}
+hipError_t launch_tl2_gemv(const int8_t*, const float*, const int32_t*, int64_t, int, const uint8_t*,
+                           int64_t, const float*, int, float*, hipStream_t) {
+  return record("tl2_gemv");
+}
 hipError_t launch_gemv(const int8_t*, const float*, int64_t, int, const uint8_t*, int64_t,
                        const float*, int, float*, int32_t*, hipStream_t, bool, const int32_t*) {
   return record("gemv");

@@ -353,6 +353,25 @@ def test_tl2_sizes_and_validation(lib):
     assert f(None, _lib.BF16, 0, 256, None, 16, None, 8, None, None) == _lib.OK
 
 
+def test_tl2_batched_sizes_and_validation(lib):
+    w = lib.bitnet_tl2_forward_workspace_bytes
+    assert w(1, 2560) == 0                               # one token: the single-token kernel
+    assert w(1, 4672) == 5120 + 2 * 256                  # K past it: 4992 codes, 256-B rounded
+    assert w(16, 16384) == 16 * 16512 + 2 * 256          # 43 blocks of 384 codes per row
+    assert w(17, 64) == 0 and w(4, 100) == 0 and w(0, 64) == 0
+    f = lib.bitnet_hbitlinear_forward_tl2_batched
+    args = lambda M=4, K=512, x=FAKE, ws=FAKE, ws_bytes=1 << 30, bits=8: (
+        x, _lib.BF16, M, K, FAKE, 16, FAKE, bits, FAKE, ws, ws_bytes, None)
+    assert f(*args(M=17)) == _lib.ERR_UNSUPPORTED
+    assert f(*args(bits=5)) == _lib.ERR_BAD_BITS
+    assert f(*args(K=100)) == _lib.ERR_ALIGN
+    assert f(*args(x=None)) == _lib.ERR_INVALID_ARG
+    assert f(*args(ws=None, ws_bytes=0)) == _lib.ERR_INVALID_ARG
+    assert f(*args(ws_bytes=w(4, 512) - 1)) == _lib.ERR_INVALID_ARG
+    assert f(*args(ws=FAKE + 8)) == _lib.ERR_ALIGN
+    assert f(*args(M=0, x=None, ws=None, ws_bytes=0)) == _lib.OK
+
+
 def _stages(lib, stages, M=4, K=512, N=256, bits=4, had=1, x=FAKE, ws=FAKE, ws_bytes=1 << 30):
     return lib.bitnet_hbitlinear_forward_stages(x, _lib.BF16, M, K, FAKE, N, FAKE, bits, had, FAKE,
                                                 ws, ws_bytes, stages, None)
@@ -401,6 +420,8 @@ LAUNCHING_CALLS = {
     "bitnet_kv_quantize_packed": (FAKE, _lib.BF16, 16, 128, 8, 3, FAKE, FAKE, FAKE, None),
     "bitnet_pack_tl2": (FAKE, 4, 64, FAKE, None),
     "bitnet_hbitlinear_forward_tl2": (FAKE, _lib.BF16, 1, 256, FAKE, 16, FAKE, 8, FAKE, None),
+    "bitnet_hbitlinear_forward_tl2_batched": (FAKE, _lib.BF16, 4, 512, FAKE, 16, FAKE, 8, FAKE,
+                                              FAKE, 1 << 30, None),
     "bitnet_hbitlinear_backward": (FAKE, _lib.BF16, 128, 192, FAKE, FAKE, 256, FAKE, FAKE, 8, 1,
                                    FAKE, FAKE, FAKE, 1 << 30, None),
     "bitnet_stream_read": (FAKE, 1024, FAKE, None),
@@ -488,6 +509,11 @@ def test_forward_dispatch(lib, M, K, N, bits, had, want):
 def test_other_dispatch(lib):
     ws = ctypes.create_string_buffer(1 << 16)
     a = (ctypes.addressof(ws) + 255) // 256 * 256
+    tl2 = lib.bitnet_hbitlinear_forward_tl2_batched
+    assert _calls(lib, tl2, FAKE, _lib.BF16, 1, 2560, FAKE, 64, FAKE, 8, FAKE, None, 0,
+                  None) == ["tl2_decode"]
+    assert _calls(lib, tl2, FAKE, _lib.BF16, 4, 512, FAKE, 64, FAKE, 4, FAKE, a, 1 << 14,
+                  None) == ["quantize_tl2_order", "tl2_gemv"]
     assert _calls(lib, lib.bitnet_ternarize_weights, FAKE, 4, 64, FAKE, FAKE, a, 1 << 14,
                   None) == ["absmean_partial", "ternarize_pack"]
     assert _calls(lib, lib.bitnet_ternary_gemm_i32, FAKE, 2, 64, FAKE, 3, FAKE, None) == ["matmul_i32"]

@@ -4,7 +4,8 @@ SignedUnsignedWeightPacker) on the GPU, through the C ABI.
 * bitnet_pack_tl2 re-encodes the 2-bit weights; its bytes must equal the
   oracle's TL2 encoding of the same ternary weights, bit for bit.
 * bitnet_hbitlinear_forward_tl2 is the single-token decode forward on those
-  bytes. It takes the same quantization steps as the 2-bit single-token
+  bytes, and bitnet_hbitlinear_forward_tl2_batched the forward of up to 16
+  tokens (the same kernel for one token of K <= 4608). It takes the same quantization steps as the 2-bit single-token
   kernel: with int8 (absmax, order-free) its output must equal the 2-bit
   forward's bit for bit; with int4 the absmean sums in another order, and a
   code on a rounding boundary may move. Both are compared with the fp64
@@ -100,16 +101,68 @@ def test_forward_tl2_headline_full_size():
     assert Wt.numel() == 6912 * 7 * 80
 
 
+@pytest.mark.parametrize("M,K,N,bits,xdt", [
+    (2, 256, 40, 8, "bf16"),       # two tokens, one partial block
+    (4, 640, 33, 4, "fp32"),       # a partial second block, ragged N
+    (1, 8192, 50, 8, "bf16"),      # one token past the single-token kernel's K
+    (7, 4608, 100, 8, "fp32"),
+    (16, 16384, 64, 4, "bf16"),    # the batched decode's K: 43 blocks, the last one partial
+    (13, 32768, 30, 4, "bf16"),    # the longest row
+])
+def test_forward_tl2_batched(M, K, N, bits, xdt):
+    """The batched TL2 forward (edge page, TL2KernelEdge.compute_gemv on x [B, K]):
+    its codes are the public quantizer's, stored in the product's order, so
+    its output equals the 2-bit product of those codes bit for bit, and the
+    oracle's at the forward's tolerance."""
+    _say(f"forward_tl2 batched M={M} K={K} N={N} bits={bits} x={xdt}")
+    case = workloads.make_case(M, K, N, x_dtype=xdt, n_out=max(1, K // 100), factor=30.0,
+                               seed=M + K + N + bits)
+    x = _dev_x(case["x"], xdt)
+    W = torch.from_numpy(case["W"]).to(DEV)
+    Wp, alpha = bl.ternarize_weights(W)
+    Wt = bl.pack_tl2(Wp)
+    y_tl2 = bl.hbitlinear_forward_tl2(x, Wt, alpha, bits)
+    rowsum = torch.empty((M,), dtype=torch.int32, device=DEV)
+    codes, scales = bl.quantize_activations(x, bits, 0, rowsum=rowsum)
+    y_2b = bl.ternary_linear_dequant(codes, scales, Wp, alpha, bits, rowsum=rowsum)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y_tl2.cpu().numpy(), y_2b.cpu().numpy())
+    t_ref, a_ref, _ = oracle.ternarize(case["W"])
+    ref = oracle.forward(case["x"], xdt, t_ref, a_ref, bits, 0)
+    assert_y_in_band(y_tl2.cpu().numpy(), t_ref, ref["q"], ref["p"], t_ref, ref["s"], a_ref, bits,
+                     ref["y64"])
+
+
+def test_forward_tl2_batched_decode_full_size():
+    """The batched-decode shape (M=16, K=16384, N=4096) on TL2 weights, int4,
+    without the transform: 1.672 bits per weight (43 blocks of 80 bytes)."""
+    M, K, N = 16, 16384, 4096
+    case = workloads.make_case(M, K, N, x_dtype="bf16", dist="student_t3", n_out=100, factor=30.0,
+                               seed=11)
+    x = _dev_x(case["x"], "bf16")
+    W = torch.from_numpy(case["W"]).to(DEV)
+    Wp, alpha = bl.ternarize_weights(W)
+    Wt = bl.pack_tl2(Wp)
+    assert Wt.numel() == N * 43 * 80
+    y_tl2 = bl.hbitlinear_forward_tl2(x, Wt, alpha, 4)
+    rowsum = torch.empty((M,), dtype=torch.int32, device=DEV)
+    codes, scales = bl.quantize_activations(x, 4, 0, rowsum=rowsum)
+    y_2b = bl.ternary_linear_dequant(codes, scales, Wp, alpha, 4, rowsum=rowsum)
+    torch.cuda.synchronize()
+    del W
+    np.testing.assert_array_equal(y_tl2.cpu().numpy(), y_2b.cpu().numpy())
+    t_ref, a_ref, _ = oracle.ternarize(case["W"])
+    ref = oracle.forward(case["x"], "bf16", t_ref, a_ref, 4, 0)
+    assert_y_in_band(y_tl2.cpu().numpy(), t_ref, ref["q"], ref["p"], t_ref, ref["s"], a_ref, 4,
+                     ref["y64"])
+
+
 def test_forward_tl2_limits():
-    x = torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros((17, 256), dtype=torch.bfloat16, device=DEV)
     Wt = torch.zeros((16, bl.tl2_bytes(16, 256) // 16), dtype=torch.uint8, device=DEV)
     alpha = torch.ones((1,), dtype=torch.float32, device=DEV)
     with pytest.raises(bl.BitNetError):
-        bl.hbitlinear_forward_tl2(x, Wt, alpha, 8)                      # two tokens
-    x1 = torch.zeros((1, 4672), dtype=torch.bfloat16, device=DEV)
-    Wt1 = torch.zeros((16, bl.tl2_bytes(16, 4672) // 16), dtype=torch.uint8, device=DEV)
-    with pytest.raises(bl.BitNetError):
-        bl.hbitlinear_forward_tl2(x1, Wt1, alpha, 8)                    # K past 4608
+        bl.hbitlinear_forward_tl2(x, Wt, alpha, 8)                      # 17 tokens
     y = bl.hbitlinear_forward_tl2(torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV), Wt,
                                   alpha, 8)
     assert y.shape == (0, 16)
