@@ -1,4 +1,5 @@
-// TL2 ternary weight code (1.67 bits per weight) for single-token decode.
+// TL2 ternary weight code (1.67 bits per weight): re-encoding, the single-token
+// decode forward and the batched product (up to 16 tokens).
 //
 // Edge page (Quillan-Ronin bitnet_cpp_edge.py), module docstring item 2 and
 // class SignedUnsignedWeightPacker: the 27 states of a ternary triplet
