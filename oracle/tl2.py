@@ -17,7 +17,10 @@ Readings where the page is silent or does something this library does not:
   * The page keeps indices and sign bits in two byte arrays. The device
     layout below (blocks of 128 triplets, 64 bytes of 4-bit indices and 16
     bytes of sign bits) is a contract of this library, not of the page; it
-    stores exactly 5 bits per triplet.
+    stores exactly 5 bits per triplet. A row's last block holds only the
+    groups of 32 triplets (96 weights) that the row reaches, so the padding
+    is under 96 weights and 16 bytes per row (1.67 bits per weight at
+    K = 16384, 1.70 at K = 2560).
 
 Parity status: pinned (tests/test_oracle_tl2.py: the decoded states against
 the page's own table of base triplets (tests/golden/tl2_base_triplets.json)
@@ -42,6 +45,24 @@ N_STATES = 14
 TRIPLETS_PER_BLOCK = 128
 BLOCK_K = 3 * TRIPLETS_PER_BLOCK      # 384 weights per device block
 BLOCK_BYTES = 64 + 16                 # 4-bit indices, then sign bits
+GROUP_TRIPLETS = 32                   # a group: 16 index bytes and 4 sign bytes
+
+
+def block_groups(K: int):
+    """Groups (of 32 triplets) of each block of a row of K weights: 4 for the
+    whole blocks, then, for a partial last block, the ceil(rest / 96) groups
+    it reaches."""
+    full, rest = divmod(K, BLOCK_K)
+    return [4] * full + ([-(-rest // (3 * GROUP_TRIPLETS))] if rest else [])
+
+
+def block_bytes(groups: int) -> int:
+    """Bytes of a block of `groups` groups: 20 per group, rounded up to 16."""
+    return -(-20 * groups // 16) * 16
+
+
+def row_bytes(K: int) -> int:
+    return sum(block_bytes(g) for g in block_groups(K))
 
 
 def triplet_value(t: np.ndarray) -> np.ndarray:
@@ -86,54 +107,63 @@ def decode_triplets(idx: np.ndarray, sign: np.ndarray, K: int) -> np.ndarray:
     return triplets_of_value(v).reshape(N, 3 * T)[:, :K]
 
 
-def _slot(j: int):
-    """Byte/bit position of triplet j (0..127) of a device block.
+def _slot(j: int, groups: int = 4):
+    """Byte/bit position of triplet j (0 .. 32 groups - 1) of a device block of
+    `groups` groups.
 
     Triplet j = 32 g + 4 i + tt: its index is the nibble 4 (i % 2) of byte
-    16 g + 4 (i // 2) + tt, its sign is bit i of byte 64 + 4 g + tt."""
+    16 g + 4 (i // 2) + tt, its sign is bit i of byte 16 groups + 4 g + tt
+    (64 + 4 g + tt in a whole block)."""
     g, r = divmod(j, 32)
     i, tt = divmod(r, 4)
-    return 16 * g + 4 * (i // 2) + tt, 4 * (i % 2), 64 + 4 * g + tt, i
+    return 16 * g + 4 * (i // 2) + tt, 4 * (i % 2), 16 * groups + 4 * g + tt, i
 
 
 def pack(t: np.ndarray) -> np.ndarray:
-    """Device TL2 bytes [N, ceil(K/384) * 80] of ternary t [N, K]: block b holds
-    triplets 128 b .. 128 b + 127 (weights 384 b .. 384 b + 383; the part past
-    K is zero weights)."""
+    """Device TL2 bytes [N, row_bytes(K)] of ternary t [N, K]: block b holds
+    triplets 128 b .. (weights 384 b ..), the last block only the groups of
+    32 triplets the row reaches (the part past K is zero weights), and the
+    bytes a block is rounded up by are zero."""
     t = np.asarray(t)
     N, K = t.shape
-    nblk = (K + BLOCK_K - 1) // BLOCK_K
-    full = np.zeros((N, nblk * BLOCK_K), dtype=np.int8)
+    groups = block_groups(K)
+    ntrip = TRIPLETS_PER_BLOCK * (len(groups) - 1) + GROUP_TRIPLETS * groups[-1] if groups else 0
+    full = np.zeros((N, 3 * ntrip), dtype=np.int8)
     full[:, :K] = t
     idx, sign = encode_triplets(full)
-    out = np.zeros((N, nblk * BLOCK_BYTES), dtype=np.uint8)
+    out = np.zeros((N, row_bytes(K)), dtype=np.uint8)
     for n in range(N):
-        for b in range(nblk):
-            base = b * BLOCK_BYTES
-            for j in range(TRIPLETS_PER_BLOCK):
-                nb, sh, sb, bit = _slot(j)
+        base = 0
+        for b, gb in enumerate(groups):
+            for j in range(GROUP_TRIPLETS * gb):
+                nb, sh, sb, bit = _slot(j, gb)
                 tj = b * TRIPLETS_PER_BLOCK + j
                 out[n, base + nb] |= np.uint8(int(idx[n, tj]) << sh)
                 out[n, base + sb] |= np.uint8(int(sign[n, tj]) << bit)
+            base += block_bytes(gb)
     return out
 
 
 def unpack(packed: np.ndarray, K: int) -> np.ndarray:
-    """Ternary int8 [N, K] from device TL2 bytes."""
+    """Ternary int8 [N, K] from device TL2 bytes [N, row_bytes(K)]."""
     packed = np.asarray(packed, dtype=np.uint8)
-    N, nbytes = packed.shape
-    nblk = nbytes // BLOCK_BYTES
-    idx = np.zeros((N, nblk * TRIPLETS_PER_BLOCK), dtype=np.uint8)
+    N = packed.shape[0]
+    groups = block_groups(K)
+    if packed.shape[1] != row_bytes(K):
+        raise ValueError("not the TL2 bytes of a row of K weights")
+    ntrip = TRIPLETS_PER_BLOCK * len(groups)
+    idx = np.zeros((N, ntrip), dtype=np.uint8)
     sign = np.zeros_like(idx)
     for n in range(N):
-        for b in range(nblk):
-            base = b * BLOCK_BYTES
-            for j in range(TRIPLETS_PER_BLOCK):
-                nb, sh, sb, bit = _slot(j)
+        base = 0
+        for b, gb in enumerate(groups):
+            for j in range(GROUP_TRIPLETS * gb):
+                nb, sh, sb, bit = _slot(j, gb)
                 idx[n, b * TRIPLETS_PER_BLOCK + j] = (int(packed[n, base + nb]) >> sh) & 15
                 sign[n, b * TRIPLETS_PER_BLOCK + j] = (int(packed[n, base + sb]) >> bit) & 1
-    return decode_triplets(idx, sign, nblk * BLOCK_K)[:, :K]
+            base += block_bytes(gb)
+    return decode_triplets(idx, sign, 3 * ntrip)[:, :K]
 
 
 def packed_bytes(N: int, K: int) -> int:
-    return N * ((K + BLOCK_K - 1) // BLOCK_K) * BLOCK_BYTES
+    return N * row_bytes(K)

@@ -84,7 +84,7 @@ def test_round_trips(N, K):
     assert idx.shape == (N, (K + 2) // 3)
     np.testing.assert_array_equal(tl2.decode_triplets(idx, sign, K), t)
     packed = tl2.pack(t)
-    assert packed.shape == (N, ((K + 383) // 384) * 80)
+    assert packed.shape == (N, tl2.row_bytes(K))
     np.testing.assert_array_equal(tl2.unpack(packed, K), t)
 
 
@@ -93,6 +93,12 @@ def test_five_bits_per_three_weights():
     assert tl2.BLOCK_BYTES * 8 == tl2.TRIPLETS_PER_BLOCK * 5
     assert tl2.BLOCK_BYTES * 8 / tl2.BLOCK_K == pytest.approx(5 / 3)
     assert tl2.packed_bytes(6912, 2688) == 6912 * 7 * 80
+    # a partial last block keeps only the groups of 96 weights it reaches, 20
+    # bytes each rounded up to 16: K = 2560 is 6 whole blocks and 3 groups
+    assert tl2.block_groups(2560) == [4] * 6 + [3]
+    assert tl2.packed_bytes(6912, 2560) == 6912 * (6 * 80 + 64)
+    assert tl2.packed_bytes(1, 16384) == 42 * 80 + 64      # 1.672 bits per weight
+    assert [tl2.block_bytes(g) for g in (1, 2, 3, 4)] == [32, 48, 64, 80]
 
 
 def test_hand_built_block():
@@ -115,9 +121,28 @@ def test_hand_built_block():
 
 
 def test_padding_is_zero_weight():
-    # K = 2560 is not a multiple of 3 or 384: the pad encodes zero weights
+    # K = 2560 is not a multiple of 3 or 384: the last block's three groups
+    # reach weight 2592, and the pad encodes zero weights
     rng = np.random.default_rng(9)
     t = rng.integers(-1, 2, size=(2, 2560)).astype(np.int8)
-    full = tl2.unpack(tl2.pack(t), 7 * 384)
+    packed = tl2.pack(t)
+    assert tl2.row_bytes(2592) == packed.shape[1]
+    full = tl2.unpack(packed, 2592)
     np.testing.assert_array_equal(full[:, :2560], t)
     assert not full[:, 2560:].any()
+
+
+def test_hand_built_partial_block():
+    # K = 484: one whole block, then a block of two groups (48 bytes: indices
+    # at 0..31, signs at 32..39, zeros at 40..47)
+    K = 484
+    t = np.zeros((1, K), dtype=np.int8)
+    t[0, 384:387] = (1, 0, 0)    # triplet 128, the tail's triplet 0: index 9 -> byte 80 low nibble
+    t[0, 482] = -1               # triplet 160 (g = 1, i = 0, tt = 0) = (0, 0, -1): index 1, sign 1
+    packed = tl2.pack(t)
+    expect = np.zeros(80 + 48, dtype=np.uint8)
+    expect[80] = 9
+    expect[80 + 16] = 1
+    expect[80 + 32 + 4] = 1      # sign bit 0 of byte 16 G + 4 g + tt, G = 2
+    np.testing.assert_array_equal(packed[0], expect)
+    np.testing.assert_array_equal(tl2.unpack(packed, K), t)
