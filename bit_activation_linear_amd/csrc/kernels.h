@@ -191,13 +191,21 @@ hipError_t launch_codes_transpose(const int8_t* codes, int64_t M, int64_t K, int
 hipError_t launch_fwht_f32(const float* x, int64_t M, int K, float* out, hipStream_t stream);
 
 // TL2 weight code (edge page mirror consolidation, 5 bits per 3 weights):
-// blocks of 128 triplets per column (64 index bytes, 16 sign bytes).
+// blocks of 128 triplets per column (64 index bytes, 16 sign bytes); a
+// partial last block holds only its G groups of 32 triplets (96 weights):
+// 16 G index bytes, then 4 G sign bytes, rounded up to 16 bytes.
 constexpr int kTl2MaxK = 6 * 768;  // single-token TL2 decode: six 768-weight super-blocks
 constexpr int kTl2BlockK = 384;     // weights per block
 constexpr int kTl2BlockBytes = 80;  // 64 index bytes + 16 sign bytes
-inline size_t tl2_bytes(int64_t N, int64_t K) {
-  return (size_t)N * (size_t)((K + kTl2BlockK - 1) / kTl2BlockK) * kTl2BlockBytes;
+__host__ __device__ inline int tl2_last_groups(int64_t K) {  // groups of the last block
+  const int r = (int)(K % kTl2BlockK);
+  return r ? (r + 95) / 96 : 4;
 }
+__host__ __device__ inline int64_t tl2_row_bytes(int64_t K) {
+  const int g = tl2_last_groups(K);
+  return (K / kTl2BlockK) * kTl2BlockBytes + (K % kTl2BlockK ? (20 * g + 15) / 16 * 16 : 0);
+}
+inline size_t tl2_bytes(int64_t N, int64_t K) { return (size_t)N * (size_t)tl2_row_bytes(K); }
 // 2-bit packed weights [N, K/4] -> TL2 [N, tl2_bytes / N].
 hipError_t launch_repack_tl2(const uint8_t* Wpacked, int64_t N, int K, uint8_t* Wtl2,
                              hipStream_t stream);

@@ -9,14 +9,16 @@
 // balanced-ternary value 9 w0 + 3 w1 + w2, so a triplet of value v has index
 // |v| and sign v < 0.
 //
-// Device layout, per output column, in blocks of 128 triplets (384 weights;
-// the row is padded with zero weights to whole blocks): 64 bytes of 4-bit
-// indices, then 16 bytes of sign bits. Triplet j = 32 g + 4 i + tt (group g,
-// slot i, position tt) keeps its index in nibble i % 2 of byte
-// 16 g + 4 (i / 2) + tt and its sign in bit i of byte 64 + 4 g + tt. So the
-// four triplets of one slot sit in the four bytes of one index word (one mask
-// spreads them to byte lanes) and in bit i of the four bytes of one sign
-// word.
+// Device layout, per output column, in blocks of 128 triplets (384 weights):
+// 64 bytes of 4-bit indices, then 16 bytes of sign bits. Triplet
+// j = 32 g + 4 i + tt (group g, slot i, position tt) keeps its index in
+// nibble i % 2 of byte 16 g + 4 (i / 2) + tt and its sign in bit i of byte
+// 16 G + 4 g + tt, G = 4 groups in a whole block. A partial last block keeps
+// only the G groups (96 weights each) the row reaches, padded with zero
+// weights, its 20 G bytes rounded up to 16 with zeros: 1.67 bits per weight
+// at K = 16384, 1.70 at K = 2560. So the four triplets of one slot sit in the
+// four bytes of one index word (one mask spreads them to byte lanes) and in
+// bit i of the four bytes of one sign word.
 //
 // Decode product. As in the 2-bit single-token kernel, one wave owns 16
 // output columns and all of K, quantizes the token itself and runs
@@ -48,6 +50,7 @@ constexpr int kTl2SuperK = 768;       // weights per super-block (two blocks)
 // written.
 __global__ __launch_bounds__(256) void repack_tl2_kernel(const uint8_t* __restrict__ Wp,
                                                          int64_t N, int K, int nblk,
+                                                         int64_t row_bytes,
                                                          uint8_t* __restrict__ Wt) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = N * nblk * 4;
@@ -55,6 +58,13 @@ __global__ __launch_bounds__(256) void repack_tl2_kernel(const uint8_t* __restri
   const int g = (int)(tid & 3);
   const int b = (int)((tid >> 2) % nblk);
   const int64_t n = (tid >> 2) / nblk;
+  const int gb = b == nblk - 1 ? tl2_last_groups(K) : 4;  // groups of this block
+  uint8_t* out = Wt + n * row_bytes + (int64_t)b * kTl2BlockBytes;
+  if (g == 0) {  // the bytes the block is rounded up by are zero
+    for (int o = 20 * gb; o < (20 * gb + 15) / 16 * 16; o += 4)
+      *reinterpret_cast<unsigned*>(out + o) = 0u;
+  }
+  if (g >= gb) return;
   const uint8_t* row = Wp + n * (int64_t)(K >> 2);
   unsigned idxw[4] = {0u, 0u, 0u, 0u};
   unsigned signw = 0u;
@@ -78,9 +88,8 @@ __global__ __launch_bounds__(256) void repack_tl2_kernel(const uint8_t* __restri
     idxw[i >> 1] |= idx << (8 * tt + 4 * (i & 1));
     signw |= (v < 0 ? 1u : 0u) << (8 * tt + i);
   }
-  uint8_t* out = Wt + n * (int64_t)nblk * kTl2BlockBytes + (int64_t)b * kTl2BlockBytes;
   *reinterpret_cast<uint4*>(out + 16 * g) = make_uint4(idxw[0], idxw[1], idxw[2], idxw[3]);
-  *reinterpret_cast<unsigned*>(out + 64 + 4 * g) = signw;
+  *reinterpret_cast<unsigned*>(out + 16 * gb + 4 * g) = signw;
 }
 
 // Field byte u0 | u1 << 2 | u2 << 4 (u = w + 1) of base triplets 0-7 and
@@ -161,14 +170,18 @@ __global__ __launch_bounds__(64 * WV) void tl2_decode_kernel(const void* __restr
   {
     const int n = blockIdx.x * 16 + col;
     const int nc = n < N ? n : N - 1;
-    const uint8_t* wrow = Wt + (size_t)nc * NB * kTl2BlockBytes;
+    const uint8_t* wrow = Wt + (size_t)nc * tl2_row_bytes(K);
+    const int glast = tl2_last_groups(K);
 #pragma unroll
     for (int b = 0; b < 2 * NSW; ++b) {
-      // a block past the row's end meets all-zero codes below
-      const int bg = 2 * s0 + b;
-      const uint8_t* blk = wrow + (bg < NB ? bg : NB - 1) * kTl2BlockBytes;
-      widx[b] = *reinterpret_cast<const uint4*>(blk + 16 * grp);
-      wsign[b] = *reinterpret_cast<const unsigned*>(blk + 64 + 4 * grp);
+      // a block past the row's end, and a group past a partial last block's,
+      // meet all-zero codes below
+      const int bg = 2 * s0 + b < NB ? 2 * s0 + b : NB - 1;
+      const int gb = bg == NB - 1 ? glast : 4;
+      const int gs = grp < gb ? grp : gb - 1;
+      const uint8_t* blk = wrow + bg * kTl2BlockBytes;
+      widx[b] = *reinterpret_cast<const uint4*>(blk + 16 * gs);
+      wsign[b] = *reinterpret_cast<const unsigned*>(blk + 16 * gb + 4 * gs);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -312,7 +325,8 @@ __global__ __launch_bounds__(1024) void tl2_gemv_kernel(const int8_t* __restrict
   const int nblk = (K + kTl2BlockK - 1) / kTl2BlockK;
   const int ktl2 = nblk * kTl2BlockK;
   const int n = blockIdx.x * 16 + col;
-  const uint8_t* wrow = Wt + (size_t)(n < N ? n : N - 1) * nblk * kTl2BlockBytes;
+  const uint8_t* wrow = Wt + (size_t)(n < N ? n : N - 1) * tl2_row_bytes(K);
+  const int glast = tl2_last_groups(K);
   const int8_t* crow = codes + (size_t)(col < M ? col : M - 1) * ktl2;
   // the epilogue's operands, fetched before the weight stream
   const float alpha = *alpha_p;
@@ -333,8 +347,12 @@ __global__ __launch_bounds__(1024) void tl2_gemv_kernel(const int8_t* __restrict
     for (int r = 0; r < kTl2Rounds; ++r) {
       const int b = b0 + r * nw;
       const int bc = b < nblk ? b : nblk - 1;  // a dead block reloads the last one, unused
-      widx[r] = *reinterpret_cast<const uint4*>(wrow + (size_t)bc * kTl2BlockBytes + 16 * grp);
-      wsign[r] = *reinterpret_cast<const unsigned*>(wrow + (size_t)bc * kTl2BlockBytes + 64 + 4 * grp);
+      // a group past a partial last block's reloads its last group (its codes are zero)
+      const int gb = bc == nblk - 1 ? glast : 4;
+      const int gs = grp < gb ? grp : gb - 1;
+      widx[r] = *reinterpret_cast<const uint4*>(wrow + (size_t)bc * kTl2BlockBytes + 16 * gs);
+      wsign[r] = *reinterpret_cast<const unsigned*>(wrow + (size_t)bc * kTl2BlockBytes + 16 * gb +
+                                                    4 * gs);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -417,7 +435,7 @@ hipError_t launch_repack_tl2(const uint8_t* Wpacked, int64_t N, int K, uint8_t* 
   const int64_t threads = N * nblk * 4;
   if (threads == 0) return hipSuccess;
   repack_tl2_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
-      Wpacked, N, K, nblk, Wtl2);
+      Wpacked, N, K, nblk, tl2_row_bytes(K), Wtl2);
   return hipGetLastError();
 }
 

@@ -247,11 +247,14 @@ bitnet_status bitnet_quantize_activations_prologue(const void* x, const void* up
  * SignedUnsignedWeightPacker: a ternary triplet (w0, w1, w2) is stored as the
  * 4-bit index (0..13) of one of the page's 14 base triplets (all zero, or
  * first non-zero element +1) and a sign bit that negates it, 5 bits per 3
- * weights. Layout per output column: ceil(K / 384) blocks of 80 bytes, block
- * b covering weights 384 b .. 384 b + 383 (triplet j: weights 384 b + 3 j +
- * 0..2; weights past K are zero). Triplet j = 32 g + 4 i + tt keeps its index
- * in bits 4 (i % 2) .. +3 of byte 16 g + 4 (i / 2) + tt and its sign in bit i
- * of byte 64 + 4 g + tt. The row of a column is ceil(K / 384) * 80 bytes. */
+ * weights. Layout per output column: blocks b covering weights 384 b ..
+ * 384 b + 383 (triplet j: weights 384 b + 3 j + 0..2; weights past K are
+ * zero), each of G groups of 32 triplets: G = 4 for a whole block (80 bytes),
+ * and for a partial last block the ceil((K % 384) / 96) groups it reaches,
+ * its 20 G bytes rounded up to 16 with zeros. Triplet j = 32 g + 4 i + tt
+ * keeps its index in bits 4 (i % 2) .. +3 of byte 16 g + 4 (i / 2) + tt and
+ * its sign in bit i of byte 16 G + 4 g + tt. The row of a column is
+ * bitnet_tl2_bytes(1, K) bytes (1.67 bits per weight at K = 16384). */
 
 /* Bytes of a TL2 weight buffer for [N, K] (0 for invalid sizes). */
 size_t bitnet_tl2_bytes(int64_t N, int64_t K);

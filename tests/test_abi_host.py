@@ -335,8 +335,10 @@ def test_backward_optional_outputs(lib):
 
 def test_tl2_sizes_and_validation(lib):
     # 80 bytes per column and 384-weight block (5 bits per 3 weights)
-    assert lib.bitnet_tl2_bytes(6912, 2560) == 6912 * 7 * 80
+    assert lib.bitnet_tl2_bytes(6912, 2560) == 6912 * (6 * 80 + 64)   # a last block of 3 groups
     assert lib.bitnet_tl2_bytes(3, 384) == 3 * 80
+    assert lib.bitnet_tl2_bytes(2, 448) == 2 * (80 + 32)             # ... of 1 group
+    assert lib.bitnet_tl2_bytes(1, 16384) == 42 * 80 + 64
     assert lib.bitnet_tl2_bytes(3, 100) == 0            # K not a multiple of 64
     assert lib.bitnet_tl2_bytes(0, 64) == 0
     p = lib.bitnet_pack_tl2

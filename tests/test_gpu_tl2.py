@@ -40,7 +40,7 @@ def _dev_x(x_np, x_dtype):
 
 
 @pytest.mark.parametrize("N,K", [(16, 64), (37, 384), (5, 448), (64, 2560), (3, 4608), (2, 8192),
-                                 (130, 1152)])
+                                 (130, 1152), (7, 320)])
 def test_pack_tl2_matches_oracle(N, K):
     _say(f"pack_tl2 N={N} K={K}")
     rng = np.random.default_rng(N * 7 + K)
@@ -54,7 +54,8 @@ def test_pack_tl2_matches_oracle(N, K):
 
 
 @pytest.mark.parametrize("K,N,bits,xdt", [
-    (64, 16, 8, "bf16"),       # one partial block, one super-block
+    (64, 16, 8, "bf16"),       # one partial block of one group, one super-block
+    (320, 24, 8, "fp32"),      # a partial block of four groups
     (384, 50, 8, "fp32"),      # one whole block, ragged N
     (640, 33, 4, "bf16"),
     (2560, 200, 8, "bf16"),    # the headline's K: 7 blocks, the 8th padding
@@ -97,12 +98,13 @@ def test_forward_tl2_headline_full_size():
     t_ref, a_ref, _ = oracle.ternarize(case["W"])
     ref = oracle.forward(case["x"], wl.x_dtype, t_ref, a_ref, wl.bits, 0)
     assert_y_close(y_tl2.cpu().numpy(), ref["y64"], what="TL2 headline vs oracle")
-    # 1.67 bits per weight, plus the zero padding of the last block
-    assert Wt.numel() == 6912 * 7 * 80
+    # 1.67 bits per weight, the last block holding the three groups it reaches
+    assert Wt.numel() == 6912 * (6 * 80 + 64)
 
 
 @pytest.mark.parametrize("M,K,N,bits,xdt", [
-    (2, 256, 40, 8, "bf16"),       # two tokens, one partial block
+    (2, 256, 40, 8, "bf16"),       # two tokens, one partial block (three groups)
+    (5, 448, 40, 8, "bf16"),       # a last block of one group
     (4, 640, 33, 4, "fp32"),       # a partial second block, ragged N
     (1, 8192, 50, 8, "bf16"),      # one token past the single-token kernel's K
     (7, 4608, 100, 8, "fp32"),
@@ -135,7 +137,8 @@ def test_forward_tl2_batched(M, K, N, bits, xdt):
 
 def test_forward_tl2_batched_decode_full_size():
     """The batched-decode shape (M=16, K=16384, N=4096) on TL2 weights, int4,
-    without the transform: 1.672 bits per weight (43 blocks of 80 bytes)."""
+    without the transform: 1.672 bits per weight (42 blocks of 80 bytes and a
+    last block of three groups)."""
     M, K, N = 16, 16384, 4096
     case = workloads.make_case(M, K, N, x_dtype="bf16", dist="student_t3", n_out=100, factor=30.0,
                                seed=11)
@@ -143,7 +146,7 @@ def test_forward_tl2_batched_decode_full_size():
     W = torch.from_numpy(case["W"]).to(DEV)
     Wp, alpha = bl.ternarize_weights(W)
     Wt = bl.pack_tl2(Wp)
-    assert Wt.numel() == N * 43 * 80
+    assert Wt.numel() == N * (42 * 80 + 64)
     y_tl2 = bl.hbitlinear_forward_tl2(x, Wt, alpha, 4)
     rowsum = torch.empty((M,), dtype=torch.int32, device=DEV)
     codes, scales = bl.quantize_activations(x, 4, 0, rowsum=rowsum)
