@@ -71,10 +71,11 @@
 // with byte 16 + e % 16 of that lane group when g = 1 (measured with a
 // layout probe), so lane group g's fp8 operand is the block's bytes 16 g ..
 // 16 g + 15 and then 32 + 16 g .. 32 + 16 g + 15: the same two 16-byte
-// chunks as its two int8 sub-steps. Measured at M = 2048, K = 8192, N = 2048: half as many
-// MFMA instructions, and a quarter of the unpacking, take the product from
-// 39 to 34 us (a timing variant with fp6 codes, whose MFMA runs twice as
-// fast, measured the same: the matrix pipe is not what holds this product).
+// chunks as its two int8 sub-steps. Measured at M = 2048, K = 8192,
+// N = 2048: half as many MFMA instructions and half the unpacking (a shift
+// and a mask per eight weights instead of four) take the product from 39 to
+// 34 us (a timing variant with fp6 codes, whose MFMA runs twice as fast,
+// measured the same: the matrix pipe is not what holds this product).
 //
 // Tile order. Workgroups are dispatched round-robin over the eight XCDs
 // (each with its own L2), so workgroup L runs on XCD L % 8. Each XCD gets a
