@@ -702,6 +702,87 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(
   gemv_finish<CT, false>(a, acc, red, s_row, no_rs, nw, alpha);
 }
 
+// The product of the single-token decode on the vector ALU: lane (c, g) owns
+// column c's 64-weight block 4 sb + g, whose codes lanes 16 g .. 16 g + 15 of
+// its own DPP row quantized (four consecutive codes each). Each packed dword
+// d of the block holds, in field j of byte e, the weight at 16 j + 4 d + e,
+// whose code sits in byte e of row lane 4 j + d's code word: one v_dot4c
+// with that lane's word broadcast by DPP (row_newbcast) and the field masked
+// in place (worth u, 4u or 16u) per four weights. The four row partials of a
+// column are then added across rows.
+template <int NSB>
+__device__ __forceinline__ void wave_decode_dot(const GemvArgs& a, const uint4 (&p)[NSB],
+                                                const unsigned (&cw)[NSB], int qsum, float alpha,
+                                                float st, int lane) {
+  qsum = wave_sum_int(qsum);
+  int acc1 = 0, acc4 = 0, acc16a = 0, acc16b = 0;
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    // One block per super-block, with the wait states the compiler cannot
+    // insert for instructions it does not see: every VGPR a DPP instruction
+    // reads (the code word, the masked field and the accumulator alike) must
+    // have been written at least two instructions earlier, which the leading
+    // s_nop gives for whatever the compiler places just before the block
+    // (inside it the fields are all masked before the first dot); and a dot
+    // product's result must wait three before another instruction reads it,
+    // which the trailing s_nop gives (within the block each accumulator is
+    // read only by the next dot into it, which needs no wait).
+    const uint4 pw = p[sb];
+    int t[16];
+    asm volatile(
+        "s_nop 1\n"
+        "v_and_b32 %[t0], 0x03030303, %[px]\n"
+        "v_and_b32 %[t1], 0x0c0c0c0c, %[px]\n"
+        "v_and_b32 %[t2], 0x30303030, %[px]\n"
+        "v_lshrrev_b32 %[t3], 2, %[px]\n"
+        "v_and_b32 %[t4], 0x03030303, %[py]\n"
+        "v_and_b32 %[t5], 0x0c0c0c0c, %[py]\n"
+        "v_and_b32 %[t6], 0x30303030, %[py]\n"
+        "v_lshrrev_b32 %[t7], 2, %[py]\n"
+        "v_and_b32 %[t8], 0x03030303, %[pz]\n"
+        "v_and_b32 %[t9], 0x0c0c0c0c, %[pz]\n"
+        "v_and_b32 %[t10], 0x30303030, %[pz]\n"
+        "v_lshrrev_b32 %[t11], 2, %[pz]\n"
+        "v_and_b32 %[t12], 0x03030303, %[pw]\n"
+        "v_and_b32 %[t13], 0x0c0c0c0c, %[pw]\n"
+        "v_and_b32 %[t14], 0x30303030, %[pw]\n"
+        "v_lshrrev_b32 %[t15], 2, %[pw]\n"
+        "v_and_b32 %[t3], 0x30303030, %[t3]\n"
+        "v_and_b32 %[t7], 0x30303030, %[t7]\n"
+        "v_and_b32 %[t11], 0x30303030, %[t11]\n"
+        "v_and_b32 %[t15], 0x30303030, %[t15]\n"
+        "v_dot4c_i32_i8_dpp %[a1], %[c], %[t0] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a4], %[c], %[t1] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a16], %[c], %[t2] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[b16], %[c], %[t3] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a1], %[c], %[t4] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a4], %[c], %[t5] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a16], %[c], %[t6] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[b16], %[c], %[t7] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a1], %[c], %[t8] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a4], %[c], %[t9] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a16], %[c], %[t10] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[b16], %[c], %[t11] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a1], %[c], %[t12] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a4], %[c], %[t13] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[a16], %[c], %[t14] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_dot4c_i32_i8_dpp %[b16], %[c], %[t15] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        "s_nop 2"
+        : [a1] "+v"(acc1), [a4] "+v"(acc4), [a16] "+v"(acc16a), [b16] "+v"(acc16b),
+          [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]),
+          [t4] "=&v"(t[4]), [t5] "=&v"(t[5]), [t6] "=&v"(t[6]), [t7] "=&v"(t[7]),
+          [t8] "=&v"(t[8]), [t9] "=&v"(t[9]), [t10] "=&v"(t[10]), [t11] "=&v"(t[11]),
+          [t12] "=&v"(t[12]), [t13] "=&v"(t[13]), [t14] "=&v"(t[14]), [t15] "=&v"(t[15])
+        : [c] "v"(cw[sb]), [px] "v"(pw.x), [py] "v"(pw.y), [pz] "v"(pw.z), [pw] "v"(pw.w));
+  }
+  // each partial is a multiple of its field's weight, so the shifts are exact
+  int part = acc1 + (acc4 >> 2) + ((acc16a + acc16b) >> 4);
+  part += __shfl_xor(part, 16);
+  part += __shfl_xor(part, 32);
+  const int n = blockIdx.x * 16 + lane;
+  if (lane < 16 && n < a.N) a.y[n] = (float)(part - qsum) * dequant_factor(alpha, st, a.c);
+}
+
 // Single-token decode forward, one wave per 16 output columns and all of K
 // (NSB 256-k super-blocks, NSB <= 16). Every x value the wave needs fits in
 // its registers, so it computes the whole-row statistic itself (DPP),
@@ -716,7 +797,11 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(
 // With RMS, the layer input is RMSNorm'd first (engine page HBitLinear.forward
 // step 1; gamma may be null for unit weight): the sum of squares is one more
 // DPP reduction and 1/rms enters only the scale and the code multiplier, as
-// in the other quantizer kernels.
+// in the other quantizer kernels. That variant multiplies on the vector ALU
+// (wave_decode_dot: no LDS round trip, no MFMA), which measured faster for it
+// (3.68 -> 3.60 us at K = 2560, N = 6912) and slower without RMSNorm (3.18 ->
+// 3.37 us), where the MFMAs overlap the unpacking better than the extra dot
+// instructions do.
 template <typename XT, int BITS, int NSB, bool RMS, bool FULL>
 __device__ __forceinline__ void wave_decode(const GemvArgs& a, const float* gamma,
                                             float norm_eps) {
@@ -801,6 +886,7 @@ __device__ __forceinline__ void wave_decode(const GemvArgs& a, const float* gamm
   const float lo = kMagic + ((BITS == 8) ? -128.0f : -8.0f);
   const float hi = kMagic + ((BITS == 8) ? 127.0f : 7.0f);
   int qsum = 0;  // this lane's share of the code row sum
+  unsigned cw[NSB];
 #pragma unroll
   for (int sb = 0; sb < NSB; ++sb) {
     const bool own = FULL || 256 * sb + 4 * lane < a.K;
@@ -816,7 +902,12 @@ __device__ __forceinline__ void wave_decode(const GemvArgs& a, const float* gamm
     const unsigned w23 = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
     const unsigned word = own ? (w01 | w23) : 0u;
     qsum = __builtin_amdgcn_sdot4((int)word, 0x01010101, qsum, false);
-    *reinterpret_cast<unsigned*>(qw + sb * 256 + 4 * lane) = word;
+    cw[sb] = word;
+    if constexpr (!RMS) *reinterpret_cast<unsigned*>(qw + sb * 256 + 4 * lane) = word;
+  }
+  if constexpr (RMS) {
+    wave_decode_dot<NSB>(a, p, cw, qsum, alpha, st, lane);
+    return;
   }
   if (lane < 16) *reinterpret_cast<unsigned*>(qw + NSB * 256 + 4 * lane) = 0u;
   // Codes written by this wave are read back by other lanes of it; LDS serves

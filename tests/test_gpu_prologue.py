@@ -85,6 +85,9 @@ def _run(M, K, N, bits, had, x_dtype, swiglu, rms, gamma, seed):
     (2, 128, 50, 8, 1, "bf16", True, True, True),        # fused with the transform
     (1, 256, 64, 4, 1, "fp32", False, True, False),      # fused with the transform, one row
     (1, 2560, 300, 8, 0, "bf16", False, True, True),     # decode row, RMSNorm only: one-wave kernel
+    (1, 1088, 77, 4, 0, "fp32", False, True, True),      # one-wave kernel, int4, partial super-block
+    (1, 64, 33, 8, 0, "bf16", False, True, False),       # one-wave kernel, a single 64-weight block
+    (1, 4096, 40, 4, 0, "bf16", False, True, True),      # one-wave kernel, sixteen super-blocks
     (16, 16384, 96, 4, 1, "bf16", True, True, False),    # batched decode, long rows
     (300, 1024, 260, 8, 1, "bf16", False, True, False),  # prefill tile, unit-weight norm
     (129, 8192, 130, 4, 1, "bf16", True, True, True),    # Wdown-style prefill (fp8-pair product)
