@@ -702,6 +702,41 @@ __global__ __launch_bounds__(1024) void fused_decode_kernel(
   gemv_finish<CT, false>(a, acc, red, s_row, no_rs, nw, alpha);
 }
 
+// max(|a|, |b|, c) in one instruction. Written with fmaxf, each operand is
+// first quieted (one more instruction per value in IEEE mode), although no
+// NaN reaches the statistic.
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Wave-wide max of non-negative values in the DPP steps of wave_reduce, each
+// one v_max_f32 with its first operand routed by DPP (wave_reduce moves the
+// neighbour first and quiets it before the max). The s_nops are the wait
+// states a DPP read of a VALU-written register needs, which the compiler does
+// not insert for instructions it does not see; the last one precedes the
+// readlane. The max of a set does not depend on its order, so the result is
+// wave_reduce<true>'s bit for bit.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n"
+      "s_nop 1"
+      : "+v"(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // The product of the single-token decode on the vector ALU: lane (c, g) owns
 // column c's 64-weight block 4 sb + g, whose codes lanes 16 g .. 16 g + 15 of
 // its own DPP row quantized (four consecutive codes each). Each packed dword
@@ -857,16 +892,15 @@ __device__ __forceinline__ void wave_decode(const GemvArgs& a, const float* gamm
         v[sb][e] *= g[e];
       }
     }
-    float sr;
     if (BITS == 8) {
-      sr = fmaxf(fmaxf(fabsf(v[sb][0]), fabsf(v[sb][1])), fmaxf(fabsf(v[sb][2]), fabsf(v[sb][3])));
-      st = fmaxf(st, own ? sr : 0.0f);
+      const float m = max3_abs(v[sb][2], v[sb][3], max3_abs(v[sb][0], v[sb][1], st));
+      st = own ? m : st;
     } else {
-      sr = (fabsf(v[sb][0]) + fabsf(v[sb][1])) + (fabsf(v[sb][2]) + fabsf(v[sb][3]));
+      const float sr = (fabsf(v[sb][0]) + fabsf(v[sb][1])) + (fabsf(v[sb][2]) + fabsf(v[sb][3]));
       st += own ? sr : 0.0f;
     }
   }
-  st = (BITS == 8) ? wave_reduce<true>(st) : wave_reduce<false>(st);
+  st = (BITS == 8) ? wave_max_nonneg(st) : wave_reduce<false>(st);
   if (BITS == 4) st = st / (float)a.K;
   float mult;
   if constexpr (RMS) {
