@@ -127,6 +127,7 @@ def _run_case(M, K, N, bits, had, x_dtype, seed, dist="normal", n_out=0, factor=
     (4, 1024, 70, 8, 0, "fp32"),       # multi-wave fused kernel, four rows
     (1, 4096, 50, 4, 0, "fp32"),       # one-wave kernel (single token), sixteen super-blocks
     (1, 1344, 77, 8, 0, "bf16"),       # one-wave kernel, 21 blocks: a partial last super-block
+    (1, 2624, 90, 8, 0, "fp32"),       # one-wave kernel, fp32 input, one block in the last super-block
     (3, 1344, 40, 8, 0, "bf16"),       # multi-wave fused kernel, partial last super-block
     (4, 32768, 70, 4, 1, "bf16"),      # nibble codes by pairs of super-blocks, two rounds per wave
     (16, 24576, 33, 4, 0, "bf16"),     # pairs, three per wave: a second round half live
@@ -320,6 +321,48 @@ def test_zero_rows_and_constant_weights():
     assert np.all(decode_packed(Wp.cpu().numpy()) == -1)
     assert torch.count_nonzero(codes[3]).item() == 0 and torch.count_nonzero(y[17]).item() == 0
     assert scales[3].item() == pytest.approx(1e-7)
+
+
+@pytest.mark.parametrize("K,last_only,rms", [(2560, False, False), (1344, True, False),
+                                              (1344, True, True), (2560, False, True)])
+def test_single_token_statistic_edges(K, last_only, rms):
+    """The one-wave kernel on a zero token (statistic 0: s = eps, every code
+    0, y = 0) and on a token whose only non-zero value is its last element,
+    inside a partial last super-block (lanes past K must not enter the max):
+    bit for bit the two-stage forward, codes as the oracle's."""
+    _say(f"single-token statistic edges K={K} last_only={last_only} rms={rms}")
+    N = 70
+    rng = np.random.default_rng(K + 7)
+    W = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(DEV)
+    Wp, alpha = bl.ternarize_weights(W)
+    x_np = np.zeros((1, K), dtype=np.float32)
+    if last_only:
+        x_np[0, K - 1] = -3.0
+    x = torch.from_numpy(x_np).to(DEV).to(torch.bfloat16)
+    if rms:
+        y = bl.hbitlinear_forward_prologue(x, Wp, alpha, 8, 0, rmsnorm=True)
+        torch.cuda.synchronize()
+        assert torch.isfinite(y).all()
+        if not last_only:
+            assert torch.count_nonzero(y).item() == 0
+            return
+        t_ref, a_ref, _ = oracle.ternarize(W.cpu().numpy())
+        ref = oracle.forward_prologue(x_np, "fp32", t_ref, a_ref, 8, 0, rms=True)
+        assert_y_close(y.cpu().numpy(), ref["y64"], what="RMSNorm single token, one value",
+                       tol=1e-3)
+        return
+    y = bl.hbitlinear_forward(x, Wp, alpha, 8, 0)
+    codes, scales = bl.quantize_activations(x, 8, 0)
+    y2 = bl.ternary_linear_dequant(codes, scales, Wp, alpha, 8)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), y2.cpu().numpy())
+    q_ref, _, _ = oracle.quantize_activations(x_np.astype(np.float64), 8)
+    q = codes.cpu().numpy()
+    np.testing.assert_array_equal(q, q_ref)
+    if last_only:
+        assert q[0, K - 1] == -127 and np.count_nonzero(q) == 1
+    else:
+        assert np.count_nonzero(q) == 0 and torch.count_nonzero(y).item() == 0
 
 
 def test_empty_batch_is_noop():
