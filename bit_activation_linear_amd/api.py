@@ -327,10 +327,8 @@ def kv_quantize(kv: torch.Tensor, bits: int, codes: Optional[torch.Tensor] = Non
         codes = torch.empty(kv.shape, dtype=torch.int8, device=kv.device)
     if scales is None:
         scales = torch.empty((B, H, S), dtype=torch.float32, device=kv.device)
-    _require(codes, "codes", (torch.int8,), 4)
-    _require(scales, "scales", (torch.float32,), 3)
-    if tuple(codes.shape) != tuple(kv.shape) or tuple(scales.shape) != (B, H, S):
-        raise ValueError("codes must match kv's shape and scales be [B, H, S]")
+    _check_out(codes, "codes", torch.int8, tuple(kv.shape), kv.device)
+    _check_out(scales, "scales", torch.float32, (B, H, S), kv.device)
     _lib.call("bitnet_kv_quantize", kv.data_ptr(), _x_dtype(kv), B * H * S, D, S, int(bits),
               codes.data_ptr(), scales.data_ptr(), _stream_ptr(kv))
     return codes, scales
@@ -355,12 +353,9 @@ def kv_quantize_packed(kv: torch.Tensor, bits: int, packed: Optional[torch.Tenso
         bos_codes = torch.empty((B, H, D), dtype=torch.int8, device=kv.device)
     if scales is None:
         scales = torch.empty((B, H, S), dtype=torch.float32, device=kv.device)
-    _require(packed, "packed", (torch.uint8,), 4)
-    _require(bos_codes, "bos_codes", (torch.int8,), 3)
-    _require(scales, "scales", (torch.float32,), 3)
-    if (tuple(packed.shape) != (B, H, S, row) or tuple(bos_codes.shape) != (B, H, D)
-            or tuple(scales.shape) != (B, H, S)):
-        raise ValueError("packed must be [B, H, S, D*bits/8], bos_codes [B, H, D], scales [B, H, S]")
+    _check_out(packed, "packed", torch.uint8, (B, H, S, row), kv.device)
+    _check_out(bos_codes, "bos_codes", torch.int8, (B, H, D), kv.device)
+    _check_out(scales, "scales", torch.float32, (B, H, S), kv.device)
     _lib.call("bitnet_kv_quantize_packed", kv.data_ptr(), _x_dtype(kv), B * H * S, D, S,
               int(bits), packed.data_ptr(), bos_codes.data_ptr(), scales.data_ptr(),
               _stream_ptr(kv))
