@@ -518,4 +518,15 @@ def test_binding_rejects_wrong_outputs():
     with pytest.raises(ValueError):
         bl.ternarize_weights(torch.zeros((32, 256), device=DEV),
                              out=torch.empty((32, 32), dtype=torch.uint8, device=DEV))
+    kv = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        bl.kv_quantize(kv, 4, codes=torch.empty((1, 2, 8, 32), dtype=torch.int8, device=DEV))
+    with pytest.raises(ValueError):
+        bl.kv_quantize(kv, 4, scales=torch.empty((1, 2, 8)))
+    with pytest.raises(ValueError):
+        bl.kv_quantize_packed(kv, 3, packed=torch.empty((1, 2, 8, 64), dtype=torch.uint8,
+                                                        device=DEV))
+    with pytest.raises(TypeError):
+        bl.kv_quantize_packed(kv, 4, bos_codes=torch.empty((1, 2, 64), dtype=torch.uint8,
+                                                           device=DEV))
 
